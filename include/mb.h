@@ -1,0 +1,173 @@
+/*
+ * mb.h -- C ABI of the fused Transformer epilogue kernels for AMD MI355X (gfx950).
+ *
+ * The operations are the memory-bound epilogues that Megatron-LM fuses, as
+ * described by the wmrh.cn article on Megatron-LM's megatron/core/fusions
+ * package (wmrh.cn/news/51426), cited here as [fusions §N] for its section N.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout:   tensors are row-major and contiguous. "tokens" (T) is the number
+ *           of rows, "hidden" (H) the number of columns. A bias has H entries
+ *           and is broadcast over the rows.
+ * Pointers: every pointer is a DEVICE pointer, owned by the caller. The
+ *           library allocates nothing, keeps no state between calls and never
+ *           synchronizes: work is enqueued on the caller's stream `s` and the
+ *           call returns at once. Calls are thread-safe.
+ * dtypes:   `dt` is the storage type of the inputs and outputs; arithmetic is
+ *           fp32 in registers and each output is rounded once, to nearest
+ *           even. Bias and weight gradients are always fp32.
+ * Shapes:   T >= 0; H > 0; H * sizeof(dt) must be a multiple of 16 bytes
+ *           (H % 8 == 0 for bf16/fp16, H % 4 == 0 for fp32), because every
+ *           lane moves whole 16-byte vectors.
+ * Alignment: tensor and bias pointers must be 16-byte aligned; fp32 gradient
+ *           outputs 4-byte aligned; workspaces 16-byte aligned.
+ * Aliasing: only the exact aliases listed per entry point are allowed; any
+ *           other overlap of two buffers is rejected.
+ * Errors:   arguments are validated on the host before any HIP call; a bad
+ *           argument returns an error code and enqueues nothing. After the
+ *           launches, a pending HIP error is returned as MB_ERR_HIP. Nothing
+ *           throws across the ABI.
+ * Empty:    T == 0 enqueues nothing, except that a requested bias gradient is
+ *           written as zeros.
+ */
+#ifndef MB_H
+#define MB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MB_F32 = 0, MB_F16 = 1, MB_BF16 = 2 } mb_dtype_t;
+
+typedef enum {
+  MB_OK = 0,
+  MB_ERR_NULL = 1,      /* a required pointer is NULL */
+  MB_ERR_SHAPE = 2,     /* T < 0, H <= 0, H*sizeof(dt) % 16 != 0, or size overflow */
+  MB_ERR_DTYPE = 3,     /* unknown or unsupported dtype combination */
+  MB_ERR_ALIGN = 4,     /* a pointer is not aligned as required */
+  MB_ERR_ALIAS = 5,     /* two buffers overlap in a way the entry point forbids */
+  MB_ERR_PROB = 6,      /* dropout probability is NaN or outside [0, 1] */
+  MB_ERR_WORKSPACE = 7, /* workspace missing or smaller than the query returned */
+  MB_ERR_HIP = 8        /* the HIP runtime reported an error for the launches */
+} mb_status_t;
+
+/* Human-readable name of a status code (static storage). */
+const char* mb_status_string(mb_status_t status);
+
+/* ABI version. 1: dropout keep word = Philox4x32-10 word (i mod 4) of block
+ * counter (i/4, offset), key seed, one 32-bit word per element. */
+int mb_abi_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Bias + GeLU, tanh approximation [fusions §4.2, §4.3]
+ *   z   = y + bias
+ *   out = 0.5 z (1 + tanh(0.79788456 z (1 + 0.044715 z^2)))
+ * y [T,H], bias [H] (NULL: no bias), out [T,H]; out may equal y (in place).
+ * ------------------------------------------------------------------------- */
+mb_status_t mb_bias_gelu_fwd(const void* y, const void* bias, void* out, int64_t tokens,
+                             int64_t hidden, mb_dtype_t dt, hipStream_t s);
+
+/* Bytes of workspace mb_bias_gelu_bwd needs (0 when no bias gradient is asked for
+ * is also accepted: pass with_dbias = 0). */
+size_t mb_bias_gelu_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias);
+
+/* Backward of bias + GeLU [fusions §4.2, §4.3]:
+ *   dgrad = g * gelu'(y + bias),
+ *   gelu'(z) = 0.5 (1 + t) + 0.5 z (1 - t^2)(0.79788456 + 0.1070322243 z^2),
+ *   t = tanh(0.79788456 z (1 + 0.044715 z^2));
+ *   dbias[j] = sum over rows of the fp32 dgrad[:, j] (before rounding).
+ * g, y, dgrad [T,H]; bias [H] (NULL: none); dbias [H] fp32 (NULL: not computed).
+ * dgrad may equal g or y. The reduction is deterministic and atomic-free: a
+ * second launch sums per-row-group partials kept in the workspace `ws`
+ * (ws_bytes >= mb_bias_gelu_bwd_workspace(...); unused when dbias is NULL). */
+mb_status_t mb_bias_gelu_bwd(const void* g, const void* y, const void* bias, void* dgrad,
+                             float* dbias, void* ws, size_t ws_bytes, int64_t tokens,
+                             int64_t hidden, mb_dtype_t dt, hipStream_t s);
+
+/* ---------------------------------------------------------------------------
+ * Bias + dropout + residual add [fusions §3.2, §3.3]
+ *   r'  = residual rounded to dt when residual_dt != dt (the mixed-precision
+ *         cast of the residual to x's dtype), else residual;
+ *   z   = x + bias;
+ *   train: out = r' + (keep ? z * s : 0),  s = (float)(1 / (1 - p));
+ *   infer: out = r' + z  (dropout is the identity at inference).
+ * x, out [T,H] dtype dt; bias [H] dtype dt (NULL: none); residual [T,H] of
+ * dtype residual_dt, which is dt or MB_F32. out may equal x, or residual when
+ * residual_dt == dt (in place).
+ * keep: element i = t*H + j is kept iff word >= floor(p * 2^32), where word is
+ * 32-bit word (i mod 4) of Philox4x32-10 (Salmon et al., SC'11) applied to the
+ * counter (lo32(i/4), hi32(i/4), lo32(offset), hi32(offset)) with the key
+ * (lo32(seed), hi32(seed)). The mask is therefore a pure function of
+ * (seed, offset, element index): it is reproducible and independent of the
+ * launch shape. p in [0, 1]; p = 0 keeps all, p = 1 drops all.
+ * ------------------------------------------------------------------------- */
+mb_status_t mb_bias_dropout_add_train(const void* x, const void* bias, const void* residual,
+                                      mb_dtype_t residual_dt, void* out, int64_t tokens,
+                                      int64_t hidden, mb_dtype_t dt, float p, uint64_t seed,
+                                      uint64_t offset, hipStream_t s);
+
+mb_status_t mb_bias_dropout_add_infer(const void* x, const void* bias, const void* residual,
+                                      mb_dtype_t residual_dt, void* out, int64_t tokens,
+                                      int64_t hidden, mb_dtype_t dt, hipStream_t s);
+
+/* The keep decisions mb_bias_dropout_add_train makes for (T, H, p, seed,
+ * offset), as bits: bit (i mod 8) of byte i/8 is element i = t*H + j
+ * (1 = kept). bits holds ceil(T*H/8) bytes; unused high bits of the last byte
+ * are 0. Needs H % 4 == 0. Lets a backward pass or a test regenerate the mask. */
+mb_status_t mb_dropout_mask(uint8_t* bits, int64_t tokens, int64_t hidden, float p, uint64_t seed,
+                            uint64_t offset, hipStream_t s);
+
+/* ---------------------------------------------------------------------------
+ * Bias + gated linear units [fusions §2, §9]
+ * The input row has 2H columns: a = in[t, 0:H] + bias[0:H] goes through the
+ * activation, b = in[t, H:2H] + bias[H:2H] is the linear half.
+ *   SwiGLU: out = silu(a) * b (* w[t] when weights are given),
+ *           silu(a) = a / (1 + exp(-a));
+ *   GEGLU:  out = gelu_tanh(a) * b.
+ * `hidden` is H, the output width. in [T,2H], bias [2H] (NULL: none),
+ * weights [T] of dtype weights_dt (dt or MB_F32; NULL: unweighted), out [T,H].
+ * out must not overlap in.
+ * ------------------------------------------------------------------------- */
+mb_status_t mb_bias_swiglu_fwd(const void* in, const void* bias, const void* weights,
+                               mb_dtype_t weights_dt, void* out, int64_t tokens, int64_t hidden,
+                               mb_dtype_t dt, hipStream_t s);
+
+mb_status_t mb_bias_geglu_fwd(const void* in, const void* bias, void* out, int64_t tokens,
+                              int64_t hidden, mb_dtype_t dt, hipStream_t s);
+
+/* Workspace bytes for the gated backward passes. */
+size_t mb_bias_glu_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias,
+                                 int with_dweights);
+
+/* Backward of bias + SwiGLU (weighted when weights != NULL):
+ *   da = g * w * b * silu'(a),  silu'(a) = sigmoid(a) (1 + a (1 - sigmoid(a)))
+ *   db = g * w * silu(a)
+ *   din[t, 0:H] = da, din[t, H:2H] = db          (dtype dt)
+ *   dbias[c]    = sum over rows of fp32 din[:, c] (fp32 [2H], NULL: skip)
+ *   dweights[t] = sum over j of g * silu(a) * b   (fp32 [T], NULL: skip;
+ *                                                  needs weights)
+ * g [T,H], in and din [T,2H]; din may equal in (in place); g must not
+ * overlap din. The reductions are deterministic and atomic-free (second
+ * launch over partials in ws). */
+mb_status_t mb_bias_swiglu_bwd(const void* g, const void* in, const void* bias, const void* weights,
+                               mb_dtype_t weights_dt, void* din, float* dbias, float* dweights,
+                               void* ws, size_t ws_bytes, int64_t tokens, int64_t hidden,
+                               mb_dtype_t dt, hipStream_t s);
+
+/* Backward of bias + GEGLU: da = g * b * gelu_tanh'(a), db = g * gelu_tanh(a),
+ * with gelu_tanh' as in mb_bias_gelu_bwd; din, dbias as for SwiGLU. */
+mb_status_t mb_bias_geglu_bwd(const void* g, const void* in, const void* bias, void* din,
+                              float* dbias, void* ws, size_t ws_bytes, int64_t tokens,
+                              int64_t hidden, mb_dtype_t dt, hipStream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MB_H */

@@ -1,0 +1,327 @@
+"""GPU parity of every entry point against the oracle, at sizes the oracle
+finishes in about a second that still span several column strips, several
+row groups and ragged tails in both directions, plus the edge cases.
+
+All calls go through the C ABI (the ctypes binding passes device pointers).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_elementwise_epilogues_amd as mb
+from transformer_elementwise_epilogues_amd import synthetic
+from tolerances import assert_close, assert_reduction_close, to_storage, values
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TD = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def gen(seed, shape, dt, sigma=1.0, dist="normal"):
+    return synthetic.draw(seed, shape, dist, sigma, dt)
+
+
+def st(t):
+    return to_storage(t)
+
+
+def log(name, stats):
+    print(f"[parity] {name}: {stats}", flush=True)
+
+
+# Shapes: (tokens, hidden) with hidden a multiple of the 16-byte vector. 1576
+# bf16 = 197 vectors = 3 full strips + 5 lanes; 1028 fp32 = 257 vectors.
+SHAPES = {"f32": [(777, 1028), (4, 8), (1, 4), (513, 64)],
+          "bf16": [(1000, 1576), (4, 8), (3, 8), (1, 8), (257, 512)],
+          "f16": [(999, 1576), (4, 8)]}
+CASES = [(dt, s) for dt, ss in SHAPES.items() for s in ss]
+
+
+# ------------------------------------------------------------------ GeLU
+
+@pytest.mark.parametrize("dt,shape", CASES)
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_gelu_fwd(dt, shape, with_bias):
+    T, H = shape
+    y = gen(11, shape, dt, sigma=3.0)
+    b = gen(12, (H,), dt, sigma=0.5) if with_bias else None
+    out = mb.mb_bias_gelu_fwd(y.to(DEV), None if b is None else b.to(DEV))
+    o, o64 = oracle.bias_gelu_fwd(dt, st(y), None if b is None else st(b))
+    log(f"gelu_fwd {dt} {shape}", assert_close(st(out), o, o64, None, dt, "gelu fwd"))
+
+
+@pytest.mark.parametrize("dt,shape", CASES)
+def test_gelu_bwd(dt, shape):
+    T, H = shape
+    y = gen(21, shape, dt, sigma=3.0)
+    g = gen(22, shape, dt)
+    b = gen(23, (H,), dt, sigma=0.5)
+    dgrad, dbias = mb.mb_bias_gelu_bwd(g.to(DEV), y.to(DEV), b.to(DEV))
+    d, d64, mag, db64 = oracle.bias_gelu_bwd(dt, st(g), st(y), st(b))
+    log(f"gelu_bwd {dt} {shape}", assert_close(st(dgrad), d, d64, mag, dt, "gelu bwd dgrad"))
+    log(f"gelu_dbias {dt} {shape}", assert_reduction_close(dbias.cpu().numpy(), db64, "gelu dbias"))
+
+
+def test_gelu_bwd_dbias_optional_and_deterministic():
+    y = gen(31, (640, 2048), "bf16").to(DEV)
+    g = gen(32, (640, 2048), "bf16").to(DEV)
+    b = gen(33, (2048,), "bf16", 0.02).to(DEV)
+    d1, db1 = mb.mb_bias_gelu_bwd(g, y, b)
+    d2, db2 = mb.mb_bias_gelu_bwd(g, y, b)
+    d3, none = mb.mb_bias_gelu_bwd(g, y, b, dbias=False)
+    assert none is None
+    assert torch.equal(d1.view(torch.int16), d2.view(torch.int16))
+    assert torch.equal(d1.view(torch.int16), d3.view(torch.int16))
+    assert torch.equal(db1.view(torch.int32), db2.view(torch.int32))
+
+
+def test_gelu_in_place():
+    y = gen(41, (300, 1024), "bf16").to(DEV)
+    b = gen(42, (1024,), "bf16", 0.02).to(DEV)
+    ref = mb.mb_bias_gelu_fwd(y, b)
+    y2 = y.clone()
+    mb.mb_bias_gelu_fwd(y2, b, out=y2)
+    assert torch.equal(ref.view(torch.int16), y2.view(torch.int16))
+    g = gen(43, (300, 1024), "bf16").to(DEV)
+    d_ref, db_ref = mb.mb_bias_gelu_bwd(g, y, b)
+    g2 = g.clone()
+    d_in, db_in = mb.mb_bias_gelu_bwd(g2, y, b, dgrad=g2)
+    assert d_in.data_ptr() == g2.data_ptr()
+    assert torch.equal(d_ref.view(torch.int16), g2.view(torch.int16))
+    assert torch.equal(db_ref.view(torch.int32), db_in.view(torch.int32))
+
+
+def test_gelu_extreme_values():
+    vals = np.array([0.0, -0.0, 1e-30, -1e-30, 1e-8, -0.7525, -6.0, -8.0, -9.5, -10.0, -10.3, -10.7, -11.0,
+                     -12.0, -20.0, 6.0, 12.0, 1e4, -1e4, 2e4, -2e4, 1e20, -1e20, 3e38, -3e38, np.nan], np.float32)
+    H = 32
+    y32 = np.resize(vals, (4, H)).astype(np.float32)
+    g32 = np.linspace(-2, 2, 4 * H, dtype=np.float32).reshape(4, H)
+    for dt in ("f32", "bf16", "f16"):
+        y = torch.from_numpy(y32).to(TD[dt])
+        g = torch.from_numpy(g32).to(TD[dt])
+        out = mb.mb_bias_gelu_fwd(y.to(DEV))
+        o, o64 = oracle.bias_gelu_fwd(dt, st(y), None)
+        assert_close(st(out), o, o64, None, dt, f"gelu fwd extremes {dt}")
+        dg, _ = mb.mb_bias_gelu_bwd(g.to(DEV), y.to(DEV), dbias=False)
+        d, d64, mag, _ = oracle.bias_gelu_bwd(dt, st(g), st(y), None)
+        assert_close(st(dg), d, d64, mag, dt, f"gelu bwd extremes {dt}")
+
+
+def test_gelu_empty_tokens():
+    y = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    assert mb.mb_bias_gelu_fwd(y).shape == (0, 64)
+    dg, db = mb.mb_bias_gelu_bwd(y, y, torch.zeros(64, dtype=torch.bfloat16, device=DEV))
+    assert torch.count_nonzero(db).item() == 0 and db.shape == (64,)
+
+
+# ------------------------------------------------------------------ dropout-add
+
+BDA_TYPES = [("bf16", "f32"), ("bf16", "bf16"), ("f32", "f32"), ("f16", "f16"), ("f16", "f32")]
+
+
+@pytest.mark.parametrize("dt,rdt", BDA_TYPES)
+@pytest.mark.parametrize("p,offset", [(0.1, 0), (0.5, 7), (0.0, 0), (1.0, 0), (0.1, 2**33 + 5)])
+def test_bda_train(dt, rdt, p, offset):
+    T, H = (1000, 1576) if dt != "f32" else (777, 1028)
+    x = gen(51, (T, H), dt)
+    r = gen(52, (T, H), rdt)
+    b = gen(53, (H,), dt, 0.02)
+    seed = 1234
+    out = mb.mb_bias_dropout_add_train(x.to(DEV), b.to(DEV), r.to(DEV), p, seed, offset)
+    o, o64, mag = oracle.bias_dropout_add(dt, st(x), st(b), st(r), rdt, True, p, seed, offset)
+    log(f"bda_train {dt}/{rdt} p={p}", assert_close(st(out), o, o64, mag, dt, "bda train"))
+    bits = mb.mb_dropout_mask(T, H, p, seed, offset)
+    assert np.array_equal(bits.cpu().numpy(), oracle.dropout_mask(T, H, p, seed, offset))
+
+
+@pytest.mark.parametrize("dt,rdt", BDA_TYPES)
+def test_bda_infer_and_in_place(dt, rdt):
+    T, H = (1000, 1576) if dt != "f32" else (777, 1028)
+    x = gen(61, (T, H), dt)
+    r = gen(62, (T, H), rdt)
+    b = gen(63, (H,), dt, 0.02)
+    xd = x.to(DEV)
+    out = mb.mb_bias_dropout_add_infer(xd, b.to(DEV), r.to(DEV))
+    o, o64, mag = oracle.bias_dropout_add(dt, st(x), st(b), st(r), rdt, False)
+    assert_close(st(out), o, o64, mag, dt, "bda infer")
+    res = mb.mb_bias_dropout_add_infer(xd, b.to(DEV), r.to(DEV), out=xd)
+    assert res.data_ptr() == xd.data_ptr()
+    assert torch.equal(xd.cpu().view(torch.int16 if dt != "f32" else torch.int32),
+                       out.cpu().view(torch.int16 if dt != "f32" else torch.int32))
+
+
+def test_bda_p0_equals_infer_bitwise_and_p1_is_residual():
+    T, H = 513, 2048
+    x = gen(71, (T, H), "bf16").to(DEV)
+    r = gen(72, (T, H), "f32").to(DEV)
+    b = gen(73, (H,), "bf16", 0.02).to(DEV)
+    a = mb.mb_bias_dropout_add_train(x, b, r, 0.0, 99)
+    c = mb.mb_bias_dropout_add_infer(x, b, r)
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+    one = mb.mb_bias_dropout_add_train(x, b, r, 1.0, 99)
+    cast = r.to(torch.bfloat16)
+    assert torch.equal(one.float(), cast.float())  # r' + 0 (-0 becomes +0, equal as values)
+
+
+def test_bda_train_in_place_and_deterministic():
+    T, H = 700, 4096
+    x = gen(81, (T, H), "bf16").to(DEV)
+    r = gen(82, (T, H), "bf16").to(DEV)
+    b = gen(83, (H,), "bf16", 0.02).to(DEV)
+    a = mb.mb_bias_dropout_add_train(x, b, r, 0.1, 5, 3)
+    a2 = mb.mb_bias_dropout_add_train(x, b, r, 0.1, 5, 3)
+    assert torch.equal(a.view(torch.int16), a2.view(torch.int16))
+    r2 = r.clone()
+    mb.mb_bias_dropout_add_train(x, b, r2, 0.1, 5, 3, out=r2)  # in place on the residual
+    assert torch.equal(a.view(torch.int16), r2.view(torch.int16))
+
+
+@pytest.mark.parametrize("T,H", [(1, 4), (3, 4), (5, 12), (37, 100), (1000, 1576)])
+@pytest.mark.parametrize("p", [0.1, 0.5, 1 - 2.0**-24, 2.0**-32])
+def test_mask_export_bit_exact(T, H, p):
+    bits = mb.mb_dropout_mask(T, H, p, 2024, 11)
+    assert np.array_equal(bits.cpu().numpy(), oracle.dropout_mask(T, H, p, 2024, 11))
+
+
+def test_bda_dropped_nan_does_not_propagate():
+    T, H, p, seed = 16, 64, 0.5, 3
+    bits = np.unpackbits(oracle.dropout_mask(T, H, p, seed, 0), bitorder="little")[:T * H].reshape(T, H)
+    x = gen(91, (T, H), "bf16")
+    xn = x.clone()
+    xn[torch.from_numpy(bits == 0)] = float("nan")
+    r = gen(92, (T, H), "f32")
+    out = mb.mb_bias_dropout_add_train(xn.to(DEV), None, r.to(DEV), p, seed)
+    o, o64, mag = oracle.bias_dropout_add("bf16", st(xn), None, st(r), "f32", True, p, seed, 0)
+    assert_close(st(out), o, o64, mag, "bf16", "bda nan")
+    assert not torch.isnan(out).any()
+
+
+# ------------------------------------------------------------------ gated units
+
+GLU_CASES = [("swiglu", "bf16", None), ("swiglu", "bf16", "bf16"), ("swiglu", "bf16", "f32"),
+             ("swiglu", "f32", "f32"), ("swiglu", "f16", "f16"), ("geglu", "bf16", None),
+             ("geglu", "f32", None), ("geglu", "f16", None)]
+
+
+def _glu_inputs(dt, wdt, T, H, seed, sigma=1.0):
+    x = gen(seed, (T, 2 * H), dt, sigma)
+    b = gen(seed + 1, (2 * H,), dt, 0.02)
+    g = gen(seed + 2, (T, H), dt)
+    w = gen(seed + 3, (T,), wdt, dist="uniform") if wdt else None
+    return x, b, g, w
+
+
+@pytest.mark.parametrize("act,dt,wdt", GLU_CASES)
+@pytest.mark.parametrize("shape", [(600, 1576), (5, 8), (1, 16), (130, 512)])
+def test_glu_fwd(act, dt, wdt, shape):
+    T, H = shape
+    if dt == "f32" and H % 4:
+        pytest.skip("fp32 rows need H % 4 == 0")
+    x, b, _, w = _glu_inputs(dt, wdt, T, H, 101, 2.0 if act == "geglu" else 1.0)
+    if act == "swiglu":
+        out = mb.mb_bias_swiglu_fwd(x.to(DEV), b.to(DEV), None if w is None else w.to(DEV))
+    else:
+        out = mb.mb_bias_geglu_fwd(x.to(DEV), b.to(DEV))
+    o, o64 = oracle.bias_glu_fwd(act, dt, st(x), st(b), None if w is None else st(w), wdt)
+    log(f"{act}_fwd {dt} w={wdt} {shape}", assert_close(st(out), o, o64, None, dt, f"{act} fwd"))
+
+
+@pytest.mark.parametrize("act,dt,wdt", GLU_CASES)
+@pytest.mark.parametrize("shape", [(600, 1576), (5, 8), (130, 512)])
+def test_glu_bwd(act, dt, wdt, shape):
+    T, H = shape
+    x, b, g, w = _glu_inputs(dt, wdt, T, H, 201, 2.0 if act == "geglu" else 1.0)
+    if act == "swiglu":
+        din, dbias, dw = mb.mb_bias_swiglu_bwd(g.to(DEV), x.to(DEV), b.to(DEV), None if w is None else w.to(DEV))
+    else:
+        din, dbias = mb.mb_bias_geglu_bwd(g.to(DEV), x.to(DEV), b.to(DEV))
+        dw = None
+    d, d64, mag, db64, dw64 = oracle.bias_glu_bwd(act, dt, st(g), st(x), st(b), None if w is None else st(w), wdt)
+    log(f"{act}_bwd {dt} w={wdt} {shape}", assert_close(st(din), d, d64, mag, dt, f"{act} bwd din"))
+    log(f"{act}_dbias {dt}", assert_reduction_close(dbias.cpu().numpy(), db64, f"{act} dbias"))
+    if w is not None:
+        log(f"{act}_dweights {dt}", assert_reduction_close(dw.cpu().numpy(), dw64, f"{act} dweights"))
+
+
+def test_glu_bwd_in_place_optional_outputs_and_deterministic():
+    T, H = 333, 1024
+    x, b, g, w = _glu_inputs("bf16", "bf16", T, H, 301)
+    xd, bd, gd, wd = x.to(DEV), b.to(DEV), g.to(DEV), w.to(DEV)
+    din1, db1, dw1 = mb.mb_bias_swiglu_bwd(gd, xd, bd, wd)
+    din2, db2, dw2 = mb.mb_bias_swiglu_bwd(gd, xd, bd, wd)
+    assert torch.equal(din1.view(torch.int16), din2.view(torch.int16))
+    assert torch.equal(db1.view(torch.int32), db2.view(torch.int32))
+    assert torch.equal(dw1.view(torch.int32), dw2.view(torch.int32))
+    din3, none_b, none_w = mb.mb_bias_swiglu_bwd(gd, xd, bd, wd, dbias=False, dweights=False)
+    assert none_b is None and none_w is None
+    assert torch.equal(din1.view(torch.int16), din3.view(torch.int16))
+    x2 = xd.clone()
+    din4, db4, dw4 = mb.mb_bias_swiglu_bwd(gd, x2, bd, wd, din=x2)
+    assert din4.data_ptr() == x2.data_ptr()
+    assert torch.equal(din1.view(torch.int16), x2.view(torch.int16))
+    assert torch.equal(db1.view(torch.int32), db4.view(torch.int32))
+
+
+def test_weighted_with_unit_weights_equals_unweighted():
+    T, H = 257, 1536
+    x, b, g, _ = _glu_inputs("bf16", None, T, H, 401)
+    ones = torch.ones(T, dtype=torch.bfloat16, device=DEV)
+    xd, bd, gd = x.to(DEV), b.to(DEV), g.to(DEV)
+    a = mb.mb_bias_swiglu_fwd(xd, bd)
+    c = mb.mb_bias_swiglu_fwd(xd, bd, ones)
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+    d1, db1, _ = mb.mb_bias_swiglu_bwd(gd, xd, bd)
+    d2, db2, dw2 = mb.mb_bias_swiglu_bwd(gd, xd, bd, ones)
+    assert torch.equal(d1.view(torch.int16), d2.view(torch.int16))
+    assert torch.equal(db1.view(torch.int32), db2.view(torch.int32))
+
+
+def test_glu_tail_inputs():
+    # gate values deep in the negative tail, where gelu and its derivative are
+    # tiny and the fp32 evaluation must stay out of the subnormal range
+    T, H = 64, 256
+    a = torch.linspace(-14, 4, T * H).reshape(T, H)
+    up = gen(501, (T, H), "f32", 3.0)
+    x = torch.cat([a, up], dim=1).to(torch.bfloat16)
+    g = gen(502, (T, H), "bf16")
+    for act in ("geglu", "swiglu"):
+        if act == "geglu":
+            out = mb.mb_bias_geglu_fwd(x.to(DEV))
+            din, _ = mb.mb_bias_geglu_bwd(g.to(DEV), x.to(DEV), dbias=False)
+        else:
+            out = mb.mb_bias_swiglu_fwd(x.to(DEV))
+            din, _, _ = mb.mb_bias_swiglu_bwd(g.to(DEV), x.to(DEV), dbias=False, dweights=False)
+        o, o64 = oracle.bias_glu_fwd(act, "bf16", st(x), None)
+        assert_close(st(out), o, o64, None, "bf16", f"{act} tail fwd")
+        d, d64, mag, _, _ = oracle.bias_glu_bwd(act, "bf16", st(g), st(x), None)
+        assert_close(st(din), d, d64, mag, "bf16", f"{act} tail bwd")
+
+
+def test_glu_empty_tokens():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    g = torch.empty((0, 32), dtype=torch.bfloat16, device=DEV)
+    w = torch.empty((0,), dtype=torch.bfloat16, device=DEV)
+    assert mb.mb_bias_swiglu_fwd(x, None, w).shape == (0, 32)
+    din, db, dw = mb.mb_bias_swiglu_bwd(g, x, torch.zeros(64, dtype=torch.bfloat16, device=DEV), w)
+    assert db.shape == (64,) and torch.count_nonzero(db).item() == 0 and dw.shape == (0,)
+
+
+# ------------------------------------------------------------------ errors through the binding
+
+def test_errors_on_device_tensors():
+    y = torch.zeros((8, 24), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(mb.MBError, match="MB_ERR_SHAPE"):
+        mb.mb_bias_gelu_fwd(torch.zeros((8, 20), dtype=torch.bfloat16, device=DEV))
+    flat = torch.zeros(8 * 24 + 1, dtype=torch.bfloat16, device=DEV)
+    mis = flat[1:].view(8, 24)
+    with pytest.raises(mb.MBError, match="MB_ERR_ALIGN"):
+        mb.mb_bias_gelu_fwd(mis)
+    with pytest.raises(mb.MBError, match="MB_ERR_PROB"):
+        mb.mb_bias_dropout_add_train(y, None, y.clone(), 1.5, 1)
+    x = torch.zeros((8, 48), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(mb.MBError, match="MB_ERR_ALIAS"):
+        mb.mb_bias_swiglu_fwd(x, out=x.view(-1)[:192].view(8, 24))  # output overlaps the input
+    with pytest.raises(mb.MBError, match="MB_ERR_WORKSPACE"):
+        mb.mb_bias_gelu_bwd(y, y, None, ws=torch.zeros(4, dtype=torch.uint8, device=DEV))

@@ -1,0 +1,339 @@
+// mb_abi.cpp -- the C ABI declared in include/mb.h: argument validation (on
+// the host, before any HIP call), workspace sizing, and the launches.
+#include "mb.h"
+
+#include <cmath>
+#include <cstdint>
+#include <initializer_list>
+#include <limits>
+
+#include "mb_launch.hpp"
+
+namespace {
+
+size_t esize(mb_dtype_t dt) {
+  switch (dt) {
+    case MB_F32: return 4;
+    case MB_F16: return 2;
+    case MB_BF16: return 2;
+  }
+  return 0;
+}
+
+bool dt_ok(mb_dtype_t dt) { return esize(dt) != 0; }
+
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+struct Buf {
+  const void* p;
+  size_t bytes;
+};
+
+bool overlap(const Buf& a, const Buf& b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+bool identical(const Buf& a, const Buf& b) { return a.p == b.p && a.bytes == b.bytes; }
+
+// An allowed alias: output `out` may coincide exactly with input `in`.
+struct Alias {
+  int out;
+  int in;
+};
+
+// Outputs must not overlap each other; an output may overlap an input only as
+// an exact, listed alias.
+bool aliasing_ok(std::initializer_list<Buf> outs, std::initializer_list<Buf> ins, std::initializer_list<Alias> ok) {
+  const Buf* o = outs.begin();
+  const Buf* in = ins.begin();
+  const int no = static_cast<int>(outs.size()), ni = static_cast<int>(ins.size());
+  for (int a = 0; a < no; ++a) {
+    for (int b = a + 1; b < no; ++b)
+      if (overlap(o[a], o[b])) return false;
+    for (int b = 0; b < ni; ++b) {
+      if (!overlap(o[a], in[b])) continue;
+      bool allowed = false;
+      for (const Alias& al : ok)
+        if (al.out == a && al.in == b && identical(o[a], in[b])) allowed = true;
+      if (!allowed) return false;
+    }
+  }
+  return true;
+}
+
+// Shape rule shared by every op: T >= 0, H > 0, rows made of whole 16-byte
+// vectors, byte sizes (up to `width` columns of up to 4-byte elements) that
+// fit in int64, and vectors per row that fit in int.
+mb_status_t check_shape(int64_t T, int64_t H, mb_dtype_t dt, int width = 1) {
+  if (T < 0 || H <= 0) return MB_ERR_SHAPE;
+  const size_t es = esize(dt);
+  if ((static_cast<uint64_t>(H) * es) % 16 != 0) return MB_ERR_SHAPE;
+  const int64_t maxi = std::numeric_limits<int64_t>::max();
+  if (H > maxi / (8 * width)) return MB_ERR_SHAPE;
+  if (T > 0 && T > maxi / (H * 8 * width)) return MB_ERR_SHAPE;
+  if (static_cast<uint64_t>(H) * es * width / 16 > static_cast<uint64_t>(std::numeric_limits<int>::max()))
+    return MB_ERR_SHAPE;
+  if (T > (int64_t{1} << 40)) return MB_ERR_SHAPE;  // row index bound of the kernels' 64-bit math
+  return MB_OK;
+}
+
+bool need(const void* p, size_t bytes) { return bytes == 0 || p != nullptr; }
+
+mb_status_t hip_status(hipError_t e) { return e == hipSuccess ? MB_OK : MB_ERR_HIP; }
+
+mb_status_t finish() { return hip_status(hipGetLastError()); }
+
+int nvec_of(int64_t H, mb_dtype_t dt) { return static_cast<int>(static_cast<uint64_t>(H) * esize(dt) / 16); }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool prob_ok(float p) { return !std::isnan(p) && p >= 0.0f && p <= 1.0f; }
+
+mb::DropoutArgs dropout_args(float p, uint64_t seed, uint64_t offset) {
+  mb::DropoutArgs d;
+  const double t = std::floor(static_cast<double>(p) * 4294967296.0);
+  d.theta = t >= 4294967296.0 ? (uint64_t{1} << 32) : (t <= 0.0 ? 0 : static_cast<uint64_t>(t));
+  d.scale = p < 1.0f ? static_cast<float>(1.0 / (1.0 - static_cast<double>(p))) : 0.0f;
+  d.k0 = static_cast<uint32_t>(seed);
+  d.k1 = static_cast<uint32_t>(seed >> 32);
+  d.o0 = static_cast<uint32_t>(offset);
+  d.o1 = static_cast<uint32_t>(offset >> 32);
+  return d;
+}
+
+// Partial-row workspace of a column reduction.
+size_t col_partials_bytes(const mb::Tiling& t, int64_t cols) { return static_cast<size_t>(t.G) * cols * 4; }
+
+// Second pass of a column reduction over `cols` fp32 columns.
+hipError_t reduce_columns(const float* partials, const mb::Tiling& t, int64_t cols, float* out, hipStream_t s) {
+  return mb::launch_colsum(partials, t.G, cols, out, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mb_status_string(mb_status_t status) {
+  switch (status) {
+    case MB_OK: return "MB_OK";
+    case MB_ERR_NULL: return "MB_ERR_NULL: a required pointer is NULL";
+    case MB_ERR_SHAPE: return "MB_ERR_SHAPE: bad tokens/hidden (rows must be whole 16-byte vectors)";
+    case MB_ERR_DTYPE: return "MB_ERR_DTYPE: unsupported dtype combination";
+    case MB_ERR_ALIGN: return "MB_ERR_ALIGN: pointer not aligned as required";
+    case MB_ERR_ALIAS: return "MB_ERR_ALIAS: buffers overlap in a way this entry point forbids";
+    case MB_ERR_PROB: return "MB_ERR_PROB: dropout probability is NaN or outside [0, 1]";
+    case MB_ERR_WORKSPACE: return "MB_ERR_WORKSPACE: workspace missing or too small";
+    case MB_ERR_HIP: return "MB_ERR_HIP: the HIP runtime reported an error";
+  }
+  return "unknown mb_status_t";
+}
+
+int mb_abi_version(void) { return 1; }
+
+// ------------------------------------------------------------------ GeLU
+
+mb_status_t mb_bias_gelu_fwd(const void* y, const void* bias, void* out, int64_t tokens, int64_t hidden,
+                             mb_dtype_t dt, hipStream_t s) {
+  if (!dt_ok(dt)) return MB_ERR_DTYPE;
+  if (mb_status_t st = check_shape(tokens, hidden, dt)) return st;
+  const size_t tb = static_cast<size_t>(tokens) * hidden * esize(dt), bb = hidden * esize(dt);
+  if (!need(y, tb) || !need(out, tb)) return MB_ERR_NULL;
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(bias, 16)) return MB_ERR_ALIGN;
+  if (!aliasing_ok({{out, tb}}, {{y, tb}, {bias, bias ? bb : 0}}, {{0, 0}})) return MB_ERR_ALIAS;
+  if (tokens == 0) return MB_OK;
+  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt));
+  if (hipError_t e = mb::launch_gelu_fwd(dt, y, bias, out, t, s)) return hip_status(e);
+  return finish();
+}
+
+size_t mb_bias_gelu_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias) {
+  if (!with_dbias || !dt_ok(dt) || check_shape(tokens, hidden, dt) != MB_OK || tokens == 0) return 0;
+  return col_partials_bytes(mb::plan_tiling(tokens, nvec_of(hidden, dt)), hidden);
+}
+
+mb_status_t mb_bias_gelu_bwd(const void* g, const void* y, const void* bias, void* dgrad, float* dbias, void* ws,
+                             size_t ws_bytes, int64_t tokens, int64_t hidden, mb_dtype_t dt, hipStream_t s) {
+  if (!dt_ok(dt)) return MB_ERR_DTYPE;
+  if (mb_status_t st = check_shape(tokens, hidden, dt)) return st;
+  const size_t tb = static_cast<size_t>(tokens) * hidden * esize(dt), bb = hidden * esize(dt);
+  if (!need(g, tb) || !need(y, tb) || !need(dgrad, tb)) return MB_ERR_NULL;
+  const size_t need_ws = mb_bias_gelu_bwd_workspace(tokens, hidden, dt, dbias != nullptr);
+  if (!aligned(g, 16) || !aligned(y, 16) || !aligned(dgrad, 16) || !aligned(bias, 16) || !aligned(dbias, 4) ||
+      (need_ws && !aligned(ws, 16)))
+    return MB_ERR_ALIGN;
+  if (need_ws && (!ws || ws_bytes < need_ws)) return MB_ERR_WORKSPACE;
+  const Buf wsb{need_ws ? ws : nullptr, need_ws};
+  if (!aliasing_ok({{dgrad, tb}, {dbias, dbias ? static_cast<size_t>(hidden) * 4 : 0}, wsb},
+                   {{g, tb}, {y, tb}, {bias, bias ? bb : 0}}, {{0, 0}, {0, 1}}))
+    return MB_ERR_ALIAS;
+  if (tokens == 0) {
+    if (!dbias) return MB_OK;
+    if (hipError_t e = mb::launch_fill_zero(dbias, hidden, s)) return hip_status(e);
+    return finish();
+  }
+  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt));
+  float* partials = dbias ? static_cast<float*>(ws) : nullptr;
+  if (hipError_t e = mb::launch_gelu_bwd(dt, g, y, bias, dgrad, partials, t, s)) return hip_status(e);
+  if (dbias)
+    if (hipError_t e = reduce_columns(partials, t, hidden, dbias, s)) return hip_status(e);
+  return finish();
+}
+
+// ------------------------------------------------------------------ dropout-add
+
+static mb_status_t bda_common(const void* x, const void* bias, const void* residual, mb_dtype_t residual_dt,
+                              void* out, int64_t tokens, int64_t hidden, mb_dtype_t dt, bool train, float p,
+                              uint64_t seed, uint64_t offset, hipStream_t s) {
+  if (!dt_ok(dt) || !dt_ok(residual_dt)) return MB_ERR_DTYPE;
+  if (residual_dt != dt && residual_dt != MB_F32) return MB_ERR_DTYPE;
+  if (mb_status_t st = check_shape(tokens, hidden, dt)) return st;
+  if (train && !prob_ok(p)) return MB_ERR_PROB;
+  const size_t tb = static_cast<size_t>(tokens) * hidden * esize(dt);
+  const size_t rb = static_cast<size_t>(tokens) * hidden * esize(residual_dt);
+  const size_t bb = hidden * esize(dt);
+  if (!need(x, tb) || !need(residual, rb) || !need(out, tb)) return MB_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(out, 16) || !aligned(bias, 16)) return MB_ERR_ALIGN;
+  if (!aliasing_ok({{out, tb}}, {{x, tb}, {residual, rb}, {bias, bias ? bb : 0}}, {{0, 0}, {0, 1}}))
+    return MB_ERR_ALIAS;
+  if (tokens == 0) return MB_OK;
+  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt));
+  const mb::DropoutArgs d = train ? dropout_args(p, seed, offset) : mb::DropoutArgs{};
+  if (hipError_t e = mb::launch_bda(dt, residual_dt, train, x, bias, residual, out, hidden, t, d, s))
+    return hip_status(e);
+  return finish();
+}
+
+mb_status_t mb_bias_dropout_add_train(const void* x, const void* bias, const void* residual, mb_dtype_t residual_dt,
+                                      void* out, int64_t tokens, int64_t hidden, mb_dtype_t dt, float p,
+                                      uint64_t seed, uint64_t offset, hipStream_t s) {
+  return bda_common(x, bias, residual, residual_dt, out, tokens, hidden, dt, true, p, seed, offset, s);
+}
+
+mb_status_t mb_bias_dropout_add_infer(const void* x, const void* bias, const void* residual, mb_dtype_t residual_dt,
+                                      void* out, int64_t tokens, int64_t hidden, mb_dtype_t dt, hipStream_t s) {
+  return bda_common(x, bias, residual, residual_dt, out, tokens, hidden, dt, false, 0.0f, 0, 0, s);
+}
+
+mb_status_t mb_dropout_mask(uint8_t* bits, int64_t tokens, int64_t hidden, float p, uint64_t seed, uint64_t offset,
+                            hipStream_t s) {
+  if (tokens < 0 || hidden <= 0 || hidden % 4 != 0) return MB_ERR_SHAPE;
+  if (tokens > 0 && tokens > std::numeric_limits<int64_t>::max() / hidden) return MB_ERR_SHAPE;
+  if (!prob_ok(p)) return MB_ERR_PROB;
+  const int64_t n = tokens * hidden;
+  const int64_t nbytes = (n + 7) / 8;
+  if ((nbytes + 255) / 256 > std::numeric_limits<int>::max()) return MB_ERR_SHAPE;
+  if (!need(bits, static_cast<size_t>(nbytes))) return MB_ERR_NULL;
+  if (n == 0) return MB_OK;
+  if (hipError_t e = mb::launch_dropout_mask(bits, n, dropout_args(p, seed, offset), s)) return hip_status(e);
+  return finish();
+}
+
+// ------------------------------------------------------------------ gated units
+
+static mb_status_t glu_fwd_common(int act, const void* in, const void* bias, const void* weights,
+                                  mb_dtype_t weights_dt, void* out, int64_t tokens, int64_t hidden, mb_dtype_t dt,
+                                  hipStream_t s) {
+  if (!dt_ok(dt)) return MB_ERR_DTYPE;
+  if (weights && weights_dt != dt && weights_dt != MB_F32) return MB_ERR_DTYPE;
+  if (mb_status_t st = check_shape(tokens, hidden, dt, 2)) return st;
+  const size_t ob = static_cast<size_t>(tokens) * hidden * esize(dt), ib = 2 * ob;
+  const size_t bb = 2 * hidden * esize(dt);
+  const size_t wb = weights ? static_cast<size_t>(tokens) * esize(weights_dt) : 0;
+  if (!need(in, ib) || !need(out, ob)) return MB_ERR_NULL;
+  if (!aligned(in, 16) || !aligned(out, 16) || !aligned(bias, 16) ||
+      (weights && !aligned(weights, esize(weights_dt))))
+    return MB_ERR_ALIGN;
+  if (!aliasing_ok({{out, ob}}, {{in, ib}, {bias, bias ? bb : 0}, {weights, wb}}, {})) return MB_ERR_ALIAS;
+  if (tokens == 0) return MB_OK;
+  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt));
+  if (hipError_t e = mb::launch_glu_fwd(act, dt, in, bias, weights, weights ? weights_dt : dt, out, hidden, t, s))
+    return hip_status(e);
+  return finish();
+}
+
+mb_status_t mb_bias_swiglu_fwd(const void* in, const void* bias, const void* weights, mb_dtype_t weights_dt,
+                               void* out, int64_t tokens, int64_t hidden, mb_dtype_t dt, hipStream_t s) {
+  return glu_fwd_common(mb::kSwiGLU, in, bias, weights, weights_dt, out, tokens, hidden, dt, s);
+}
+
+mb_status_t mb_bias_geglu_fwd(const void* in, const void* bias, void* out, int64_t tokens, int64_t hidden,
+                              mb_dtype_t dt, hipStream_t s) {
+  return glu_fwd_common(mb::kGEGLU, in, bias, nullptr, dt, out, tokens, hidden, dt, s);
+}
+
+namespace {
+struct GluWs {
+  size_t bias_off, bias_bytes, w_off, w_bytes, total;
+};
+GluWs glu_ws(int64_t tokens, int64_t hidden, mb_dtype_t dt, bool with_dbias, bool with_dw) {
+  GluWs w{0, 0, 0, 0, 0};
+  if (tokens == 0) return w;
+  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt));
+  w.bias_bytes = with_dbias ? col_partials_bytes(t, 2 * hidden) : 0;
+  w.w_off = round_up(w.bias_bytes, 256);
+  w.w_bytes = with_dw ? static_cast<size_t>(t.strips) * tokens * 4 : 0;
+  w.total = w.w_bytes ? w.w_off + w.w_bytes : w.bias_bytes;
+  return w;
+}
+}  // namespace
+
+size_t mb_bias_glu_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias, int with_dweights) {
+  if (!dt_ok(dt) || check_shape(tokens, hidden, dt, 2) != MB_OK) return 0;
+  return glu_ws(tokens, hidden, dt, with_dbias != 0, with_dweights != 0).total;
+}
+
+static mb_status_t glu_bwd_common(int act, const void* g, const void* in, const void* bias, const void* weights,
+                                  mb_dtype_t weights_dt, void* din, float* dbias, float* dweights, void* ws,
+                                  size_t ws_bytes, int64_t tokens, int64_t hidden, mb_dtype_t dt, hipStream_t s) {
+  if (!dt_ok(dt)) return MB_ERR_DTYPE;
+  if (weights && weights_dt != dt && weights_dt != MB_F32) return MB_ERR_DTYPE;
+  if (mb_status_t st = check_shape(tokens, hidden, dt, 2)) return st;
+  const size_t gb = static_cast<size_t>(tokens) * hidden * esize(dt), ib = 2 * gb;
+  const size_t bb = 2 * hidden * esize(dt);
+  const size_t wb = weights ? static_cast<size_t>(tokens) * esize(weights_dt) : 0;
+  if (!need(g, gb) || !need(in, ib) || !need(din, ib)) return MB_ERR_NULL;
+  if (dweights && !weights) return MB_ERR_NULL;
+  const GluWs w = glu_ws(tokens, hidden, dt, dbias != nullptr, dweights != nullptr);
+  if (!aligned(g, 16) || !aligned(in, 16) || !aligned(din, 16) || !aligned(bias, 16) || !aligned(dbias, 4) ||
+      !aligned(dweights, 4) || (weights && !aligned(weights, esize(weights_dt))) || (w.total && !aligned(ws, 16)))
+    return MB_ERR_ALIGN;
+  if (w.total && (!ws || ws_bytes < w.total)) return MB_ERR_WORKSPACE;
+  const Buf wsb{w.total ? ws : nullptr, w.total};
+  if (!aliasing_ok({{din, ib}, {dbias, dbias ? static_cast<size_t>(hidden) * 8 : 0},
+                    {dweights, dweights ? static_cast<size_t>(tokens) * 4 : 0}, wsb},
+                   {{g, gb}, {in, ib}, {bias, bias ? bb : 0}, {weights, wb}}, {{0, 1}}))
+    return MB_ERR_ALIAS;
+  if (tokens == 0) {
+    if (!dbias) return MB_OK;
+    if (hipError_t e = mb::launch_fill_zero(dbias, 2 * hidden, s)) return hip_status(e);
+    return finish();
+  }
+  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt));
+  float* bp = dbias ? static_cast<float*>(ws) : nullptr;
+  float* wp = dweights ? reinterpret_cast<float*>(static_cast<char*>(ws) + w.w_off) : nullptr;
+  if (hipError_t e = mb::launch_glu_bwd(act, dt, g, in, bias, weights, weights ? weights_dt : dt, din, bp, wp, hidden,
+                                        t, s))
+    return hip_status(e);
+  if (dbias)
+    if (hipError_t e = reduce_columns(bp, t, 2 * hidden, dbias, s)) return hip_status(e);
+  if (dweights)
+    if (hipError_t e = mb::launch_colsum(wp, t.strips, tokens, dweights, s)) return hip_status(e);
+  return finish();
+}
+
+mb_status_t mb_bias_swiglu_bwd(const void* g, const void* in, const void* bias, const void* weights,
+                               mb_dtype_t weights_dt, void* din, float* dbias, float* dweights, void* ws,
+                               size_t ws_bytes, int64_t tokens, int64_t hidden, mb_dtype_t dt, hipStream_t s) {
+  return glu_bwd_common(mb::kSwiGLU, g, in, bias, weights, weights_dt, din, dbias, dweights, ws, ws_bytes, tokens,
+                        hidden, dt, s);
+}
+
+mb_status_t mb_bias_geglu_bwd(const void* g, const void* in, const void* bias, void* din, float* dbias, void* ws,
+                              size_t ws_bytes, int64_t tokens, int64_t hidden, mb_dtype_t dt, hipStream_t s) {
+  return glu_bwd_common(mb::kGEGLU, g, in, bias, nullptr, dt, din, dbias, nullptr, ws, ws_bytes, tokens, hidden, dt,
+                        s);
+}
+
+}  // extern "C"

@@ -1,0 +1,283 @@
+// mb_device.hpp -- device-side building blocks shared by the epilogue kernels
+// (gfx950, wave64).
+//
+// 16-byte vector I/O with streaming (non-temporal) hints, fp32 <-> bf16/fp16
+// conversion (round to nearest even in hardware), Philox4x32-10, and the
+// logistic function in a cancellation- and overflow-free form that the GeLU
+// and SiLU paths use.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mb {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+enum class DT : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+// Elements per 16-byte vector.
+template <DT D> struct Vec;
+template <> struct Vec<DT::F32> { static constexpr int N = 4; static constexpr int BYTES = 4; };
+template <> struct Vec<DT::F16> { static constexpr int N = 8; static constexpr int BYTES = 2; };
+template <> struct Vec<DT::BF16> { static constexpr int N = 8; static constexpr int BYTES = 2; };
+
+// Geometry of every tiled kernel: a block is 4 waves; a wave covers one strip
+// of 64 consecutive 16-byte column vectors (1 KiB of a row) and walks rows.
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStrip = 64;
+
+// ---------------------------------------------------------------- vector I/O
+
+// Streaming tensors are read and written once: non-temporal hints keep them
+// from displacing reused lines (bias) in the caches.
+__device__ __forceinline__ u32x4 ld_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st_stream(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 ld_keep(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Bit casts always take a plain scalar or whole vector: clang lowers a
+// __builtin_bit_cast of an ext_vector element expression (v[k]) as a cast of
+// element 0, so vector elements are first copied into scalars.
+__device__ __forceinline__ float as_float(unsigned u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ unsigned as_uint(float f) { return __builtin_bit_cast(unsigned, f); }
+__device__ __forceinline__ unsigned pk_bf16(float a, float b) {
+  const f32x2 x = {a, b};
+  const bf16x2 h = __builtin_convertvector(x, bf16x2);  // v_cvt_pk_bf16_f32, nearest even
+  return __builtin_bit_cast(unsigned, h);
+}
+__device__ __forceinline__ unsigned pk_f16(float a, float b) {
+  const f32x2 x = {a, b};
+  const f16x2 h = __builtin_convertvector(x, f16x2);  // v_cvt_pk_f16_f32, nearest even
+  return __builtin_bit_cast(unsigned, h);
+}
+
+template <DT D> __device__ __forceinline__ void unpack(u32x4 v, float* f);
+
+template <> __device__ __forceinline__ void unpack<DT::F32>(u32x4 v, float* f) {
+  const unsigned w0 = v.x, w1 = v.y, w2 = v.z, w3 = v.w;
+  f[0] = as_float(w0);
+  f[1] = as_float(w1);
+  f[2] = as_float(w2);
+  f[3] = as_float(w3);
+}
+template <> __device__ __forceinline__ void unpack<DT::BF16>(u32x4 v, float* f) {
+  const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    f[2 * k] = as_float(w[k] << 16);
+    f[2 * k + 1] = as_float(w[k] & 0xffff0000u);
+  }
+}
+template <> __device__ __forceinline__ void unpack<DT::F16>(u32x4 v, float* f) {
+  const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const unsigned u = w[k];
+    const f16x2 h = __builtin_bit_cast(f16x2, u);
+    const f32x2 x = __builtin_convertvector(h, f32x2);
+    f[2 * k] = x.x;
+    f[2 * k + 1] = x.y;
+  }
+}
+
+template <DT D> __device__ __forceinline__ u32x4 pack(const float* f);
+
+template <> __device__ __forceinline__ u32x4 pack<DT::F32>(const float* f) {
+  return u32x4{as_uint(f[0]), as_uint(f[1]), as_uint(f[2]), as_uint(f[3])};
+}
+template <> __device__ __forceinline__ u32x4 pack<DT::BF16>(const float* f) {
+  return u32x4{pk_bf16(f[0], f[1]), pk_bf16(f[2], f[3]), pk_bf16(f[4], f[5]), pk_bf16(f[6], f[7])};
+}
+template <> __device__ __forceinline__ u32x4 pack<DT::F16>(const float* f) {
+  return u32x4{pk_f16(f[0], f[1]), pk_f16(f[2], f[3]), pk_f16(f[4], f[5]), pk_f16(f[6], f[7])};
+}
+
+// Four fp32 values to a 16-byte aligned address.
+__device__ __forceinline__ void store_f32x4(float* dst, const float* s) {
+  *reinterpret_cast<f32x4*>(dst) = f32x4{s[0], s[1], s[2], s[3]};
+}
+
+// Load the V = Vec<D>::N elements of a 16-byte aligned group as fp32, for a
+// tensor of storage type S that may be wider than D (an fp32 residual next to
+// bf16 activations occupies 32 bytes per group).
+template <DT S, int V> __device__ __forceinline__ void load_group(const char* p, float* f, bool stream) {
+  constexpr int per = Vec<S>::N;
+#pragma unroll
+  for (int q = 0; q < V / per; ++q) {
+    u32x4 v = stream ? ld_stream(p + 16 * q) : ld_keep(p + 16 * q);
+    unpack<S>(v, f + q * per);
+  }
+}
+
+// Value of fp32 x after rounding to storage type D (the residual cast).
+template <DT D> __device__ __forceinline__ float round_to(float x);
+template <> __device__ __forceinline__ float round_to<DT::F32>(float x) { return x; }
+template <> __device__ __forceinline__ float round_to<DT::BF16>(float x) {
+  return as_float(pk_bf16(x, 0.0f) << 16);
+}
+template <> __device__ __forceinline__ float round_to<DT::F16>(float x) {
+  return static_cast<float>(static_cast<_Float16>(x));
+}
+
+// ---------------------------------------------------------------- Philox
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 32x32->64-bit products and an xor with the round key; the key advances by
+// the Weyl increments after every round. On gfx950 each product is a single
+// v_mad_u64_u32; the key lives in scalar registers.
+__device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t m0 = static_cast<uint64_t>(0xD2511F53u) * c[0];
+    const uint64_t m1 = static_cast<uint64_t>(0xCD9E8D57u) * c[2];
+    const uint32_t n0 = static_cast<uint32_t>(m1 >> 32) ^ c[1] ^ k0;
+    const uint32_t n2 = static_cast<uint32_t>(m0 >> 32) ^ c[3] ^ k1;
+    c[1] = static_cast<uint32_t>(m1);
+    c[3] = static_cast<uint32_t>(m0);
+    c[0] = n0;
+    c[2] = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
+// Keep flags of the 4 consecutive elements 4q .. 4q+3: counter (q, offset),
+// key seed; element 4q+k keeps iff word k >= theta (theta <= 2^32).
+__device__ __forceinline__ void keep4(uint64_t q, uint32_t o0, uint32_t o1, uint32_t k0, uint32_t k1,
+                                      uint64_t theta, bool* keep) {
+  uint32_t c[4] = {static_cast<uint32_t>(q), static_cast<uint32_t>(q >> 32), o0, o1};
+  philox4x32_10(c, k0, k1);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) keep[k] = static_cast<uint64_t>(c[k]) >= theta;
+}
+
+// ---------------------------------------------------------------- activations
+
+// Logistic function sigma(t) for an argument given in base-2 units,
+// x = t * log2(e). With e = 2^-|x| and r = 1 / (1 + e):
+//   sigma(t)  = x >= 0 ? r     : e * r
+//   sigma(-t) = x >= 0 ? e * r : r
+// so neither 1 - sigma nor exp of a large positive number is ever formed.
+// `es` is e pre-scaled by 2^32 (valid down to |x| = 158), so that products
+// that end in the subnormal range keep their precision; callers multiply by
+// the deferred scale `sc` (1 or 2^-32) last.
+struct Logistic {
+  float r;   // 1 / (1 + e)
+  float e;   // 2^-|x|
+  float es;  // 2^(32 - |x|)
+  bool pos;  // x >= 0
+};
+
+__device__ __forceinline__ Logistic logistic_b2(float x) {
+  Logistic L;
+  L.es = __builtin_amdgcn_exp2f(32.0f - __builtin_fabsf(x));
+  L.e = L.es * 0x1p-32f;
+  L.r = __builtin_amdgcn_rcpf(1.0f + L.e);
+  L.pos = x >= 0.0f;
+  return L;
+}
+
+constexpr double kLog2e = 1.4426950408889634;
+// tanh-approximation constants as printed with the Megatron-LM fusions
+// (bias_gelu): sqrt(2/pi), the cubic coefficient, and sqrt(2/pi) * 3 * 0.044715.
+constexpr double kGeluK = 0.79788456;
+constexpr double kGeluC = 0.044715;
+constexpr double kGeluKD = 0.1070322243;
+// 0.5 (1 + tanh(u)) = sigma(2u): the logistic argument in base-2 units is
+// x = z * (A0 + A1 z^2) with A0 = 2 k log2(e), A1 = 2 k c log2(e).
+constexpr float kGeluA0 = static_cast<float>(2.0 * kGeluK * kLog2e);
+constexpr float kGeluA1 = static_cast<float>(2.0 * kGeluK * kGeluC * kLog2e);
+constexpr float kSiluA = static_cast<float>(kLog2e);
+constexpr float kScaleDown = 0x1p-32f;
+
+// gelu_tanh(z) = 0.5 z (1 + tanh u) = z * sigma(2u)
+//   value = (z * r * (pos ? 1 : es)) * sc
+struct GeluF {
+  float v;   // scaled value
+  float sc;  // deferred scale
+};
+__device__ __forceinline__ GeluF gelu_tanh_fwd(float z) {
+  const float x = z * __builtin_fmaf(z * z, kGeluA1, kGeluA0);
+  const Logistic L = logistic_b2(x);
+  const float zr = z * L.r;
+  GeluF o;
+  o.v = L.pos ? zr : zr * L.es;
+  o.sc = L.pos ? 1.0f : kScaleDown;
+  return o;
+}
+
+// gelu_tanh and its derivative. With s = sigma(2u), 1 - t^2 = 4 s (1 - s) and
+// s (1 - s) = e r^2, the derivative 0.5 (1+t) + 0.5 z (1-t^2)(k + k' z^2) is
+//   x >= 0:  r (1 + e q)        x < 0:  e r (1 + q)      with q = 2 z r (k + k' z^2).
+// Both branches carry the same deferred scale as the forward value. The
+// derivative is evaluated at z clamped to +-1e4 (where it is exactly 1 or 0 in
+// fp32) so that no 0 * inf arises; z - z restores NaN for NaN / inf inputs.
+struct GeluB {
+  float v;   // scaled gelu_tanh(z)
+  float d;   // scaled gelu_tanh'(z)
+  float sc;  // deferred scale of both
+};
+__device__ __forceinline__ GeluB gelu_tanh_fwd_bwd(float z) {
+  const float zc = __builtin_amdgcn_fmed3f(z, -1e4f, 1e4f);
+  const float z2 = zc * zc;
+  const float x = zc * __builtin_fmaf(z2, kGeluA1, kGeluA0);
+  const Logistic L = logistic_b2(x);
+  const float P = __builtin_fmaf(z2, static_cast<float>(kGeluKD), static_cast<float>(kGeluK));
+  const float zr = zc * L.r;
+  const float q = 2.0f * zr * P;
+  GeluB o;
+  const float A = L.pos ? L.r : L.es * L.r;
+  const float B = L.pos ? __builtin_fmaf(L.e, q, 1.0f) : 1.0f + q;
+  const float nanfix = z - z;  // +0 for finite z, NaN for NaN or inf
+  o.d = A * B + nanfix;
+  o.v = (L.pos ? zr : zr * L.es) + nanfix;
+  o.sc = L.pos ? 1.0f : kScaleDown;
+  // the clamped z only changes the value for |z| > 1e4, where gelu(z) is z,
+  // or z * 0 (-0, and NaN for -inf as the formula gives) with the scale 2^-32
+  if (__builtin_fabsf(z) > 1e4f) o.v = z > 0.0f ? z : z * 0.0f;
+  return o;
+}
+
+// silu(a) = a * sigma(a); silu'(a) = sigma(a) (1 + a sigma(-a)):
+//   a >= 0:  r (1 + a e r)      a < 0:  e r (1 + a r)      (deferred scale as above)
+struct SiluB {
+  float v;
+  float d;
+  float sc;
+};
+__device__ __forceinline__ SiluB silu_fwd_bwd(float a) {
+  const Logistic L = logistic_b2(a * kSiluA);
+  const float ar = a * L.r;
+  SiluB o;
+  o.v = L.pos ? ar : ar * L.es;
+  o.d = L.pos ? L.r * __builtin_fmaf(ar, L.e, 1.0f) : (L.es * L.r) * (1.0f + ar);
+  o.sc = L.pos ? 1.0f : kScaleDown;
+  return o;
+}
+
+__device__ __forceinline__ float silu_fwd(float a, float* sc) {
+  const Logistic L = logistic_b2(a * kSiluA);
+  const float ar = a * L.r;
+  *sc = L.pos ? 1.0f : kScaleDown;
+  return L.pos ? ar : ar * L.es;
+}
+
+// ---------------------------------------------------------------- reductions
+
+// Sum over the 64 lanes of a wave, in a fixed butterfly order (deterministic).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+}  // namespace mb

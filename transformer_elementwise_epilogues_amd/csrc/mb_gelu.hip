@@ -1,0 +1,188 @@
+// mb_gelu.hip -- bias + GeLU (tanh approximation), forward and backward with
+// the fused bias-gradient column reduction.
+//
+// Method: Megatron-LM's bias_gelu / bias_gelu_back as described by the
+// wmrh.cn article on megatron/core/fusions, section 4.2 (formulas and
+// constants) and section 4.3 (the bias gradient is the per-element gradient
+// summed over tokens). The kernels evaluate the same functions through the
+// logistic identities in mb_device.hpp.
+//
+// One pass per op: each lane owns one 16-byte column vector (8 bf16/fp16 or
+// 4 fp32 values), holds its bias slice in registers for every row it visits,
+// and streams rows with U loads in flight. The backward pass accumulates the
+// fp32 gradient per lane, combines the 4 waves of a block in LDS in a fixed
+// order and writes one partial row per row group; a second launch sums the
+// partial rows in order (no atomics, bit-reproducible).
+#include "mb_device.hpp"
+#include "mb_launch.hpp"
+
+namespace mb {
+
+namespace {
+
+constexpr int kUnrollFwd = 4;
+constexpr int kUnrollBwd = 4;
+
+template <DT D>
+__device__ __forceinline__ void load_bias(const char* bias, int cv, float* b) {
+  constexpr int V = Vec<D>::N;
+  if (bias) {
+    unpack<D>(ld_keep(bias + static_cast<size_t>(cv) * 16), b);
+  } else {
+#pragma unroll
+    for (int k = 0; k < V; ++k) b[k] = 0.0f;
+  }
+}
+
+template <DT D>
+__device__ __forceinline__ u32x4 gelu_vec(u32x4 yv, const float* b) {
+  constexpr int V = Vec<D>::N;
+  float f[V];
+  unpack<D>(yv, f);
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
+    const GeluF r = gelu_tanh_fwd(f[k] + b[k]);
+    f[k] = r.v * r.sc;
+  }
+  return pack<D>(f);
+}
+
+template <DT D, int U>
+__global__ __launch_bounds__(kThreads) void gelu_fwd_kernel(const char* y, const char* bias, char* out,
+                                                            int64_t T, int nvec) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int cv = blockIdx.x * kStrip + lane;
+  if (cv >= nvec) return;
+  float b[Vec<D>::N];
+  load_bias<D>(bias, cv, b);
+  const size_t pitch = static_cast<size_t>(nvec) * 16;
+  const int64_t S = static_cast<int64_t>(gridDim.y) * kWaves;
+  const char* yp = y + static_cast<size_t>(cv) * 16;
+  char* op = out + static_cast<size_t>(cv) * 16;
+  int64_t t = static_cast<int64_t>(blockIdx.y) * kWaves + wave;
+  for (; t + (U - 1) * S < T; t += U * S) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = ld_stream(yp + (t + u * S) * pitch);
+#pragma unroll
+    for (int u = 0; u < U; ++u) st_stream(op + (t + u * S) * pitch, gelu_vec<D>(v[u], b));
+  }
+  for (; t < T; t += S) st_stream(op + t * pitch, gelu_vec<D>(ld_stream(yp + t * pitch), b));
+}
+
+template <DT D>
+__device__ __forceinline__ u32x4 gelu_grad_vec(u32x4 gv, u32x4 yv, const float* b, float* acc) {
+  constexpr int V = Vec<D>::N;
+  float g[V], f[V];
+  unpack<D>(gv, g);
+  unpack<D>(yv, f);
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
+    const GeluB r = gelu_tanh_fwd_bwd(f[k] + b[k]);
+    const float d = (g[k] * r.d) * r.sc;
+    acc[k] += d;
+    f[k] = d;
+  }
+  return pack<D>(f);
+}
+
+template <DT D, int U, bool DBIAS>
+__global__ __launch_bounds__(kThreads) void gelu_bwd_kernel(const char* g, const char* y, const char* bias,
+                                                            char* dgrad, float* partials, int64_t T,
+                                                            int nvec) {
+  constexpr int V = Vec<D>::N;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int cv = blockIdx.x * kStrip + lane;
+  const bool active = cv < nvec;
+  float acc[V];
+#pragma unroll
+  for (int k = 0; k < V; ++k) acc[k] = 0.0f;
+  if (active) {
+    float b[V];
+    load_bias<D>(bias, cv, b);
+    const size_t pitch = static_cast<size_t>(nvec) * 16;
+    const int64_t S = static_cast<int64_t>(gridDim.y) * kWaves;
+    const size_t col = static_cast<size_t>(cv) * 16;
+    int64_t t = static_cast<int64_t>(blockIdx.y) * kWaves + wave;
+    for (; t + (U - 1) * S < T; t += U * S) {
+      u32x4 gv[U], yv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const size_t o = (t + u * S) * pitch + col;
+        gv[u] = ld_stream(g + o);
+        yv[u] = ld_stream(y + o);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) st_stream(dgrad + (t + u * S) * pitch + col, gelu_grad_vec<D>(gv[u], yv[u], b, acc));
+    }
+    for (; t < T; t += S) {
+      const size_t o = t * pitch + col;
+      st_stream(dgrad + o, gelu_grad_vec<D>(ld_stream(g + o), ld_stream(y + o), b, acc));
+    }
+  }
+  if constexpr (DBIAS) {
+    __shared__ float red[kWaves][V][64];
+#pragma unroll
+    for (int k = 0; k < V; ++k) red[wave][k][lane] = acc[k];
+    __syncthreads();
+    if (wave == 0 && active) {
+      float s[V];
+#pragma unroll
+      for (int k = 0; k < V; ++k) s[k] = ((red[0][k][lane] + red[1][k][lane]) + red[2][k][lane]) + red[3][k][lane];
+      float* dst = partials + static_cast<size_t>(blockIdx.y) * nvec * V + static_cast<size_t>(cv) * V;
+#pragma unroll
+      for (int q = 0; q < V / 4; ++q) store_f32x4(dst + 4 * q, s + 4 * q);
+    }
+  }
+}
+
+template <DT D>
+hipError_t gelu_fwd_dispatch(const void* y, const void* bias, void* out, const Tiling& t, hipStream_t s) {
+  dim3 grid(t.strips, t.G);
+  hipLaunchKernelGGL((gelu_fwd_kernel<D, kUnrollFwd>), grid, dim3(kThreads), 0, s,
+                     static_cast<const char*>(y), static_cast<const char*>(bias), static_cast<char*>(out), t.T,
+                     t.nvec);
+  return hipGetLastError();
+}
+
+template <DT D>
+hipError_t gelu_bwd_dispatch(const void* g, const void* y, const void* bias, void* dgrad, float* partials,
+                             const Tiling& t, hipStream_t s) {
+  dim3 grid(t.strips, t.G);
+  auto gp = static_cast<const char*>(g);
+  auto yp = static_cast<const char*>(y);
+  auto bp = static_cast<const char*>(bias);
+  auto dp = static_cast<char*>(dgrad);
+  if (partials)
+    hipLaunchKernelGGL((gelu_bwd_kernel<D, kUnrollBwd, true>), grid, dim3(kThreads), 0, s, gp, yp, bp, dp, partials,
+                       t.T, t.nvec);
+  else
+    hipLaunchKernelGGL((gelu_bwd_kernel<D, kUnrollBwd, false>), grid, dim3(kThreads), 0, s, gp, yp, bp, dp, partials,
+                       t.T, t.nvec);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gelu_fwd(int dt, const void* y, const void* bias, void* out, const Tiling& t, hipStream_t s) {
+  switch (static_cast<DT>(dt)) {
+    case DT::F32: return gelu_fwd_dispatch<DT::F32>(y, bias, out, t, s);
+    case DT::F16: return gelu_fwd_dispatch<DT::F16>(y, bias, out, t, s);
+    case DT::BF16: return gelu_fwd_dispatch<DT::BF16>(y, bias, out, t, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gelu_bwd(int dt, const void* g, const void* y, const void* bias, void* dgrad, float* partials,
+                           const Tiling& t, hipStream_t s) {
+  switch (static_cast<DT>(dt)) {
+    case DT::F32: return gelu_bwd_dispatch<DT::F32>(g, y, bias, dgrad, partials, t, s);
+    case DT::F16: return gelu_bwd_dispatch<DT::F16>(g, y, bias, dgrad, partials, t, s);
+    case DT::BF16: return gelu_bwd_dispatch<DT::BF16>(g, y, bias, dgrad, partials, t, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mb

@@ -1,0 +1,53 @@
+// mb_launch.hpp -- host-side launch interface between the C ABI (mb_abi.cpp)
+// and the kernels. Arguments reaching these functions are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mb {
+
+// Row tiling of a [T, nvec] array of 16-byte column vectors: grid.x covers
+// column strips of 64 vectors (one wave each), grid.y = G row groups; wave w
+// of row group y walks rows y*4 + w, y*4 + w + 4G, ...
+struct Tiling {
+  int64_t T = 0;     // rows
+  int nvec = 0;      // 16-byte vectors per (output) row
+  int strips = 0;    // ceil(nvec / 64)
+  int G = 0;         // row groups
+};
+
+// The tiling every kernel of one call uses; also sizes the workspaces.
+Tiling plan_tiling(int64_t T, int nvec);
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+// out[c] = sum over r < R of in[r * C + c], r ascending (fp32).
+hipError_t launch_colsum(const float* in, int R, int64_t C, float* out, hipStream_t s);
+
+hipError_t launch_gelu_fwd(int dt, const void* y, const void* bias, void* out, const Tiling& t,
+                           hipStream_t s);
+// partials: [G, H] fp32 or nullptr (no bias gradient)
+hipError_t launch_gelu_bwd(int dt, const void* g, const void* y, const void* bias, void* dgrad,
+                           float* partials, const Tiling& t, hipStream_t s);
+
+struct DropoutArgs {
+  uint64_t theta;  // keep iff word >= theta
+  float scale;     // survivor scale
+  uint32_t k0, k1; // key = seed
+  uint32_t o0, o1; // counter high words = offset
+};
+hipError_t launch_bda(int dt, int res_dt, bool train, const void* x, const void* bias,
+                      const void* residual, void* out, int64_t H, const Tiling& t,
+                      const DropoutArgs& d, hipStream_t s);
+hipError_t launch_dropout_mask(uint8_t* bits, int64_t n, const DropoutArgs& d, hipStream_t s);
+
+enum Act { kSwiGLU = 0, kGEGLU = 1 };
+hipError_t launch_glu_fwd(int act, int dt, const void* in, const void* bias, const void* w,
+                          int w_dt, void* out, int64_t H, const Tiling& t, hipStream_t s);
+// bias_partials: [G, 2H] or nullptr; w_partials: [strips, T] or nullptr
+hipError_t launch_glu_bwd(int act, int dt, const void* g, const void* in, const void* bias,
+                          const void* w, int w_dt, void* din, float* bias_partials,
+                          float* w_partials, int64_t H, const Tiling& t, hipStream_t s);
+
+}  // namespace mb
