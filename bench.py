@@ -1,0 +1,355 @@
+"""Benchmark of the fused Transformer epilogues on one MI355X.
+
+One step = one pass of every fused op at its full synthetic workload:
+  bias-dropout-add, bf16 x [8192, 4096] with fp32 residual, p = 0.1
+      (train, and inference in place on a copy of x)
+  bias-SwiGLU fwd + bwd, bf16 [8192, 28672] -> [8192, 14336], unweighted and
+      per-token weighted
+  bias-GEGLU fwd + bwd, bf16 [16384, 16384] ~ N(0, 2) -> [16384, 8192]
+  layer epilogue chain, bf16, 16384 tokens, hidden 8192, ffn 32768:
+      attention-out dropout-add -> bias-GeLU fwd -> bias-GeLU bwd (+ dbias)
+      -> MLP-out dropout-add
+Inputs are resident in HBM before timing starts. `value` is the algorithmic
+bytes of a step (each tensor read or written once, bias and gradients of the
+bias included, reduction partials excluded) divided by the step time.
+
+Prints one JSON line (see the keys below). `--gpus N` with N > 1 exits: this
+build runs on a single GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic_gelu_bwd_t16384_h32768.json")
+WORKLOAD = "all_epilogues_full_size: bda_bf16_8192x4096_res_f32 (train+infer) + swiglu_bf16_8192x14336 " \
+           "(plain+weighted, fwd+bwd) + geglu_bf16_16384x8192 (fwd+bwd) + layer_chain_bf16_t16384_h8192_f32768"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Op:
+    def __init__(self, name, fn, nbytes, kernels):
+        self.name, self.fn, self.nbytes, self.kernels = name, fn, nbytes, kernels
+        self.ms = []
+
+
+def build_ops(dev):
+    import torch
+
+    import transformer_elementwise_epilogues_amd as mb
+    from transformer_elementwise_epilogues_amd.synthetic import WORKLOADS
+
+    host = {}  # CPU copies for the oracle baseline
+    ops = []
+
+    def load(wname, tname):
+        t = WORKLOADS[wname].tensor(tname)
+        host[(wname, tname)] = t
+        return t.to(dev)
+
+    # -- bias-dropout-add, bf16 with fp32 residual
+    w = WORKLOADS["bda_bf16_8192x4096_res_f32"]
+    x, b, r = (load(w.name, k) for k in ("x", "bias", "residual"))
+    T, H = x.shape
+    out = torch.empty_like(x)
+    xi, ri = x.clone(), r.clone()  # the in-place inference pass gets its own buffers
+    p, seed, off = w.params["p"], w.params["seed"], w.params["offset"]
+    bda_bytes = T * H * (2 + 4 + 2) + H * 2
+    ops.append(Op("bda_train_bf16_res_f32_8192x4096",
+                  lambda: mb.mb_bias_dropout_add_train(x, b, r, p, seed, off, out=out), bda_bytes, ["bda"]))
+    ops.append(Op("bda_infer_inplace_bf16_res_f32_8192x4096",
+                  lambda: mb.mb_bias_dropout_add_infer(xi, b, ri, out=xi), bda_bytes, ["bda"]))
+
+    # -- SwiGLU, plain and weighted
+    w = WORKLOADS["swiglu_bf16_8192x14336"]
+    xin, b2, g3, wt = (load(w.name, k) for k in ("in", "bias", "g", "weights"))
+    T, H2 = xin.shape
+    H = H2 // 2
+    o3 = torch.empty((T, H), dtype=xin.dtype, device=dev)
+    din3 = torch.empty_like(xin)
+    db3 = torch.empty(2 * H, dtype=torch.float32, device=dev)
+    dw3 = torch.empty(T, dtype=torch.float32, device=dev)
+    ws3 = torch.empty(max(1, mb.mb_bias_glu_bwd_workspace(T, H, xin.dtype, True, True)), dtype=torch.uint8,
+                      device=dev)
+    fwd_b = T * H * 3 * 2 + 2 * H * 2
+    bwd_b = T * H * 5 * 2 + 2 * H * 2 + 2 * H * 4
+    ops.append(Op("swiglu_fwd_bf16_8192x14336", lambda: mb.mb_bias_swiglu_fwd(xin, b2, out=o3), fwd_b, ["glu_fwd"]))
+    ops.append(Op("swiglu_bwd_bf16_8192x14336",
+                  lambda: mb.mb_bias_swiglu_bwd(g3, xin, b2, din=din3, dbias=db3, dweights=False, ws=ws3),
+                  bwd_b, ["glu_bwd", "colsum"]))
+    ops.append(Op("weighted_swiglu_fwd_bf16_8192x14336", lambda: mb.mb_bias_swiglu_fwd(xin, b2, wt, out=o3),
+                  fwd_b + T * 2, ["glu_fwd"]))
+    ops.append(Op("weighted_swiglu_bwd_bf16_8192x14336",
+                  lambda: mb.mb_bias_swiglu_bwd(g3, xin, b2, wt, din=din3, dbias=db3, dweights=dw3, ws=ws3),
+                  bwd_b + T * 2 + T * 4, ["glu_bwd", "colsum", "colsum"]))
+
+    # -- GEGLU
+    w = WORKLOADS["geglu_bf16_16384x8192"]
+    xin4, b4, g4 = (load(w.name, k) for k in ("in", "bias", "g"))
+    T, H2 = xin4.shape
+    H = H2 // 2
+    o4 = torch.empty((T, H), dtype=xin4.dtype, device=dev)
+    din4 = torch.empty_like(xin4)
+    db4 = torch.empty(2 * H, dtype=torch.float32, device=dev)
+    ws4 = torch.empty(max(1, mb.mb_bias_glu_bwd_workspace(T, H, xin4.dtype, True, False)), dtype=torch.uint8,
+                      device=dev)
+    ops.append(Op("geglu_fwd_bf16_16384x8192", lambda: mb.mb_bias_geglu_fwd(xin4, b4, out=o4),
+                  T * H * 3 * 2 + 2 * H * 2, ["glu_fwd"]))
+    ops.append(Op("geglu_bwd_bf16_16384x8192",
+                  lambda: mb.mb_bias_geglu_bwd(g4, xin4, b4, din=din4, dbias=db4, ws=ws4),
+                  T * H * 5 * 2 + 2 * H * 2 + 2 * H * 4, ["glu_bwd", "colsum"]))
+
+    # -- layer epilogue chain
+    w = WORKLOADS["layer_chain_bf16_t16384_h8192_f32768"]
+    ax, ar, ab = (load(w.name, k) for k in ("attn_x", "attn_residual", "attn_bias"))
+    gy, gb, gg = (load(w.name, k) for k in ("gelu_y", "gelu_bias", "gelu_g"))
+    mx, mr, mbias = (load(w.name, k) for k in ("mlp_x", "mlp_residual", "mlp_bias"))
+    aout, mout = torch.empty_like(ax), torch.empty_like(mx)
+    gout, dgr = torch.empty_like(gy), torch.empty_like(gy)
+    T, H = gy.shape
+    dbg = torch.empty(H, dtype=torch.float32, device=dev)
+    wsg = torch.empty(max(1, mb.mb_bias_gelu_bwd_workspace(T, H, gy.dtype, True)), dtype=torch.uint8, device=dev)
+    Ta, Ha = ax.shape
+    p5, s_attn, s_mlp, off5 = w.params["p"], w.params["attn_seed"], w.params["mlp_seed"], w.params["offset"]
+    bda5 = Ta * Ha * 6 + Ha * 2
+    ops.append(Op("chain_attn_bda_train_bf16_16384x8192",
+                  lambda: mb.mb_bias_dropout_add_train(ax, ab, ar, p5, s_attn, off5, out=aout), bda5, ["bda"]))
+    ops.append(Op("chain_gelu_fwd_bf16_16384x32768", lambda: mb.mb_bias_gelu_fwd(gy, gb, out=gout),
+                  T * H * 4 + H * 2, ["gelu_fwd"]))
+    ops.append(Op("chain_gelu_bwd_bf16_16384x32768",
+                  lambda: mb.mb_bias_gelu_bwd(gg, gy, gb, dgrad=dgr, dbias=dbg, ws=wsg),
+                  T * H * 6 + H * 2 + H * 4, ["gelu_bwd", "colsum"]))
+    ops.append(Op("chain_mlp_bda_train_bf16_16384x8192",
+                  lambda: mb.mb_bias_dropout_add_train(mx, mbias, mr, p5, s_mlp, off5, out=mout), bda5, ["bda"]))
+    return ops, host
+
+
+def copy_ceiling(dev):
+    """A plain device copy of known size (torch's copy kernel), also the counter calibration."""
+    import torch
+
+    n = 1 << 28  # 1 GiB of fp32
+    a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    c = torch.empty_like(a)
+    c.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(5):
+        e0.record()
+        c.copy_(a)
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    ms = times[len(times) // 2]
+    del a, c
+    return {"bytes": 2 * n * 4, "ms": ms, "gbs": 2 * n * 4 / ms / 1e6}
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+TRAFFIC_SOURCES = ["transformer_elementwise_epilogues_amd/csrc/mb_gelu.hip",
+                   "transformer_elementwise_epilogues_amd/csrc/mb_device.hpp",
+                   "transformer_elementwise_epilogues_amd/csrc/mb_reduce.hip"]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant op from the committed rocprofv3 counter
+    summary, or None when it is missing or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash(TRAFFIC_SOURCES):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(host, seconds):
+    """The oracle (single-threaded C, fp64) on the first rows of every op's inputs,
+    as the same algorithmic bytes per second."""
+    import numpy as np
+
+    import oracle
+    from transformer_elementwise_epilogues_amd.synthetic import WORKLOADS
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from tolerances import to_storage as st
+
+    def rows(wname, tname, n):
+        return st(host[(wname, tname)][:n])
+
+    def vec(wname, tname):
+        return st(host[(wname, tname)])
+
+    plan = []
+    c2 = "bda_bf16_8192x4096_res_f32"
+    c3 = "swiglu_bf16_8192x14336"
+    c4 = "geglu_bf16_16384x8192"
+    c5 = "layer_chain_bf16_t16384_h8192_f32768"
+    plan.append(("bda_train_c2", lambda n: oracle.bias_dropout_add("bf16", rows(c2, "x", n), vec(c2, "bias"),
+                                                                     rows(c2, "residual", n), "f32", True, 0.1, 1234, 0),
+                 lambda n: n * 4096 * 8 + 4096 * 2))
+    plan.append(("bda_infer_c2", lambda n: oracle.bias_dropout_add("bf16", rows(c2, "x", n), vec(c2, "bias"),
+                                                                     rows(c2, "residual", n), "f32", False),
+                 lambda n: n * 4096 * 8 + 4096 * 2))
+    for name, wt in (("swiglu", None), ("weighted_swiglu", "weights")):
+        plan.append((f"{name}_fwd_c3", lambda n, wt=wt: oracle.bias_glu_fwd(
+            "swiglu", "bf16", rows(c3, "in", n), vec(c3, "bias"), None if wt is None else rows(c3, wt, n)),
+            lambda n: n * 14336 * 6 + 28672 * 2))
+        plan.append((f"{name}_bwd_c3", lambda n, wt=wt: oracle.bias_glu_bwd(
+            "swiglu", "bf16", rows(c3, "g", n), rows(c3, "in", n), vec(c3, "bias"),
+            None if wt is None else rows(c3, wt, n)), lambda n: n * 14336 * 10 + 28672 * 6))
+    plan.append(("geglu_fwd_c4", lambda n: oracle.bias_glu_fwd("geglu", "bf16", rows(c4, "in", n), vec(c4, "bias")),
+                 lambda n: n * 8192 * 6 + 16384 * 2))
+    plan.append(("geglu_bwd_c4", lambda n: oracle.bias_glu_bwd("geglu", "bf16", rows(c4, "g", n), rows(c4, "in", n),
+                                                                 vec(c4, "bias")), lambda n: n * 8192 * 10 + 16384 * 6))
+    plan.append(("chain_attn_bda_c5", lambda n: oracle.bias_dropout_add(
+        "bf16", rows(c5, "attn_x", n), vec(c5, "attn_bias"), rows(c5, "attn_residual", n), "bf16", True, 0.1, 5001, 0),
+        lambda n: n * 8192 * 6 + 8192 * 2))
+    plan.append(("chain_gelu_fwd_c5", lambda n: oracle.bias_gelu_fwd("bf16", rows(c5, "gelu_y", n),
+                                                                      vec(c5, "gelu_bias")),
+                 lambda n: n * 32768 * 4 + 32768 * 2))
+    plan.append(("chain_gelu_bwd_c5", lambda n: oracle.bias_gelu_bwd(
+        "bf16", rows(c5, "gelu_g", n), rows(c5, "gelu_y", n), vec(c5, "gelu_bias")),
+        lambda n: n * 32768 * 6 + 32768 * 6))
+    plan.append(("chain_mlp_bda_c5", lambda n: oracle.bias_dropout_add(
+        "bf16", rows(c5, "mlp_x", n), vec(c5, "mlp_bias"), rows(c5, "mlp_residual", n), "bf16", True, 0.1, 5002, 0),
+        lambda n: n * 8192 * 6 + 8192 * 2))
+    # calibrate: 2 rows of every op, then scale the row count to the time target
+    t0 = time.perf_counter()
+    for _, f, _ in plan:
+        f(2)
+    probe = time.perf_counter() - t0
+    n = max(2, int(2 * seconds / max(probe, 1e-6)))
+    n = min(n, 8192)
+    total_b, total_s, per = 0, 0.0, {}
+    for name, f, nb in plan:
+        t0 = time.perf_counter()
+        f(n)
+        dt = time.perf_counter() - t0
+        total_b += nb(n)
+        total_s += dt
+        per[name] = round(nb(n) / dt / 1e9, 4)
+    return {"value": round(total_b / total_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} rows of every op's inputs (same ops, shapes and seeds as the GPU step), "
+                      f"single-threaded fp64 C oracle, {total_s:.1f} s",
+            "per_op_gbs": per}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the fused epilogues are per-token and would shard by rows with a dbias all-reduce, "
+              "which is not built here.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    t_setup = time.perf_counter()
+    ops, host = build_ops(dev)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    ceiling = copy_ceiling(dev)
+    for _ in range(args.warmup):
+        for op in ops:
+            op.fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
+              for _ in range(args.steps)]
+    step0, step1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    step0.record(stream)
+    for s in range(args.steps):
+        for op, (e0, e1) in zip(ops, events[s]):
+            e0.record(stream)
+            op.fn()
+            e1.record(stream)
+    step1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = step0.elapsed_time(step1)
+    for s in range(args.steps):
+        for op, (e0, e1) in zip(ops, events[s]):
+            op.ms.append(e0.elapsed_time(e1))
+    ms_per_step = total_ms / args.steps
+    step_bytes = sum(op.nbytes for op in ops)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    per_op = {}
+    for op in ops:
+        avg = sum(op.ms) / len(op.ms)
+        gbs = op.nbytes / (avg * 1e-3) / 1e9
+        per_op[op.name] = {"us": round(avg * 1e3, 2), "bytes": op.nbytes, "gbs": round(gbs, 1),
+                           "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
+                           "frac_copy": round(gbs / ceiling["gbs"], 4), "kernels": op.kernels}
+    dom = max(ops, key=lambda o: sum(o.ms))
+    dom_avg = sum(dom.ms) / len(dom.ms)
+    achieved = dom.nbytes / (dom_avg * 1e-3) / 1e9
+    traffic = measured_traffic() if dom.name == "chain_gelu_bwd_bf16_16384x32768" else None
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "kernel": dom.name, "launches": dom.kernels, "algorithmic_bytes_per_launch": dom.nbytes,
+                "avg_us": round(dom_avg * 1e3, 2)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(host, args.cpu_seconds)
+    line = {
+        "metric": "achieved HBM GB/s and % of MI355X peak per fused op (fwd+bwd), 1 GPU",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded numpy normal/uniform, cast to bf16; resident in HBM before timing)",
+        "config": {"workload": WORKLOAD, "storage": "bf16 (fp32 residual in the 8192x4096 dropout-add)",
+                   "step_bytes": step_bytes, "frac_peak": round(value / PEAK_HBM_GBS, 4),
+                   "copy_ceiling_gbs": round(ceiling["gbs"], 1)},
+        "per_op": per_op,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 3),
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
