@@ -1,0 +1,217 @@
+"""GPU parity at the full benchmark workloads, in the launch configuration
+bench.py times (same shapes, so the same tiling), against the oracle:
+
+- outputs on sampled row blocks (first, a seeded middle block, last), each
+  evaluated by the oracle with its global row index (dropout needs it);
+- bias gradients on sampled columns: the columns are gathered over all rows
+  and the oracle evaluates that compact tensor (the gradient of a column
+  depends only on that column);
+- dropout masks compared bit for bit over the whole tensor;
+- properties over every element: the kept fraction is within 1 - p +- 3 sigma,
+  dropped elements equal the cast residual exactly, every column's bias
+  gradient equals the column sum of the rounded gradients within their
+  rounding noise, repeated calls are bit-identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_elementwise_epilogues_amd as mb
+from transformer_elementwise_epilogues_amd.synthetic import WORKLOADS
+from tolerances import assert_close, assert_reduction_close, to_storage as st
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(msg):
+    print(f"[fullsize] {msg}", flush=True)
+
+
+def load(wname, tname):
+    return WORKLOADS[wname].tensor(tname).to(DEV)
+
+
+def row_blocks(T, n=16, seed=0):
+    mid = int(np.random.default_rng(seed).integers(n, T - 2 * n))
+    return [(0, n), (mid, n), (T - n, n)]
+
+
+def sample_cols(H, k=48, seed=1):
+    c = np.random.default_rng(seed).choice(H, size=k, replace=False)
+    return np.unique(np.concatenate([c, [0, H - 1]]))
+
+
+def dbias_noise_bound(rounded: torch.Tensor) -> torch.Tensor:
+    """6 sigma of the per-column sum of the rounding errors of bf16 values
+    (uniform on +-ulp/2 each) plus the fp32 accumulation error."""
+    v = rounded.double()
+    _, e = torch.frexp(v)
+    ulp = torch.ldexp(torch.ones_like(v), (e - 8).to(torch.int32))
+    var = (ulp * ulp / 12).sum(0)
+    return 6 * var.sqrt() + 1e-6 * v.abs().sum(0) + 1e-30
+
+
+def check_rows_dt(kernel_out, oracle_fn, blocks, dt, what):
+    stats = []
+    for r0, n in blocks:
+        o, o64, mag = oracle_fn(r0, n)
+        stats.append(assert_close(st(kernel_out[r0:r0 + n]), o, o64, mag, dt, f"{what} rows {r0}+{n}"))
+    say(f"{what}: {stats}")
+
+
+# ------------------------------------------------------------------ GeLU fp32 [512, 4096], entire tensor
+
+def test_gelu_f32_512x4096_full():
+    w = WORKLOADS["gelu_f32_512x4096"]
+    y, b, g = (w.tensor(k) for k in ("y", "bias", "g"))
+    out = mb.mb_bias_gelu_fwd(y.to(DEV), b.to(DEV))
+    o, o64 = oracle.bias_gelu_fwd("f32", st(y), st(b))
+    say(f"gelu fwd f32 full: {assert_close(st(out), o, o64, None, 'f32', 'gelu fwd C1')}")
+    dg, db = mb.mb_bias_gelu_bwd(g.to(DEV), y.to(DEV), b.to(DEV))
+    d, d64, mag, db64 = oracle.bias_gelu_bwd("f32", st(g), st(y), st(b))
+    say(f"gelu bwd f32 full: {assert_close(st(dg), d, d64, mag, 'f32', 'gelu bwd C1')}")
+    say(f"gelu dbias f32 full: {assert_reduction_close(db.cpu().numpy(), db64, 'gelu dbias C1')}")
+
+
+# ------------------------------------------------------------------ dropout-add bf16 [8192, 4096], fp32 residual
+
+def _bda_full_checks(x, b, r, rdt, p, seed, off, out, what):
+    T, H = x.shape
+    bits = mb.mb_dropout_mask(T, H, p, seed, off)
+    want = oracle.dropout_mask(T, H, p, seed, off)
+    assert np.array_equal(bits.cpu().numpy(), want), f"{what}: mask differs from the oracle"
+    keep = torch.from_numpy(np.unpackbits(want, bitorder="little")[:T * H].reshape(T, H).astype(bool)).to(DEV)
+    frac = keep.double().mean().item()
+    sigma = (p * (1 - p) / (T * H)) ** 0.5
+    assert abs(frac - (1 - p)) <= 3 * sigma, (what, frac)
+    cast = r.to(x.dtype).float()
+    dropped_ok = torch.equal(out.float()[~keep], cast[~keep])  # r' + 0: equal as values
+    assert dropped_ok, f"{what}: a dropped element differs from the cast residual"
+    xs, rs = st(x.cpu()), st(r.cpu())
+    bs = st(b.cpu())
+    check_rows_dt(out, lambda r0, n: oracle.bias_dropout_add("bf16", xs[r0:r0 + n], bs, rs[r0:r0 + n], rdt, True,
+                                                             p, seed, off, row0=r0),
+                  row_blocks(T), "bf16", what)
+    say(f"{what}: kept fraction {frac:.6f} (1-p = {1 - p}, 3 sigma = {3 * sigma:.2e})")
+
+
+def test_bda_8192x4096_res_f32_train_and_infer():
+    w = WORKLOADS["bda_bf16_8192x4096_res_f32"]
+    x, b, r = (load(w.name, k) for k in ("x", "bias", "residual"))
+    p, seed, off = w.params["p"], w.params["seed"], w.params["offset"]
+    out = mb.mb_bias_dropout_add_train(x, b, r, p, seed, off)
+    _bda_full_checks(x, b, r, "f32", p, seed, off, out, "bda C2 train")
+    out2 = mb.mb_bias_dropout_add_train(x, b, r, p, seed, off)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    # inference in place on a copy of x (x kept pristine), p = 0 equals inference
+    xi = x.clone()
+    mb.mb_bias_dropout_add_infer(xi, b, r, out=xi)
+    xs, rs, bs = st(x.cpu()), st(r.cpu()), st(b.cpu())
+    check_rows_dt(xi, lambda r0, n: oracle.bias_dropout_add("bf16", xs[r0:r0 + n], bs, rs[r0:r0 + n], "f32", False),
+                  row_blocks(x.shape[0], seed=3), "bf16", "bda C2 infer in place")
+    p0 = mb.mb_bias_dropout_add_train(x, b, r, 0.0, seed, off)
+    assert torch.equal(p0.view(torch.int16), xi.view(torch.int16))
+
+
+# ------------------------------------------------------------------ gated units
+
+def _glu_full(act, wname, weighted):
+    w = WORKLOADS[wname]
+    xin, b, g = (load(w.name, k) for k in ("in", "bias", "g"))
+    wt = load(w.name, "weights") if weighted else None
+    T, H2 = xin.shape
+    H = H2 // 2
+    if act == "swiglu":
+        out = mb.mb_bias_swiglu_fwd(xin, b, wt)
+        din, dbias, dw = mb.mb_bias_swiglu_bwd(g, xin, b, wt)
+    else:
+        out = mb.mb_bias_geglu_fwd(xin, b)
+        din, dbias = mb.mb_bias_geglu_bwd(g, xin, b)
+        dw = None
+    name = f"{act}{'(weighted)' if weighted else ''} {tuple(xin.shape)}"
+    bs = st(b.cpu())
+    ws = st(wt.cpu()) if weighted else None
+    fwd_stats, bwd_stats = [], []
+    for r0, n in row_blocks(T):
+        xr, gr = st(xin[r0:r0 + n].cpu()), st(g[r0:r0 + n].cpu())
+        wr = ws[r0:r0 + n] if weighted else None
+        o, o64 = oracle.bias_glu_fwd(act, "bf16", xr, bs, wr)
+        fwd_stats.append(assert_close(st(out[r0:r0 + n]), o, o64, None, "bf16", f"{name} fwd rows {r0}"))
+        d, d64, mag, _, dw64 = oracle.bias_glu_bwd(act, "bf16", gr, xr, bs, wr)
+        bwd_stats.append(assert_close(st(din[r0:r0 + n]), d, d64, mag, "bf16", f"{name} bwd rows {r0}"))
+        if weighted:
+            assert_reduction_close(dw[r0:r0 + n].cpu().numpy(), dw64, f"{name} dweights rows {r0}")
+    say(f"{name} fwd: {fwd_stats}")
+    say(f"{name} bwd: {bwd_stats}")
+    # bias gradient: sampled columns of both halves, over all rows
+    cols = sample_cols(H)
+    ci = torch.from_numpy(np.concatenate([cols, cols + H])).to(DEV)
+    xc = st(xin.index_select(1, ci).cpu())
+    gc = st(g.index_select(1, torch.from_numpy(cols).to(DEV)).cpu())
+    bc = st(b.index_select(0, ci).cpu())
+    wc = ws if weighted else None
+    _, _, _, db64, _ = oracle.bias_glu_bwd(act, "bf16", gc, xc, bc, wc)
+    say(f"{name} dbias sampled columns: "
+        f"{assert_reduction_close(dbias.index_select(0, ci).cpu().numpy(), db64, f'{name} dbias')}")
+    # every column: dbias is the column sum of the rounded gradients within rounding noise
+    err = (dbias.double() - din.double().sum(0)).abs()
+    bound = dbias_noise_bound(din)
+    assert bool((err <= bound).all()), f"{name}: dbias vs column sums, worst {float((err / bound).max()):.2f}"
+    # determinism
+    if act == "swiglu":
+        din2, dbias2, dw2 = mb.mb_bias_swiglu_bwd(g, xin, b, wt)
+    else:
+        din2, dbias2 = mb.mb_bias_geglu_bwd(g, xin, b)
+    assert torch.equal(din.view(torch.int16), din2.view(torch.int16))
+    assert torch.equal(dbias.view(torch.int32), dbias2.view(torch.int32))
+
+
+def test_swiglu_8192x14336():
+    _glu_full("swiglu", "swiglu_bf16_8192x14336", False)
+
+
+def test_weighted_swiglu_8192x14336():
+    _glu_full("swiglu", "swiglu_bf16_8192x14336", True)
+
+
+def test_geglu_16384x8192():
+    _glu_full("geglu", "geglu_bf16_16384x8192", False)
+
+
+# ------------------------------------------------------------------ layer chain
+
+def test_layer_chain_t16384_h8192_f32768():
+    w = WORKLOADS["layer_chain_bf16_t16384_h8192_f32768"]
+    p, off = w.params["p"], w.params["offset"]
+    for pre, seed in (("attn", w.params["attn_seed"]), ("mlp", w.params["mlp_seed"])):
+        x, r, b = (load(w.name, f"{pre}_{k}") for k in ("x", "residual", "bias"))
+        out = mb.mb_bias_dropout_add_train(x, b, r, p, seed, off)
+        _bda_full_checks(x, b, r, "bf16", p, seed, off, out, f"chain {pre} bda")
+        del x, r, out
+    y, b, g = (load(w.name, k) for k in ("gelu_y", "gelu_bias", "gelu_g"))
+    T, H = y.shape
+    out = mb.mb_bias_gelu_fwd(y, b)
+    dg, dbias = mb.mb_bias_gelu_bwd(g, y, b)
+    bs = st(b.cpu())
+    fs, bws = [], []
+    for r0, n in row_blocks(T):
+        yr, gr = st(y[r0:r0 + n].cpu()), st(g[r0:r0 + n].cpu())
+        o, o64 = oracle.bias_gelu_fwd("bf16", yr, bs)
+        fs.append(assert_close(st(out[r0:r0 + n]), o, o64, None, "bf16", f"chain gelu fwd rows {r0}"))
+        d, d64, mag, _ = oracle.bias_gelu_bwd("bf16", gr, yr, bs)
+        bws.append(assert_close(st(dg[r0:r0 + n]), d, d64, mag, "bf16", f"chain gelu bwd rows {r0}"))
+    say(f"chain gelu fwd: {fs}")
+    say(f"chain gelu bwd: {bws}")
+    cols = torch.from_numpy(sample_cols(H)).to(DEV)
+    _, _, _, db64 = oracle.bias_gelu_bwd("bf16", st(g.index_select(1, cols).cpu()), st(y.index_select(1, cols).cpu()),
+                                         st(b.index_select(0, cols).cpu()))
+    say(f"chain gelu dbias sampled columns: "
+        f"{assert_reduction_close(dbias.index_select(0, cols).cpu().numpy(), db64, 'chain gelu dbias')}")
+    err = (dbias.double() - dg.double().sum(0)).abs()
+    bound = dbias_noise_bound(dg)
+    assert bool((err <= bound).all()), f"chain gelu dbias vs column sums, worst {float((err / bound).max()):.2f}"
+    dg2, dbias2 = mb.mb_bias_gelu_bwd(g, y, b)
+    assert torch.equal(dg.view(torch.int16), dg2.view(torch.int16))
+    assert torch.equal(dbias.view(torch.int32), dbias2.view(torch.int32))
