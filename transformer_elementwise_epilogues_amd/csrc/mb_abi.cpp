@@ -76,6 +76,8 @@ mb_status_t check_shape(int64_t T, int64_t H, mb_dtype_t dt, int width = 1) {
   if (static_cast<uint64_t>(H) * es * width / 16 > static_cast<uint64_t>(std::numeric_limits<int>::max()))
     return MB_ERR_SHAPE;
   if (T > (int64_t{1} << 40)) return MB_ERR_SHAPE;  // row index bound of the kernels' 64-bit math
+  // column strips of 64 vectors form one grid dimension (at most 65535)
+  if (static_cast<uint64_t>(H) * es / 16 > uint64_t{65535} * 64) return MB_ERR_SHAPE;
   return MB_OK;
 }
 
@@ -143,14 +145,14 @@ mb_status_t mb_bias_gelu_fwd(const void* y, const void* bias, void* out, int64_t
   if (!aligned(y, 16) || !aligned(out, 16) || !aligned(bias, 16)) return MB_ERR_ALIGN;
   if (!aliasing_ok({{out, tb}}, {{y, tb}, {bias, bias ? bb : 0}}, {{0, 0}})) return MB_ERR_ALIAS;
   if (tokens == 0) return MB_OK;
-  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt));
+  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GELU_FWD_BLOCKS);
   if (hipError_t e = mb::launch_gelu_fwd(dt, y, bias, out, t, s)) return hip_status(e);
   return finish();
 }
 
 size_t mb_bias_gelu_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias) {
   if (!with_dbias || !dt_ok(dt) || check_shape(tokens, hidden, dt) != MB_OK || tokens == 0) return 0;
-  return col_partials_bytes(mb::plan_tiling(tokens, nvec_of(hidden, dt)), hidden);
+  return col_partials_bytes(mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GELU_BWD_BLOCKS), hidden);
 }
 
 mb_status_t mb_bias_gelu_bwd(const void* g, const void* y, const void* bias, void* dgrad, float* dbias, void* ws,
@@ -173,7 +175,7 @@ mb_status_t mb_bias_gelu_bwd(const void* g, const void* y, const void* bias, voi
     if (hipError_t e = mb::launch_fill_zero(dbias, hidden, s)) return hip_status(e);
     return finish();
   }
-  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt));
+  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GELU_BWD_BLOCKS);
   float* partials = dbias ? static_cast<float*>(ws) : nullptr;
   if (hipError_t e = mb::launch_gelu_bwd(dt, g, y, bias, dgrad, partials, t, s)) return hip_status(e);
   if (dbias)
@@ -198,7 +200,7 @@ static mb_status_t bda_common(const void* x, const void* bias, const void* resid
   if (!aliasing_ok({{out, tb}}, {{x, tb}, {residual, rb}, {bias, bias ? bb : 0}}, {{0, 0}, {0, 1}}))
     return MB_ERR_ALIAS;
   if (tokens == 0) return MB_OK;
-  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt));
+  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_BDA_BLOCKS);
   const mb::DropoutArgs d = train ? dropout_args(p, seed, offset) : mb::DropoutArgs{};
   if (hipError_t e = mb::launch_bda(dt, residual_dt, train, x, bias, residual, out, hidden, t, d, s))
     return hip_status(e);
@@ -247,7 +249,7 @@ static mb_status_t glu_fwd_common(int act, const void* in, const void* bias, con
     return MB_ERR_ALIGN;
   if (!aliasing_ok({{out, ob}}, {{in, ib}, {bias, bias ? bb : 0}, {weights, wb}}, {})) return MB_ERR_ALIAS;
   if (tokens == 0) return MB_OK;
-  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt));
+  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GLU_FWD_BLOCKS);
   if (hipError_t e = mb::launch_glu_fwd(act, dt, in, bias, weights, weights ? weights_dt : dt, out, hidden, t, s))
     return hip_status(e);
   return finish();
@@ -270,7 +272,7 @@ struct GluWs {
 GluWs glu_ws(int64_t tokens, int64_t hidden, mb_dtype_t dt, bool with_dbias, bool with_dw) {
   GluWs w{0, 0, 0, 0, 0};
   if (tokens == 0) return w;
-  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt));
+  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GLU_BWD_BLOCKS);
   w.bias_bytes = with_dbias ? col_partials_bytes(t, 2 * hidden) : 0;
   w.w_off = round_up(w.bias_bytes, 256);
   w.w_bytes = with_dw ? static_cast<size_t>(t.strips) * tokens * 4 : 0;
@@ -310,7 +312,7 @@ static mb_status_t glu_bwd_common(int act, const void* g, const void* in, const 
     if (hipError_t e = mb::launch_fill_zero(dbias, 2 * hidden, s)) return hip_status(e);
     return finish();
   }
-  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt));
+  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GLU_BWD_BLOCKS);
   float* bp = dbias ? static_cast<float*>(ws) : nullptr;
   float* wp = dweights ? reinterpret_cast<float*>(static_cast<char*>(ws) + w.w_off) : nullptr;
   if (hipError_t e = mb::launch_glu_bwd(act, dt, g, in, bias, weights, weights ? weights_dt : dt, din, bp, wp, hidden,

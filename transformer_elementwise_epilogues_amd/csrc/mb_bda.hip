@@ -19,7 +19,7 @@ namespace mb {
 
 namespace {
 
-constexpr int kUnroll = 4;
+constexpr int kUnroll = MB_BDA_UNROLL;
 
 template <DT D, DT R, bool TRAIN>
 __device__ __forceinline__ u32x4 bda_vec(u32x4 xv, const u32x4* rv, const float* b, uint64_t i0,
@@ -54,7 +54,8 @@ __global__ __launch_bounds__(kThreads) void bda_kernel(const char* x, const char
   constexpr int RV = V / Vec<R>::N;  // 16-byte residual vectors per group
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int cv = blockIdx.x * kStrip + lane;
+  const TileIdx ti = tile_idx();
+  const int cv = ti.strip * kStrip + lane;
   if (cv >= nvec) return;
   float b[V];
   if (bias) {
@@ -65,12 +66,12 @@ __global__ __launch_bounds__(kThreads) void bda_kernel(const char* x, const char
   }
   const size_t px = static_cast<size_t>(nvec) * 16;
   const size_t pr = px * RV;
-  const int64_t S = static_cast<int64_t>(gridDim.y) * kWaves;
+  const int64_t S = static_cast<int64_t>(ti.G) * kWaves;
   const char* xp = x + static_cast<size_t>(cv) * 16;
   const char* rp = res + static_cast<size_t>(cv) * 16 * RV;
   char* op = out + static_cast<size_t>(cv) * 16;
   const uint64_t j0 = static_cast<uint64_t>(cv) * V;
-  int64_t t = static_cast<int64_t>(blockIdx.y) * kWaves + wave;
+  int64_t t = static_cast<int64_t>(ti.rg) * kWaves + wave;
   for (; t + (U - 1) * S < T; t += U * S) {
     u32x4 xv[U], rv[U][RV];
 #pragma unroll
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(256) void mask_kernel(uint8_t* bits, int64_t n, Dro
 template <DT D, DT R>
 hipError_t bda_dispatch(bool train, const void* x, const void* bias, const void* res, void* out, int64_t H,
                         const Tiling& t, const DropoutArgs& d, hipStream_t s) {
-  dim3 grid(t.strips, t.G);
+  const dim3 grid = tile_grid(t.strips, t.G);
   auto xp = static_cast<const char*>(x);
   auto bp = static_cast<const char*>(bias);
   auto rp = static_cast<const char*>(res);

@@ -32,15 +32,47 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStrip = 64;
 
+// Block order. Workgroups are dealt to the 8 XCDs round-robin by linear block
+// id. With the row group as the fast grid dimension, every XCD works on all
+// column strips (and so on all memory channels a row spans) rather than on a
+// fixed 1-in-8 subset of columns.
+#ifndef MB_RG_MAJOR
+#define MB_RG_MAJOR 0
+#endif
+struct TileIdx {
+  int strip;  // column strip of 64 vectors
+  int rg;     // row group
+  int G;      // row groups in the grid
+};
+__device__ __forceinline__ TileIdx tile_idx() {
+  if constexpr (MB_RG_MAJOR) return TileIdx{static_cast<int>(blockIdx.y), static_cast<int>(blockIdx.x),
+                                            static_cast<int>(gridDim.x)};
+  return TileIdx{static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y), static_cast<int>(gridDim.y)};
+}
+__host__ __forceinline__ dim3 tile_grid(int strips, int G) {
+  if constexpr (MB_RG_MAJOR) return dim3(G, strips);
+  return dim3(strips, G);
+}
+
 // ---------------------------------------------------------------- vector I/O
 
 // Streaming tensors are read and written once: non-temporal hints keep them
 // from displacing reused lines (bias) in the caches.
+#ifndef MB_NT_LOAD
+#define MB_NT_LOAD 1
+#endif
+#ifndef MB_NT_STORE
+#define MB_NT_STORE 1
+#endif
 __device__ __forceinline__ u32x4 ld_stream(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  if constexpr (MB_NT_LOAD) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return *reinterpret_cast<const u32x4*>(p);
 }
 __device__ __forceinline__ void st_stream(void* p, u32x4 v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  if constexpr (MB_NT_STORE)
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  else
+    *reinterpret_cast<u32x4*>(p) = v;
 }
 __device__ __forceinline__ u32x4 ld_keep(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 

@@ -20,8 +20,8 @@ namespace mb {
 
 namespace {
 
-constexpr int kUnrollFwd = 4;
-constexpr int kUnrollBwd = 4;
+constexpr int kUnrollFwd = MB_GELU_FWD_UNROLL;
+constexpr int kUnrollBwd = MB_GELU_BWD_UNROLL;
 
 template <DT D>
 __device__ __forceinline__ void load_bias(const char* bias, int cv, float* b) {
@@ -52,15 +52,16 @@ __global__ __launch_bounds__(kThreads) void gelu_fwd_kernel(const char* y, const
                                                             int64_t T, int nvec) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int cv = blockIdx.x * kStrip + lane;
+  const TileIdx ti = tile_idx();
+  const int cv = ti.strip * kStrip + lane;
   if (cv >= nvec) return;
   float b[Vec<D>::N];
   load_bias<D>(bias, cv, b);
   const size_t pitch = static_cast<size_t>(nvec) * 16;
-  const int64_t S = static_cast<int64_t>(gridDim.y) * kWaves;
+  const int64_t S = static_cast<int64_t>(ti.G) * kWaves;
   const char* yp = y + static_cast<size_t>(cv) * 16;
   char* op = out + static_cast<size_t>(cv) * 16;
-  int64_t t = static_cast<int64_t>(blockIdx.y) * kWaves + wave;
+  int64_t t = static_cast<int64_t>(ti.rg) * kWaves + wave;
   for (; t + (U - 1) * S < T; t += U * S) {
     u32x4 v[U];
 #pragma unroll
@@ -94,7 +95,8 @@ __global__ __launch_bounds__(kThreads) void gelu_bwd_kernel(const char* g, const
   constexpr int V = Vec<D>::N;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int cv = blockIdx.x * kStrip + lane;
+  const TileIdx ti = tile_idx();
+  const int cv = ti.strip * kStrip + lane;
   const bool active = cv < nvec;
   float acc[V];
 #pragma unroll
@@ -103,9 +105,9 @@ __global__ __launch_bounds__(kThreads) void gelu_bwd_kernel(const char* g, const
     float b[V];
     load_bias<D>(bias, cv, b);
     const size_t pitch = static_cast<size_t>(nvec) * 16;
-    const int64_t S = static_cast<int64_t>(gridDim.y) * kWaves;
+    const int64_t S = static_cast<int64_t>(ti.G) * kWaves;
     const size_t col = static_cast<size_t>(cv) * 16;
-    int64_t t = static_cast<int64_t>(blockIdx.y) * kWaves + wave;
+    int64_t t = static_cast<int64_t>(ti.rg) * kWaves + wave;
     for (; t + (U - 1) * S < T; t += U * S) {
       u32x4 gv[U], yv[U];
 #pragma unroll
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void gelu_bwd_kernel(const char* g, const
       float s[V];
 #pragma unroll
       for (int k = 0; k < V; ++k) s[k] = ((red[0][k][lane] + red[1][k][lane]) + red[2][k][lane]) + red[3][k][lane];
-      float* dst = partials + static_cast<size_t>(blockIdx.y) * nvec * V + static_cast<size_t>(cv) * V;
+      float* dst = partials + static_cast<size_t>(ti.rg) * nvec * V + static_cast<size_t>(cv) * V;
 #pragma unroll
       for (int q = 0; q < V / 4; ++q) store_f32x4(dst + 4 * q, s + 4 * q);
     }
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void gelu_bwd_kernel(const char* g, const
 
 template <DT D>
 hipError_t gelu_fwd_dispatch(const void* y, const void* bias, void* out, const Tiling& t, hipStream_t s) {
-  dim3 grid(t.strips, t.G);
+  const dim3 grid = tile_grid(t.strips, t.G);
   hipLaunchKernelGGL((gelu_fwd_kernel<D, kUnrollFwd>), grid, dim3(kThreads), 0, s,
                      static_cast<const char*>(y), static_cast<const char*>(bias), static_cast<char*>(out), t.T,
                      t.nvec);
@@ -150,7 +152,7 @@ hipError_t gelu_fwd_dispatch(const void* y, const void* bias, void* out, const T
 template <DT D>
 hipError_t gelu_bwd_dispatch(const void* g, const void* y, const void* bias, void* dgrad, float* partials,
                              const Tiling& t, hipStream_t s) {
-  dim3 grid(t.strips, t.G);
+  const dim3 grid = tile_grid(t.strips, t.G);
   auto gp = static_cast<const char*>(g);
   auto yp = static_cast<const char*>(y);
   auto bp = static_cast<const char*>(bias);

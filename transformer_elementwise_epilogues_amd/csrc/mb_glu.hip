@@ -22,8 +22,8 @@ namespace mb {
 
 namespace {
 
-constexpr int kUnrollFwd = 4;
-constexpr int kUnrollBwd = 2;
+constexpr int kUnrollFwd = MB_GLU_FWD_UNROLL;
+constexpr int kUnrollBwd = MB_GLU_BWD_UNROLL;
 
 template <DT D>
 __device__ __forceinline__ void load_bias_pair(const char* bias, int cv, int nvec, float* ba, float* bb) {
@@ -37,9 +37,12 @@ __device__ __forceinline__ void load_bias_pair(const char* bias, int cv, int nve
   }
 }
 
-template <DT W>
+// Per-token weight of row t, or 1 for the unweighted op. The weighted and
+// unweighted ops are separate instantiations: a null test inside the row loop
+// makes the compiler wait for every outstanding load (vmcnt(0)) at each row.
+template <bool WEIGHTED, DT W>
 __device__ __forceinline__ float load_weight(const char* w, int64_t t) {
-  if (!w) return 1.0f;
+  if constexpr (!WEIGHTED) return 1.0f;
   if constexpr (W == DT::F32) return reinterpret_cast<const float*>(w)[t];
   if constexpr (W == DT::BF16) {
     const unsigned h = reinterpret_cast<const uint16_t*>(w)[t];
@@ -71,23 +74,24 @@ __device__ __forceinline__ u32x4 glu_vec(u32x4 av, u32x4 bv, const float* ba, co
   return pack<D>(a);
 }
 
-template <DT D, int ACT, DT W, int U>
+template <DT D, int ACT, bool WEIGHTED, DT W, int U>
 __global__ __launch_bounds__(kThreads) void glu_fwd_kernel(const char* in, const char* bias, const char* w,
                                                            char* out, int64_t T, int nvec) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int cv = blockIdx.x * kStrip + lane;
+  const TileIdx ti = tile_idx();
+  const int cv = ti.strip * kStrip + lane;
   if (cv >= nvec) return;
   constexpr int V = Vec<D>::N;
   float ba[V], bb[V];
   load_bias_pair<D>(bias, cv, nvec, ba, bb);
   const size_t po = static_cast<size_t>(nvec) * 16;
   const size_t pi = 2 * po;
-  const int64_t S = static_cast<int64_t>(gridDim.y) * kWaves;
+  const int64_t S = static_cast<int64_t>(ti.G) * kWaves;
   const char* ap = in + static_cast<size_t>(cv) * 16;
   const char* bp = ap + po;
   char* op = out + static_cast<size_t>(cv) * 16;
-  int64_t t = static_cast<int64_t>(blockIdx.y) * kWaves + wave;
+  int64_t t = static_cast<int64_t>(ti.rg) * kWaves + wave;
   for (; t + (U - 1) * S < T; t += U * S) {
     u32x4 av[U], bv[U];
     float wt[U];
@@ -95,13 +99,13 @@ __global__ __launch_bounds__(kThreads) void glu_fwd_kernel(const char* in, const
     for (int u = 0; u < U; ++u) {
       av[u] = ld_stream(ap + (t + u * S) * pi);
       bv[u] = ld_stream(bp + (t + u * S) * pi);
-      wt[u] = load_weight<W>(w, t + u * S);
+      wt[u] = load_weight<WEIGHTED, W>(w, t + u * S);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) st_stream(op + (t + u * S) * po, glu_vec<D, ACT>(av[u], bv[u], ba, bb, wt[u]));
   }
   for (; t < T; t += S)
-    st_stream(op + t * po, glu_vec<D, ACT>(ld_stream(ap + t * pi), ld_stream(bp + t * pi), ba, bb, load_weight<W>(w, t)));
+    st_stream(op + t * po, glu_vec<D, ACT>(ld_stream(ap + t * pi), ld_stream(bp + t * pi), ba, bb, load_weight<WEIGHTED, W>(w, t)));
 }
 
 // Backward of one column vector of one row. Returns the row's contribution to
@@ -142,14 +146,15 @@ __device__ __forceinline__ float glu_grad_vec(u32x4 gv, u32x4 av, u32x4 bv, cons
   return rowsum;
 }
 
-template <DT D, int ACT, DT W, int U, bool DBIAS, bool DW>
+template <DT D, int ACT, bool WEIGHTED, DT W, int U, bool DBIAS, bool DW>
 __global__ __launch_bounds__(kThreads) void glu_bwd_kernel(const char* g, const char* in, const char* bias,
                                                            const char* w, char* din, float* bpart, float* wpart,
                                                            int64_t T, int nvec) {
   constexpr int V = Vec<D>::N;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int cv = blockIdx.x * kStrip + lane;
+  const TileIdx ti = tile_idx();
+  const int cv = ti.strip * kStrip + lane;
   const bool active = cv < nvec;
   float acc_a[V], acc_b[V];
 #pragma unroll
@@ -164,8 +169,8 @@ __global__ __launch_bounds__(kThreads) void glu_bwd_kernel(const char* g, const 
   const size_t po = static_cast<size_t>(nvec) * 16;
   const size_t pi = 2 * po;
   const size_t col = static_cast<size_t>(cv) * 16;
-  const int64_t S = static_cast<int64_t>(gridDim.y) * kWaves;
-  int64_t t = static_cast<int64_t>(blockIdx.y) * kWaves + wave;
+  const int64_t S = static_cast<int64_t>(ti.G) * kWaves;
+  int64_t t = static_cast<int64_t>(ti.rg) * kWaves + wave;
   // Row loop is uniform across the wave (t depends on the wave only), so the
   // weights-gradient butterfly below sees every lane.
   for (; t + (U - 1) * S < T; t += U * S) {
@@ -181,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void glu_bwd_kernel(const char* g, const 
       } else {
         gv[u] = av[u] = bv[u] = u32x4{0, 0, 0, 0};
       }
-      wt[u] = load_weight<W>(w, tt);
+      wt[u] = load_weight<WEIGHTED, W>(w, tt);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void glu_bwd_kernel(const char* g, const 
       }
       if constexpr (DW) {
         rs = wave_sum(active ? rs : 0.0f);
-        if (lane == 0) wpart[static_cast<size_t>(blockIdx.x) * T + tt] = rs;
+        if (lane == 0) wpart[static_cast<size_t>(ti.strip) * T + tt] = rs;
       }
     }
   }
@@ -206,14 +211,14 @@ __global__ __launch_bounds__(kThreads) void glu_bwd_kernel(const char* g, const 
       bv = ld_stream(in + t * pi + po + col);
     }
     u32x4 dav, dbv;
-    float rs = glu_grad_vec<D, ACT, DW>(gv, av, bv, ba, bb, load_weight<W>(w, t), acc_a, acc_b, &dav, &dbv);
+    float rs = glu_grad_vec<D, ACT, DW>(gv, av, bv, ba, bb, load_weight<WEIGHTED, W>(w, t), acc_a, acc_b, &dav, &dbv);
     if (active) {
       st_stream(din + t * pi + col, dav);
       st_stream(din + t * pi + po + col, dbv);
     }
     if constexpr (DW) {
       rs = wave_sum(active ? rs : 0.0f);
-      if (lane == 0) wpart[static_cast<size_t>(blockIdx.x) * T + t] = rs;
+      if (lane == 0) wpart[static_cast<size_t>(ti.strip) * T + t] = rs;
     }
   }
   if constexpr (DBIAS) {
@@ -232,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void glu_bwd_kernel(const char* g, const 
         sb[k] = ((red[0][V + k][lane] + red[1][V + k][lane]) + red[2][V + k][lane]) + red[3][V + k][lane];
       }
       const size_t C = 2 * static_cast<size_t>(nvec) * V;
-      float* dst_a = bpart + blockIdx.y * C + static_cast<size_t>(cv) * V;
+      float* dst_a = bpart + static_cast<size_t>(ti.rg) * C + static_cast<size_t>(cv) * V;
       float* dst_b = dst_a + static_cast<size_t>(nvec) * V;
 #pragma unroll
       for (int q = 0; q < V / 4; ++q) {
@@ -246,19 +251,30 @@ __global__ __launch_bounds__(kThreads) void glu_bwd_kernel(const char* g, const 
 template <DT D, int ACT, DT W>
 hipError_t glu_fwd_dispatch(const void* in, const void* bias, const void* w, void* out, const Tiling& t,
                             hipStream_t s) {
-  dim3 grid(t.strips, t.G);
-  hipLaunchKernelGGL((glu_fwd_kernel<D, ACT, W, kUnrollFwd>), grid, dim3(kThreads), 0, s,
-                     static_cast<const char*>(in), static_cast<const char*>(bias), static_cast<const char*>(w),
-                     static_cast<char*>(out), t.T, t.nvec);
+  const dim3 grid = tile_grid(t.strips, t.G);
+  auto ip = static_cast<const char*>(in);
+  auto bp = static_cast<const char*>(bias);
+  auto wp = static_cast<const char*>(w);
+  auto op = static_cast<char*>(out);
+  if (w)
+    hipLaunchKernelGGL((glu_fwd_kernel<D, ACT, true, W, kUnrollFwd>), grid, dim3(kThreads), 0, s, ip, bp, wp, op, t.T,
+                       t.nvec);
+  else
+    hipLaunchKernelGGL((glu_fwd_kernel<D, ACT, false, W, kUnrollFwd>), grid, dim3(kThreads), 0, s, ip, bp, wp, op,
+                       t.T, t.nvec);
   return hipGetLastError();
 }
 
 template <DT D, int ACT, DT W, bool DBIAS, bool DW>
 hipError_t glu_bwd_launch(const char* g, const char* in, const char* bias, const char* w, char* din, float* bp,
                           float* wp, const Tiling& t, hipStream_t s) {
-  dim3 grid(t.strips, t.G);
-  hipLaunchKernelGGL((glu_bwd_kernel<D, ACT, W, kUnrollBwd, DBIAS, DW>), grid, dim3(kThreads), 0, s, g, in, bias, w,
-                     din, bp, wp, t.T, t.nvec);
+  const dim3 grid = tile_grid(t.strips, t.G);
+  if (w)
+    hipLaunchKernelGGL((glu_bwd_kernel<D, ACT, true, W, kUnrollBwd, DBIAS, DW>), grid, dim3(kThreads), 0, s, g, in,
+                       bias, w, din, bp, wp, t.T, t.nvec);
+  else
+    hipLaunchKernelGGL((glu_bwd_kernel<D, ACT, false, W, kUnrollBwd, DBIAS, false>), grid, dim3(kThreads), 0, s, g,
+                       in, bias, w, din, bp, wp, t.T, t.nvec);
   return hipGetLastError();
 }
 

@@ -18,8 +18,43 @@ struct Tiling {
   int G = 0;         // row groups
 };
 
+// Launch shape per kernel family: blocks of 256 threads to aim for (row groups
+// are rounded down so the grid never exceeds it by a partial wave of blocks)
+// and rows in flight per wave. Measured on MI355X (rocprofv3 + bench.py): the
+// write path saturates with 1-2 resident blocks per CU, not with more.
+#ifndef MB_GELU_FWD_BLOCKS
+#define MB_GELU_FWD_BLOCKS 768
+#endif
+#ifndef MB_GELU_FWD_UNROLL
+#define MB_GELU_FWD_UNROLL 2
+#endif
+#ifndef MB_GELU_BWD_BLOCKS
+#define MB_GELU_BWD_BLOCKS 256
+#endif
+#ifndef MB_GELU_BWD_UNROLL
+#define MB_GELU_BWD_UNROLL 8
+#endif
+#ifndef MB_BDA_BLOCKS
+#define MB_BDA_BLOCKS 512
+#endif
+#ifndef MB_BDA_UNROLL
+#define MB_BDA_UNROLL 1
+#endif
+#ifndef MB_GLU_FWD_BLOCKS
+#define MB_GLU_FWD_BLOCKS 512
+#endif
+#ifndef MB_GLU_FWD_UNROLL
+#define MB_GLU_FWD_UNROLL 2
+#endif
+#ifndef MB_GLU_BWD_BLOCKS
+#define MB_GLU_BWD_BLOCKS 512
+#endif
+#ifndef MB_GLU_BWD_UNROLL
+#define MB_GLU_BWD_UNROLL 1
+#endif
+
 // The tiling every kernel of one call uses; also sizes the workspaces.
-Tiling plan_tiling(int64_t T, int nvec);
+Tiling plan_tiling(int64_t T, int nvec, int target_blocks);
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 // out[c] = sum over r < R of in[r * C + c], r ascending (fp32).

@@ -9,12 +9,6 @@
 #include "mb_device.hpp"
 #include "mb_launch.hpp"
 
-#ifndef MB_TARGET_BLOCKS
-// Blocks of 256 threads per launch the row groups aim for: 4 per CU on the
-// 256 CUs of MI355X.
-#define MB_TARGET_BLOCKS 1024
-#endif
-
 namespace mb {
 
 namespace {
@@ -44,12 +38,14 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
 
 }  // namespace
 
-Tiling plan_tiling(int64_t T, int nvec) {
+Tiling plan_tiling(int64_t T, int nvec, int target_blocks) {
   Tiling t;
   t.T = T;
   t.nvec = nvec;
   t.strips = (nvec + kStrip - 1) / kStrip;
-  const int64_t want = std::max<int64_t>(1, (MB_TARGET_BLOCKS + t.strips - 1) / t.strips);
+  // Round down: a grid slightly larger than the resident capacity would leave a
+  // few straggler blocks running alone after the rest finish.
+  const int64_t want = std::max<int64_t>(1, target_blocks / t.strips);
   const int64_t most = std::max<int64_t>(1, (T + kWaves - 1) / kWaves);  // every row group owns a row
   t.G = static_cast<int>(std::min<int64_t>(std::min(want, most), 65535));
   return t;
