@@ -53,6 +53,7 @@ def lib() -> ctypes.CDLL:
             L.orc_bias_gelu_bwd.argtypes = [I, P, P, P, P, P, P, P, I64, I64]
             L.orc_bias_dropout_add.argtypes = [I, P, P, P, I, P, P, P, I64, I64, I, F, U64, U64, I64]
             L.orc_dropout_mask.argtypes = [P, I64, I64, F, U64, U64, I64]
+            L.orc_bias_dropout_add_bwd.argtypes = [I, P, I, P, P, P, P, I64, I64, F, U64, U64, I64]
             L.orc_bias_glu_fwd.argtypes = [I, I, P, P, P, I, P, P, I64, I64]
             L.orc_bias_glu_bwd.argtypes = [I, I, P, P, P, P, I, P, P, P, P, P, I64, I64]
             L.orc_philox4x32_10.argtypes = [P, P, P]
@@ -210,6 +211,19 @@ def bias_dropout_add(dt, x, bias, residual, res_dt, train, p=0.0, seed=0, offset
                                    _ptr(out), _ptr(out64), _ptr(mag), T, H, int(bool(train)),
                                    float(p), int(seed), int(offset), int(row0)))
     return out, out64, mag
+
+
+def bias_dropout_add_bwd(dt, g, res_dt, p, seed, offset=0, row0=0, want_dres=True):
+    """Returns dx (dt storage), dx64, dresidual (res_dt storage or None), dbias64."""
+    T, H = g.shape
+    g = _check_in(g, dt, name="g")
+    dx = np.empty((T, H), _storage(dt))
+    dx64 = np.empty((T, H), np.float64)
+    dres = np.empty((T, H), _storage(res_dt)) if want_dres else None
+    dbias = np.empty((H,), np.float64)
+    _ok(lib().orc_bias_dropout_add_bwd(DTYPES[dt], _ptr(g), DTYPES[res_dt], _ptr(dx), _ptr(dx64), _ptr(dres),
+                                       _ptr(dbias), T, H, float(p), int(seed), int(offset), int(row0)))
+    return dx, dx64, dres, dbias
 
 
 def dropout_mask(T, H, p, seed, offset, row0=0):

@@ -392,6 +392,36 @@ int orc_bias_dropout_add(int dt, const void* x, const void* bias, const void* re
   return ORC_OK;
 }
 
+/* Backward of bias-dropout-add, train [fusions §3.2, §3.3; the unit test of
+ * §9 compares gradients too]. With out = r' + keep * (x + bias) * s:
+ *   dx[t, j]        = g * s if kept, else 0                    (dtype dt)
+ *   dresidual[t, j] = g, in the residual's dtype (nullable); the cast of the
+ *                     residual to dt passes the gradient straight through
+ *   dbias[j]        = sum over t of the unrounded dx[t, j]     (double, nullable)
+ * The keep decisions are regenerated from (p, seed, offset) exactly as the
+ * forward made them. */
+int orc_bias_dropout_add_bwd(int dt, const void* g, int res_dt, void* dx, double* dx64, void* dres,
+                             double* dbias, int64_t T, int64_t H, float p, uint64_t seed,
+                             uint64_t offset, int64_t row0) {
+  if (!dtype_ok(dt) || !dtype_ok(res_dt) || T < 0 || H <= 0 || row0 < 0 || !prob_ok(p)) return ORC_BAD;
+  uint64_t theta = drop_threshold(p);
+  double s = (double)orc_keep_scale(p);
+  if (dbias)
+    for (int64_t j = 0; j < H; ++j) dbias[j] = 0.0;
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t j = 0; j < H; ++j) {
+      int64_t i = t * H + j;
+      double gv = load_elem(dt, g, i);
+      uint64_t gi = (uint64_t)(row0 + t) * (uint64_t)H + (uint64_t)j;
+      double v = element_kept(gi, theta, seed, offset) ? gv * s : 0.0;
+      store_elem(dt, dx, i, v);
+      if (dx64) dx64[i] = v;
+      if (dres) store_elem(res_dt, dres, i, gv);
+      if (dbias) dbias[j] += v;
+    }
+  return ORC_OK;
+}
+
 static double act_fwd(int act, double a) { return act == ORC_SWIGLU ? orc_silu(a) : orc_gelu_tanh(a); }
 static double act_grad(int act, double a) {
   return act == ORC_SWIGLU ? orc_silu_grad(a) : orc_gelu_tanh_grad(a);

@@ -304,3 +304,49 @@ def test_glu_empty_tokens():
     g = np.zeros((0, 16), np.uint16)
     _, _, _, db, dw = oracle.bias_glu_bwd("swiglu", "bf16", g, x, None, np.zeros(0, np.uint16))
     assert np.array_equal(db, np.zeros(32)) and dw.shape == (0,)
+
+
+# ---------------------------------------------------------------- dropout-add backward
+
+@pytest.mark.parametrize("p", [0.1, 0.5])
+def test_bda_bwd_brute_force_jacobian(p):
+    """Finite differences through the oracle's own train forward (double storage):
+    d out / d x = keep * s, d out / d bias summed over rows, d out / d residual = 1."""
+    r = rng(19)
+    T, H, seed, off = 4, 8, 77, 3
+    x = r.standard_normal((T, H))
+    b = r.standard_normal(H) * 0.3
+    res = r.standard_normal((T, H))
+    g = r.standard_normal((T, H))
+    dx, dx64, dres, db64 = oracle.bias_dropout_add_bwd("f64", g, "f64", p, seed, off)
+
+    def loss():
+        _, o, _ = oracle.bias_dropout_add("f64", x, b, res, "f64", True, p, seed, off)
+        return float(np.sum(g * o))
+
+    assert np.all(_close(dx64, _fd_grad(loss, x), 1.0))
+    assert np.all(_close(db64, _fd_grad(loss, b), 1.0))
+    assert np.all(_close(dres, _fd_grad(loss, res), 1.0))
+
+
+def test_bda_bwd_follows_the_forward_mask_and_widens_the_residual_grad():
+    T, H, p, seed, off = 16, 64, 0.3, 9, 2**32 + 1
+    g = bf16_bits(rng(20).standard_normal((T, H)).astype(np.float32))
+    dx, dx64, dres, db64 = oracle.bias_dropout_add_bwd("bf16", g, "f32", p, seed, off)
+    bits = np.unpackbits(oracle.dropout_mask(T, H, p, seed, off), bitorder="little")[:T * H].reshape(T, H)
+    s = float(np.float32(1.0 / (1.0 - float(np.float32(p)))))
+    gv = bf16_value(g)
+    assert np.array_equal(dx64, np.where(bits == 1, gv * s, 0.0))
+    assert np.array_equal(dres.astype(np.float64), gv)       # bf16 -> fp32 is exact
+    assert np.allclose(db64, dx64.sum(axis=0), rtol=1e-13, atol=1e-13)
+    # row sampling gives the same rows
+    dxp, *_ = oracle.bias_dropout_add_bwd("bf16", g[5:9], "f32", p, seed, off, row0=5)
+    assert np.array_equal(dxp, dx[5:9])
+
+
+def test_bda_bwd_p0_is_identity_and_p1_is_zero():
+    g = bf16_bits(rng(21).standard_normal((8, 32)).astype(np.float32))
+    dx, _, dres, db = oracle.bias_dropout_add_bwd("bf16", g, "bf16", 0.0, 1, 0)
+    assert np.array_equal(dx, g) and np.array_equal(dres, g)
+    dx1, d641, _, db1 = oracle.bias_dropout_add_bwd("bf16", g, "bf16", 1.0, 1, 0)
+    assert np.all(d641 == 0.0) and np.all(db1 == 0.0)
