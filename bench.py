@@ -2,13 +2,15 @@
 
 One step = one pass of every fused op at its full synthetic workload:
   bias-dropout-add, bf16 x [8192, 4096] with fp32 residual, p = 0.1
-      (train, and inference in place on a copy of x)
+      (train, its backward with the fp32 residual gradient, and inference in
+      place on a copy of x)
   bias-SwiGLU fwd + bwd, bf16 [8192, 28672] -> [8192, 14336], unweighted and
       per-token weighted
   bias-GEGLU fwd + bwd, bf16 [16384, 16384] ~ N(0, 2) -> [16384, 8192]
-  layer epilogue chain, bf16, 16384 tokens, hidden 8192, ffn 32768:
-      attention-out dropout-add -> bias-GeLU fwd -> bias-GeLU bwd (+ dbias)
-      -> MLP-out dropout-add
+  layer epilogue chain, bf16, 16384 tokens, hidden 8192, ffn 32768, forward
+      then backward: attention-out dropout-add -> bias-GeLU -> MLP-out
+      dropout-add -> their backward passes in reverse order (dropout-add
+      backward regenerates the mask; the residual gradient is g itself)
 Inputs are resident in HBM before timing starts. `value` is the algorithmic
 bytes of a step (each tensor read or written once, bias and gradients of the
 bias included, reduction partials excluded) divided by the step time.
@@ -31,8 +33,9 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic_gelu_bwd_t16384_h32768.json")
-WORKLOAD = "all_epilogues_full_size: bda_bf16_8192x4096_res_f32 (train+infer) + swiglu_bf16_8192x14336 " \
-           "(plain+weighted, fwd+bwd) + geglu_bf16_16384x8192 (fwd+bwd) + layer_chain_bf16_t16384_h8192_f32768"
+WORKLOAD = "all_epilogues_full_size: bda_bf16_8192x4096_res_f32 (train+bwd+infer) + swiglu_bf16_8192x14336 " \
+           "(plain+weighted, fwd+bwd) + geglu_bf16_16384x8192 (fwd+bwd) + layer_chain_bf16_t16384_h8192_f32768 " \
+           "(attn bda, gelu, mlp bda: fwd then bwd)"
 
 
 def parse():
@@ -68,14 +71,22 @@ def build_ops(dev):
 
     # -- bias-dropout-add, bf16 with fp32 residual
     w = WORKLOADS["bda_bf16_8192x4096_res_f32"]
-    x, b, r = (load(w.name, k) for k in ("x", "bias", "residual"))
+    x, b, r, g2 = (load(w.name, k) for k in ("x", "bias", "residual", "g"))
     T, H = x.shape
     out = torch.empty_like(x)
     xi, ri = x.clone(), r.clone()  # the in-place inference pass gets its own buffers
     p, seed, off = w.params["p"], w.params["seed"], w.params["offset"]
     bda_bytes = T * H * (2 + 4 + 2) + H * 2
+    dx2, dr2 = torch.empty_like(x), torch.empty_like(r)
+    db2 = torch.empty(H, dtype=torch.float32, device=dev)
+    ws2 = torch.empty(max(1, mb.mb_bias_dropout_add_bwd_workspace(T, H, x.dtype, True)), dtype=torch.uint8,
+                      device=dev)
     ops.append(Op("bda_train_bf16_res_f32_8192x4096",
                   lambda: mb.mb_bias_dropout_add_train(x, b, r, p, seed, off, out=out), bda_bytes, ["bda"]))
+    ops.append(Op("bda_bwd_bf16_res_f32_8192x4096",
+                  lambda: mb.mb_bias_dropout_add_bwd(g2, p, seed, off, residual_dtype=torch.float32, dx=dx2,
+                                                     dresidual=dr2, dbias=db2, ws=ws2),
+                  T * H * (2 + 2 + 4) + H * 4, ["bda_bwd", "colsum"]))
     ops.append(Op("bda_infer_inplace_bf16_res_f32_8192x4096",
                   lambda: mb.mb_bias_dropout_add_infer(xi, b, ri, out=xi), bda_bytes, ["bda"]))
 
@@ -120,26 +131,37 @@ def build_ops(dev):
 
     # -- layer epilogue chain
     w = WORKLOADS["layer_chain_bf16_t16384_h8192_f32768"]
-    ax, ar, ab = (load(w.name, k) for k in ("attn_x", "attn_residual", "attn_bias"))
+    ax, ar, ab, ag = (load(w.name, k) for k in ("attn_x", "attn_residual", "attn_bias", "attn_g"))
     gy, gb, gg = (load(w.name, k) for k in ("gelu_y", "gelu_bias", "gelu_g"))
-    mx, mr, mbias = (load(w.name, k) for k in ("mlp_x", "mlp_residual", "mlp_bias"))
+    mx, mr, mbias, mg = (load(w.name, k) for k in ("mlp_x", "mlp_residual", "mlp_bias", "mlp_g"))
     aout, mout = torch.empty_like(ax), torch.empty_like(mx)
+    adx, mdx = torch.empty_like(ax), torch.empty_like(mx)
     gout, dgr = torch.empty_like(gy), torch.empty_like(gy)
     T, H = gy.shape
     dbg = torch.empty(H, dtype=torch.float32, device=dev)
     wsg = torch.empty(max(1, mb.mb_bias_gelu_bwd_workspace(T, H, gy.dtype, True)), dtype=torch.uint8, device=dev)
     Ta, Ha = ax.shape
+    adb, mdb = (torch.empty(Ha, dtype=torch.float32, device=dev) for _ in range(2))
+    wsb = torch.empty(max(1, mb.mb_bias_dropout_add_bwd_workspace(Ta, Ha, ax.dtype, True)), dtype=torch.uint8,
+                      device=dev)
     p5, s_attn, s_mlp, off5 = w.params["p"], w.params["attn_seed"], w.params["mlp_seed"], w.params["offset"]
     bda5 = Ta * Ha * 6 + Ha * 2
+    bwd5 = Ta * Ha * 4 + Ha * 4  # read g, write dx, dbias; the residual gradient is g itself
     ops.append(Op("chain_attn_bda_train_bf16_16384x8192",
                   lambda: mb.mb_bias_dropout_add_train(ax, ab, ar, p5, s_attn, off5, out=aout), bda5, ["bda"]))
     ops.append(Op("chain_gelu_fwd_bf16_16384x32768", lambda: mb.mb_bias_gelu_fwd(gy, gb, out=gout),
                   T * H * 4 + H * 2, ["gelu_fwd"]))
+    ops.append(Op("chain_mlp_bda_train_bf16_16384x8192",
+                  lambda: mb.mb_bias_dropout_add_train(mx, mbias, mr, p5, s_mlp, off5, out=mout), bda5, ["bda"]))
+    ops.append(Op("chain_mlp_bda_bwd_bf16_16384x8192",
+                  lambda: mb.mb_bias_dropout_add_bwd(mg, p5, s_mlp, off5, dx=mdx, dresidual=False, dbias=mdb, ws=wsb),
+                  bwd5, ["bda_bwd", "colsum"]))
     ops.append(Op("chain_gelu_bwd_bf16_16384x32768",
                   lambda: mb.mb_bias_gelu_bwd(gg, gy, gb, dgrad=dgr, dbias=dbg, ws=wsg),
                   T * H * 6 + H * 2 + H * 4, ["gelu_bwd", "colsum"]))
-    ops.append(Op("chain_mlp_bda_train_bf16_16384x8192",
-                  lambda: mb.mb_bias_dropout_add_train(mx, mbias, mr, p5, s_mlp, off5, out=mout), bda5, ["bda"]))
+    ops.append(Op("chain_attn_bda_bwd_bf16_16384x8192",
+                  lambda: mb.mb_bias_dropout_add_bwd(ag, p5, s_attn, off5, dx=adx, dresidual=False, dbias=adb, ws=wsb),
+                  bwd5, ["bda_bwd", "colsum"]))
     return ops, host
 
 
@@ -217,6 +239,8 @@ def cpu_baseline(host, seconds):
     plan.append(("bda_train_c2", lambda n: oracle.bias_dropout_add("bf16", rows(c2, "x", n), vec(c2, "bias"),
                                                                      rows(c2, "residual", n), "f32", True, 0.1, 1234, 0),
                  lambda n: n * 4096 * 8 + 4096 * 2))
+    plan.append(("bda_bwd_c2", lambda n: oracle.bias_dropout_add_bwd("bf16", rows(c2, "g", n), "f32", 0.1, 1234, 0),
+                 lambda n: n * 4096 * 8 + 4096 * 4))
     plan.append(("bda_infer_c2", lambda n: oracle.bias_dropout_add("bf16", rows(c2, "x", n), vec(c2, "bias"),
                                                                      rows(c2, "residual", n), "f32", False),
                  lambda n: n * 4096 * 8 + 4096 * 2))
@@ -243,6 +267,9 @@ def cpu_baseline(host, seconds):
     plan.append(("chain_mlp_bda_c5", lambda n: oracle.bias_dropout_add(
         "bf16", rows(c5, "mlp_x", n), vec(c5, "mlp_bias"), rows(c5, "mlp_residual", n), "bf16", True, 0.1, 5002, 0),
         lambda n: n * 8192 * 6 + 8192 * 2))
+    for pre, sd in (("mlp", 5002), ("attn", 5001)):
+        plan.append((f"chain_{pre}_bda_bwd_c5", lambda n, pre=pre, sd=sd: oracle.bias_dropout_add_bwd(
+            "bf16", rows(c5, f"{pre}_g", n), "bf16", 0.1, sd, 0, want_dres=False), lambda n: n * 8192 * 4 + 8192 * 4))
     # calibrate: 2 rows of every op, then scale the row count to the time target
     t0 = time.perf_counter()
     for _, f, _ in plan:

@@ -116,6 +116,26 @@ mb_status_t mb_bias_dropout_add_infer(const void* x, const void* bias, const voi
                                       mb_dtype_t residual_dt, void* out, int64_t tokens,
                                       int64_t hidden, mb_dtype_t dt, hipStream_t s);
 
+/* Bytes of workspace mb_bias_dropout_add_bwd needs for the bias gradient
+ * (0 when with_dbias = 0 or tokens = 0). */
+size_t mb_bias_dropout_add_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias);
+
+/* Backward of mb_bias_dropout_add_train for the same (p, seed, offset): with
+ * g = d loss / d out [T,H] (dtype dt),
+ *   dx[t, j]        = g * s where the element was kept, 0 where dropped
+ *                     (the keep decisions are regenerated, nothing is stored);
+ *   dresidual[t, j] = g in the residual's dtype residual_dt (dt or MB_F32):
+ *                     the cast of the residual passes the gradient through;
+ *                     NULL skips it (with residual_dt == dt it equals g);
+ *   dbias[j]        = sum over rows of the fp32 dx[:, j] (NULL: skip; the bias
+ *                     gradient equals that of x summed over tokens [fusions §4.3]).
+ * dx may equal g (in place); dresidual may equal g only when residual_dt == dt.
+ * The reduction is deterministic and atomic-free (second launch over partials
+ * in ws, ws_bytes >= mb_bias_dropout_add_bwd_workspace(...)). Needs p in [0, 1]. */
+mb_status_t mb_bias_dropout_add_bwd(const void* g, void* dx, void* dresidual, mb_dtype_t residual_dt,
+                                    float* dbias, void* ws, size_t ws_bytes, int64_t tokens, int64_t hidden,
+                                    mb_dtype_t dt, float p, uint64_t seed, uint64_t offset, hipStream_t s);
+
 /* The keep decisions mb_bias_dropout_add_train makes for (T, H, p, seed,
  * offset), as bits: bit (i mod 8) of byte i/8 is element i = t*H + j
  * (1 = kept). bits holds ceil(T*H/8) bytes; unused high bits of the last byte

@@ -215,3 +215,36 @@ def test_layer_chain_t16384_h8192_f32768():
     dg2, dbias2 = mb.mb_bias_gelu_bwd(g, y, b)
     assert torch.equal(dg.view(torch.int16), dg2.view(torch.int16))
     assert torch.equal(dbias.view(torch.int32), dbias2.view(torch.int32))
+
+
+# ------------------------------------------------------------------ dropout-add backward at full size
+
+@pytest.mark.parametrize("wname,pre,rdt", [("bda_bf16_8192x4096_res_f32", "", "f32"),
+                                           ("layer_chain_bf16_t16384_h8192_f32768", "mlp_", "bf16")])
+def test_bda_bwd_full(wname, pre, rdt):
+    w = WORKLOADS[wname]
+    # an upstream gradient of the activation's shape and dtype (its rows reversed)
+    g = load(w.name, pre + "x").flip(0).contiguous()
+    p = w.params["p"]
+    seed = w.params.get("seed", w.params.get("mlp_seed"))
+    off = w.params["offset"]
+    T, H = g.shape
+    rt = torch.float32 if rdt == "f32" else torch.bfloat16
+    dx, dres, db = mb.mb_bias_dropout_add_bwd(g, p, seed, off, residual_dtype=rt)
+    gs = st(g.cpu())
+    for r0, n in row_blocks(T):
+        odx, odx64, odres, _ = oracle.bias_dropout_add_bwd("bf16", gs[r0:r0 + n], rdt, p, seed, off, row0=r0)
+        assert_close(st(dx[r0:r0 + n]), odx, odx64, None, "bf16", f"bda bwd {wname} rows {r0}")
+        assert np.array_equal(st(dres[r0:r0 + n]), odres)
+    # the oracle over the whole tensor for the bias gradient (a column's mask
+    # depends on its global element indices)
+    _, _, _, odb = oracle.bias_dropout_add_bwd("bf16", gs, rdt, p, seed, off, want_dres=False)
+    say(f"bda bwd {wname} dbias (all columns): {assert_reduction_close(db.cpu().numpy(), odb, 'bda bwd dbias')}")
+    err = (db.double() - dx.double().sum(0)).abs()
+    bound = dbias_noise_bound(dx)
+    assert bool((err <= bound).all()), f"bda bwd dbias vs column sums, worst {float((err / bound).max()):.2f}"
+    bits = np.unpackbits(mb.mb_dropout_mask(T, H, p, seed, off).cpu().numpy(), bitorder="little")[:T * H]
+    assert np.array_equal(bits, np.unpackbits(oracle.dropout_mask(T, H, p, seed, off), bitorder="little")[:T * H])
+    dropped = torch.from_numpy(bits.reshape(T, H) == 0).to(DEV)
+    assert torch.count_nonzero(dx[dropped]).item() == 0
+    say(f"bda bwd {wname}: rows, dresidual, dbias property and mask consistency ok")

@@ -325,3 +325,56 @@ def test_errors_on_device_tensors():
         mb.mb_bias_swiglu_fwd(x, out=x.view(-1)[:192].view(8, 24))  # output overlaps the input
     with pytest.raises(mb.MBError, match="MB_ERR_WORKSPACE"):
         mb.mb_bias_gelu_bwd(y, y, None, ws=torch.zeros(4, dtype=torch.uint8, device=DEV))
+
+
+# ------------------------------------------------------------------ dropout-add backward
+
+@pytest.mark.parametrize("dt,rdt", BDA_TYPES)
+@pytest.mark.parametrize("p,offset", [(0.1, 0), (0.5, 7), (0.0, 0), (1.0, 0), (0.3, 2**33 + 5)])
+def test_bda_bwd(dt, rdt, p, offset):
+    T, H = (1000, 1576) if dt != "f32" else (777, 1028)
+    g = gen(111, (T, H), dt)
+    seed = 4321
+    dx, dres, dbias = mb.mb_bias_dropout_add_bwd(g.to(DEV), p, seed, offset, residual_dtype=TD[rdt])
+    odx, odx64, odres, odb = oracle.bias_dropout_add_bwd(dt, st(g), rdt, p, seed, offset)
+    log(f"bda_bwd {dt}/{rdt} p={p}", assert_close(st(dx), odx, odx64, None, dt, "bda bwd dx"))
+    assert np.array_equal(st(dres), odres), "dresidual must be g in the residual dtype, bit for bit"
+    log(f"bda_bwd dbias {dt}", assert_reduction_close(dbias.cpu().numpy(), odb, "bda bwd dbias"))
+    bits = np.unpackbits(mb.mb_dropout_mask(T, H, p, seed, offset).cpu().numpy(), bitorder="little")[:T * H]
+    dropped = torch.from_numpy(bits.reshape(T, H) == 0)
+    assert torch.count_nonzero(dx.cpu()[dropped]).item() == 0
+
+
+def test_bda_bwd_matches_forward_mask_in_place_and_deterministic():
+    T, H, p, seed, off = 640, 2048, 0.1, 99, 3
+    x = gen(121, (T, H), "bf16").to(DEV)
+    r = gen(122, (T, H), "f32").to(DEV)
+    g = gen(123, (T, H), "bf16").to(DEV)
+    out = mb.mb_bias_dropout_add_train(x, None, r, p, seed, off)
+    dx, dres, db = mb.mb_bias_dropout_add_bwd(g, p, seed, off, residual_dtype=torch.float32)
+    # the forward's keep decisions (mask export) decide where dx is g*s and where 0;
+    # a dropped element of the forward is exactly the cast residual
+    bits = np.unpackbits(mb.mb_dropout_mask(T, H, p, seed, off).cpu().numpy(), bitorder="little")[:T * H]
+    keep = torch.from_numpy(bits.reshape(T, H) == 1).to(DEV)
+    assert torch.count_nonzero(dx[~keep]).item() == 0
+    assert torch.equal((dx[keep] != 0), (g[keep] != 0))
+    assert torch.equal(out.float()[~keep], r.to(torch.bfloat16).float()[~keep])
+    dx2, dres2, db2 = mb.mb_bias_dropout_add_bwd(g, p, seed, off, residual_dtype=torch.float32)
+    assert torch.equal(dx.view(torch.int16), dx2.view(torch.int16))
+    assert torch.equal(db.view(torch.int32), db2.view(torch.int32))
+    g2 = g.clone()
+    dx3, _, db3 = mb.mb_bias_dropout_add_bwd(g2, p, seed, off, residual_dtype=torch.float32, dx=g2, dresidual=False)
+    assert dx3.data_ptr() == g2.data_ptr()
+    assert torch.equal(dx.view(torch.int16), g2.view(torch.int16))
+    assert torch.equal(db.view(torch.int32), db3.view(torch.int32))
+
+
+def test_bda_bwd_empty_and_errors():
+    g = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    dx, dres, db = mb.mb_bias_dropout_add_bwd(g, 0.1, 1)
+    assert db.shape == (64,) and torch.count_nonzero(db).item() == 0
+    g = torch.zeros((8, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(mb.MBError, match="MB_ERR_PROB"):
+        mb.mb_bias_dropout_add_bwd(g, 1.5, 1)
+    with pytest.raises(mb.MBError, match="MB_ERR_ALIAS"):
+        mb.mb_bias_dropout_add_bwd(g, 0.1, 1, dx=g, dresidual=g)  # two outputs on one buffer

@@ -19,6 +19,7 @@ __all__ = [
     "MBError", "lib", "abi_version",
     "mb_bias_gelu_fwd", "mb_bias_gelu_bwd", "mb_bias_gelu_bwd_workspace",
     "mb_bias_dropout_add_train", "mb_bias_dropout_add_infer", "mb_dropout_mask",
+    "mb_bias_dropout_add_bwd", "mb_bias_dropout_add_bwd_workspace",
     "mb_bias_swiglu_fwd", "mb_bias_swiglu_bwd", "mb_bias_geglu_fwd", "mb_bias_geglu_bwd",
     "mb_bias_glu_bwd_workspace",
 ]
@@ -58,6 +59,8 @@ def lib() -> ctypes.CDLL:
                 "mb_bias_dropout_add_train": ([P, P, P, I, P, I64, I64, I, F, U64, U64, P], I),
                 "mb_bias_dropout_add_infer": ([P, P, P, I, P, I64, I64, I, P], I),
                 "mb_dropout_mask": ([P, I64, I64, F, U64, U64, P], I),
+                "mb_bias_dropout_add_bwd_workspace": ([I64, I64, I, I], SZ),
+                "mb_bias_dropout_add_bwd": ([P, P, P, I, P, P, SZ, I64, I64, I, F, U64, U64, P], I),
                 "mb_bias_swiglu_fwd": ([P, P, P, I, P, I64, I64, I, P], I),
                 "mb_bias_geglu_fwd": ([P, P, P, I64, I64, I, P], I),
                 "mb_bias_glu_bwd_workspace": ([I64, I64, I, I, I], SZ),
@@ -169,6 +172,31 @@ def mb_bias_dropout_add_infer(x, bias, residual, out=None, stream=None):
     _check("mb_bias_dropout_add_infer", lib().mb_bias_dropout_add_infer(
         _p(x), _p(bias), _p(residual), _dt(residual), _p(out), T, H, _dt(x), _stream(x, stream)))
     return out
+
+
+def mb_bias_dropout_add_bwd_workspace(tokens, hidden, dtype, with_dbias=True) -> int:
+    return int(lib().mb_bias_dropout_add_bwd_workspace(tokens, hidden, DTYPES[dtype], int(bool(with_dbias))))
+
+
+def mb_bias_dropout_add_bwd(g, p, seed, offset=0, residual_dtype=None, dx=None, dresidual=True, dbias=True,
+                            ws=None, stream=None):
+    """Returns (dx, dresidual or None, dbias or None) for the train forward with (p, seed, offset).
+    residual_dtype defaults to g's dtype; dresidual=True allocates it, False skips it."""
+    T, H = _rows(g, "g")
+    rdt = residual_dtype or g.dtype
+    dx = torch.empty_like(g) if dx is None else dx
+    if dresidual is True:
+        dresidual = torch.empty((T, H), dtype=rdt, device=g.device)
+    elif dresidual is False:
+        dresidual = None
+    dbias = _grad_out(dbias, H, g.device)
+    nws = mb_bias_dropout_add_bwd_workspace(T, H, g.dtype, dbias is not None)
+    if ws is None and nws:
+        ws = torch.empty(nws, dtype=torch.uint8, device=g.device)
+    _check("mb_bias_dropout_add_bwd", lib().mb_bias_dropout_add_bwd(
+        _p(g), _p(dx), _p(dresidual), DTYPES[rdt], _p(dbias), _p(ws), ws.numel() if ws is not None else 0, T, H,
+        _dt(g), float(p), int(seed), int(offset), _stream(g, stream)))
+    return dx, dresidual, dbias
 
 
 def mb_dropout_mask(tokens, hidden, p, seed, offset=0, device="cuda", out=None, stream=None):

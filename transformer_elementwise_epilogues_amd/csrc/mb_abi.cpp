@@ -200,7 +200,8 @@ static mb_status_t bda_common(const void* x, const void* bias, const void* resid
   if (!aliasing_ok({{out, tb}}, {{x, tb}, {residual, rb}, {bias, bias ? bb : 0}}, {{0, 0}, {0, 1}}))
     return MB_ERR_ALIAS;
   if (tokens == 0) return MB_OK;
-  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_BDA_BLOCKS);
+  const int lanes = static_cast<int>(hidden / mb::bda_elems_per_lane(dt, residual_dt));
+  const mb::Tiling t = mb::plan_tiling(tokens, lanes, MB_BDA_BLOCKS);
   const mb::DropoutArgs d = train ? dropout_args(p, seed, offset) : mb::DropoutArgs{};
   if (hipError_t e = mb::launch_bda(dt, residual_dt, train, x, bias, residual, out, hidden, t, d, s))
     return hip_status(e);
@@ -216,6 +217,57 @@ mb_status_t mb_bias_dropout_add_train(const void* x, const void* bias, const voi
 mb_status_t mb_bias_dropout_add_infer(const void* x, const void* bias, const void* residual, mb_dtype_t residual_dt,
                                       void* out, int64_t tokens, int64_t hidden, mb_dtype_t dt, hipStream_t s) {
   return bda_common(x, bias, residual, residual_dt, out, tokens, hidden, dt, false, 0.0f, 0, 0, s);
+}
+
+// Row groups of the dropout-add backward. The lane count depends on the
+// residual dtype; the workspace is sized for the wider lanes (fewer strips,
+// so more row groups), which covers both.
+static mb::Tiling bda_bwd_tiling(int64_t tokens, int64_t hidden, mb_dtype_t dt, mb_dtype_t residual_dt) {
+  const int lanes = static_cast<int>(hidden / mb::bda_elems_per_lane(dt, residual_dt));
+  return mb::plan_tiling(tokens, lanes, MB_BDA_BWD_BLOCKS);
+}
+
+size_t mb_bias_dropout_add_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias) {
+  if (!with_dbias || !dt_ok(dt) || check_shape(tokens, hidden, dt) != MB_OK || tokens == 0) return 0;
+  return col_partials_bytes(bda_bwd_tiling(tokens, hidden, dt, dt), hidden);
+}
+
+mb_status_t mb_bias_dropout_add_bwd(const void* g, void* dx, void* dresidual, mb_dtype_t residual_dt, float* dbias,
+                                    void* ws, size_t ws_bytes, int64_t tokens, int64_t hidden, mb_dtype_t dt,
+                                    float p, uint64_t seed, uint64_t offset, hipStream_t s) {
+  if (!dt_ok(dt) || !dt_ok(residual_dt)) return MB_ERR_DTYPE;
+  if (residual_dt != dt && residual_dt != MB_F32) return MB_ERR_DTYPE;
+  if (mb_status_t st = check_shape(tokens, hidden, dt)) return st;
+  if (!prob_ok(p)) return MB_ERR_PROB;
+  const size_t tb = static_cast<size_t>(tokens) * hidden * esize(dt);
+  const size_t rb = static_cast<size_t>(tokens) * hidden * esize(residual_dt);
+  if (!need(g, tb) || !need(dx, tb)) return MB_ERR_NULL;
+  const size_t need_ws = mb_bias_dropout_add_bwd_workspace(tokens, hidden, dt, dbias != nullptr);
+  if (!aligned(g, 16) || !aligned(dx, 16) || !aligned(dresidual, 16) || !aligned(dbias, 4) ||
+      (need_ws && !aligned(ws, 16)))
+    return MB_ERR_ALIGN;
+  if (need_ws && (!ws || ws_bytes < need_ws)) return MB_ERR_WORKSPACE;
+  const Buf wsb{need_ws ? ws : nullptr, need_ws};
+  const Buf resb{dresidual, dresidual ? rb : 0};
+  const Buf dbb{dbias, dbias ? static_cast<size_t>(hidden) * 4 : 0};
+  if (residual_dt == dt) {
+    if (!aliasing_ok({{dx, tb}, resb, dbb, wsb}, {{g, tb}}, {{0, 0}, {1, 0}})) return MB_ERR_ALIAS;
+  } else {
+    if (!aliasing_ok({{dx, tb}, resb, dbb, wsb}, {{g, tb}}, {{0, 0}})) return MB_ERR_ALIAS;
+  }
+  if (tokens == 0) {
+    if (!dbias) return MB_OK;
+    if (hipError_t e = mb::launch_fill_zero(dbias, hidden, s)) return hip_status(e);
+    return finish();
+  }
+  const mb::Tiling t = bda_bwd_tiling(tokens, hidden, dt, residual_dt);
+  float* partials = dbias ? static_cast<float*>(ws) : nullptr;
+  if (hipError_t e = mb::launch_bda_bwd(dt, residual_dt, g, dx, dresidual, partials, hidden, t,
+                                        dropout_args(p, seed, offset), s))
+    return hip_status(e);
+  if (dbias)
+    if (hipError_t e = reduce_columns(partials, t, hidden, dbias, s)) return hip_status(e);
+  return finish();
 }
 
 mb_status_t mb_dropout_mask(uint8_t* bits, int64_t tokens, int64_t hidden, float p, uint64_t seed, uint64_t offset,

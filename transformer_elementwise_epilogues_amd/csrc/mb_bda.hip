@@ -1,5 +1,5 @@
-// mb_bda.hip -- bias + dropout + residual add (train and inference) and the
-// keep-mask export.
+// mb_bda.hip -- bias + dropout + residual add (train, inference, backward) and
+// the keep-mask export.
 //
 // Method: Megatron-LM's _bias_dropout_add_func as described by the wmrh.cn
 // article on megatron/core/fusions, section 3.2 (one fused branch; the
@@ -7,11 +7,18 @@
 // (separate train and inference entry points).
 //
 // The keep decision of element i = t*H + j comes from Philox4x32-10 with
-// counter (i/4, offset) and key seed: the 8 (bf16/fp16) or 4 (fp32) elements
-// of a lane's 16-byte vector are exactly 2 or 1 Philox blocks, so no random
-// word is wasted and the mask does not depend on the launch shape. The
-// residual cast is done in registers (an fp32 residual is read once, never
-// materialised in x's dtype).
+// counter (i/4, offset) and key seed: a lane's 4 or 8 elements are exactly 1 or
+// 2 Philox blocks, so no random word is wasted and the mask does not depend on
+// the launch shape. The residual cast is done in registers (an fp32 residual
+// is read once, never materialised in x's dtype).
+//
+// Elements per lane (EPL): 8 for bf16/fp16 (one 16-byte vector), 4 for fp32,
+// and 4 when an fp32 residual (or residual gradient) sits beside bf16/fp16
+// activations. With 4, the activations move in 8-byte and the residual in
+// 16-byte pieces, so every load and store instruction of a wave covers one
+// contiguous 512 B / 1 KiB span. (With 8 elements per lane the fp32 tensor
+// would be stored 16 B per lane at a 32 B stride: half-line non-temporal
+// stores, measured at under 3 TB/s.)
 #include "mb_device.hpp"
 #include "mb_launch.hpp"
 
@@ -21,78 +28,122 @@ namespace {
 
 constexpr int kUnroll = MB_BDA_UNROLL;
 
-template <DT D, DT R, bool TRAIN>
-__device__ __forceinline__ u32x4 bda_vec(u32x4 xv, const u32x4* rv, const float* b, uint64_t i0,
-                                         const DropoutArgs& d) {
-  constexpr int V = Vec<D>::N;
-  constexpr int RPER = Vec<R>::N;
-  float x[V], r[V];
-  unpack<D>(xv, x);
-#pragma unroll
-  for (int q = 0; q < V / RPER; ++q) unpack<R>(rv[q], r + q * RPER);
-  bool keep[V];
-  if constexpr (TRAIN) {
-#pragma unroll
-    for (int q = 0; q < V / 4; ++q) keep4((i0 >> 2) + q, d.o0, d.o1, d.k0, d.k1, d.theta, keep + 4 * q);
-  }
-#pragma unroll
-  for (int k = 0; k < V; ++k) {
-    const float rp = (R == D) ? r[k] : round_to<D>(r[k]);
-    const float z = x[k] + b[k];
-    if constexpr (TRAIN)
-      x[k] = __builtin_fmaf(keep[k] ? z : 0.0f, d.scale, rp);
-    else
-      x[k] = rp + z;
-  }
-  return pack<D>(x);
+template <DT D, DT R>
+constexpr int epl() {
+  return (R == DT::F32 && D != DT::F32) ? 4 : Vec<D>::N;
 }
 
+// Keep flags of N consecutive elements starting at i0 (a multiple of 4).
+template <int N>
+__device__ __forceinline__ void keep_n(uint64_t i0, const DropoutArgs& d, bool* keep) {
+#pragma unroll
+  for (int q = 0; q < N / 4; ++q) keep4((i0 >> 2) + q, d.o0, d.o1, d.k0, d.k1, d.theta, keep + 4 * q);
+}
+
+// Forward. The U rows' loads are issued before any of their stores.
 template <DT D, DT R, bool TRAIN, int U>
 __global__ __launch_bounds__(kThreads) void bda_kernel(const char* x, const char* bias, const char* res, char* out,
-                                                       int64_t T, int nvec, int64_t H, DropoutArgs d) {
-  constexpr int V = Vec<D>::N;
-  constexpr int RV = V / Vec<R>::N;  // 16-byte residual vectors per group
+                                                       int64_t T, int lanes, int64_t H, DropoutArgs d) {
+  constexpr int N = epl<D, R>();
+  constexpr int XB = N * Vec<D>::BYTES, RB = N * Vec<R>::BYTES;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const TileIdx ti = tile_idx();
   const int cv = ti.strip * kStrip + lane;
-  if (cv >= nvec) return;
-  float b[V];
+  if (cv >= lanes) return;
+  float b[N];
   if (bias) {
-    unpack<D>(ld_keep(bias + static_cast<size_t>(cv) * 16), b);
+    ld_elems<D, N>(bias + static_cast<size_t>(cv) * XB, b);
   } else {
 #pragma unroll
-    for (int k = 0; k < V; ++k) b[k] = 0.0f;
+    for (int k = 0; k < N; ++k) b[k] = 0.0f;
   }
-  const size_t px = static_cast<size_t>(nvec) * 16;
-  const size_t pr = px * RV;
+  const size_t px = static_cast<size_t>(lanes) * XB, pr = static_cast<size_t>(lanes) * RB;
   const int64_t S = static_cast<int64_t>(ti.G) * kWaves;
-  const char* xp = x + static_cast<size_t>(cv) * 16;
-  const char* rp = res + static_cast<size_t>(cv) * 16 * RV;
-  char* op = out + static_cast<size_t>(cv) * 16;
-  const uint64_t j0 = static_cast<uint64_t>(cv) * V;
+  const char* xp = x + static_cast<size_t>(cv) * XB;
+  const char* rp = res + static_cast<size_t>(cv) * RB;
+  char* op = out + static_cast<size_t>(cv) * XB;
+  const uint64_t j0 = static_cast<uint64_t>(cv) * N;
   int64_t t = static_cast<int64_t>(ti.rg) * kWaves + wave;
-  for (; t + (U - 1) * S < T; t += U * S) {
-    u32x4 xv[U], rv[U][RV];
+  for (; t < T; t += U * S) {
+    // rows t, t+S, ... (at most U of them); the loads of all of them first
+    float xv[U][N], rv[U][N];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (t + u * S < T) {
+        ld_elems<D, N>(xp + (t + u * S) * px, xv[u]);
+        ld_elems<R, N>(rp + (t + u * S) * pr, rv[u]);
+      }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      xv[u] = ld_stream(xp + (t + u * S) * px);
+      const int64_t tt = t + u * S;
+      if (tt >= T) break;
+      bool keep[N];
+      if constexpr (TRAIN) keep_n<N>(static_cast<uint64_t>(tt) * static_cast<uint64_t>(H) + j0, d, keep);
+      float o[N];
 #pragma unroll
-      for (int q = 0; q < RV; ++q) rv[u][q] = ld_stream(rp + (t + u * S) * pr + 16 * q);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint64_t i0 = static_cast<uint64_t>(t + u * S) * static_cast<uint64_t>(H) + j0;
-      st_stream(op + (t + u * S) * px, bda_vec<D, R, TRAIN>(xv[u], rv[u], b, i0, d));
+      for (int k = 0; k < N; ++k) {
+        const float r2 = (R == D) ? rv[u][k] : round_to<D>(rv[u][k]);
+        const float z = xv[u][k] + b[k];
+        if constexpr (TRAIN)
+          o[k] = __builtin_fmaf(keep[k] ? z : 0.0f, d.scale, r2);
+        else
+          o[k] = r2 + z;
+      }
+      st_elems<D, N>(op + tt * px, o);
     }
   }
-  for (; t < T; t += S) {
-    u32x4 xv = ld_stream(xp + t * px), rv[RV];
+}
+
+// Backward: dx = keep ? g * s : 0 with the keep decisions regenerated from
+// (seed, offset, element index); dresidual = g in the residual's dtype; the
+// fp32 dx values are summed per column into one partial row per row group.
+template <DT D, DT R, int U, bool DBIAS, bool DRES>
+__global__ __launch_bounds__(kThreads) void bda_bwd_kernel(const char* g, char* dx, char* dres, float* partials,
+                                                           int64_t T, int lanes, int64_t H, DropoutArgs d) {
+  // the lane layout depends on the dtypes only, so dx and dbias come out bit
+  // for bit the same whether or not the residual gradient is requested
+  constexpr int N = epl<D, R>();
+  constexpr int XB = N * Vec<D>::BYTES, RB = N * Vec<R>::BYTES;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const TileIdx ti = tile_idx();
+  const int cv = ti.strip * kStrip + lane;
+  const bool active = cv < lanes;
+  float acc[N];
 #pragma unroll
-    for (int q = 0; q < RV; ++q) rv[q] = ld_stream(rp + t * pr + 16 * q);
-    const uint64_t i0 = static_cast<uint64_t>(t) * static_cast<uint64_t>(H) + j0;
-    st_stream(op + t * px, bda_vec<D, R, TRAIN>(xv, rv, b, i0, d));
+  for (int k = 0; k < N; ++k) acc[k] = 0.0f;
+  if (active) {
+    const size_t px = static_cast<size_t>(lanes) * XB, pr = static_cast<size_t>(lanes) * RB;
+    const size_t cx = static_cast<size_t>(cv) * XB, cr = static_cast<size_t>(cv) * RB;
+    const int64_t S = static_cast<int64_t>(ti.G) * kWaves;
+    const uint64_t j0 = static_cast<uint64_t>(cv) * N;
+    int64_t t = static_cast<int64_t>(ti.rg) * kWaves + wave;
+    for (; t < T; t += U * S) {
+      float gv[U][N];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (t + u * S < T) ld_elems<D, N>(g + (t + u * S) * px + cx, gv[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t tt = t + u * S;
+        if (tt >= T) break;
+        if constexpr (DRES) st_elems<R, N>(dres + tt * pr + cr, gv[u]);  // exact: g widened or copied
+        bool keep[N];
+        keep_n<N>(static_cast<uint64_t>(tt) * static_cast<uint64_t>(H) + j0, d, keep);
+        float f[N];
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+          f[k] = keep[k] ? gv[u][k] * d.scale : 0.0f;
+          acc[k] += f[k];
+        }
+        st_elems<D, N>(dx + tt * px + cx, f);
+      }
+    }
   }
+  if constexpr (DBIAS)
+    block_column_partials<N>(acc, wave, lane, active,
+                             partials + static_cast<size_t>(ti.rg) * lanes * N + static_cast<size_t>(cv) * N);
 }
 
 // One byte (8 elements) per thread; n is a multiple of 4.
@@ -125,7 +176,42 @@ hipError_t bda_dispatch(bool train, const void* x, const void* bias, const void*
   return hipGetLastError();
 }
 
+template <DT D, DT R>
+hipError_t bda_bwd_dispatch(const void* g, void* dx, void* dres, float* partials, int64_t H, const Tiling& t,
+                            const DropoutArgs& d, hipStream_t s) {
+  const dim3 grid = tile_grid(t.strips, t.G);
+  auto gp = static_cast<const char*>(g);
+  auto xp = static_cast<char*>(dx);
+  auto rp = static_cast<char*>(dres);
+  constexpr int U = MB_BDA_BWD_UNROLL;
+  if (partials && dres)
+    hipLaunchKernelGGL((bda_bwd_kernel<D, R, U, true, true>), grid, dim3(kThreads), 0, s, gp, xp, rp, partials, t.T, t.nvec, H, d);
+  else if (partials)
+    hipLaunchKernelGGL((bda_bwd_kernel<D, R, U, true, false>), grid, dim3(kThreads), 0, s, gp, xp, rp, partials, t.T, t.nvec, H, d);
+  else if (dres)
+    hipLaunchKernelGGL((bda_bwd_kernel<D, R, U, false, true>), grid, dim3(kThreads), 0, s, gp, xp, rp, partials, t.T, t.nvec, H, d);
+  else
+    hipLaunchKernelGGL((bda_bwd_kernel<D, R, U, false, false>), grid, dim3(kThreads), 0, s, gp, xp, rp, partials, t.T, t.nvec, H, d);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+int bda_elems_per_lane(int dt, int res_dt) {
+  if (static_cast<DT>(dt) == DT::F32) return 4;
+  return static_cast<DT>(res_dt) == DT::F32 ? 4 : 8;
+}
+
+hipError_t launch_bda_bwd(int dt, int res_dt, const void* g, void* dx, void* dres, float* partials, int64_t H,
+                          const Tiling& t, const DropoutArgs& d, hipStream_t s) {
+  const DT D = static_cast<DT>(dt), R = static_cast<DT>(res_dt);
+  if (D == DT::F32 && R == DT::F32) return bda_bwd_dispatch<DT::F32, DT::F32>(g, dx, dres, partials, H, t, d, s);
+  if (D == DT::BF16 && R == DT::BF16) return bda_bwd_dispatch<DT::BF16, DT::BF16>(g, dx, dres, partials, H, t, d, s);
+  if (D == DT::BF16 && R == DT::F32) return bda_bwd_dispatch<DT::BF16, DT::F32>(g, dx, dres, partials, H, t, d, s);
+  if (D == DT::F16 && R == DT::F16) return bda_bwd_dispatch<DT::F16, DT::F16>(g, dx, dres, partials, H, t, d, s);
+  if (D == DT::F16 && R == DT::F32) return bda_bwd_dispatch<DT::F16, DT::F32>(g, dx, dres, partials, H, t, d, s);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_bda(int dt, int res_dt, bool train, const void* x, const void* bias, const void* residual,
                       void* out, int64_t H, const Tiling& t, const DropoutArgs& d, hipStream_t s) {

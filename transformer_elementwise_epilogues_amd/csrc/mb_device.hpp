@@ -13,6 +13,7 @@
 namespace mb {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -138,15 +139,36 @@ __device__ __forceinline__ void store_f32x4(float* dst, const float* s) {
   *reinterpret_cast<f32x4*>(dst) = f32x4{s[0], s[1], s[2], s[3]};
 }
 
-// Load the V = Vec<D>::N elements of a 16-byte aligned group as fp32, for a
-// tensor of storage type S that may be wider than D (an fp32 residual next to
-// bf16 activations occupies 32 bytes per group).
-template <DT S, int V> __device__ __forceinline__ void load_group(const char* p, float* f, bool stream) {
-  constexpr int per = Vec<S>::N;
+// N consecutive elements of storage type D as fp32, for groups of 8 or 16
+// bytes (4 bf16/fp16, or a full 16-byte vector). Used where a lane's element
+// count is set by a wider tensor next to this one (an fp32 residual beside
+// bf16 activations), so that every load and store instruction of the wave
+// still covers one contiguous span of memory.
+template <DT D, int N> __device__ __forceinline__ void ld_elems(const char* p, float* f) {
+  if constexpr (N * Vec<D>::BYTES == 16) {
+    unpack<D>(ld_stream(p), f);
+  } else {
+    static_assert(N == 4 && Vec<D>::BYTES == 2, "8-byte groups hold 4 bf16/fp16 values");
+    u32x2 v;
+    if constexpr (MB_NT_LOAD) v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    else v = *reinterpret_cast<const u32x2*>(p);
+    const u32x4 w = {v.x, v.y, 0u, 0u};
+    float t[8];
+    unpack<D>(w, t);
 #pragma unroll
-  for (int q = 0; q < V / per; ++q) {
-    u32x4 v = stream ? ld_stream(p + 16 * q) : ld_keep(p + 16 * q);
-    unpack<S>(v, f + q * per);
+    for (int k = 0; k < 4; ++k) f[k] = t[k];
+  }
+}
+template <DT D, int N> __device__ __forceinline__ void st_elems(char* p, const float* f) {
+  if constexpr (N * Vec<D>::BYTES == 16) {
+    st_stream(p, pack<D>(f));
+  } else {
+    static_assert(N == 4 && Vec<D>::BYTES == 2, "8-byte groups hold 4 bf16/fp16 values");
+    const unsigned w0 = D == DT::BF16 ? pk_bf16(f[0], f[1]) : pk_f16(f[0], f[1]);
+    const unsigned w1 = D == DT::BF16 ? pk_bf16(f[2], f[3]) : pk_f16(f[2], f[3]);
+    const u32x2 v = {w0, w1};
+    if constexpr (MB_NT_STORE) __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+    else *reinterpret_cast<u32x2*>(p) = v;
   }
 }
 
@@ -304,6 +326,25 @@ __device__ __forceinline__ float silu_fwd(float a, float* sc) {
 }
 
 // ---------------------------------------------------------------- reductions
+
+// Combine the 4 waves' per-lane column sums of one block in LDS, in a fixed
+// order, and write them as one partial row: dst[0 .. N) for this lane's
+// columns (dst already offset to the block's row group and the lane's
+// columns; 16-byte aligned). Every thread of the block must call it.
+template <int N>
+__device__ __forceinline__ void block_column_partials(const float* acc, int wave, int lane, bool active, float* dst) {
+  __shared__ float red[kWaves][N][64];
+#pragma unroll
+  for (int k = 0; k < N; ++k) red[wave][k][lane] = acc[k];
+  __syncthreads();
+  if (wave == 0 && active) {
+    float sum[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) sum[k] = ((red[0][k][lane] + red[1][k][lane]) + red[2][k][lane]) + red[3][k][lane];
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) store_f32x4(dst + 4 * q, sum + 4 * q);
+  }
+}
 
 // Sum over the 64 lanes of a wave, in a fixed butterfly order (deterministic).
 __device__ __forceinline__ float wave_sum(float v) {

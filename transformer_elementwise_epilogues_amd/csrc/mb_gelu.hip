@@ -124,20 +124,9 @@ __global__ __launch_bounds__(kThreads) void gelu_bwd_kernel(const char* g, const
       st_stream(dgrad + o, gelu_grad_vec<D>(ld_stream(g + o), ld_stream(y + o), b, acc));
     }
   }
-  if constexpr (DBIAS) {
-    __shared__ float red[kWaves][V][64];
-#pragma unroll
-    for (int k = 0; k < V; ++k) red[wave][k][lane] = acc[k];
-    __syncthreads();
-    if (wave == 0 && active) {
-      float s[V];
-#pragma unroll
-      for (int k = 0; k < V; ++k) s[k] = ((red[0][k][lane] + red[1][k][lane]) + red[2][k][lane]) + red[3][k][lane];
-      float* dst = partials + static_cast<size_t>(ti.rg) * nvec * V + static_cast<size_t>(cv) * V;
-#pragma unroll
-      for (int q = 0; q < V / 4; ++q) store_f32x4(dst + 4 * q, s + 4 * q);
-    }
-  }
+  if constexpr (DBIAS)
+    block_column_partials<V>(acc, wave, lane, active,
+                             partials + static_cast<size_t>(ti.rg) * nvec * V + static_cast<size_t>(cv) * V);
 }
 
 template <DT D>

@@ -38,7 +38,13 @@ struct Tiling {
 #define MB_BDA_BLOCKS 512
 #endif
 #ifndef MB_BDA_UNROLL
-#define MB_BDA_UNROLL 1
+#define MB_BDA_UNROLL 2
+#endif
+#ifndef MB_BDA_BWD_BLOCKS
+#define MB_BDA_BWD_BLOCKS 768
+#endif
+#ifndef MB_BDA_BWD_UNROLL
+#define MB_BDA_BWD_UNROLL 2
 #endif
 #ifndef MB_GLU_FWD_BLOCKS
 #define MB_GLU_FWD_BLOCKS 512
@@ -72,10 +78,17 @@ struct DropoutArgs {
   uint32_t k0, k1; // key = seed
   uint32_t o0, o1; // counter high words = offset
 };
+// Elements a dropout-add lane handles: 8 bf16/fp16 values, or 4 when the
+// residual (and so its gradient) is fp32 beside them, or 4 fp32 values. The
+// tiling's vectors per row are hidden / this.
+int bda_elems_per_lane(int dt, int res_dt);
 hipError_t launch_bda(int dt, int res_dt, bool train, const void* x, const void* bias,
                       const void* residual, void* out, int64_t H, const Tiling& t,
                       const DropoutArgs& d, hipStream_t s);
 hipError_t launch_dropout_mask(uint8_t* bits, int64_t n, const DropoutArgs& d, hipStream_t s);
+// dres (residual dtype res_dt) and partials ([G, H]) are optional
+hipError_t launch_bda_bwd(int dt, int res_dt, const void* g, void* dx, void* dres, float* partials, int64_t H,
+                          const Tiling& t, const DropoutArgs& d, hipStream_t s);
 
 enum Act { kSwiGLU = 0, kGEGLU = 1 };
 hipError_t launch_glu_fwd(int act, int dt, const void* in, const void* bias, const void* w,

@@ -90,6 +90,7 @@ WORKLOADS = {
         "x": Tensor(0, (8192, 4096), "bf16"),
         "bias": Tensor(1, (4096,), "bf16", sigma=0.02),
         "residual": Tensor(2, (8192, 4096), "f32"),
+        "g": Tensor(3, (8192, 4096), "bf16"),  # upstream gradient for the backward
     }, p=0.1, seed=1234, offset=0),
     "swiglu_bf16_8192x14336": _w(3, "swiglu_bf16_8192x14336", {
         "in": Tensor(0, (8192, 28672), "bf16"),
@@ -112,5 +113,7 @@ WORKLOADS = {
         "mlp_x": Tensor(6, (16384, 8192), "bf16"),
         "mlp_residual": Tensor(7, (16384, 8192), "bf16"),
         "mlp_bias": Tensor(8, (8192,), "bf16", sigma=0.02),
+        "attn_g": Tensor(9, (16384, 8192), "bf16"),  # upstream gradients of the two dropout-adds
+        "mlp_g": Tensor(10, (16384, 8192), "bf16"),
     }, p=0.1, attn_seed=5001, mlp_seed=5002, offset=0),
 }
