@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
                                     ctypes.c_float, ctypes.c_uint64)
             L.orc_bias_gelu_fwd.argtypes = [I, P, P, P, P, I64, I64]
             L.orc_bias_gelu_bwd.argtypes = [I, P, P, P, P, P, P, P, I64, I64]
+            L.orc_bias_gelu_erf_fwd.argtypes = [I, P, P, P, P, I64, I64]
+            L.orc_bias_gelu_erf_bwd.argtypes = [I, P, P, P, P, P, P, P, I64, I64]
             L.orc_bias_dropout_add.argtypes = [I, P, P, P, I, P, P, P, I64, I64, I, F, U64, U64, I64]
             L.orc_dropout_mask.argtypes = [P, I64, I64, F, U64, U64, I64]
             L.orc_bias_dropout_add_bwd.argtypes = [I, P, I, P, P, P, P, I64, I64, F, U64, U64, I64]
@@ -173,17 +175,19 @@ def keep_scale(p: float) -> float:
 
 # --- fused ops -------------------------------------------------------------
 
-def bias_gelu_fwd(dt, y, bias):
+def bias_gelu_fwd(dt, y, bias, exact=False):
+    """tanh-approximated GeLU, or the exact erf form with exact=True."""
     T, H = y.shape
     y = _check_in(y, dt, name="y")
     bias = _check_in(bias, dt, (H,), "bias")
     out = np.empty((T, H), _storage(dt))
     out64 = np.empty((T, H), np.float64)
-    _ok(lib().orc_bias_gelu_fwd(DTYPES[dt], _ptr(y), _ptr(bias), _ptr(out), _ptr(out64), T, H))
+    f = lib().orc_bias_gelu_erf_fwd if exact else lib().orc_bias_gelu_fwd
+    _ok(f(DTYPES[dt], _ptr(y), _ptr(bias), _ptr(out), _ptr(out64), T, H))
     return out, out64
 
 
-def bias_gelu_bwd(dt, g, y, bias):
+def bias_gelu_bwd(dt, g, y, bias, exact=False):
     """Returns dgrad (dt storage), dgrad64, mag64, dbias64."""
     T, H = y.shape
     y = _check_in(y, dt, name="y")
@@ -193,8 +197,8 @@ def bias_gelu_bwd(dt, g, y, bias):
     d64 = np.empty((T, H), np.float64)
     mag = np.empty((T, H), np.float64)
     dbias = np.empty((H,), np.float64)
-    _ok(lib().orc_bias_gelu_bwd(DTYPES[dt], _ptr(g), _ptr(y), _ptr(bias), _ptr(dgrad), _ptr(d64),
-                                _ptr(mag), _ptr(dbias), T, H))
+    f = lib().orc_bias_gelu_erf_bwd if exact else lib().orc_bias_gelu_bwd
+    _ok(f(DTYPES[dt], _ptr(g), _ptr(y), _ptr(bias), _ptr(dgrad), _ptr(d64), _ptr(mag), _ptr(dbias), T, H))
     return dgrad, d64, mag, dbias
 
 

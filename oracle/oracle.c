@@ -348,6 +348,49 @@ int orc_bias_gelu_bwd(int dt, const void* g, const void* y, const void* bias, vo
   return ORC_OK;
 }
 
+/* Magnitude of the larger of the two summands of orc_gelu_erf_grad. */
+static double gelu_erf_grad_mag(double z) {
+  double t1 = fabs(0.5 * erfc(-K_ERF * z));
+  double t2 = fabs(z * K_PDF * exp(-0.5 * z * z));
+  return t1 > t2 ? t1 : t2;
+}
+
+/* Exact (erf) bias-GeLU forward [fusions §4.2]: out = gelu_erf(y + bias). */
+int orc_bias_gelu_erf_fwd(int dt, const void* y, const void* bias, void* out, double* out64, int64_t T,
+                          int64_t H) {
+  if (!dtype_ok(dt) || T < 0 || H <= 0) return ORC_BAD;
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t j = 0; j < H; ++j) {
+      int64_t i = t * H + j;
+      double z = load_elem(dt, y, i) + (bias ? load_elem(dt, bias, j) : 0.0);
+      double v = orc_gelu_erf(z);
+      store_elem(dt, out, i, v);
+      if (out64) out64[i] = v;
+    }
+  return ORC_OK;
+}
+
+/* Exact (erf) bias-GeLU backward: dgrad = g * gelu_erf'(y + bias), dbias as for
+ * the tanh form; mag = |g| times the larger summand of gelu_erf'. */
+int orc_bias_gelu_erf_bwd(int dt, const void* g, const void* y, const void* bias, void* dgrad,
+                          double* dgrad64, double* mag, double* dbias, int64_t T, int64_t H) {
+  if (!dtype_ok(dt) || T < 0 || H <= 0) return ORC_BAD;
+  if (dbias)
+    for (int64_t j = 0; j < H; ++j) dbias[j] = 0.0;
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t j = 0; j < H; ++j) {
+      int64_t i = t * H + j;
+      double z = load_elem(dt, y, i) + (bias ? load_elem(dt, bias, j) : 0.0);
+      double gv = load_elem(dt, g, i);
+      double v = gv * orc_gelu_erf_grad(z);
+      store_elem(dt, dgrad, i, v);
+      if (dgrad64) dgrad64[i] = v;
+      if (mag) mag[i] = fabs(gv) * gelu_erf_grad_mag(z);
+      if (dbias) dbias[j] += v;
+    }
+  return ORC_OK;
+}
+
 /* Bias-dropout-add [fusions §3.2, §3.3].
  *   r' = residual rounded to dt when its dtype differs (the AMP-O1 cast);
  *   z  = x + bias;

@@ -350,3 +350,44 @@ def test_bda_bwd_p0_is_identity_and_p1_is_zero():
     assert np.array_equal(dx, g) and np.array_equal(dres, g)
     dx1, d641, _, db1 = oracle.bias_dropout_add_bwd("bf16", g, "bf16", 1.0, 1, 0)
     assert np.all(d641 == 0.0) and np.all(db1 == 0.0)
+
+
+# ---------------------------------------------------------------- exact (erf) GeLU ops
+
+def test_gelu_erf_fwd_matches_torch_broadcast():
+    r = rng(22)
+    y = r.standard_normal((48, 72)).astype(np.float32) * 3
+    b = (r.standard_normal(72) * 0.5).astype(np.float32)
+    out, out64 = oracle.bias_gelu_fwd("f32", y, b, exact=True)
+    z = torch.from_numpy(y).double() + torch.from_numpy(b).double()
+    ref = F.gelu(z, approximate="none").numpy()
+    # 0.70710678 vs 1/sqrt(2): 1.7e-9 relative in the argument, magnified ~z^2 in the tail
+    tol = 2e-9 * (z.numpy() ** 2 + 2)
+    assert np.all(np.abs(out64 - ref) <= tol * np.abs(ref) + 1e-15)
+    assert np.array_equal(out, out64.astype(np.float32))
+
+
+def test_gelu_erf_bwd_brute_force_jacobian_4x8():
+    r = rng(23)
+    y = r.standard_normal((4, 8)) * 2
+    b = r.standard_normal(8) * 0.3
+    g = r.standard_normal((4, 8))
+    _, d64, mag, db64 = oracle.bias_gelu_bwd("f64", g, y, b, exact=True)
+
+    def loss():
+        _, o = oracle.bias_gelu_fwd("f64", y, b, exact=True)
+        return float(np.sum(g * o))
+
+    # the printed 0.3989423 and 0.70710678 agree to ~5e-8 (see the scalar pins)
+    assert np.all(np.abs(d64 - _fd_grad(loss, y)) <= 1e-7 * np.abs(d64) + 5e-8)
+    assert np.all(np.abs(db64 - _fd_grad(loss, b)) <= 1e-7 * np.abs(db64) + 5e-7)
+    assert np.all(mag * 2 >= np.abs(d64))
+
+
+def test_gelu_erf_differs_from_tanh_by_at_most_1e3():
+    r = rng(24)
+    y = (r.standard_normal((16, 64)) * 2).astype(np.float32)
+    _, a = oracle.bias_gelu_fwd("f32", y, None)
+    _, e = oracle.bias_gelu_fwd("f32", y, None, exact=True)
+    d = np.abs(a - e)
+    assert d.max() <= 1e-3 and d.max() > 1e-5
