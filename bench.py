@@ -15,6 +15,10 @@ Inputs are resident in HBM before timing starts. `value` is the algorithmic
 bytes of a step (each tensor read or written once, bias and gradients of the
 bias included, reduction partials excluded) divided by the step time.
 
+The ops beyond the step (the exact erf GeLU at the chain's MLP shape) are
+timed after the step loop, the same way, and reported under "next_rows";
+they are not part of `value`.
+
 Prints one JSON line (see the keys below). `--gpus N` with N > 1 exits: this
 build runs on a single GPU.
 """
@@ -162,7 +166,14 @@ def build_ops(dev):
     ops.append(Op("chain_attn_bda_bwd_bf16_16384x8192",
                   lambda: mb.mb_bias_dropout_add_bwd(ag, p5, s_attn, off5, dx=adx, dresidual=False, dbias=adb, ws=wsb),
                   bwd5, ["bda_bwd", "colsum"]))
-    return ops, host
+
+    # -- beyond the step: the exact (erf) GeLU on the chain's MLP activation
+    extra = [Op("erf_gelu_fwd_bf16_16384x32768", lambda: mb.mb_bias_gelu_erf_fwd(gy, gb, out=gout),
+                T * H * 4 + H * 2, ["gelu_fwd"]),
+             Op("erf_gelu_bwd_bf16_16384x32768",
+                lambda: mb.mb_bias_gelu_erf_bwd(gg, gy, gb, dgrad=dgr, dbias=dbg, ws=wsg),
+                T * H * 6 + H * 2 + H * 4, ["gelu_bwd", "colsum"])]
+    return ops, extra, host
 
 
 def copy_ceiling(dev):
@@ -305,7 +316,7 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     t_setup = time.perf_counter()
-    ops, host = build_ops(dev)
+    ops, extra, host = build_ops(dev)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
     ceiling = copy_ceiling(dev)
@@ -335,13 +346,33 @@ def main():
     ms_per_step = total_ms / args.steps
     step_bytes = sum(op.nbytes for op in ops)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    per_op = {}
-    for op in ops:
-        avg = sum(op.ms) / len(op.ms)
-        gbs = op.nbytes / (avg * 1e-3) / 1e9
-        per_op[op.name] = {"us": round(avg * 1e3, 2), "bytes": op.nbytes, "gbs": round(gbs, 1),
-                           "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
-                           "frac_copy": round(gbs / ceiling["gbs"], 4), "kernels": op.kernels}
+    # the ops beyond the step, after it, in a loop of their own
+    for _ in range(args.warmup):
+        for op in extra:
+            op.fn()
+    xev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in extra]
+           for _ in range(args.steps)]
+    for s in range(args.steps):
+        for op, (e0, e1) in zip(extra, xev[s]):
+            e0.record(stream)
+            op.fn()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        for op, (e0, e1) in zip(extra, xev[s]):
+            op.ms.append(e0.elapsed_time(e1))
+
+    def stats(group):
+        res = {}
+        for op in group:
+            avg = sum(op.ms) / len(op.ms)
+            gbs = op.nbytes / (avg * 1e-3) / 1e9
+            res[op.name] = {"us": round(avg * 1e3, 2), "bytes": op.nbytes, "gbs": round(gbs, 1),
+                            "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
+                            "frac_copy": round(gbs / ceiling["gbs"], 4), "kernels": op.kernels}
+        return res
+
+    per_op, next_rows = stats(ops), stats(extra)
     dom = max(ops, key=lambda o: sum(o.ms))
     dom_avg = sum(dom.ms) / len(dom.ms)
     achieved = dom.nbytes / (dom_avg * 1e-3) / 1e9
@@ -370,6 +401,7 @@ def main():
                    "step_bytes": step_bytes, "frac_peak": round(value / PEAK_HBM_GBS, 4),
                    "copy_ceiling_gbs": round(ceiling["gbs"], 1)},
         "per_op": per_op,
+        "next_rows": next_rows,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),

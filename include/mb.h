@@ -90,6 +90,20 @@ mb_status_t mb_bias_gelu_bwd(const void* g, const void* y, const void* bias, voi
                              float* dbias, void* ws, size_t ws_bytes, int64_t tokens,
                              int64_t hidden, mb_dtype_t dt, hipStream_t s);
 
+/* Exact GeLU [fusions §4.2, the erf definition with its printed constants]:
+ *   out = 0.5 z (1 + erf(0.70710678 z)),  z = y + bias;
+ * same arguments, aliasing and errors as mb_bias_gelu_fwd. */
+mb_status_t mb_bias_gelu_erf_fwd(const void* y, const void* bias, void* out, int64_t tokens,
+                                 int64_t hidden, mb_dtype_t dt, hipStream_t s);
+
+/* Backward of the exact GeLU:
+ *   dgrad = g * (0.5 (1 + erf(0.70710678 z)) + z * 0.3989423 * exp(-z^2 / 2)),
+ *   dbias as for mb_bias_gelu_bwd; the workspace is sized by
+ *   mb_bias_gelu_bwd_workspace (same tiling). */
+mb_status_t mb_bias_gelu_erf_bwd(const void* g, const void* y, const void* bias, void* dgrad,
+                                 float* dbias, void* ws, size_t ws_bytes, int64_t tokens,
+                                 int64_t hidden, mb_dtype_t dt, hipStream_t s);
+
 /* ---------------------------------------------------------------------------
  * Bias + dropout + residual add [fusions §3.2, §3.3]
  *   r'  = residual rounded to dt when residual_dt != dt (the mixed-precision

@@ -63,16 +63,19 @@ def check_rows_dt(kernel_out, oracle_fn, blocks, dt, what):
 
 # ------------------------------------------------------------------ GeLU fp32 [512, 4096], entire tensor
 
-def test_gelu_f32_512x4096_full():
+@pytest.mark.parametrize("exact", [False, True], ids=["tanh", "erf"])
+def test_gelu_f32_512x4096_full(exact):
     w = WORKLOADS["gelu_f32_512x4096"]
     y, b, g = (w.tensor(k) for k in ("y", "bias", "g"))
-    out = mb.mb_bias_gelu_fwd(y.to(DEV), b.to(DEV))
-    o, o64 = oracle.bias_gelu_fwd("f32", st(y), st(b))
-    say(f"gelu fwd f32 full: {assert_close(st(out), o, o64, None, 'f32', 'gelu fwd C1')}")
-    dg, db = mb.mb_bias_gelu_bwd(g.to(DEV), y.to(DEV), b.to(DEV))
-    d, d64, mag, db64 = oracle.bias_gelu_bwd("f32", st(g), st(y), st(b))
-    say(f"gelu bwd f32 full: {assert_close(st(dg), d, d64, mag, 'f32', 'gelu bwd C1')}")
-    say(f"gelu dbias f32 full: {assert_reduction_close(db.cpu().numpy(), db64, 'gelu dbias C1')}")
+    fwd, bwd = ((mb.mb_bias_gelu_erf_fwd, mb.mb_bias_gelu_erf_bwd) if exact
+                else (mb.mb_bias_gelu_fwd, mb.mb_bias_gelu_bwd))
+    out = fwd(y.to(DEV), b.to(DEV))
+    o, o64 = oracle.bias_gelu_fwd("f32", st(y), st(b), exact=exact)
+    say(f"gelu fwd exact={exact} f32 full: {assert_close(st(out), o, o64, None, 'f32', 'gelu fwd C1')}")
+    dg, db = bwd(g.to(DEV), y.to(DEV), b.to(DEV))
+    d, d64, mag, db64 = oracle.bias_gelu_bwd("f32", st(g), st(y), st(b), exact=exact)
+    say(f"gelu bwd exact={exact} f32 full: {assert_close(st(dg), d, d64, mag, 'f32', 'gelu bwd C1')}")
+    say(f"gelu dbias exact={exact} f32 full: {assert_reduction_close(db.cpu().numpy(), db64, 'gelu dbias C1')}")
 
 
 # ------------------------------------------------------------------ dropout-add bf16 [8192, 4096], fp32 residual
@@ -215,6 +218,34 @@ def test_layer_chain_t16384_h8192_f32768():
     dg2, dbias2 = mb.mb_bias_gelu_bwd(g, y, b)
     assert torch.equal(dg.view(torch.int16), dg2.view(torch.int16))
     assert torch.equal(dbias.view(torch.int32), dbias2.view(torch.int32))
+
+
+def test_gelu_erf_bf16_t16384_f32768():
+    # the exact form at the MLP activation's shape, in the launch configuration
+    # of the tanh form (the two share the tiling)
+    w = WORKLOADS["layer_chain_bf16_t16384_h8192_f32768"]
+    y, b, g = (load(w.name, k) for k in ("gelu_y", "gelu_bias", "gelu_g"))
+    T, H = y.shape
+    out = mb.mb_bias_gelu_erf_fwd(y, b)
+    dg, dbias = mb.mb_bias_gelu_erf_bwd(g, y, b)
+    bs = st(b.cpu())
+    fs, bws = [], []
+    for r0, n in row_blocks(T, seed=5):
+        yr, gr = st(y[r0:r0 + n].cpu()), st(g[r0:r0 + n].cpu())
+        o, o64 = oracle.bias_gelu_fwd("bf16", yr, bs, exact=True)
+        fs.append(assert_close(st(out[r0:r0 + n]), o, o64, None, "bf16", f"erf gelu fwd rows {r0}"))
+        d, d64, mag, _ = oracle.bias_gelu_bwd("bf16", gr, yr, bs, exact=True)
+        bws.append(assert_close(st(dg[r0:r0 + n]), d, d64, mag, "bf16", f"erf gelu bwd rows {r0}"))
+    say(f"erf gelu fwd: {fs}")
+    say(f"erf gelu bwd: {bws}")
+    cols = torch.from_numpy(sample_cols(H, seed=6)).to(DEV)
+    _, _, _, db64 = oracle.bias_gelu_bwd("bf16", st(g.index_select(1, cols).cpu()), st(y.index_select(1, cols).cpu()),
+                                         st(b.index_select(0, cols).cpu()), exact=True)
+    say(f"erf gelu dbias sampled columns: "
+        f"{assert_reduction_close(dbias.index_select(0, cols).cpu().numpy(), db64, 'erf gelu dbias')}")
+    err = (dbias.double() - dg.double().sum(0)).abs()
+    bound = dbias_noise_bound(dg)
+    assert bool((err <= bound).all()), f"erf gelu dbias vs column sums, worst {float((err / bound).max()):.2f}"
 
 
 # ------------------------------------------------------------------ dropout-add backward at full size

@@ -40,59 +40,82 @@ CASES = [(dt, s) for dt, ss in SHAPES.items() for s in ss]
 
 # ------------------------------------------------------------------ GeLU
 
+# exact=False: the tanh approximation; exact=True: the erf form.
+GELU_FWD = {False: mb.mb_bias_gelu_fwd, True: mb.mb_bias_gelu_erf_fwd}
+GELU_BWD = {False: mb.mb_bias_gelu_bwd, True: mb.mb_bias_gelu_erf_bwd}
+EXACT = pytest.mark.parametrize("exact", [False, True], ids=["tanh", "erf"])
+
+
+@EXACT
 @pytest.mark.parametrize("dt,shape", CASES)
 @pytest.mark.parametrize("with_bias", [True, False])
-def test_gelu_fwd(dt, shape, with_bias):
+def test_gelu_fwd(dt, shape, with_bias, exact):
     T, H = shape
     y = gen(11, shape, dt, sigma=3.0)
     b = gen(12, (H,), dt, sigma=0.5) if with_bias else None
-    out = mb.mb_bias_gelu_fwd(y.to(DEV), None if b is None else b.to(DEV))
-    o, o64 = oracle.bias_gelu_fwd(dt, st(y), None if b is None else st(b))
-    log(f"gelu_fwd {dt} {shape}", assert_close(st(out), o, o64, None, dt, "gelu fwd"))
+    out = GELU_FWD[exact](y.to(DEV), None if b is None else b.to(DEV))
+    o, o64 = oracle.bias_gelu_fwd(dt, st(y), None if b is None else st(b), exact=exact)
+    log(f"gelu_fwd exact={exact} {dt} {shape}", assert_close(st(out), o, o64, None, dt, "gelu fwd"))
 
 
+@EXACT
 @pytest.mark.parametrize("dt,shape", CASES)
-def test_gelu_bwd(dt, shape):
+def test_gelu_bwd(dt, shape, exact):
     T, H = shape
     y = gen(21, shape, dt, sigma=3.0)
     g = gen(22, shape, dt)
     b = gen(23, (H,), dt, sigma=0.5)
-    dgrad, dbias = mb.mb_bias_gelu_bwd(g.to(DEV), y.to(DEV), b.to(DEV))
-    d, d64, mag, db64 = oracle.bias_gelu_bwd(dt, st(g), st(y), st(b))
-    log(f"gelu_bwd {dt} {shape}", assert_close(st(dgrad), d, d64, mag, dt, "gelu bwd dgrad"))
-    log(f"gelu_dbias {dt} {shape}", assert_reduction_close(dbias.cpu().numpy(), db64, "gelu dbias"))
+    dgrad, dbias = GELU_BWD[exact](g.to(DEV), y.to(DEV), b.to(DEV))
+    d, d64, mag, db64 = oracle.bias_gelu_bwd(dt, st(g), st(y), st(b), exact=exact)
+    log(f"gelu_bwd exact={exact} {dt} {shape}", assert_close(st(dgrad), d, d64, mag, dt, "gelu bwd dgrad"))
+    log(f"gelu_dbias exact={exact} {dt} {shape}",
+        assert_reduction_close(dbias.cpu().numpy(), db64, "gelu dbias"))
 
 
-def test_gelu_bwd_dbias_optional_and_deterministic():
+def test_gelu_erf_differs_from_tanh():
+    # the two forms agree to about 1e-3 relative near |z| ~ 1-3 but not bit for
+    # bit: a path that silently ran one for the other would be caught here
+    y = gen(24, (64, 512), "f32", sigma=2.0).to(DEV)
+    a = mb.mb_bias_gelu_fwd(y)
+    e = mb.mb_bias_gelu_erf_fwd(y)
+    diff = (a - e).abs().max().item()
+    assert 1e-5 < diff < 1e-2
+
+
+@EXACT
+def test_gelu_bwd_dbias_optional_and_deterministic(exact):
     y = gen(31, (640, 2048), "bf16").to(DEV)
     g = gen(32, (640, 2048), "bf16").to(DEV)
     b = gen(33, (2048,), "bf16", 0.02).to(DEV)
-    d1, db1 = mb.mb_bias_gelu_bwd(g, y, b)
-    d2, db2 = mb.mb_bias_gelu_bwd(g, y, b)
-    d3, none = mb.mb_bias_gelu_bwd(g, y, b, dbias=False)
+    bwd = GELU_BWD[exact]
+    d1, db1 = bwd(g, y, b)
+    d2, db2 = bwd(g, y, b)
+    d3, none = bwd(g, y, b, dbias=False)
     assert none is None
     assert torch.equal(d1.view(torch.int16), d2.view(torch.int16))
     assert torch.equal(d1.view(torch.int16), d3.view(torch.int16))
     assert torch.equal(db1.view(torch.int32), db2.view(torch.int32))
 
 
-def test_gelu_in_place():
+@EXACT
+def test_gelu_in_place(exact):
     y = gen(41, (300, 1024), "bf16").to(DEV)
     b = gen(42, (1024,), "bf16", 0.02).to(DEV)
-    ref = mb.mb_bias_gelu_fwd(y, b)
+    ref = GELU_FWD[exact](y, b)
     y2 = y.clone()
-    mb.mb_bias_gelu_fwd(y2, b, out=y2)
+    GELU_FWD[exact](y2, b, out=y2)
     assert torch.equal(ref.view(torch.int16), y2.view(torch.int16))
     g = gen(43, (300, 1024), "bf16").to(DEV)
-    d_ref, db_ref = mb.mb_bias_gelu_bwd(g, y, b)
+    d_ref, db_ref = GELU_BWD[exact](g, y, b)
     g2 = g.clone()
-    d_in, db_in = mb.mb_bias_gelu_bwd(g2, y, b, dgrad=g2)
+    d_in, db_in = GELU_BWD[exact](g2, y, b, dgrad=g2)
     assert d_in.data_ptr() == g2.data_ptr()
     assert torch.equal(d_ref.view(torch.int16), g2.view(torch.int16))
     assert torch.equal(db_ref.view(torch.int32), db_in.view(torch.int32))
 
 
-def test_gelu_extreme_values():
+@EXACT
+def test_gelu_extreme_values(exact):
     vals = np.array([0.0, -0.0, 1e-30, -1e-30, 1e-8, -0.7525, -6.0, -8.0, -9.5, -10.0, -10.3, -10.7, -11.0,
                      -12.0, -20.0, 6.0, 12.0, 1e4, -1e4, 2e4, -2e4, 1e20, -1e20, 3e38, -3e38, np.nan], np.float32)
     H = 32
@@ -101,18 +124,19 @@ def test_gelu_extreme_values():
     for dt in ("f32", "bf16", "f16"):
         y = torch.from_numpy(y32).to(TD[dt])
         g = torch.from_numpy(g32).to(TD[dt])
-        out = mb.mb_bias_gelu_fwd(y.to(DEV))
-        o, o64 = oracle.bias_gelu_fwd(dt, st(y), None)
+        out = GELU_FWD[exact](y.to(DEV))
+        o, o64 = oracle.bias_gelu_fwd(dt, st(y), None, exact=exact)
         assert_close(st(out), o, o64, None, dt, f"gelu fwd extremes {dt}")
-        dg, _ = mb.mb_bias_gelu_bwd(g.to(DEV), y.to(DEV), dbias=False)
-        d, d64, mag, _ = oracle.bias_gelu_bwd(dt, st(g), st(y), None)
+        dg, _ = GELU_BWD[exact](g.to(DEV), y.to(DEV), dbias=False)
+        d, d64, mag, _ = oracle.bias_gelu_bwd(dt, st(g), st(y), None, exact=exact)
         assert_close(st(dg), d, d64, mag, dt, f"gelu bwd extremes {dt}")
 
 
-def test_gelu_empty_tokens():
+@EXACT
+def test_gelu_empty_tokens(exact):
     y = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
-    assert mb.mb_bias_gelu_fwd(y).shape == (0, 64)
-    dg, db = mb.mb_bias_gelu_bwd(y, y, torch.zeros(64, dtype=torch.bfloat16, device=DEV))
+    assert GELU_FWD[exact](y).shape == (0, 64)
+    dg, db = GELU_BWD[exact](y, y, torch.zeros(64, dtype=torch.bfloat16, device=DEV))
     assert torch.count_nonzero(db).item() == 0 and db.shape == (64,)
 
 

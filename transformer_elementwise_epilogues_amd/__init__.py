@@ -18,6 +18,7 @@ import torch
 __all__ = [
     "MBError", "lib", "abi_version",
     "mb_bias_gelu_fwd", "mb_bias_gelu_bwd", "mb_bias_gelu_bwd_workspace",
+    "mb_bias_gelu_erf_fwd", "mb_bias_gelu_erf_bwd",
     "mb_bias_dropout_add_train", "mb_bias_dropout_add_infer", "mb_dropout_mask",
     "mb_bias_dropout_add_bwd", "mb_bias_dropout_add_bwd_workspace",
     "mb_bias_swiglu_fwd", "mb_bias_swiglu_bwd", "mb_bias_geglu_fwd", "mb_bias_geglu_bwd",
@@ -56,6 +57,8 @@ def lib() -> ctypes.CDLL:
                 "mb_bias_gelu_fwd": ([P, P, P, I64, I64, I, P], I),
                 "mb_bias_gelu_bwd_workspace": ([I64, I64, I, I], SZ),
                 "mb_bias_gelu_bwd": ([P, P, P, P, P, P, SZ, I64, I64, I, P], I),
+                "mb_bias_gelu_erf_fwd": ([P, P, P, I64, I64, I, P], I),
+                "mb_bias_gelu_erf_bwd": ([P, P, P, P, P, P, SZ, I64, I64, I, P], I),
                 "mb_bias_dropout_add_train": ([P, P, P, I, P, I64, I64, I, F, U64, U64, P], I),
                 "mb_bias_dropout_add_infer": ([P, P, P, I, P, I64, I64, I, P], I),
                 "mb_dropout_mask": ([P, I64, I64, F, U64, U64, P], I),
@@ -119,35 +122,50 @@ def _vec(t, n, name):
 
 # ------------------------------------------------------------------ GeLU
 
-def mb_bias_gelu_fwd(y, bias=None, out=None, stream=None):
+def _gelu_fwd(fn, y, bias, out, stream):
     T, H = _rows(y, "y")
     _vec(bias, H, "bias")
     out = torch.empty_like(y) if out is None else out
-    _check("mb_bias_gelu_fwd", lib().mb_bias_gelu_fwd(_p(y), _p(bias), _p(out), T, H, _dt(y), _stream(y, stream)))
+    _check(fn, getattr(lib(), fn)(_p(y), _p(bias), _p(out), T, H, _dt(y), _stream(y, stream)))
     return out
+
+
+def mb_bias_gelu_fwd(y, bias=None, out=None, stream=None):
+    """tanh-approximated GeLU of y + bias; out=y runs in place."""
+    return _gelu_fwd("mb_bias_gelu_fwd", y, bias, out, stream)
+
+
+def mb_bias_gelu_erf_fwd(y, bias=None, out=None, stream=None):
+    """Exact (erf) GeLU of y + bias; out=y runs in place."""
+    return _gelu_fwd("mb_bias_gelu_erf_fwd", y, bias, out, stream)
 
 
 def mb_bias_gelu_bwd_workspace(tokens, hidden, dtype, with_dbias=True) -> int:
     return int(lib().mb_bias_gelu_bwd_workspace(tokens, hidden, DTYPES[dtype], int(bool(with_dbias))))
 
 
-def mb_bias_gelu_bwd(g, y, bias=None, dgrad=None, dbias=True, ws=None, stream=None):
-    """Returns (dgrad, dbias or None). dbias=True allocates the fp32 bias gradient."""
+def _gelu_bwd(fn, g, y, bias, dgrad, dbias, ws, stream):
     T, H = _rows(y, "y")
     _rows(g, "g", H)
     _vec(bias, H, "bias")
     dgrad = torch.empty_like(y) if dgrad is None else dgrad
-    if dbias is True:
-        dbias = torch.empty(H, dtype=torch.float32, device=y.device)
-    elif dbias is False:
-        dbias = None
+    dbias = _grad_out(dbias, H, y.device)
     nws = mb_bias_gelu_bwd_workspace(T, H, y.dtype, dbias is not None)
     if ws is None and nws:
         ws = torch.empty(nws, dtype=torch.uint8, device=y.device)
-    _check("mb_bias_gelu_bwd", lib().mb_bias_gelu_bwd(
-        _p(g), _p(y), _p(bias), _p(dgrad), _p(dbias), _p(ws), ws.numel() if ws is not None else 0, T, H, _dt(y),
-        _stream(y, stream)))
+    _check(fn, getattr(lib(), fn)(_p(g), _p(y), _p(bias), _p(dgrad), _p(dbias), _p(ws),
+                                  ws.numel() if ws is not None else 0, T, H, _dt(y), _stream(y, stream)))
     return dgrad, dbias
+
+
+def mb_bias_gelu_bwd(g, y, bias=None, dgrad=None, dbias=True, ws=None, stream=None):
+    """Returns (dgrad, dbias or None). dbias=True allocates the fp32 bias gradient."""
+    return _gelu_bwd("mb_bias_gelu_bwd", g, y, bias, dgrad, dbias, ws, stream)
+
+
+def mb_bias_gelu_erf_bwd(g, y, bias=None, dgrad=None, dbias=True, ws=None, stream=None):
+    """Backward of the exact (erf) GeLU; returns (dgrad, dbias or None)."""
+    return _gelu_bwd("mb_bias_gelu_erf_bwd", g, y, bias, dgrad, dbias, ws, stream)
 
 
 # ------------------------------------------------------------------ dropout-add

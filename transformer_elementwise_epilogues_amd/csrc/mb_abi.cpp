@@ -136,8 +136,8 @@ int mb_abi_version(void) { return 1; }
 
 // ------------------------------------------------------------------ GeLU
 
-mb_status_t mb_bias_gelu_fwd(const void* y, const void* bias, void* out, int64_t tokens, int64_t hidden,
-                             mb_dtype_t dt, hipStream_t s) {
+static mb_status_t gelu_fwd_common(bool exact, const void* y, const void* bias, void* out, int64_t tokens,
+                                   int64_t hidden, mb_dtype_t dt, hipStream_t s) {
   if (!dt_ok(dt)) return MB_ERR_DTYPE;
   if (mb_status_t st = check_shape(tokens, hidden, dt)) return st;
   const size_t tb = static_cast<size_t>(tokens) * hidden * esize(dt), bb = hidden * esize(dt);
@@ -146,8 +146,18 @@ mb_status_t mb_bias_gelu_fwd(const void* y, const void* bias, void* out, int64_t
   if (!aliasing_ok({{out, tb}}, {{y, tb}, {bias, bias ? bb : 0}}, {{0, 0}})) return MB_ERR_ALIAS;
   if (tokens == 0) return MB_OK;
   const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GELU_FWD_BLOCKS);
-  if (hipError_t e = mb::launch_gelu_fwd(dt, y, bias, out, t, s)) return hip_status(e);
+  if (hipError_t e = mb::launch_gelu_fwd(dt, exact, y, bias, out, t, s)) return hip_status(e);
   return finish();
+}
+
+mb_status_t mb_bias_gelu_fwd(const void* y, const void* bias, void* out, int64_t tokens, int64_t hidden,
+                             mb_dtype_t dt, hipStream_t s) {
+  return gelu_fwd_common(false, y, bias, out, tokens, hidden, dt, s);
+}
+
+mb_status_t mb_bias_gelu_erf_fwd(const void* y, const void* bias, void* out, int64_t tokens, int64_t hidden,
+                                 mb_dtype_t dt, hipStream_t s) {
+  return gelu_fwd_common(true, y, bias, out, tokens, hidden, dt, s);
 }
 
 size_t mb_bias_gelu_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias) {
@@ -155,8 +165,9 @@ size_t mb_bias_gelu_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt,
   return col_partials_bytes(mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GELU_BWD_BLOCKS), hidden);
 }
 
-mb_status_t mb_bias_gelu_bwd(const void* g, const void* y, const void* bias, void* dgrad, float* dbias, void* ws,
-                             size_t ws_bytes, int64_t tokens, int64_t hidden, mb_dtype_t dt, hipStream_t s) {
+static mb_status_t gelu_bwd_common(bool exact, const void* g, const void* y, const void* bias, void* dgrad,
+                                   float* dbias, void* ws, size_t ws_bytes, int64_t tokens, int64_t hidden,
+                                   mb_dtype_t dt, hipStream_t s) {
   if (!dt_ok(dt)) return MB_ERR_DTYPE;
   if (mb_status_t st = check_shape(tokens, hidden, dt)) return st;
   const size_t tb = static_cast<size_t>(tokens) * hidden * esize(dt), bb = hidden * esize(dt);
@@ -177,10 +188,21 @@ mb_status_t mb_bias_gelu_bwd(const void* g, const void* y, const void* bias, voi
   }
   const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GELU_BWD_BLOCKS);
   float* partials = dbias ? static_cast<float*>(ws) : nullptr;
-  if (hipError_t e = mb::launch_gelu_bwd(dt, g, y, bias, dgrad, partials, t, s)) return hip_status(e);
+  if (hipError_t e = mb::launch_gelu_bwd(dt, exact, g, y, bias, dgrad, partials, t, s)) return hip_status(e);
   if (dbias)
     if (hipError_t e = reduce_columns(partials, t, hidden, dbias, s)) return hip_status(e);
   return finish();
+}
+
+mb_status_t mb_bias_gelu_bwd(const void* g, const void* y, const void* bias, void* dgrad, float* dbias, void* ws,
+                             size_t ws_bytes, int64_t tokens, int64_t hidden, mb_dtype_t dt, hipStream_t s) {
+  return gelu_bwd_common(false, g, y, bias, dgrad, dbias, ws, ws_bytes, tokens, hidden, dt, s);
+}
+
+mb_status_t mb_bias_gelu_erf_bwd(const void* g, const void* y, const void* bias, void* dgrad, float* dbias,
+                                 void* ws, size_t ws_bytes, int64_t tokens, int64_t hidden, mb_dtype_t dt,
+                                 hipStream_t s) {
+  return gelu_bwd_common(true, g, y, bias, dgrad, dbias, ws, ws_bytes, tokens, hidden, dt, s);
 }
 
 // ------------------------------------------------------------------ dropout-add

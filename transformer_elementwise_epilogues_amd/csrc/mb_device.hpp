@@ -325,6 +325,20 @@ __device__ __forceinline__ float silu_fwd(float a, float* sc) {
   return L.pos ? ar : ar * L.es;
 }
 
+// Exact GeLU through the complementary error function (1 + erf(x) = erfc(-x),
+// which keeps the negative tail from cancelling), with the constants printed
+// with Megatron-LM's fusions: 1/sqrt(2) and 1/sqrt(2 pi). Library erfcf/expf
+// (ocml), not the fast approximations, to hold fp32 outputs to ~1e-6.
+constexpr float kErfK = 0.70710678f;
+constexpr float kErfPdf = 0.3989423f;
+__device__ __forceinline__ float gelu_erf_fwd(float z) { return 0.5f * z * erfcf(-kErfK * z); }
+// d/dz 0.5 z erfc(-k z) = 0.5 erfc(-k z) + z * 0.3989423 * exp(-z^2 / 2)
+__device__ __forceinline__ float gelu_erf_fwd_bwd(float z, float* value) {
+  const float c = erfcf(-kErfK * z);
+  *value = 0.5f * z * c;
+  return __builtin_fmaf(z * kErfPdf, expf(-0.5f * z * z), 0.5f * c);
+}
+
 // ---------------------------------------------------------------- reductions
 
 // Combine the 4 waves' per-lane column sums of one block in LDS, in a fixed

@@ -34,20 +34,26 @@ __device__ __forceinline__ void load_bias(const char* bias, int cv, float* b) {
   }
 }
 
-template <DT D>
+enum Kind { kTanh = 0, kErf = 1 };
+
+template <DT D, int KIND>
 __device__ __forceinline__ u32x4 gelu_vec(u32x4 yv, const float* b) {
   constexpr int V = Vec<D>::N;
   float f[V];
   unpack<D>(yv, f);
 #pragma unroll
   for (int k = 0; k < V; ++k) {
-    const GeluF r = gelu_tanh_fwd(f[k] + b[k]);
-    f[k] = r.v * r.sc;
+    if constexpr (KIND == kTanh) {
+      const GeluF r = gelu_tanh_fwd(f[k] + b[k]);
+      f[k] = r.v * r.sc;
+    } else {
+      f[k] = gelu_erf_fwd(f[k] + b[k]);
+    }
   }
   return pack<D>(f);
 }
 
-template <DT D, int U>
+template <DT D, int KIND, int U>
 __global__ __launch_bounds__(kThreads) void gelu_fwd_kernel(const char* y, const char* bias, char* out,
                                                             int64_t T, int nvec) {
   const int lane = threadIdx.x & 63;
@@ -67,12 +73,12 @@ __global__ __launch_bounds__(kThreads) void gelu_fwd_kernel(const char* y, const
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] = ld_stream(yp + (t + u * S) * pitch);
 #pragma unroll
-    for (int u = 0; u < U; ++u) st_stream(op + (t + u * S) * pitch, gelu_vec<D>(v[u], b));
+    for (int u = 0; u < U; ++u) st_stream(op + (t + u * S) * pitch, gelu_vec<D, KIND>(v[u], b));
   }
-  for (; t < T; t += S) st_stream(op + t * pitch, gelu_vec<D>(ld_stream(yp + t * pitch), b));
+  for (; t < T; t += S) st_stream(op + t * pitch, gelu_vec<D, KIND>(ld_stream(yp + t * pitch), b));
 }
 
-template <DT D>
+template <DT D, int KIND>
 __device__ __forceinline__ u32x4 gelu_grad_vec(u32x4 gv, u32x4 yv, const float* b, float* acc) {
   constexpr int V = Vec<D>::N;
   float g[V], f[V];
@@ -80,15 +86,21 @@ __device__ __forceinline__ u32x4 gelu_grad_vec(u32x4 gv, u32x4 yv, const float* 
   unpack<D>(yv, f);
 #pragma unroll
   for (int k = 0; k < V; ++k) {
-    const GeluB r = gelu_tanh_fwd_bwd(f[k] + b[k]);
-    const float d = (g[k] * r.d) * r.sc;
+    float d;
+    if constexpr (KIND == kTanh) {
+      const GeluB r = gelu_tanh_fwd_bwd(f[k] + b[k]);
+      d = (g[k] * r.d) * r.sc;
+    } else {
+      float unused;
+      d = g[k] * gelu_erf_fwd_bwd(f[k] + b[k], &unused);
+    }
     acc[k] += d;
     f[k] = d;
   }
   return pack<D>(f);
 }
 
-template <DT D, int U, bool DBIAS>
+template <DT D, int KIND, int U, bool DBIAS>
 __global__ __launch_bounds__(kThreads) void gelu_bwd_kernel(const char* g, const char* y, const char* bias,
                                                             char* dgrad, float* partials, int64_t T,
                                                             int nvec) {
@@ -117,11 +129,11 @@ __global__ __launch_bounds__(kThreads) void gelu_bwd_kernel(const char* g, const
         yv[u] = ld_stream(y + o);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) st_stream(dgrad + (t + u * S) * pitch + col, gelu_grad_vec<D>(gv[u], yv[u], b, acc));
+      for (int u = 0; u < U; ++u) st_stream(dgrad + (t + u * S) * pitch + col, gelu_grad_vec<D, KIND>(gv[u], yv[u], b, acc));
     }
     for (; t < T; t += S) {
       const size_t o = t * pitch + col;
-      st_stream(dgrad + o, gelu_grad_vec<D>(ld_stream(g + o), ld_stream(y + o), b, acc));
+      st_stream(dgrad + o, gelu_grad_vec<D, KIND>(ld_stream(g + o), ld_stream(y + o), b, acc));
     }
   }
   if constexpr (DBIAS)
@@ -129,16 +141,16 @@ __global__ __launch_bounds__(kThreads) void gelu_bwd_kernel(const char* g, const
                              partials + static_cast<size_t>(ti.rg) * nvec * V + static_cast<size_t>(cv) * V);
 }
 
-template <DT D>
+template <DT D, int KIND>
 hipError_t gelu_fwd_dispatch(const void* y, const void* bias, void* out, const Tiling& t, hipStream_t s) {
   const dim3 grid = tile_grid(t.strips, t.G);
-  hipLaunchKernelGGL((gelu_fwd_kernel<D, kUnrollFwd>), grid, dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((gelu_fwd_kernel<D, KIND, kUnrollFwd>), grid, dim3(kThreads), 0, s,
                      static_cast<const char*>(y), static_cast<const char*>(bias), static_cast<char*>(out), t.T,
                      t.nvec);
   return hipGetLastError();
 }
 
-template <DT D>
+template <DT D, int KIND>
 hipError_t gelu_bwd_dispatch(const void* g, const void* y, const void* bias, void* dgrad, float* partials,
                              const Tiling& t, hipStream_t s) {
   const dim3 grid = tile_grid(t.strips, t.G);
@@ -147,33 +159,46 @@ hipError_t gelu_bwd_dispatch(const void* g, const void* y, const void* bias, voi
   auto bp = static_cast<const char*>(bias);
   auto dp = static_cast<char*>(dgrad);
   if (partials)
-    hipLaunchKernelGGL((gelu_bwd_kernel<D, kUnrollBwd, true>), grid, dim3(kThreads), 0, s, gp, yp, bp, dp, partials,
+    hipLaunchKernelGGL((gelu_bwd_kernel<D, KIND, kUnrollBwd, true>), grid, dim3(kThreads), 0, s, gp, yp, bp, dp, partials,
                        t.T, t.nvec);
   else
-    hipLaunchKernelGGL((gelu_bwd_kernel<D, kUnrollBwd, false>), grid, dim3(kThreads), 0, s, gp, yp, bp, dp, partials,
+    hipLaunchKernelGGL((gelu_bwd_kernel<D, KIND, kUnrollBwd, false>), grid, dim3(kThreads), 0, s, gp, yp, bp, dp, partials,
                        t.T, t.nvec);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gelu_fwd(int dt, const void* y, const void* bias, void* out, const Tiling& t, hipStream_t s) {
+template <int KIND>
+hipError_t gelu_fwd_any(int dt, const void* y, const void* bias, void* out, const Tiling& t, hipStream_t s) {
   switch (static_cast<DT>(dt)) {
-    case DT::F32: return gelu_fwd_dispatch<DT::F32>(y, bias, out, t, s);
-    case DT::F16: return gelu_fwd_dispatch<DT::F16>(y, bias, out, t, s);
-    case DT::BF16: return gelu_fwd_dispatch<DT::BF16>(y, bias, out, t, s);
+    case DT::F32: return gelu_fwd_dispatch<DT::F32, KIND>(y, bias, out, t, s);
+    case DT::F16: return gelu_fwd_dispatch<DT::F16, KIND>(y, bias, out, t, s);
+    case DT::BF16: return gelu_fwd_dispatch<DT::BF16, KIND>(y, bias, out, t, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gelu_bwd(int dt, const void* g, const void* y, const void* bias, void* dgrad, float* partials,
-                           const Tiling& t, hipStream_t s) {
+template <int KIND>
+hipError_t gelu_bwd_any(int dt, const void* g, const void* y, const void* bias, void* dgrad, float* partials,
+                        const Tiling& t, hipStream_t s) {
   switch (static_cast<DT>(dt)) {
-    case DT::F32: return gelu_bwd_dispatch<DT::F32>(g, y, bias, dgrad, partials, t, s);
-    case DT::F16: return gelu_bwd_dispatch<DT::F16>(g, y, bias, dgrad, partials, t, s);
-    case DT::BF16: return gelu_bwd_dispatch<DT::BF16>(g, y, bias, dgrad, partials, t, s);
+    case DT::F32: return gelu_bwd_dispatch<DT::F32, KIND>(g, y, bias, dgrad, partials, t, s);
+    case DT::F16: return gelu_bwd_dispatch<DT::F16, KIND>(g, y, bias, dgrad, partials, t, s);
+    case DT::BF16: return gelu_bwd_dispatch<DT::BF16, KIND>(g, y, bias, dgrad, partials, t, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gelu_fwd(int dt, bool exact, const void* y, const void* bias, void* out, const Tiling& t,
+                           hipStream_t s) {
+  return exact ? gelu_fwd_any<kErf>(dt, y, bias, out, t, s) : gelu_fwd_any<kTanh>(dt, y, bias, out, t, s);
+}
+
+hipError_t launch_gelu_bwd(int dt, bool exact, const void* g, const void* y, const void* bias, void* dgrad,
+                           float* partials, const Tiling& t, hipStream_t s) {
+  return exact ? gelu_bwd_any<kErf>(dt, g, y, bias, dgrad, partials, t, s)
+               : gelu_bwd_any<kTanh>(dt, g, y, bias, dgrad, partials, t, s);
 }
 
 }  // namespace mb

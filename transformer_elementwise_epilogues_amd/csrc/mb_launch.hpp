@@ -66,10 +66,11 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 // out[c] = sum over r < R of in[r * C + c], r ascending (fp32).
 hipError_t launch_colsum(const float* in, int R, int64_t C, float* out, hipStream_t s);
 
-hipError_t launch_gelu_fwd(int dt, const void* y, const void* bias, void* out, const Tiling& t,
+// exact = false: tanh approximation; true: the erf form
+hipError_t launch_gelu_fwd(int dt, bool exact, const void* y, const void* bias, void* out, const Tiling& t,
                            hipStream_t s);
 // partials: [G, H] fp32 or nullptr (no bias gradient)
-hipError_t launch_gelu_bwd(int dt, const void* g, const void* y, const void* bias, void* dgrad,
+hipError_t launch_gelu_bwd(int dt, bool exact, const void* g, const void* y, const void* bias, void* dgrad,
                            float* partials, const Tiling& t, hipStream_t s);
 
 struct DropoutArgs {
