@@ -325,18 +325,59 @@ __device__ __forceinline__ float silu_fwd(float a, float* sc) {
   return L.pos ? ar : ar * L.es;
 }
 
-// Exact GeLU through the complementary error function (1 + erf(x) = erfc(-x),
-// which keeps the negative tail from cancelling), with the constants printed
-// with Megatron-LM's fusions: 1/sqrt(2) and 1/sqrt(2 pi). Library erfcf/expf
-// (ocml), not the fast approximations, to hold fp32 outputs to ~1e-6.
+// Exact GeLU, 0.5 z (1 + erf(k z)) = z Phi(z), with the constants printed with
+// Megatron-LM's fusions: k = 0.70710678 (1/sqrt 2) and 0.3989423 (1/sqrt(2 pi)).
+// 1 + erf(k z) = erfc(-k z), and for x = k |z| >= 0 the complementary error
+// function is evaluated branch-free as
+//   erfc(x) = t exp(-x^2 + P(t)),   t = 1 / (1 + x / 2),
+// with the degree-9 Chebyshev-fitted P of the erfcc routine in Numerical
+// Recipes (Press, Teukolsky, Vetterling, Flannery, 2nd ed., section 6.2),
+// whose fractional error is below 1.2e-7 for every x >= 0. Then
+//   z >= 0:  Phi = 1 - erfc(x) / 2        z < 0:  Phi = erfc(x) / 2
+// so the negative tail is a product, never a difference. Below z = -12 the
+// exponent is shifted by 64 (results are subnormal there) and the caller
+// multiplies by the deferred scale 2^-64 last, like the tanh form.
 constexpr float kErfK = 0.70710678f;
 constexpr float kErfPdf = 0.3989423f;
-__device__ __forceinline__ float gelu_erf_fwd(float z) { return 0.5f * z * erfcf(-kErfK * z); }
-// d/dz 0.5 z erfc(-k z) = 0.5 erfc(-k z) + z * 0.3989423 * exp(-z^2 / 2)
-__device__ __forceinline__ float gelu_erf_fwd_bwd(float z, float* value) {
-  const float c = erfcf(-kErfK * z);
-  *value = 0.5f * z * c;
-  return __builtin_fmaf(z * kErfPdf, expf(-0.5f * z * z), 0.5f * c);
+constexpr float kErfcP[10] = {-1.26551223f, 1.00002368f, 0.37409196f, 0.09678418f, -0.18628806f,
+                              0.27886807f,  -1.13520398f, 1.48851587f, -0.82215223f, 0.17087277f};
+constexpr float kErfTail = -12.0f;
+constexpr float kErfShift = 64.0f;
+constexpr float kErfScaleDown = 0x1p-64f;
+
+// 0.5 erfc(k |z|) times 2^shift; the 1/2 is the -1 in the exponent
+__device__ __forceinline__ float half_erfc_abs(float z, float shift) {
+  const float x = __builtin_fabsf(z) * kErfK;
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, x, 1.0f));
+  float p = kErfcP[9];
+#pragma unroll
+  for (int k = 8; k >= 0; --k) p = __builtin_fmaf(p, t, kErfcP[k]);
+  const float a = __builtin_fmaf(-x, x, p);  // -x^2 + P(t), rounded once
+  return t * __builtin_amdgcn_exp2f(__builtin_fmaf(a, static_cast<float>(kLog2e), shift - 1.0f));
+}
+
+__device__ __forceinline__ GeluF gelu_erf_fwd(float z) {
+  const bool tail = z < kErfTail;
+  const float h = half_erfc_abs(z, tail ? kErfShift : 0.0f);
+  GeluF o;
+  o.v = z * (z < 0.0f ? h : 1.0f - h);  // not z - z h: inf * 0 at z = inf
+  o.sc = tail ? kErfScaleDown : 1.0f;
+  return o;
+}
+
+// gelu_erf'(z) = Phi(z) + z * 0.3989423 * exp(-z^2 / 2), both terms carrying the
+// same deferred scale (only `d` and `sc` are set)
+__device__ __forceinline__ GeluB gelu_erf_fwd_bwd(float z) {
+  const bool tail = z < kErfTail;
+  const float shift = tail ? kErfShift : 0.0f;
+  const float h = half_erfc_abs(z, shift);
+  const float zphi = (z * kErfPdf) *
+                     __builtin_amdgcn_exp2f(__builtin_fmaf(z * z, static_cast<float>(-0.5 * kLog2e), shift));
+  GeluB o;
+  o.v = 0.0f;
+  o.d = (z < 0.0f ? h : 1.0f - h) + zphi;
+  o.sc = tail ? kErfScaleDown : 1.0f;
+  return o;
 }
 
 // ---------------------------------------------------------------- reductions

@@ -43,12 +43,8 @@ __device__ __forceinline__ u32x4 gelu_vec(u32x4 yv, const float* b) {
   unpack<D>(yv, f);
 #pragma unroll
   for (int k = 0; k < V; ++k) {
-    if constexpr (KIND == kTanh) {
-      const GeluF r = gelu_tanh_fwd(f[k] + b[k]);
-      f[k] = r.v * r.sc;
-    } else {
-      f[k] = gelu_erf_fwd(f[k] + b[k]);
-    }
+    const GeluF r = KIND == kTanh ? gelu_tanh_fwd(f[k] + b[k]) : gelu_erf_fwd(f[k] + b[k]);
+    f[k] = r.v * r.sc;
   }
   return pack<D>(f);
 }
@@ -86,14 +82,8 @@ __device__ __forceinline__ u32x4 gelu_grad_vec(u32x4 gv, u32x4 yv, const float* 
   unpack<D>(yv, f);
 #pragma unroll
   for (int k = 0; k < V; ++k) {
-    float d;
-    if constexpr (KIND == kTanh) {
-      const GeluB r = gelu_tanh_fwd_bwd(f[k] + b[k]);
-      d = (g[k] * r.d) * r.sc;
-    } else {
-      float unused;
-      d = g[k] * gelu_erf_fwd_bwd(f[k] + b[k], &unused);
-    }
+    const GeluB r = KIND == kTanh ? gelu_tanh_fwd_bwd(f[k] + b[k]) : gelu_erf_fwd_bwd(f[k] + b[k]);
+    const float d = (g[k] * r.d) * r.sc;
     acc[k] += d;
     f[k] = d;
   }
