@@ -17,6 +17,8 @@
  *   §4.3  the bias gradient is the per-element gradient reduced over tokens
  *   §2    bias-SwiGLU / bias-GEGLU gated activations, weighted SwiGLU
  *   §9    weighted SwiGLU equals unweighted SwiGLU times the weights
+ *   §5    the fused LayerNorm (eps, zero-centred gamma), here behind a
+ *         residual add
  *
  * Evaluation rules (readings where the pages are silent):
  *   - every input is decoded exactly to double; every formula is evaluated in
@@ -42,6 +44,7 @@
  * s = (float)(1 / (1 - p)).
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -462,6 +465,131 @@ int orc_bias_dropout_add_bwd(int dt, const void* g, int res_dt, void* dx, double
       if (dres) store_elem(res_dt, dres, i, gv);
       if (dbias) dbias[j] += v;
     }
+  return ORC_OK;
+}
+
+/* Residual add + LayerNorm [fusions §5: the fused LayerNorm wrapped for the
+ * listed hidden sizes, eps (default 1e-5) in the denominator, and the
+ * zero-centred gamma applied as weight + 1]. The pages do not print the
+ * normalisation itself; it is the standard LayerNorm over the hidden
+ * dimension with the biased (1/H) variance. The residual add in front reads
+ * the residual as §3.2 does (cast to x's dtype when they differ), so
+ *   h[t, j] = x + r'                                   rounded to dt (stored)
+ *   mean_t  = (1/H) sum_j h,   var_t = (1/H) sum_j (h - mean_t)^2
+ *   rstd_t  = 1 / sqrt(var_t + eps)
+ *   xhat    = (h - mean_t) * rstd_t
+ *   y[t, j] = xhat * gamma'_j + beta_j,  gamma' = gamma (+ 1 if zero_centered)
+ * The normalisation reads the ROUNDED h, as an unfused LayerNorm applied to
+ * the stored sum would. gamma, beta (nullable: 0) are dt vectors; eps is the
+ * float the caller passes, widened exactly.
+ * Outputs: h (dt, nullable), y (dt), y64, mean/rstd (double [T], nullable),
+ * mag (nullable): |gamma'| * (|xhat| + rstd * mean_j |h|) + |beta|, the size
+ * of the terms an fp32 evaluation of y combines. */
+static double ln_gamma(int dt, const void* gamma, int64_t j, int zero_centered) {
+  return load_elem(dt, gamma, j) + (zero_centered ? 1.0 : 0.0);
+}
+
+int orc_add_layer_norm_fwd(int dt, const void* x, const void* residual, int res_dt, const void* gamma,
+                           const void* beta, int zero_centered, float eps, void* h_out, void* y, double* y64,
+                           double* mag, double* mean_out, double* rstd_out, int64_t T, int64_t H) {
+  if (!dtype_ok(dt) || !dtype_ok(res_dt) || T < 0 || H <= 0 || !gamma || isnan(eps) || eps < 0.0f) return ORC_BAD;
+  double* h = (double*)malloc(sizeof(double) * (size_t)H);
+  if (!h) return ORC_BAD;
+  for (int64_t t = 0; t < T; ++t) {
+    double sum = 0.0, asum = 0.0;
+    for (int64_t j = 0; j < H; ++j) {
+      int64_t i = t * H + j;
+      double rv = load_elem(res_dt, residual, i);
+      if (res_dt != dt) rv = to_dtype(dt, rv);
+      h[j] = to_dtype(dt, load_elem(dt, x, i) + rv);
+      if (h_out) store_elem(dt, h_out, i, h[j]);
+      sum += h[j];
+      asum += fabs(h[j]);
+    }
+    double mean = sum / (double)H, var = 0.0;
+    for (int64_t j = 0; j < H; ++j) var += (h[j] - mean) * (h[j] - mean);
+    var /= (double)H;
+    double rstd = 1.0 / sqrt(var + (double)eps);
+    for (int64_t j = 0; j < H; ++j) {
+      int64_t i = t * H + j;
+      double xhat = (h[j] - mean) * rstd;
+      double gj = ln_gamma(dt, gamma, j, zero_centered);
+      double bj = beta ? load_elem(dt, beta, j) : 0.0;
+      double v = xhat * gj + bj;
+      store_elem(dt, y, i, v);
+      if (y64) y64[i] = v;
+      if (mag) mag[i] = fabs(gj) * (fabs(xhat) + rstd * asum / (double)H) + fabs(bj);
+    }
+    if (mean_out) mean_out[t] = mean;
+    if (rstd_out) rstd_out[t] = rstd;
+  }
+  free(h);
+  return ORC_OK;
+}
+
+/* Backward of residual add + LayerNorm. With a = dy * gamma' and xhat as in
+ * the forward (recomputed here from h):
+ *   dh[t, j]   = rstd_t * (a - mean_j a - xhat * mean_j (a * xhat)) + dh_in
+ *   dx         = dh rounded to dt;  dresidual = dh rounded to res_dt (nullable)
+ *   dgamma[j]  = sum_t dy * xhat,   dbeta[j] = sum_t dy        (double, nullable)
+ * dh_in (res_dt, nullable) is the gradient reaching h from its other use as
+ * the next residual; h = x + r' passes dh unchanged to both x and the
+ * residual. mag (nullable): rstd * (|a| + mean|a| + (|xhat| + rstd mean|h|)
+ * * mean|a xhat|) + |dh_in|. */
+int orc_add_layer_norm_bwd(int dt, const void* dy, const void* h_in, const void* gamma, int zero_centered,
+                           float eps, const void* dh_in, int res_dt, void* dx, double* dx64, double* mag,
+                           void* dres, double* dgamma, double* dbeta, int64_t T, int64_t H) {
+  if (!dtype_ok(dt) || !dtype_ok(res_dt) || T < 0 || H <= 0 || !gamma || isnan(eps) || eps < 0.0f) return ORC_BAD;
+  double* h = (double*)malloc(sizeof(double) * (size_t)H);
+  double* a = (double*)malloc(sizeof(double) * (size_t)H);
+  if (!h || !a) {
+    free(h);
+    free(a);
+    return ORC_BAD;
+  }
+  if (dgamma)
+    for (int64_t j = 0; j < H; ++j) dgamma[j] = 0.0;
+  if (dbeta)
+    for (int64_t j = 0; j < H; ++j) dbeta[j] = 0.0;
+  for (int64_t t = 0; t < T; ++t) {
+    double sum = 0.0, asum_h = 0.0;
+    for (int64_t j = 0; j < H; ++j) {
+      h[j] = load_elem(dt, h_in, t * H + j);
+      sum += h[j];
+      asum_h += fabs(h[j]);
+    }
+    double mean = sum / (double)H, var = 0.0;
+    for (int64_t j = 0; j < H; ++j) var += (h[j] - mean) * (h[j] - mean);
+    var /= (double)H;
+    double rstd = 1.0 / sqrt(var + (double)eps);
+    double sa = 0.0, sax = 0.0, abs_a = 0.0, abs_ax = 0.0;
+    for (int64_t j = 0; j < H; ++j) {
+      double xhat = (h[j] - mean) * rstd;
+      double dyv = load_elem(dt, dy, t * H + j);
+      a[j] = dyv * ln_gamma(dt, gamma, j, zero_centered);
+      sa += a[j];
+      sax += a[j] * xhat;
+      abs_a += fabs(a[j]);
+      abs_ax += fabs(a[j] * xhat);
+      if (dgamma) dgamma[j] += dyv * xhat;
+      if (dbeta) dbeta[j] += dyv;
+    }
+    double ma = sa / (double)H, max_ = sax / (double)H;
+    for (int64_t j = 0; j < H; ++j) {
+      int64_t i = t * H + j;
+      double xhat = (h[j] - mean) * rstd;
+      double up = dh_in ? load_elem(res_dt, dh_in, i) : 0.0;
+      double v = rstd * (a[j] - ma - xhat * max_) + up;
+      store_elem(dt, dx, i, v);
+      if (dx64) dx64[i] = v;
+      if (dres) store_elem(res_dt, dres, i, v);
+      if (mag)
+        mag[i] = rstd * (fabs(a[j]) + abs_a / (double)H + (fabs(xhat) + rstd * asum_h / (double)H) * abs_ax / (double)H) +
+                 fabs(up);
+    }
+  }
+  free(h);
+  free(a);
   return ORC_OK;
 }
 
