@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
             L.orc_bias_dropout_add_bwd.argtypes = [I, P, I, P, P, P, P, I64, I64, F, U64, U64, I64]
             L.orc_bias_glu_fwd.argtypes = [I, I, P, P, P, I, P, P, I64, I64]
             L.orc_bias_glu_bwd.argtypes = [I, I, P, P, P, P, I, P, P, P, P, P, I64, I64]
+            L.orc_add_layer_norm_fwd.argtypes = [I, P, P, I, P, P, I, F, P, P, P, P, P, P, I64, I64]
+            L.orc_add_layer_norm_bwd.argtypes = [I, P, P, P, I, F, P, I, P, P, P, P, P, P, I64, I64]
             L.orc_philox4x32_10.argtypes = [P, P, P]
             L.orc_philox4x32_10.restype = None
             for name in ("orc_gelu_tanh", "orc_gelu_tanh_grad", "orc_gelu_erf", "orc_gelu_erf_grad",
@@ -228,6 +230,48 @@ def bias_dropout_add_bwd(dt, g, res_dt, p, seed, offset=0, row0=0, want_dres=Tru
     _ok(lib().orc_bias_dropout_add_bwd(DTYPES[dt], _ptr(g), DTYPES[res_dt], _ptr(dx), _ptr(dx64), _ptr(dres),
                                        _ptr(dbias), T, H, float(p), int(seed), int(offset), int(row0)))
     return dx, dx64, dres, dbias
+
+
+def add_layer_norm_fwd(dt, x, residual, res_dt, gamma, beta=None, eps=1e-5, zero_centered=False):
+    """Residual add + LayerNorm. Returns h (dt storage), y (dt storage), y64,
+    mag64, mean64 [T], rstd64 [T]."""
+    T, H = x.shape
+    x = _check_in(x, dt, name="x")
+    residual = _check_in(residual, res_dt, (T, H), "residual")
+    gamma = _check_in(gamma, dt, (H,), "gamma")
+    beta = _check_in(beta, dt, (H,), "beta")
+    h = np.empty((T, H), _storage(dt))
+    y = np.empty((T, H), _storage(dt))
+    y64 = np.empty((T, H), np.float64)
+    mag = np.empty((T, H), np.float64)
+    mean = np.empty((T,), np.float64)
+    rstd = np.empty((T,), np.float64)
+    _ok(lib().orc_add_layer_norm_fwd(DTYPES[dt], _ptr(x), _ptr(residual), DTYPES[res_dt], _ptr(gamma), _ptr(beta),
+                                     int(bool(zero_centered)), float(eps), _ptr(h), _ptr(y), _ptr(y64), _ptr(mag),
+                                     _ptr(mean), _ptr(rstd), T, H))
+    return h, y, y64, mag, mean, rstd
+
+
+def add_layer_norm_bwd(dt, dy, h, gamma, eps=1e-5, zero_centered=False, dh_in=None, res_dt=None,
+                       want_dres=True):
+    """Returns dx (dt storage), dx64, mag64, dresidual (res_dt storage or None),
+    dgamma64 [H], dbeta64 [H]."""
+    T, H = h.shape
+    res_dt = res_dt or dt
+    dy = _check_in(dy, dt, (T, H), "dy")
+    h = _check_in(h, dt, name="h")
+    gamma = _check_in(gamma, dt, (H,), "gamma")
+    dh_in = _check_in(dh_in, res_dt, (T, H), "dh_in")
+    dx = np.empty((T, H), _storage(dt))
+    dx64 = np.empty((T, H), np.float64)
+    mag = np.empty((T, H), np.float64)
+    dres = np.empty((T, H), _storage(res_dt)) if want_dres else None
+    dgamma = np.empty((H,), np.float64)
+    dbeta = np.empty((H,), np.float64)
+    _ok(lib().orc_add_layer_norm_bwd(DTYPES[dt], _ptr(dy), _ptr(h), _ptr(gamma), int(bool(zero_centered)),
+                                     float(eps), _ptr(dh_in), DTYPES[res_dt], _ptr(dx), _ptr(dx64), _ptr(mag),
+                                     _ptr(dres), _ptr(dgamma), _ptr(dbeta), T, H))
+    return dx, dx64, mag, dres, dgamma, dbeta
 
 
 def dropout_mask(T, H, p, seed, offset, row0=0):

@@ -574,12 +574,12 @@ int orc_add_layer_norm_bwd(int dt, const void* dy, const void* h_in, const void*
       if (dgamma) dgamma[j] += dyv * xhat;
       if (dbeta) dbeta[j] += dyv;
     }
-    double ma = sa / (double)H, max_ = sax / (double)H;
+    double ma = sa / (double)H, max = sax / (double)H;
     for (int64_t j = 0; j < H; ++j) {
       int64_t i = t * H + j;
       double xhat = (h[j] - mean) * rstd;
       double up = dh_in ? load_elem(res_dt, dh_in, i) : 0.0;
-      double v = rstd * (a[j] - ma - xhat * max_) + up;
+      double v = rstd * (a[j] - ma - xhat * max) + up;
       store_elem(dt, dx, i, v);
       if (dx64) dx64[i] = v;
       if (dres) store_elem(res_dt, dres, i, v);
