@@ -200,6 +200,58 @@ mb_status_t mb_bias_geglu_bwd(const void* g, const void* in, const void* bias, v
                               float* dbias, void* ws, size_t ws_bytes, int64_t tokens,
                               int64_t hidden, mb_dtype_t dt, hipStream_t s);
 
+/* ---------------------------------------------------------------------------
+ * Residual add + LayerNorm [fusions §5.1-§5.4: the fused LayerNorm that
+ * Megatron-LM wraps, its eps (default 1e-5) in the denominator, and the
+ * zero-centred gamma applied as weight + 1], fused with the residual add that
+ * precedes it on a layer's residual path. The normalisation is the standard
+ * one over the hidden dimension with the biased (1/H) variance:
+ *   h[t, j] = x + residual'     residual' = residual cast to dt when it is fp32
+ *                               (as in the dropout-add); h rounded to dt
+ *   mean_t  = (1/H) sum_j h,  var_t = (1/H) sum_j (h - mean_t)^2
+ *   rstd_t  = 1 / sqrt(var_t + eps)
+ *   y[t, j] = (h - mean_t) * rstd_t * gamma'_j + beta_j
+ *   gamma'  = gamma + 1 when zero_centered_gamma != 0, else gamma
+ * computed in fp32 from the ROUNDED h.
+ *
+ * x, y, h_out [T,H] dt; residual [T,H] residual_dt (= dt, or MB_F32 beside
+ * fp16/bf16); gamma [H] dt (required), beta [H] dt or NULL (0); h_out NULL
+ * skips storing h; mean, rstd [T] fp32, both or neither (the backward needs
+ * them). hidden: a multiple of 8 elements for fp16/bf16 rows (4 with an fp32
+ * residual, and for fp32) and at most 65536 fp16/bf16 or 32768 fp32 (or
+ * fp16/bf16 with an fp32 residual) elements. eps: finite, >= 0.
+ * Aliasing: h_out and y may each equal x or residual exactly (same dtype),
+ * never each other; nothing else may overlap. Errors: MB_ERR_DTYPE,
+ * MB_ERR_SHAPE, MB_ERR_NULL, MB_ERR_ALIGN (16-byte tensors, 4-byte mean/rstd),
+ * MB_ERR_ALIAS, MB_ERR_PROB (eps out of range), MB_ERR_HIP. */
+mb_status_t mb_add_layer_norm_fwd(const void* x, const void* residual, mb_dtype_t residual_dt,
+                                  const void* gamma, const void* beta, float eps,
+                                  int zero_centered_gamma, void* h_out, void* y, float* mean,
+                                  float* rstd, int64_t tokens, int64_t hidden, mb_dtype_t dt,
+                                  hipStream_t s);
+
+/* Workspace bytes for mb_add_layer_norm_bwd (0 when no parameter gradient is
+ * requested). */
+size_t mb_add_layer_norm_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt,
+                                       mb_dtype_t residual_dt, int with_param_grads);
+
+/* Backward of residual add + LayerNorm, from the forward's h, mean and rstd.
+ * With a = dy * gamma' and xhat = (h - mean) * rstd:
+ *   dh[t, j]  = rstd * (a - (1/H) sum_j a - xhat (1/H) sum_j a xhat) + dh_in
+ *   dx        = dh in dt;  dresidual = dh in residual_dt (NULL: skip)
+ *   dgamma[j] = sum_t dy * xhat,  dbeta[j] = sum_t dy   (fp32 [H], NULL: skip)
+ * dh_in [T,H] residual_dt or NULL: the gradient reaching h from its use as the
+ * next residual. dx may equal dy or h exactly; dresidual may equal dh_in, or
+ * dy or h when residual_dt == dt. The parameter gradients are deterministic
+ * and atomic-free (partials in ws, sized by mb_add_layer_norm_bwd_workspace,
+ * then ordered column sums). Errors as for the forward, plus MB_ERR_WORKSPACE. */
+mb_status_t mb_add_layer_norm_bwd(const void* dy, const void* h, const void* gamma,
+                                  const float* mean, const float* rstd, int zero_centered_gamma,
+                                  const void* dh_in, mb_dtype_t residual_dt, void* dx,
+                                  void* dresidual, float* dgamma, float* dbeta, void* ws,
+                                  size_t ws_bytes, int64_t tokens, int64_t hidden, mb_dtype_t dt,
+                                  hipStream_t s);
+
 #ifdef __cplusplus
 }
 #endif

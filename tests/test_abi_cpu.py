@@ -112,3 +112,36 @@ def test_glu_validation():
     assert bw(A, B, None, E, BF16, C, D, D + 4096 * 4, None, 0, 64, 512, BF16, None) == WORKSPACE
     assert bw(A, B, None, None, BF16, A, None, None, None, 0, 64, 512, BF16, None) == ALIAS  # din over g
     assert bw(A, B, None, None, BF16, B, None, None, None, 0, 0, 512, BF16, None) == OK      # in place, empty
+
+
+def test_layer_norm_validation():
+    fw, bw, wsf = L().mb_add_layer_norm_fwd, L().mb_add_layer_norm_bwd, L().mb_add_layer_norm_bwd_workspace
+    # (x, residual, residual_dt, gamma, beta, eps, zero_centered, h_out, y, mean, rstd, T, H, dt, stream)
+    assert fw(A, B, BF16, C, None, 1e-5, 0, None, D, None, None, 4, 60, BF16, None) == SHAPE   # not whole vectors
+    assert fw(A, B, BF16, C, None, 1e-5, 0, None, D, None, None, 0, 65536, BF16, None) == OK
+    assert fw(A, B, BF16, C, None, 1e-5, 0, None, D, None, None, 4, 65536 + 8, BF16, None) == SHAPE  # too wide
+    assert fw(A, B, F32, C, None, 1e-5, 0, None, D, None, None, 0, 32768, BF16, None) == OK
+    assert fw(A, B, F32, C, None, 1e-5, 0, None, D, None, None, 4, 32768 + 4, BF16, None) == SHAPE
+    assert fw(A, B, F32, C, None, 1e-5, 0, None, D, None, None, 0, 36, BF16, None) == OK       # 4-element pieces
+    assert fw(A, B, F32, C, None, 1e-5, 0, None, D, None, None, 4, 32772, F32, None) == SHAPE
+    assert fw(A, B, F16, C, None, 1e-5, 0, None, D, None, None, 4, 64, BF16, None) == DTYPE     # residual dt or fp32
+    for eps in (-1.0, float("nan"), float("inf")):
+        assert fw(A, B, BF16, C, None, eps, 0, None, D, None, None, 4, 64, BF16, None) == PROB
+    assert fw(A, B, BF16, None, None, 1e-5, 0, None, D, None, None, 4, 64, BF16, None) == NULL  # gamma required
+    assert fw(A, B, BF16, C, None, 1e-5, 0, None, D, E, None, 4, 64, BF16, None) == NULL        # mean without rstd
+    assert fw(A + 8, B, BF16, C, None, 1e-5, 0, None, D, None, None, 4, 64, BF16, None) == ALIGN
+    assert fw(A, B, BF16, C, None, 1e-5, 0, D, D, None, None, 4, 64, BF16, None) == ALIAS       # h_out == y
+    assert fw(A, B, BF16, C, None, 1e-5, 0, None, C, None, None, 4, 64, BF16, None) == ALIAS    # y over gamma
+    assert fw(A, B, BF16, C, None, 1e-5, 0, A, B, None, None, 0, 64, BF16, None) == OK          # h into x, y into r
+    assert fw(A, B, F32, C, None, 1e-5, 0, None, B, None, None, 4, 64, BF16, None) == ALIAS     # y over fp32 residual
+    # backward (dy, h, gamma, mean, rstd, zc, dh_in, rdt, dx, dres, dgamma, dbeta, ws, ws_bytes, T, H, dt, stream)
+    ws = wsf(1024, 8192, BF16, BF16, 1)
+    assert ws > 0 and wsf(1024, 8192, BF16, BF16, 0) == 0 and wsf(0, 8192, BF16, BF16, 1) == 0
+    assert wsf(1024, 65536, BF16, BF16, 1) > 0
+    assert bw(A, B, C, D, E, 0, None, BF16, 0x60000000, None, 0x70000000, None, None, 0, 1024, 8192, BF16,
+              None) == WORKSPACE
+    assert bw(A, B, C, D, None, 0, None, BF16, 0x60000000, None, None, None, None, 0, 1024, 8192, BF16,
+              None) == NULL
+    assert bw(A, B, C, D, E, 0, None, BF16, A + 16, None, None, None, None, 0, 1024, 8192, BF16, None) == ALIAS
+    assert bw(A, B, C, D, E, 0, None, BF16, A, B, None, None, None, 0, 0, 8192, BF16, None) == OK  # dx = dy, dres = h
+    assert bw(A, B, C, D, E, 0, None, F32, A, B, None, None, None, 0, 4, 8192, BF16, None) == ALIAS

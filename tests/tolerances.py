@@ -107,3 +107,35 @@ def assert_reduction_close(kernel: np.ndarray, oracle64: np.ndarray, what=""):
         raise AssertionError(f"{what}: {int(bad.sum())}/{o.size} out of 1e-3 tolerance; first {list(zip(i, k[i], o[i]))}")
     worst = float(np.max(np.abs(k - o) / (np.abs(o) + rms + 1e-300))) if o.size else 0.0
     return {"n": int(o.size), "max_rel_to_rms": worst}
+
+
+def assert_close_bounded(kernel, oracle_out, o64, bound, dt, what=""):
+    """For ops whose fp32 evaluation error has a derived bound per element
+    (row reductions such as LayerNorm): passes when the bits are equal, both
+    are NaN, |k - o| <= 1 ulp of the once-rounded oracle value (bf16/fp16), or
+    |k - o64| <= bound + the output rounding (half an fp32 ulp, one bf16/fp16
+    ulp)."""
+    k = values(kernel, dt)
+    o = values(oracle_out, dt)
+    same_bits = kernel.view(np.uint32 if dt == "f32" else np.uint16) == oracle_out.view(
+        np.uint32 if dt == "f32" else np.uint16)
+    both_nan = np.isnan(k) & np.isnan(o)
+    with np.errstate(invalid="ignore"):
+        if dt == "f32":
+            ok = np.abs(k - o64) <= bound + 2.0**-24 * np.abs(o64)
+        else:
+            ok = (np.abs(k - o) <= ulp(o, dt)) | (np.abs(k - o64) <= bound + ulp(o64, dt))
+    passed = same_bits | both_nan | ok
+    err = np.abs(k - o64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        ratio = np.where(bound > 0, err / bound, 0.0)
+    stats = {"n": int(k.size), "fail": int((~passed).sum()), "bit_equal": int(same_bits.sum()),
+             "max_err_over_bound": float(np.nanmax(ratio)) if ratio.size else 0.0,
+             "max_abs": float(np.nanmax(err)) if err.size else 0.0}
+    if stats["fail"]:
+        idx = np.flatnonzero(~passed.reshape(-1))[:8]
+        ex = [(int(i), float(k.reshape(-1)[i]), float(o64.reshape(-1)[i]), float(np.reshape(bound, -1)[i]))
+              for i in idx]
+        raise AssertionError(f"{what}: {stats['fail']}/{stats['n']} out of bound; first (index, kernel, oracle64, "
+                             f"bound): {ex}; stats {stats}")
+    return stats

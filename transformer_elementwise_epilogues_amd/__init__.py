@@ -23,6 +23,7 @@ __all__ = [
     "mb_bias_dropout_add_bwd", "mb_bias_dropout_add_bwd_workspace",
     "mb_bias_swiglu_fwd", "mb_bias_swiglu_bwd", "mb_bias_geglu_fwd", "mb_bias_geglu_bwd",
     "mb_bias_glu_bwd_workspace",
+    "mb_add_layer_norm_fwd", "mb_add_layer_norm_bwd", "mb_add_layer_norm_bwd_workspace",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmb.so")
@@ -69,6 +70,9 @@ def lib() -> ctypes.CDLL:
                 "mb_bias_glu_bwd_workspace": ([I64, I64, I, I, I], SZ),
                 "mb_bias_swiglu_bwd": ([P, P, P, P, I, P, P, P, P, SZ, I64, I64, I, P], I),
                 "mb_bias_geglu_bwd": ([P, P, P, P, P, P, SZ, I64, I64, I, P], I),
+                "mb_add_layer_norm_fwd": ([P, P, I, P, P, F, I, P, P, P, P, I64, I64, I, P], I),
+                "mb_add_layer_norm_bwd_workspace": ([I64, I64, I, I, I], SZ),
+                "mb_add_layer_norm_bwd": ([P, P, P, P, P, I, P, I, P, P, P, P, P, SZ, I64, I64, I, P], I),
             }
             for name, (args, res) in sig.items():
                 f = getattr(L, name)
@@ -301,3 +305,68 @@ def mb_bias_geglu_bwd(g, inp, bias=None, din=None, dbias=True, ws=None, stream=N
         _p(g), _p(inp), _p(bias), _p(din), _p(dbias), _p(ws), ws.numel() if ws is not None else 0, T, H,
         _dt(inp), _stream(inp, stream)))
     return din, dbias
+
+
+# ------------------------------------------------------------------ residual add + LayerNorm
+
+def mb_add_layer_norm_fwd(x, residual, gamma, beta=None, eps=1e-5, zero_centered_gamma=False, h_out=True,
+                          y=None, stats=True, stream=None):
+    """h = x + residual (cast to x's dtype), y = LayerNorm(h) * gamma' + beta.
+    Returns (y, h or None, mean or None, rstd or None). h_out=True allocates h
+    (False skips it; a tensor, e.g. x itself, receives it); stats=True
+    allocates the fp32 mean / rstd the backward needs."""
+    T, H = _rows(x, "x")
+    _rows(residual, "residual", H)
+    if residual.shape[0] != T:
+        raise ValueError("residual must have x's shape")
+    _vec(gamma, H, "gamma")
+    _vec(beta, H, "beta")
+    if h_out is True:
+        h_out = torch.empty_like(x)
+    elif h_out is False:
+        h_out = None
+    y = torch.empty_like(x) if y is None else y
+    mean = rstd = None
+    if stats:
+        mean = torch.empty(T, dtype=torch.float32, device=x.device)
+        rstd = torch.empty(T, dtype=torch.float32, device=x.device)
+    _check("mb_add_layer_norm_fwd", lib().mb_add_layer_norm_fwd(
+        _p(x), _p(residual), _dt(residual), _p(gamma), _p(beta), float(eps), int(bool(zero_centered_gamma)),
+        _p(h_out), _p(y), _p(mean), _p(rstd), T, H, _dt(x), _stream(x, stream)))
+    return y, h_out, mean, rstd
+
+
+def mb_add_layer_norm_bwd_workspace(tokens, hidden, dtype, residual_dtype=None, with_param_grads=True) -> int:
+    rdt = residual_dtype or dtype
+    return int(lib().mb_add_layer_norm_bwd_workspace(tokens, hidden, DTYPES[dtype], DTYPES[rdt],
+                                                     int(bool(with_param_grads))))
+
+
+def mb_add_layer_norm_bwd(dy, h, gamma, mean, rstd, zero_centered_gamma=False, dh_in=None, residual_dtype=None,
+                          dx=None, dresidual=False, dgamma=True, dbeta=True, ws=None, stream=None):
+    """Returns (dx, dresidual or None, dgamma or None, dbeta or None).
+    residual_dtype (default: dh_in's dtype, else h's) is the dtype of dh_in and
+    dresidual; dresidual=True allocates it."""
+    T, H = _rows(h, "h")
+    _rows(dy, "dy", H)
+    _vec(gamma, H, "gamma")
+    _vec(mean, T, "mean")
+    _vec(rstd, T, "rstd")
+    rdt = residual_dtype or (dh_in.dtype if dh_in is not None else h.dtype)
+    if dh_in is not None:
+        _rows(dh_in, "dh_in", H)
+    dx = torch.empty_like(h) if dx is None else dx
+    if dresidual is True:
+        dresidual = torch.empty((T, H), dtype=rdt, device=h.device)
+    elif dresidual is False:
+        dresidual = None
+    dgamma = _grad_out(dgamma, H, h.device)
+    dbeta = _grad_out(dbeta, H, h.device)
+    nws = mb_add_layer_norm_bwd_workspace(T, H, h.dtype, rdt, dgamma is not None or dbeta is not None)
+    if ws is None and nws:
+        ws = torch.empty(nws, dtype=torch.uint8, device=h.device)
+    _check("mb_add_layer_norm_bwd", lib().mb_add_layer_norm_bwd(
+        _p(dy), _p(h), _p(gamma), _p(mean), _p(rstd), int(bool(zero_centered_gamma)), _p(dh_in), DTYPES[rdt],
+        _p(dx), _p(dresidual), _p(dgamma), _p(dbeta), _p(ws), ws.numel() if ws is not None else 0, T, H,
+        _dt(h), _stream(h, stream)))
+    return dx, dresidual, dgamma, dbeta

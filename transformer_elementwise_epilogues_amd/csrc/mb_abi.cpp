@@ -412,4 +412,151 @@ mb_status_t mb_bias_geglu_bwd(const void* g, const void* in, const void* bias, v
                         s);
 }
 
+// ------------------------------------------------------------------ residual add + LayerNorm
+
+static bool ln_dtypes_ok(mb_dtype_t dt, mb_dtype_t rdt) { return dt_ok(dt) && (rdt == dt || rdt == MB_F32); }
+
+// Shape rule of the LayerNorm rows: whole vectors, a row-group shape that holds
+// the row, sizes within the kernels' index math.
+static mb_status_t ln_shape(int64_t T, int64_t H, mb_dtype_t dt, mb_dtype_t rdt, mb::LnPlan* plan) {
+  if (T < 0 || H <= 0 || T > (int64_t{1} << 40) || H > (int64_t{1} << 20)) return MB_ERR_SHAPE;
+  const int E = mb::ln_elems_per_vector(dt, rdt);
+  if (H % E != 0) return MB_ERR_SHAPE;
+  *plan = mb::plan_ln(T, H, dt, rdt, MB_LN_BWD_BLOCKS);
+  if (plan->shape < 0) return MB_ERR_SHAPE;
+  return MB_OK;
+}
+
+static bool eps_ok(float eps) { return std::isfinite(eps) && eps >= 0.0f; }
+
+mb_status_t mb_add_layer_norm_fwd(const void* x, const void* residual, mb_dtype_t residual_dt, const void* gamma,
+                                  const void* beta, float eps, int zero_centered_gamma, void* h_out, void* y,
+                                  float* mean, float* rstd, int64_t tokens, int64_t hidden, mb_dtype_t dt,
+                                  hipStream_t s) {
+  if (!ln_dtypes_ok(dt, residual_dt)) return MB_ERR_DTYPE;
+  mb::LnPlan plan;
+  if (mb_status_t st = ln_shape(tokens, hidden, dt, residual_dt, &plan)) return st;
+  if (!eps_ok(eps)) return MB_ERR_PROB;
+  const size_t n = static_cast<size_t>(tokens) * hidden;
+  const size_t tb = n * esize(dt), rb = n * esize(residual_dt), hb = static_cast<size_t>(hidden) * esize(dt),
+               sb = static_cast<size_t>(tokens) * 4;
+  if (!gamma || !need(x, tb) || !need(residual, rb) || !need(y, tb)) return MB_ERR_NULL;
+  if ((mean == nullptr) != (rstd == nullptr)) return MB_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(gamma, 16) || !aligned(beta, 16) ||
+      !aligned(h_out, 16) || !aligned(y, 16) || !aligned(mean, 4) || !aligned(rstd, 4))
+    return MB_ERR_ALIGN;
+  if (!aliasing_ok({{h_out, h_out ? tb : 0}, {y, tb}, {mean, mean ? sb : 0}, {rstd, rstd ? sb : 0}},
+                   {{x, tb}, {residual, rb}, {gamma, hb}, {beta, beta ? hb : 0}}, {{0, 0}, {1, 0}, {0, 1}, {1, 1}}))
+    return MB_ERR_ALIAS;
+  if (tokens == 0) return MB_OK;
+  mb::LnArgs a;
+  a.dt = dt;
+  a.rdt = residual_dt;
+  a.T = tokens;
+  a.H = hidden;
+  a.eps = eps;
+  a.gshift = zero_centered_gamma ? 1.0f : 0.0f;
+  a.x = x;
+  a.res = residual;
+  a.gamma = gamma;
+  a.beta = beta;
+  a.hout = h_out;
+  a.y = y;
+  a.mean = mean;
+  a.rstd = rstd;
+  const mb::LnPlan fp = mb::plan_ln(tokens, hidden, dt, residual_dt, MB_LN_FWD_BLOCKS);
+  if (hipError_t e = mb::launch_ln_fwd(a, fp, s)) return hip_status(e);
+  return finish();
+}
+
+// Workspace layout: partial rows of dgamma, then of dbeta, then the chunk sums
+// of each when there are more than 32 partial rows (256-byte aligned pieces).
+struct LnWs {
+  size_t pg = 0, pb = 0, tg = 0, tb = 0, total = 0;
+};
+static LnWs ln_ws_layout(const mb::LnPlan& p, int64_t H) {
+  LnWs w;
+  const size_t part = round_up(static_cast<size_t>(p.partial_rows) * H * 4, 256);
+  const size_t tmp = round_up(static_cast<size_t>(mb::colsum_tall_tmp_floats(p.partial_rows, H)) * 4, 256);
+  w.pg = 0;
+  w.pb = part;
+  w.tg = 2 * part;
+  w.tb = 2 * part + tmp;
+  w.total = 2 * part + 2 * tmp;
+  return w;
+}
+
+size_t mb_add_layer_norm_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, mb_dtype_t residual_dt,
+                                       int with_param_grads) {
+  if (!with_param_grads || !ln_dtypes_ok(dt, residual_dt) || tokens == 0) return 0;
+  mb::LnPlan plan;
+  if (ln_shape(tokens, hidden, dt, residual_dt, &plan) != MB_OK) return 0;
+  return ln_ws_layout(plan, hidden).total;
+}
+
+mb_status_t mb_add_layer_norm_bwd(const void* dy, const void* h, const void* gamma, const float* mean,
+                                  const float* rstd, int zero_centered_gamma, const void* dh_in,
+                                  mb_dtype_t residual_dt, void* dx, void* dresidual, float* dgamma, float* dbeta,
+                                  void* ws, size_t ws_bytes, int64_t tokens, int64_t hidden, mb_dtype_t dt,
+                                  hipStream_t s) {
+  if (!ln_dtypes_ok(dt, residual_dt)) return MB_ERR_DTYPE;
+  mb::LnPlan plan;
+  if (mb_status_t st = ln_shape(tokens, hidden, dt, residual_dt, &plan)) return st;
+  const size_t n = static_cast<size_t>(tokens) * hidden;
+  const size_t tb = n * esize(dt), rb = n * esize(residual_dt), hb = static_cast<size_t>(hidden) * esize(dt),
+               sb = static_cast<size_t>(tokens) * 4;
+  if (!gamma || !need(dy, tb) || !need(h, tb) || !need(dx, tb) || !need(mean, sb) || !need(rstd, sb))
+    return MB_ERR_NULL;
+  if (!aligned(dy, 16) || !aligned(h, 16) || !aligned(gamma, 16) || !aligned(dh_in, 16) || !aligned(dx, 16) ||
+      !aligned(dresidual, 16) || !aligned(mean, 4) || !aligned(rstd, 4) || !aligned(dgamma, 16) ||
+      !aligned(dbeta, 16) || !aligned(ws, 16))
+    return MB_ERR_ALIGN;
+  const bool params = dgamma || dbeta;
+  const LnWs lay = ln_ws_layout(plan, hidden);
+  const size_t need_ws = params && tokens > 0 ? lay.total : 0;
+  if (need_ws && (!ws || ws_bytes < need_ws)) return MB_ERR_WORKSPACE;
+  const size_t pb4 = static_cast<size_t>(hidden) * 4;
+  if (!aliasing_ok({{dx, tb}, {dresidual, dresidual ? rb : 0}, {dgamma, dgamma ? pb4 : 0},
+                    {dbeta, dbeta ? pb4 : 0}, {ws, need_ws}},
+                   {{dy, tb}, {h, tb}, {gamma, hb}, {mean, sb}, {rstd, sb}, {dh_in, dh_in ? rb : 0}},
+                   {{0, 0}, {0, 1}, {1, 5}, {1, 0}, {1, 1}}))
+    return MB_ERR_ALIAS;
+  if (tokens == 0) {
+    if (dgamma)
+      if (hipError_t e = mb::launch_fill_zero(dgamma, hidden, s)) return hip_status(e);
+    if (dbeta)
+      if (hipError_t e = mb::launch_fill_zero(dbeta, hidden, s)) return hip_status(e);
+    return dgamma || dbeta ? finish() : MB_OK;
+  }
+  mb::LnArgs a;
+  a.dt = dt;
+  a.rdt = residual_dt;
+  a.T = tokens;
+  a.H = hidden;
+  a.gshift = zero_centered_gamma ? 1.0f : 0.0f;
+  a.dy = dy;
+  a.h = h;
+  a.gamma = gamma;
+  a.cmean = mean;
+  a.crstd = rstd;
+  a.dh_in = dh_in;
+  a.dx = dx;
+  a.dres = dresidual;
+  char* w = static_cast<char*>(ws);
+  if (params) {
+    a.pg = reinterpret_cast<float*>(w + lay.pg);
+    a.pb = reinterpret_cast<float*>(w + lay.pb);
+  }
+  if (hipError_t e = mb::launch_ln_bwd(a, plan, s)) return hip_status(e);
+  if (dgamma)
+    if (hipError_t e = mb::launch_colsum_tall(a.pg, plan.partial_rows, hidden, reinterpret_cast<float*>(w + lay.tg),
+                                              dgamma, s))
+      return hip_status(e);
+  if (dbeta)
+    if (hipError_t e = mb::launch_colsum_tall(a.pb, plan.partial_rows, hidden, reinterpret_cast<float*>(w + lay.tb),
+                                              dbeta, s))
+      return hip_status(e);
+  return finish();
+}
+
 }  // extern "C"

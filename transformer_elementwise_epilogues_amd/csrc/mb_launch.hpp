@@ -60,9 +60,23 @@ struct Tiling {
 #endif
 
 // The tiling every kernel of one call uses; also sizes the workspaces.
+#ifndef MB_LN_FWD_BLOCKS
+#define MB_LN_FWD_BLOCKS 2048
+#endif
+#ifndef MB_LN_BWD_BLOCKS
+#define MB_LN_BWD_BLOCKS 512
+#endif
+#ifndef MB_LN_DGB_BLOCKS
+#define MB_LN_DGB_BLOCKS 512
+#endif
+
 Tiling plan_tiling(int64_t T, int nvec, int target_blocks);
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+// As launch_colsum for many partial rows: rows are first summed in ascending
+// chunks of 32 into tmp ([ceil(R / 32), C]), then the chunk sums in order.
+hipError_t launch_colsum_tall(const float* in, int R, int64_t C, float* tmp, float* out, hipStream_t s);
+int64_t colsum_tall_tmp_floats(int R, int64_t C);
 // out[c] = sum over r < R of in[r * C + c], r ascending (fp32).
 hipError_t launch_colsum(const float* in, int R, int64_t C, float* out, hipStream_t s);
 
@@ -98,5 +112,43 @@ hipError_t launch_glu_fwd(int act, int dt, const void* in, const void* bias, con
 hipError_t launch_glu_bwd(int act, int dt, const void* g, const void* in, const void* bias,
                           const void* w, int w_dt, void* din, float* bias_partials,
                           float* w_partials, int64_t H, const Tiling& t, hipStream_t s);
+
+// ---- residual add + LayerNorm
+struct LnArgs {
+  int dt = 0, rdt = 0;  // activation and residual dtypes (DT values)
+  int64_t T = 0, H = 0;
+  float eps = 0.0f, gshift = 0.0f;  // gshift: 1 for a zero-centred gamma, else 0
+  // forward
+  const void* x = nullptr;
+  const void* res = nullptr;
+  const void* gamma = nullptr;
+  const void* beta = nullptr;  // nullable
+  void* hout = nullptr;        // nullable
+  void* y = nullptr;
+  float* mean = nullptr;  // nullable (with rstd)
+  float* rstd = nullptr;
+  // backward
+  const void* dy = nullptr;
+  const void* h = nullptr;
+  const float* cmean = nullptr;
+  const float* crstd = nullptr;
+  const void* dh_in = nullptr;  // nullable
+  void* dx = nullptr;
+  void* dres = nullptr;  // nullable
+  float* pg = nullptr;   // partial rows of dgamma / dbeta [partial_rows, H]; nullable
+  float* pb = nullptr;
+};
+struct LnPlan {
+  int nvec = 0;           // vectors of ln_elems_per_vector elements per row
+  int shape = -1;         // row-group shape; -1: the row is too wide
+  int grid = 0;           // blocks of the row kernels
+  bool split = false;     // dgamma / dbeta by the column-strip kernel
+  Tiling dgb;             // its tiling
+  int partial_rows = 0;   // partial rows the backward writes
+};
+int ln_elems_per_vector(int dt, int rdt);
+LnPlan plan_ln(int64_t T, int64_t H, int dt, int rdt, int target_blocks);
+hipError_t launch_ln_fwd(const LnArgs& a, const LnPlan& p, hipStream_t s);
+hipError_t launch_ln_bwd(const LnArgs& a, const LnPlan& p, hipStream_t s);
 
 }  // namespace mb

@@ -1,0 +1,569 @@
+// mb_ln.hip -- residual add + LayerNorm, forward and backward, on gfx950.
+//
+// [fusions §5]: Megatron-LM wraps a fused LayerNorm (a persistent kernel for a
+// fixed list of hidden sizes up to 65536, eps in the denominator, optional
+// zero-centred gamma used as weight + 1). Here it is fused with the residual
+// add in front of it, the step that follows the bias-dropout-add on both
+// residual paths of a layer:
+//   h = x + residual'   (residual cast to x's dtype first, h rounded to it)
+//   y = (h - mean) * rstd * gamma' + beta,   rstd = 1 / sqrt(var + eps)
+// with the biased (1/H) variance of the ROUNDED h.
+//
+// A row is normalised by one group of TPR threads (64, 256 or 1024) that holds
+// it in registers: thread l of the group owns the 16-byte vectors l, l + TPR,
+// ..., l + (NV-1) TPR of the row (E elements each), so every load and store
+// instruction of a wave covers one contiguous span. Row sums are a wave
+// butterfly and, across the group's waves, a fixed-order sum through LDS,
+// so results do not depend on scheduling. Groups of 64 threads run 4 rows per
+// block with no barrier at all. The mean and the variance are two passes over
+// the registers (no E[h^2] - E[h]^2 cancellation).
+//
+// The backward reads the forward's mean and rstd and computes, with
+// a = dy * gamma' and xhat = (h - mean) * rstd,
+//   dh = rstd * (a - mean_j a - xhat * mean_j (a xhat)) + dh_in
+// stored to dx (x's dtype) and optionally to dresidual (the residual's dtype).
+// dgamma = sum_t dy xhat and dbeta = sum_t dy accumulate per thread over the
+// block's rows (a block owns the same columns on every row it visits), are
+// written as one partial row per block, and summed in a fixed order by the
+// column-sum passes. For rows wider than 16384 bf16 elements (1024 threads of
+// 4 or 8 vectors each) the accumulators would not fit in registers beside the
+// row; there the row kernel writes dx only and a column-strip kernel re-reads
+// dy and h for the two parameter gradients.
+#include <algorithm>
+#include <type_traits>
+
+#include "mb_device.hpp"
+#include "mb_launch.hpp"
+
+namespace mb {
+
+namespace {
+
+// Elements per vector: 4 when an fp32 residual sits beside 16-bit activations
+// (8-byte activation pieces, 16-byte residual pieces), else one 16-byte vector.
+template <DT D, DT R> constexpr int ln_epl() { return (R == DT::F32 && D != DT::F32) ? 4 : Vec<D>::N; }
+
+// E elements of D kept packed in registers (8 or 16 bytes): rows live in
+// registers in their storage format and are unpacked for each pass, which is
+// exact for h (it is rounded to D by definition) and for dy and gamma.
+template <DT D, int E> struct Pk {
+  static constexpr int BYTES = E * Vec<D>::BYTES;
+  static_assert(BYTES == 8 || BYTES == 16, "8- or 16-byte pieces");
+  using T = typename std::conditional<BYTES == 16, u32x4, u32x2>::type;
+};
+
+template <DT D, int E> __device__ __forceinline__ typename Pk<D, E>::T pk_load(const char* p) {
+  using T = typename Pk<D, E>::T;
+  if constexpr (MB_NT_LOAD) return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+  return *reinterpret_cast<const T*>(p);
+}
+template <DT D, int E> __device__ __forceinline__ typename Pk<D, E>::T pk_load_keep(const char* p) {
+  return *reinterpret_cast<const typename Pk<D, E>::T*>(p);
+}
+template <DT D, int E> __device__ __forceinline__ void pk_store(char* p, typename Pk<D, E>::T v) {
+  using T = typename Pk<D, E>::T;
+  if constexpr (MB_NT_STORE)
+    __builtin_nontemporal_store(v, reinterpret_cast<T*>(p));
+  else
+    *reinterpret_cast<T*>(p) = v;
+}
+template <DT D, int E> __device__ __forceinline__ void pk_unpack(typename Pk<D, E>::T v, float* f) {
+  if constexpr (Pk<D, E>::BYTES == 16) {
+    unpack<D>(v, f);
+  } else {
+    const unsigned v0 = v.x, v1 = v.y;
+    const u32x4 w = {v0, v1, 0u, 0u};
+    float t[8];
+    unpack<D>(w, t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = t[e];
+  }
+}
+template <DT D, int E> __device__ __forceinline__ typename Pk<D, E>::T pk_pack(const float* f) {
+  if constexpr (Pk<D, E>::BYTES == 16) {
+    return pack<D>(f);
+  } else {
+    const unsigned w0 = D == DT::BF16 ? pk_bf16(f[0], f[1]) : pk_f16(f[0], f[1]);
+    const unsigned w1 = D == DT::BF16 ? pk_bf16(f[2], f[3]) : pk_f16(f[2], f[3]);
+    return typename Pk<D, E>::T{w0, w1};
+  }
+}
+
+// Makes the compiler treat a packed value as changed, so that a later pass
+// unpacks it again instead of keeping the unpacked floats of an earlier pass
+// alive across the row reduction (twice the registers). Emits no instruction.
+template <typename V> __device__ __forceinline__ void opaque(V& v) { asm volatile("" : "+v"(v)); }
+
+// LDS of the in-row reductions: [row in block][slot][wave of the row].
+template <int W, int RPB> struct RowLds {
+  float v[RPB][4][W];
+};
+
+// Sum of `v` over the row group's W waves. W == 1: a wave butterfly, no
+// barrier. W > 1: every thread of the block must call it (RPB is 1 then).
+template <int W, int RPB>
+__device__ __forceinline__ float row_sum(float v, RowLds<W, RPB>& lds, int sub, int wr, int lane, int slot) {
+  v = wave_sum(v);
+  if constexpr (W == 1) {
+    return v;
+  } else {
+    if (lane == 0) lds.v[sub][slot][wr] = v;
+    __syncthreads();
+    float t = lds.v[sub][slot][0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) t += lds.v[sub][slot][w];
+    return t;
+  }
+}
+
+// Two sums with one barrier (slots `slot`, `slot + 1`).
+template <int W, int RPB>
+__device__ __forceinline__ void row_sum2(float& a, float& b, RowLds<W, RPB>& lds, int sub, int wr, int lane,
+                                         int slot) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  if constexpr (W > 1) {
+    if (lane == 0) {
+      lds.v[sub][slot][wr] = a;
+      lds.v[sub][slot + 1][wr] = b;
+    }
+    __syncthreads();
+    a = lds.v[sub][slot][0];
+    b = lds.v[sub][slot + 1][0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) {
+      a += lds.v[sub][slot][w];
+      b += lds.v[sub][slot + 1][w];
+    }
+  }
+}
+
+// Parameters (gamma, beta) stay packed in registers unless the row slice is
+// the widest one (8 vectors per thread), where they are re-read from cache.
+template <int NV> constexpr bool hold_params() { return NV <= 4; }
+
+template <DT D, DT R, int TPR, int NV, int RPB>
+__global__ __launch_bounds__(TPR* RPB) void ln_fwd_kernel(const char* __restrict__ x, const char* __restrict__ res,
+                                                           const char* __restrict__ gamma,
+                                                           const char* __restrict__ beta, char* hout, char* y,
+                                                           float* __restrict__ mean_out,
+                                                           float* __restrict__ rstd_out, int64_t T, int H,
+                                                           float eps, float gshift) {
+  constexpr int E = ln_epl<D, R>();
+  constexpr int W = TPR / 64;
+  constexpr int XB = E * Vec<D>::BYTES, RB = E * Vec<R>::BYTES;
+  constexpr bool HOLD = hold_params<NV>();
+  using PD = typename Pk<D, E>::T;
+  using PR = typename Pk<R, E>::T;
+  __shared__ RowLds<W, RPB> lds;
+  const int tid = threadIdx.x, sub = tid / TPR, lt = tid % TPR, wr = lt / 64, lane = tid & 63;
+  const int nvec = H / E;
+  const float fh = static_cast<float>(H);
+
+  int vc[NV];   // clamped vector index (always in bounds)
+  bool ok[NV];  // the vector exists in the row
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int v = lt + k * TPR;
+    ok[k] = v < nvec;
+    vc[k] = ok[k] ? v : 0;
+  }
+  PD gp[HOLD ? NV : 1], bp[HOLD ? NV : 1];
+  if constexpr (HOLD) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      gp[k] = pk_load_keep<D, E>(gamma + static_cast<size_t>(vc[k]) * XB);
+      bp[k] = beta ? pk_load_keep<D, E>(beta + static_cast<size_t>(vc[k]) * XB) : PD{};
+    }
+  }
+
+  const int64_t step = static_cast<int64_t>(gridDim.x) * RPB;
+  for (int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + sub; row < T; row += step) {
+    const size_t xo = static_cast<size_t>(row) * H * Vec<D>::BYTES;
+    const size_t ro = static_cast<size_t>(row) * H * Vec<R>::BYTES;
+    PD xp[NV];
+    PR rp[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      xp[k] = pk_load<D, E>(x + xo + static_cast<size_t>(vc[k]) * XB);
+      rp[k] = pk_load<R, E>(res + ro + static_cast<size_t>(vc[k]) * RB);
+    }
+    PD hp[NV];  // h, rounded to D
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      float xv[E], rv[E];
+      pk_unpack<D, E>(xp[k], xv);
+      pk_unpack<R, E>(rp[k], rv);
+#pragma unroll
+      for (int e = 0; e < E; ++e) xv[e] += R == D ? rv[e] : round_to<D>(rv[e]);
+      hp[k] = pk_pack<D, E>(xv);
+      if (hout && ok[k]) pk_store<D, E>(hout + xo + static_cast<size_t>(vc[k]) * XB, hp[k]);
+      float hv[E];
+      pk_unpack<D, E>(hp[k], hv);
+#pragma unroll
+      for (int e = 0; e < E; ++e) s += ok[k] ? hv[e] : 0.0f;
+    }
+    const float mean = row_sum<W, RPB>(s, lds, sub, wr, lane, 0) / fh;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) opaque(hp[k]);
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      float hv[E];
+      pk_unpack<D, E>(hp[k], hv);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float d = hv[e] - mean;
+        ss += ok[k] ? d * d : 0.0f;
+      }
+    }
+    const float var = row_sum<W, RPB>(ss, lds, sub, wr, lane, 1) / fh;
+    const float rstd = 1.0f / __builtin_sqrtf(var + eps);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) opaque(hp[k]);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      if (!ok[k]) continue;
+      float hv[E], g[E], b[E];
+      pk_unpack<D, E>(hp[k], hv);
+      if constexpr (HOLD) {
+        pk_unpack<D, E>(gp[k], g);
+        pk_unpack<D, E>(bp[k], b);
+      } else {
+        pk_unpack<D, E>(pk_load_keep<D, E>(gamma + static_cast<size_t>(vc[k]) * XB), g);
+        if (beta) {
+          pk_unpack<D, E>(pk_load_keep<D, E>(beta + static_cast<size_t>(vc[k]) * XB), b);
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) b[e] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) hv[e] = __builtin_fmaf((hv[e] - mean) * rstd, g[e] + gshift, b[e]);
+      pk_store<D, E>(y + xo + static_cast<size_t>(vc[k]) * XB, pk_pack<D, E>(hv));
+    }
+    if (lt == 0 && mean_out) {
+      mean_out[row] = mean;
+      rstd_out[row] = rstd;
+    }
+  }
+}
+
+template <DT D, DT R, int TPR, int NV, int RPB, bool DGB>
+__global__ __launch_bounds__(TPR* RPB) void ln_bwd_kernel(const char* __restrict__ dy, const char* __restrict__ h,
+                                                           const char* __restrict__ gamma,
+                                                           const float* __restrict__ mean,
+                                                           const float* __restrict__ rstd, const char* dh_in,
+                                                           char* dx, char* dres, float* __restrict__ pg,
+                                                           float* __restrict__ pb, int64_t T, int H, float gshift) {
+  constexpr int E = ln_epl<D, R>();
+  constexpr int W = TPR / 64;
+  constexpr int XB = E * Vec<D>::BYTES, RB = E * Vec<R>::BYTES;
+  constexpr bool HOLD = hold_params<NV>();
+  using PD = typename Pk<D, E>::T;
+  using PR = typename Pk<R, E>::T;
+  __shared__ RowLds<W, RPB> lds;
+  const int tid = threadIdx.x, sub = tid / TPR, lt = tid % TPR, wr = lt / 64, lane = tid & 63;
+  const int nvec = H / E;
+  const float fh = static_cast<float>(H);
+
+  int vc[NV];
+  bool ok[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int v = lt + k * TPR;
+    ok[k] = v < nvec;
+    vc[k] = ok[k] ? v : 0;
+  }
+  PD gp[HOLD ? NV : 1];
+  if constexpr (HOLD) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) gp[k] = pk_load_keep<D, E>(gamma + static_cast<size_t>(vc[k]) * XB);
+  }
+  float ag[DGB ? NV : 1][E], ab[DGB ? NV : 1][E];
+  if constexpr (DGB) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+      for (int e = 0; e < E; ++e) ag[k][e] = ab[k][e] = 0.0f;
+  }
+
+  int slot = 0;  // alternates between the two pairs of LDS slots by row
+  const int64_t step = static_cast<int64_t>(gridDim.x) * RPB;
+  for (int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + sub; row < T; row += step) {
+    const size_t xo = static_cast<size_t>(row) * H * Vec<D>::BYTES;
+    const size_t ro = static_cast<size_t>(row) * H * Vec<R>::BYTES;
+    const float mu = mean[row], rs = rstd[row];
+    PD gyp[NV], hp[NV];
+    PR up[HOLD ? NV : 1];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      gyp[k] = pk_load<D, E>(dy + xo + static_cast<size_t>(vc[k]) * XB);
+      hp[k] = pk_load<D, E>(h + xo + static_cast<size_t>(vc[k]) * XB);
+    }
+    if constexpr (HOLD) {
+      if (dh_in) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) up[k] = pk_load<R, E>(dh_in + ro + static_cast<size_t>(vc[k]) * RB);
+      }
+    }
+    // pass 1: the two row sums (and the parameter-gradient terms)
+    float sa = 0.0f, sax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      float gv[E], hv[E], g[E];
+      pk_unpack<D, E>(gyp[k], gv);
+      pk_unpack<D, E>(hp[k], hv);
+      pk_unpack<D, E>(HOLD ? gp[k] : pk_load_keep<D, E>(gamma + static_cast<size_t>(vc[k]) * XB), g);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float xv = (hv[e] - mu) * rs;
+        const float dyv = ok[k] ? gv[e] : 0.0f;
+        const float a = dyv * (g[e] + gshift);
+        sa += a;
+        sax = __builtin_fmaf(a, xv, sax);
+        if constexpr (DGB) {
+          ag[k][e] = __builtin_fmaf(dyv, xv, ag[k][e]);
+          ab[k][e] += dyv;
+        }
+      }
+    }
+    row_sum2<W, RPB>(sa, sax, lds, sub, wr, lane, slot);
+    slot ^= 2;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      opaque(gyp[k]);
+      opaque(hp[k]);
+      if constexpr (HOLD) opaque(gp[k]);
+    }
+    const float ma = sa / fh, mx = sax / fh;
+    // pass 2: recompute a and xhat from the packed row, form dh
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      if (!ok[k]) continue;
+      float gv[E], hv[E], g[E], u[E];
+      pk_unpack<D, E>(gyp[k], gv);
+      pk_unpack<D, E>(hp[k], hv);
+      pk_unpack<D, E>(HOLD ? gp[k] : pk_load_keep<D, E>(gamma + static_cast<size_t>(vc[k]) * XB), g);
+      if (dh_in) {
+        if constexpr (HOLD) pk_unpack<R, E>(up[k], u);
+        else pk_unpack<R, E>(pk_load<R, E>(dh_in + ro + static_cast<size_t>(vc[k]) * RB), u);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) u[e] = 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float xv = (hv[e] - mu) * rs;
+        const float a = gv[e] * (g[e] + gshift);
+        gv[e] = __builtin_fmaf(rs, __builtin_fmaf(-xv, mx, a - ma), u[e]);
+      }
+      pk_store<D, E>(dx + xo + static_cast<size_t>(vc[k]) * XB, pk_pack<D, E>(gv));
+      if (dres) pk_store<R, E>(dres + ro + static_cast<size_t>(vc[k]) * RB, pk_pack<R, E>(gv));
+    }
+  }
+
+  if constexpr (DGB) {
+    // one partial row per block: the RPB rows in flight combined in order
+    float* rowg = pg + static_cast<size_t>(blockIdx.x) * H;
+    float* rowb = pb + static_cast<size_t>(blockIdx.x) * H;
+    if constexpr (RPB == 1) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        if (!ok[k]) continue;
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) {
+          store_f32x4(rowg + static_cast<size_t>(vc[k]) * E + 4 * q, ag[k] + 4 * q);
+          store_f32x4(rowb + static_cast<size_t>(vc[k]) * E + 4 * q, ab[k] + 4 * q);
+        }
+      }
+    } else {
+      __shared__ float buf[RPB][TPR][E];
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+          const float* src = which ? ab[k] : ag[k];
+#pragma unroll
+          for (int e = 0; e < E; ++e) buf[sub][lt][e] = src[e];
+          __syncthreads();
+          if (sub == 0 && ok[k]) {
+            float sum[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              float t = buf[0][lt][e];
+#pragma unroll
+              for (int r = 1; r < RPB; ++r) t += buf[r][lt][e];
+              sum[e] = t;
+            }
+            float* dst = (which ? rowb : rowg) + static_cast<size_t>(vc[k]) * E;
+#pragma unroll
+            for (int q = 0; q < E / 4; ++q) store_f32x4(dst + 4 * q, sum + 4 * q);
+          }
+          __syncthreads();
+        }
+      }
+    }
+  }
+}
+
+// dgamma / dbeta partials by column strips (the widest rows): lane = one
+// 16-byte vector of dy and h, wave w of row group y walks rows 4y + w + 4Gk.
+template <DT D>
+__global__ __launch_bounds__(kThreads) void ln_dgb_kernel(const char* __restrict__ dy, const char* __restrict__ h,
+                                                          const float* __restrict__ mean,
+                                                          const float* __restrict__ rstd, float* __restrict__ pg,
+                                                          float* __restrict__ pb, int64_t T, int nvec) {
+  constexpr int V = Vec<D>::N;
+  const TileIdx ti = tile_idx();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int cv = ti.strip * kStrip + lane;
+  const bool active = cv < nvec;
+  const size_t pitch = static_cast<size_t>(nvec) * 16, col = static_cast<size_t>(cv) * 16;
+  float ag[V], ab[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) ag[e] = ab[e] = 0.0f;
+  if (active) {
+    for (int64_t t = static_cast<int64_t>(ti.rg) * kWaves + w; t < T; t += static_cast<int64_t>(kWaves) * ti.G) {
+      float g[V], x[V];
+      unpack<D>(ld_stream(dy + t * pitch + col), g);
+      unpack<D>(ld_stream(h + t * pitch + col), x);
+      const float mu = mean[t], rs = rstd[t];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        ag[e] = __builtin_fmaf(g[e], (x[e] - mu) * rs, ag[e]);
+        ab[e] += g[e];
+      }
+    }
+  }
+  __shared__ float red[kWaves][2 * V][64];
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    red[w][e][lane] = ag[e];
+    red[w][V + e][lane] = ab[e];
+  }
+  __syncthreads();
+  if (w == 0 && active) {
+    float sg[V], sb[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      sg[e] = ((red[0][e][lane] + red[1][e][lane]) + red[2][e][lane]) + red[3][e][lane];
+      sb[e] = ((red[0][V + e][lane] + red[1][V + e][lane]) + red[2][V + e][lane]) + red[3][V + e][lane];
+    }
+    const size_t o = static_cast<size_t>(ti.rg) * nvec * V + static_cast<size_t>(cv) * V;
+#pragma unroll
+    for (int q = 0; q < V / 4; ++q) {
+      store_f32x4(pg + o + 4 * q, sg + 4 * q);
+      store_f32x4(pb + o + 4 * q, sb + 4 * q);
+    }
+  }
+}
+
+// Row-group shapes: (threads per row, vectors per thread, rows per block).
+struct Shape {
+  int tpr, nv, rpb;
+};
+constexpr Shape kShapes[] = {{64, 1, 4},  {64, 2, 4},  {64, 4, 4},  {256, 2, 1},
+                             {256, 4, 1}, {1024, 2, 1}, {1024, 4, 1}, {1024, 8, 1}};
+constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
+// From this shape on, dgamma / dbeta come from the column-strip kernel: the
+// per-thread accumulators would not fit beside the row in the 128 registers
+// a thread of a 1024-thread block has.
+constexpr int kSplitShape = 6;
+
+template <DT D, DT R, int S>
+hipError_t fwd_shape(const LnArgs& a, const LnPlan& p, hipStream_t s) {
+  constexpr Shape sh = kShapes[S];
+  hipLaunchKernelGGL((ln_fwd_kernel<D, R, sh.tpr, sh.nv, sh.rpb>), dim3(p.grid), dim3(sh.tpr * sh.rpb), 0, s,
+                     static_cast<const char*>(a.x), static_cast<const char*>(a.res),
+                     static_cast<const char*>(a.gamma), static_cast<const char*>(a.beta),
+                     static_cast<char*>(a.hout), static_cast<char*>(a.y), a.mean, a.rstd, a.T,
+                     static_cast<int>(a.H), a.eps, a.gshift);
+  return hipGetLastError();
+}
+
+template <DT D, DT R, int S>
+hipError_t bwd_shape(const LnArgs& a, const LnPlan& p, hipStream_t s) {
+  constexpr Shape sh = kShapes[S];
+  const auto dy = static_cast<const char*>(a.dy);
+  const auto h = static_cast<const char*>(a.h);
+  const auto gamma = static_cast<const char*>(a.gamma);
+  const auto dh_in = static_cast<const char*>(a.dh_in);
+  const auto dx = static_cast<char*>(a.dx);
+  const auto dres = static_cast<char*>(a.dres);
+  const int H = static_cast<int>(a.H);
+  const dim3 grid(p.grid), block(sh.tpr * sh.rpb);
+  if constexpr (S >= kSplitShape) {
+    // the column pass reads dy and h before the row pass may overwrite them
+    // (dx and dresidual may alias dy or h)
+    if (a.pg) {
+      hipLaunchKernelGGL((ln_dgb_kernel<D>), tile_grid(p.dgb.strips, p.dgb.G), dim3(kThreads), 0, s, dy, h, a.cmean,
+                         a.crstd, a.pg, a.pb, a.T, p.dgb.nvec);
+      if (hipError_t e = hipGetLastError()) return e;
+    }
+    hipLaunchKernelGGL((ln_bwd_kernel<D, R, sh.tpr, sh.nv, sh.rpb, false>), grid, block, 0, s, dy, h, gamma, a.cmean,
+                       a.crstd, dh_in, dx, dres, nullptr, nullptr, a.T, H, a.gshift);
+  } else if (a.pg) {
+    hipLaunchKernelGGL((ln_bwd_kernel<D, R, sh.tpr, sh.nv, sh.rpb, true>), grid, block, 0, s, dy, h, gamma, a.cmean,
+                       a.crstd, dh_in, dx, dres, a.pg, a.pb, a.T, H, a.gshift);
+  } else {
+    hipLaunchKernelGGL((ln_bwd_kernel<D, R, sh.tpr, sh.nv, sh.rpb, false>), grid, block, 0, s, dy, h, gamma, a.cmean,
+                       a.crstd, dh_in, dx, dres, nullptr, nullptr, a.T, H, a.gshift);
+  }
+  return hipGetLastError();
+}
+
+template <DT D, DT R, bool BWD, int S = 0>
+hipError_t by_shape(const LnArgs& a, const LnPlan& p, hipStream_t s) {
+  if constexpr (S < kNumShapes) {
+    if (p.shape == S) return BWD ? bwd_shape<D, R, S>(a, p, s) : fwd_shape<D, R, S>(a, p, s);
+    return by_shape<D, R, BWD, S + 1>(a, p, s);
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
+template <bool BWD>
+hipError_t by_dtype(const LnArgs& a, const LnPlan& p, hipStream_t s) {
+  const DT d = static_cast<DT>(a.dt), r = static_cast<DT>(a.rdt);
+  if (d == DT::F32 && r == DT::F32) return by_shape<DT::F32, DT::F32, BWD>(a, p, s);
+  if (d == DT::BF16 && r == DT::BF16) return by_shape<DT::BF16, DT::BF16, BWD>(a, p, s);
+  if (d == DT::BF16 && r == DT::F32) return by_shape<DT::BF16, DT::F32, BWD>(a, p, s);
+  if (d == DT::F16 && r == DT::F16) return by_shape<DT::F16, DT::F16, BWD>(a, p, s);
+  if (d == DT::F16 && r == DT::F32) return by_shape<DT::F16, DT::F32, BWD>(a, p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int ln_elems_per_vector(int dt, int rdt) {
+  if (rdt == static_cast<int>(DT::F32) && dt != static_cast<int>(DT::F32)) return 4;
+  return dt == static_cast<int>(DT::F32) ? 4 : 8;
+}
+
+LnPlan plan_ln(int64_t T, int64_t H, int dt, int rdt, int target_blocks) {
+  LnPlan p;
+  const int E = ln_elems_per_vector(dt, rdt);
+  p.nvec = static_cast<int>(H / E);
+  p.shape = -1;
+  for (int i = 0; i < kNumShapes; ++i)
+    if (p.nvec <= kShapes[i].tpr * kShapes[i].nv) {
+      p.shape = i;
+      break;
+    }
+  if (p.shape < 0) return p;
+  const Shape sh = kShapes[p.shape];
+  const int64_t groups = (T + sh.rpb - 1) / sh.rpb;
+  p.grid = static_cast<int>(std::min<int64_t>(std::max<int64_t>(groups, 1), target_blocks));
+  p.split = p.shape >= kSplitShape;
+  const int v16 = static_cast<int>(H * (dt == static_cast<int>(DT::F32) ? 4 : 2) / 16);
+  p.dgb = plan_tiling(T, v16, MB_LN_DGB_BLOCKS);
+  p.partial_rows = p.split ? p.dgb.G : p.grid;
+  return p;
+}
+
+hipError_t launch_ln_fwd(const LnArgs& a, const LnPlan& p, hipStream_t s) { return by_dtype<false>(a, p, s); }
+hipError_t launch_ln_bwd(const LnArgs& a, const LnPlan& p, hipStream_t s) { return by_dtype<true>(a, p, s); }
+
+}  // namespace mb
