@@ -15,9 +15,10 @@ Inputs are resident in HBM before timing starts. `value` is the algorithmic
 bytes of a step (each tensor read or written once, bias and gradients of the
 bias included, reduction partials excluded) divided by the step time.
 
-The ops beyond the step (the exact erf GeLU at the chain's MLP shape) are
-timed after the step loop, the same way, and reported under "next_rows";
-they are not part of `value`.
+The ops beyond the step (the exact erf GeLU at the chain's MLP shape, and
+residual add + LayerNorm at the chain's hidden size) are timed after the step
+loop, the same way, and reported under "next_rows"; they are not part of
+`value`.
 
 Prints one JSON line (see the keys below). `--gpus N` with N > 1 exits: this
 build runs on a single GPU.
@@ -173,6 +174,24 @@ def build_ops(dev):
              Op("erf_gelu_bwd_bf16_16384x32768",
                 lambda: mb.mb_bias_gelu_erf_bwd(gg, gy, gb, dgrad=dgr, dbias=dbg, ws=wsg),
                 T * H * 6 + H * 2 + H * 4, ["gelu_bwd", "colsum"])]
+
+    # -- beyond the step: residual add + LayerNorm, bf16 [16384, 8192]
+    w = WORKLOADS["add_ln_bf16_16384x8192"]
+    lx, lr, lg, lb, ldy, lup = (load(w.name, k) for k in ("x", "residual", "gamma", "beta", "dy", "dh_in"))
+    T, H = lx.shape
+    lh, ly, ldx = torch.empty_like(lx), torch.empty_like(lx), torch.empty_like(lx)
+    lmean, lrstd = (torch.empty(T, dtype=torch.float32, device=dev) for _ in range(2))
+    ldg, ldb = (torch.empty(H, dtype=torch.float32, device=dev) for _ in range(2))
+    lws = torch.empty(max(1, mb.mb_add_layer_norm_bwd_workspace(T, H, lx.dtype)), dtype=torch.uint8, device=dev)
+    eps, zc = w.params["eps"], w.params["zero_centered_gamma"]
+    extra.append(Op("add_ln_fwd_bf16_16384x8192",
+                    lambda: mb.mb_add_layer_norm_fwd(lx, lr, lg, lb, eps, zc, h_out=lh, y=ly, stats=(lmean, lrstd)),
+                    T * H * 8 + H * 4 + T * 8, ["ln_fwd"]))
+    extra.append(Op("add_ln_bwd_bf16_16384x8192",
+                    lambda: mb.mb_add_layer_norm_bwd(ldy, lh, lg, lmean, lrstd, zc, dh_in=lup, dx=ldx, dgamma=ldg,
+                                                     dbeta=ldb, ws=lws),
+                    T * H * 8 + H * 2 + T * 8 + H * 8, ["ln_bwd", "colsum_chunk", "colsum", "colsum_chunk",
+                                                        "colsum"]))
     return ops, extra, host
 
 

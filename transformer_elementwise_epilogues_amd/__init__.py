@@ -314,7 +314,7 @@ def mb_add_layer_norm_fwd(x, residual, gamma, beta=None, eps=1e-5, zero_centered
     """h = x + residual (cast to x's dtype), y = LayerNorm(h) * gamma' + beta.
     Returns (y, h or None, mean or None, rstd or None). h_out=True allocates h
     (False skips it; a tensor, e.g. x itself, receives it); stats=True
-    allocates the fp32 mean / rstd the backward needs."""
+    allocates the fp32 mean / rstd the backward needs (or pass the pair)."""
     T, H = _rows(x, "x")
     _rows(residual, "residual", H)
     if residual.shape[0] != T:
@@ -327,9 +327,13 @@ def mb_add_layer_norm_fwd(x, residual, gamma, beta=None, eps=1e-5, zero_centered
         h_out = None
     y = torch.empty_like(x) if y is None else y
     mean = rstd = None
-    if stats:
+    if stats is True:
         mean = torch.empty(T, dtype=torch.float32, device=x.device)
         rstd = torch.empty(T, dtype=torch.float32, device=x.device)
+    elif stats:
+        mean, rstd = stats
+        _vec(mean, T, "mean")
+        _vec(rstd, T, "rstd")
     _check("mb_add_layer_norm_fwd", lib().mb_add_layer_norm_fwd(
         _p(x), _p(residual), _dt(residual), _p(gamma), _p(beta), float(eps), int(bool(zero_centered_gamma)),
         _p(h_out), _p(y), _p(mean), _p(rstd), T, H, _dt(x), _stream(x, stream)))

@@ -422,7 +422,8 @@ static mb_status_t ln_shape(int64_t T, int64_t H, mb_dtype_t dt, mb_dtype_t rdt,
   if (T < 0 || H <= 0 || T > (int64_t{1} << 40) || H > (int64_t{1} << 20)) return MB_ERR_SHAPE;
   const int E = mb::ln_elems_per_vector(dt, rdt);
   if (H % E != 0) return MB_ERR_SHAPE;
-  *plan = mb::plan_ln(T, H, dt, rdt, MB_LN_BWD_BLOCKS);
+  const int blocks = H / E >= 1024 ? MB_LN_BWD_BLOCKS_WIDE : MB_LN_BWD_BLOCKS;
+  *plan = mb::plan_ln(T, H, dt, rdt, blocks, MB_LN_BWD_NV);
   if (plan->shape < 0) return MB_ERR_SHAPE;
   return MB_OK;
 }
@@ -464,7 +465,8 @@ mb_status_t mb_add_layer_norm_fwd(const void* x, const void* residual, mb_dtype_
   a.y = y;
   a.mean = mean;
   a.rstd = rstd;
-  const mb::LnPlan fp = mb::plan_ln(tokens, hidden, dt, residual_dt, MB_LN_FWD_BLOCKS);
+  const mb::LnPlan fp = mb::plan_ln(tokens, hidden, dt, residual_dt, MB_LN_FWD_BLOCKS, MB_LN_FWD_NV);
+  if (fp.shape < 0) return MB_ERR_SHAPE;
   if (hipError_t e = mb::launch_ln_fwd(a, fp, s)) return hip_status(e);
   return finish();
 }

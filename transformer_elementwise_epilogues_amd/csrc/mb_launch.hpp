@@ -63,11 +63,23 @@ struct Tiling {
 #ifndef MB_LN_FWD_BLOCKS
 #define MB_LN_FWD_BLOCKS 2048
 #endif
+// backward blocks = partial rows of dgamma / dbeta: fewer for wide rows
+// (1024 or more vectors), where each partial row is large
 #ifndef MB_LN_BWD_BLOCKS
 #define MB_LN_BWD_BLOCKS 512
 #endif
+#ifndef MB_LN_BWD_BLOCKS_WIDE
+#define MB_LN_BWD_BLOCKS_WIDE 256
+#endif
 #ifndef MB_LN_DGB_BLOCKS
 #define MB_LN_DGB_BLOCKS 512
+#endif
+// preferred vectors per thread (the row is split over more threads below it)
+#ifndef MB_LN_FWD_NV
+#define MB_LN_FWD_NV 4
+#endif
+#ifndef MB_LN_BWD_NV
+#define MB_LN_BWD_NV 2
 #endif
 
 Tiling plan_tiling(int64_t T, int nvec, int target_blocks);
@@ -147,7 +159,7 @@ struct LnPlan {
   int partial_rows = 0;   // partial rows the backward writes
 };
 int ln_elems_per_vector(int dt, int rdt);
-LnPlan plan_ln(int64_t T, int64_t H, int dt, int rdt, int target_blocks);
+LnPlan plan_ln(int64_t T, int64_t H, int dt, int rdt, int target_blocks, int nv_pref);
 hipError_t launch_ln_fwd(const LnArgs& a, const LnPlan& p, hipStream_t s);
 hipError_t launch_ln_bwd(const LnArgs& a, const LnPlan& p, hipStream_t s);
 

@@ -138,6 +138,18 @@ __device__ __forceinline__ void row_sum2(float& a, float& b, RowLds<W, RPB>& lds
   }
 }
 
+// 1024-thread rows of 2 vectors per thread keep the parameter-gradient sums
+// in LDS (2 H floats: at most 128 KiB, as such rows hold at most 16384
+// elements).
+constexpr bool acc_in_lds(int tpr, int nv) { return tpr == 1024 && nv == 2; }
+
+#ifndef MB_LN_PREFETCH
+#define MB_LN_PREFETCH 1
+#endif
+// The next row is prefetched into registers, except for 1024-thread rows of
+// 4 or more vectors per thread, which have no registers to spare.
+template <int TPR, int NV> constexpr bool prefetch() { return MB_LN_PREFETCH && !(TPR == 1024 && NV >= 4); }
+
 // Parameters (gamma, beta) stay packed in registers unless the row slice is
 // the widest one (8 vectors per thread), where they are re-read from cache.
 template <int NV> constexpr bool hold_params() { return NV <= 4; }
@@ -178,15 +190,31 @@ __global__ __launch_bounds__(TPR* RPB) void ln_fwd_kernel(const char* __restrict
   }
 
   const int64_t step = static_cast<int64_t>(gridDim.x) * RPB;
-  for (int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + sub; row < T; row += step) {
+  // the next row's x and residual are loaded while this row is reduced
+  PD xn[NV];
+  PR rn[NV];
+  auto fetch = [&](int64_t r) {
+    const size_t xo = static_cast<size_t>(r) * H * Vec<D>::BYTES;
+    const size_t ro = static_cast<size_t>(r) * H * Vec<R>::BYTES;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      xn[k] = pk_load<D, E>(x + xo + static_cast<size_t>(vc[k]) * XB);
+      rn[k] = pk_load<R, E>(res + ro + static_cast<size_t>(vc[k]) * RB);
+    }
+  };
+  int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + sub;
+  if (row < T) fetch(row);
+  for (; row < T; row += step) {
     const size_t xo = static_cast<size_t>(row) * H * Vec<D>::BYTES;
-    const size_t ro = static_cast<size_t>(row) * H * Vec<R>::BYTES;
     PD xp[NV];
     PR rp[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-      xp[k] = pk_load<D, E>(x + xo + static_cast<size_t>(vc[k]) * XB);
-      rp[k] = pk_load<R, E>(res + ro + static_cast<size_t>(vc[k]) * RB);
+      xp[k] = xn[k];
+      rp[k] = rn[k];
+    }
+    if constexpr (prefetch<TPR, NV>()) {
+      if (row + step < T) fetch(row + step);
     }
     PD hp[NV];  // h, rounded to D
     float s = 0.0f;
@@ -247,6 +275,9 @@ __global__ __launch_bounds__(TPR* RPB) void ln_fwd_kernel(const char* __restrict
       mean_out[row] = mean;
       rstd_out[row] = rstd;
     }
+    if constexpr (!prefetch<TPR, NV>()) {
+      if (row + step < T) fetch(row + step);
+    }
   }
 }
 
@@ -281,32 +312,66 @@ __global__ __launch_bounds__(TPR* RPB) void ln_bwd_kernel(const char* __restrict
 #pragma unroll
     for (int k = 0; k < NV; ++k) gp[k] = pk_load_keep<D, E>(gamma + static_cast<size_t>(vc[k]) * XB);
   }
-  float ag[DGB ? NV : 1][E], ab[DGB ? NV : 1][E];
-  if constexpr (DGB) {
+  // parameter-gradient sums: in registers, or (ACC_LDS) in this block's LDS,
+  // [2][H] floats of which each thread touches only its own columns (so no
+  // barrier is needed), to leave the registers to the next row's prefetch
+  constexpr bool ACC_LDS = acc_in_lds(TPR, NV);
+  constexpr bool REG = DGB && !ACC_LDS;
+  extern __shared__ float lds_acc[];
+  float ag[REG ? NV : 1][E], ab[REG ? NV : 1][E];
+  if constexpr (REG) {
 #pragma unroll
     for (int k = 0; k < NV; ++k)
 #pragma unroll
       for (int e = 0; e < E; ++e) ag[k][e] = ab[k][e] = 0.0f;
   }
+  if constexpr (DGB && ACC_LDS) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+      if (ok[k])
+#pragma unroll
+        for (int e = 0; e < E; ++e) lds_acc[vc[k] * E + e] = lds_acc[H + vc[k] * E + e] = 0.0f;
+  }
 
   int slot = 0;  // alternates between the two pairs of LDS slots by row
   const int64_t step = static_cast<int64_t>(gridDim.x) * RPB;
-  for (int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + sub; row < T; row += step) {
-    const size_t xo = static_cast<size_t>(row) * H * Vec<D>::BYTES;
-    const size_t ro = static_cast<size_t>(row) * H * Vec<R>::BYTES;
-    const float mu = mean[row], rs = rstd[row];
-    PD gyp[NV], hp[NV];
-    PR up[HOLD ? NV : 1];
+  // the next row's dy, h (and dh_in) are loaded while this row is reduced
+  PD gyn[NV], hn[NV];
+  PR upn[HOLD ? NV : 1];
+  float mun = 0.0f, rsn = 0.0f;
+  auto fetch = [&](int64_t r) {
+    const size_t xo = static_cast<size_t>(r) * H * Vec<D>::BYTES;
+    const size_t ro = static_cast<size_t>(r) * H * Vec<R>::BYTES;
+    mun = mean[r];
+    rsn = rstd[r];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-      gyp[k] = pk_load<D, E>(dy + xo + static_cast<size_t>(vc[k]) * XB);
-      hp[k] = pk_load<D, E>(h + xo + static_cast<size_t>(vc[k]) * XB);
+      gyn[k] = pk_load<D, E>(dy + xo + static_cast<size_t>(vc[k]) * XB);
+      hn[k] = pk_load<D, E>(h + xo + static_cast<size_t>(vc[k]) * XB);
     }
     if constexpr (HOLD) {
       if (dh_in) {
 #pragma unroll
-        for (int k = 0; k < NV; ++k) up[k] = pk_load<R, E>(dh_in + ro + static_cast<size_t>(vc[k]) * RB);
+        for (int k = 0; k < NV; ++k) upn[k] = pk_load<R, E>(dh_in + ro + static_cast<size_t>(vc[k]) * RB);
       }
+    }
+  };
+  int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + sub;
+  if (row < T) fetch(row);
+  for (; row < T; row += step) {
+    const size_t xo = static_cast<size_t>(row) * H * Vec<D>::BYTES;
+    const size_t ro = static_cast<size_t>(row) * H * Vec<R>::BYTES;
+    const float mu = mun, rs = rsn;
+    PD gyp[NV], hp[NV];
+    PR up[HOLD ? NV : 1];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      gyp[k] = gyn[k];
+      hp[k] = hn[k];
+      if constexpr (HOLD) up[k] = upn[k];
+    }
+    if constexpr (prefetch<TPR, NV>()) {
+      if (row + step < T) fetch(row + step);
     }
     // pass 1: the two row sums (and the parameter-gradient terms)
     float sa = 0.0f, sax = 0.0f;
@@ -316,6 +381,7 @@ __global__ __launch_bounds__(TPR* RPB) void ln_bwd_kernel(const char* __restrict
       pk_unpack<D, E>(gyp[k], gv);
       pk_unpack<D, E>(hp[k], hv);
       pk_unpack<D, E>(HOLD ? gp[k] : pk_load_keep<D, E>(gamma + static_cast<size_t>(vc[k]) * XB), g);
+      float xa[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const float xv = (hv[e] - mu) * rs;
@@ -323,9 +389,25 @@ __global__ __launch_bounds__(TPR* RPB) void ln_bwd_kernel(const char* __restrict
         const float a = dyv * (g[e] + gshift);
         sa += a;
         sax = __builtin_fmaf(a, xv, sax);
-        if constexpr (DGB) {
-          ag[k][e] = __builtin_fmaf(dyv, xv, ag[k][e]);
-          ab[k][e] += dyv;
+        xa[e] = xv;
+        gv[e] = dyv;
+      }
+      if constexpr (REG) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          ag[k][e] = __builtin_fmaf(gv[e], xa[e], ag[k][e]);
+          ab[k][e] += gv[e];
+        }
+      }
+      if constexpr (DGB && ACC_LDS) {
+        if (ok[k]) {
+          float* cg = lds_acc + vc[k] * E;
+          float* cb = cg + H;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            cg[e] = __builtin_fmaf(gv[e], xa[e], cg[e]);
+            cb[e] += gv[e];
+          }
         }
       }
     }
@@ -362,13 +444,26 @@ __global__ __launch_bounds__(TPR* RPB) void ln_bwd_kernel(const char* __restrict
       pk_store<D, E>(dx + xo + static_cast<size_t>(vc[k]) * XB, pk_pack<D, E>(gv));
       if (dres) pk_store<R, E>(dres + ro + static_cast<size_t>(vc[k]) * RB, pk_pack<R, E>(gv));
     }
+    if constexpr (!prefetch<TPR, NV>()) {
+      if (row + step < T) fetch(row + step);
+    }
   }
 
   if constexpr (DGB) {
     // one partial row per block: the RPB rows in flight combined in order
     float* rowg = pg + static_cast<size_t>(blockIdx.x) * H;
     float* rowb = pb + static_cast<size_t>(blockIdx.x) * H;
-    if constexpr (RPB == 1) {
+    if constexpr (ACC_LDS) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        if (!ok[k]) continue;
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) {
+          store_f32x4(rowg + static_cast<size_t>(vc[k]) * E + 4 * q, lds_acc + vc[k] * E + 4 * q);
+          store_f32x4(rowb + static_cast<size_t>(vc[k]) * E + 4 * q, lds_acc + H + vc[k] * E + 4 * q);
+        }
+      }
+    } else if constexpr (RPB == 1) {
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
         if (!ok[k]) continue;
@@ -461,16 +556,19 @@ __global__ __launch_bounds__(kThreads) void ln_dgb_kernel(const char* __restrict
 }
 
 // Row-group shapes: (threads per row, vectors per thread, rows per block).
+// Groups of 64 threads run 4 rows per block (no barrier); wider groups are the
+// whole block.
 struct Shape {
   int tpr, nv, rpb;
 };
-constexpr Shape kShapes[] = {{64, 1, 4},  {64, 2, 4},  {64, 4, 4},  {256, 2, 1},
-                             {256, 4, 1}, {1024, 2, 1}, {1024, 4, 1}, {1024, 8, 1}};
+constexpr Shape kShapes[] = {{64, 1, 4},  {64, 2, 4},  {64, 4, 4},  {256, 1, 1},  {256, 2, 1},
+                             {256, 4, 1}, {512, 1, 1}, {512, 2, 1}, {512, 4, 1},  {1024, 1, 1},
+                             {1024, 2, 1}, {1024, 4, 1}, {1024, 8, 1}};
 constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
-// From this shape on, dgamma / dbeta come from the column-strip kernel: the
-// per-thread accumulators would not fit beside the row in the 128 registers
-// a thread of a 1024-thread block has.
-constexpr int kSplitShape = 6;
+// dgamma / dbeta come from the column-strip kernel for 1024-thread rows of
+// more than 2 vectors per thread: the per-thread accumulators would not fit
+// beside the row in the 128 registers a thread of such a block has.
+constexpr bool split_shape(int s) { return kShapes[s].tpr == 1024 && kShapes[s].nv > 2; }
 
 template <DT D, DT R, int S>
 hipError_t fwd_shape(const LnArgs& a, const LnPlan& p, hipStream_t s) {
@@ -494,7 +592,7 @@ hipError_t bwd_shape(const LnArgs& a, const LnPlan& p, hipStream_t s) {
   const auto dres = static_cast<char*>(a.dres);
   const int H = static_cast<int>(a.H);
   const dim3 grid(p.grid), block(sh.tpr * sh.rpb);
-  if constexpr (S >= kSplitShape) {
+  if constexpr (split_shape(S)) {
     // the column pass reads dy and h before the row pass may overwrite them
     // (dx and dresidual may alias dy or h)
     if (a.pg) {
@@ -505,8 +603,9 @@ hipError_t bwd_shape(const LnArgs& a, const LnPlan& p, hipStream_t s) {
     hipLaunchKernelGGL((ln_bwd_kernel<D, R, sh.tpr, sh.nv, sh.rpb, false>), grid, block, 0, s, dy, h, gamma, a.cmean,
                        a.crstd, dh_in, dx, dres, nullptr, nullptr, a.T, H, a.gshift);
   } else if (a.pg) {
-    hipLaunchKernelGGL((ln_bwd_kernel<D, R, sh.tpr, sh.nv, sh.rpb, true>), grid, block, 0, s, dy, h, gamma, a.cmean,
-                       a.crstd, dh_in, dx, dres, a.pg, a.pb, a.T, H, a.gshift);
+    const size_t shm = acc_in_lds(sh.tpr, sh.nv) ? 2 * static_cast<size_t>(H) * sizeof(float) : 0;
+    hipLaunchKernelGGL((ln_bwd_kernel<D, R, sh.tpr, sh.nv, sh.rpb, true>), grid, block, shm, s, dy, h, gamma,
+                       a.cmean, a.crstd, dh_in, dx, dres, a.pg, a.pb, a.T, H, a.gshift);
   } else {
     hipLaunchKernelGGL((ln_bwd_kernel<D, R, sh.tpr, sh.nv, sh.rpb, false>), grid, block, 0, s, dy, h, gamma, a.cmean,
                        a.crstd, dh_in, dx, dres, nullptr, nullptr, a.T, H, a.gshift);
@@ -542,21 +641,25 @@ int ln_elems_per_vector(int dt, int rdt) {
   return dt == static_cast<int>(DT::F32) ? 4 : 8;
 }
 
-LnPlan plan_ln(int64_t T, int64_t H, int dt, int rdt, int target_blocks) {
+// Threads per row: the smallest of 64, 256, 512, 1024 that holds the row in
+// at most `nv_pref` vectors per thread (1024 takes up to 8).
+LnPlan plan_ln(int64_t T, int64_t H, int dt, int rdt, int target_blocks, int nv_pref) {
   LnPlan p;
   const int E = ln_elems_per_vector(dt, rdt);
   p.nvec = static_cast<int>(H / E);
   p.shape = -1;
+  int tpr = 64;
+  while (tpr < 1024 && static_cast<int64_t>(tpr) * nv_pref < p.nvec) tpr = tpr == 64 ? 256 : tpr * 2;
+  int nv = 1;
+  while (nv < 8 && static_cast<int64_t>(tpr) * nv < p.nvec) nv *= 2;
+  if (static_cast<int64_t>(tpr) * nv < p.nvec) return p;  // wider than 8192 vectors
   for (int i = 0; i < kNumShapes; ++i)
-    if (p.nvec <= kShapes[i].tpr * kShapes[i].nv) {
-      p.shape = i;
-      break;
-    }
+    if (kShapes[i].tpr == tpr && kShapes[i].nv == nv) p.shape = i;
   if (p.shape < 0) return p;
   const Shape sh = kShapes[p.shape];
   const int64_t groups = (T + sh.rpb - 1) / sh.rpb;
   p.grid = static_cast<int>(std::min<int64_t>(std::max<int64_t>(groups, 1), target_blocks));
-  p.split = p.shape >= kSplitShape;
+  p.split = split_shape(p.shape);
   const int v16 = static_cast<int>(H * (dt == static_cast<int>(DT::F32) ? 4 : 2) / 16);
   p.dgb = plan_tiling(T, v16, MB_LN_DGB_BLOCKS);
   p.partial_rows = p.split ? p.dgb.G : p.grid;

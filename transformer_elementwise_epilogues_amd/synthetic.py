@@ -116,4 +116,14 @@ WORKLOADS = {
         "attn_g": Tensor(9, (16384, 8192), "bf16"),  # upstream gradients of the two dropout-adds
         "mlp_g": Tensor(10, (16384, 8192), "bf16"),
     }, p=0.1, attn_seed=5001, mlp_seed=5002, offset=0),
+    # residual add + LayerNorm after a layer's residual path, at the chain's
+    # hidden size (8192 is on the persistent-kernel list); zero-centred gamma
+    "add_ln_bf16_16384x8192": _w(6, "add_ln_bf16_16384x8192", {
+        "x": Tensor(0, (16384, 8192), "bf16"),
+        "residual": Tensor(1, (16384, 8192), "bf16"),
+        "gamma": Tensor(2, (8192,), "bf16", sigma=0.02),
+        "beta": Tensor(3, (8192,), "bf16", sigma=0.02),
+        "dy": Tensor(4, (16384, 8192), "bf16"),
+        "dh_in": Tensor(5, (16384, 8192), "bf16"),
+    }, eps=1e-5, zero_centered_gamma=True),
 }
