@@ -19,7 +19,7 @@ import torch
 import oracle
 import transformer_elementwise_epilogues_amd as mb
 from transformer_elementwise_epilogues_amd.synthetic import WORKLOADS
-from tolerances import assert_close, assert_reduction_close, to_storage as st
+from tolerances import assert_close, assert_close_bounded, assert_reduction_close, to_storage as st
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -279,3 +279,49 @@ def test_bda_bwd_full(wname, pre, rdt):
     dropped = torch.from_numpy(bits.reshape(T, H) == 0).to(DEV)
     assert torch.count_nonzero(dx[dropped]).item() == 0
     say(f"bda bwd {wname}: rows, dresidual, dbias property and mask consistency ok")
+
+
+# ------------------------------------------------------------------ residual add + LayerNorm at full size
+
+def test_add_layer_norm_bf16_16384x8192_full():
+    """Sampled row blocks against the oracle (the op is row-local); the
+    parameter gradients over every row by their defining column sums in
+    float64 (dbeta = sum_t dy, dgamma = sum_t dy * xhat with xhat from h and
+    float64 row statistics), within the fp32 accumulation bound."""
+    w = WORKLOADS["add_ln_bf16_16384x8192"]
+    eps, zc = w.params["eps"], w.params["zero_centered_gamma"]
+    x, r, g, b, dy, up = (load(w.name, k) for k in ("x", "residual", "gamma", "beta", "dy", "dh_in"))
+    T, H = x.shape
+    y, h, mean, rstd = mb.mb_add_layer_norm_fwd(x, r, g, b, eps, zc)
+    dx, _, dg, db = mb.mb_add_layer_norm_bwd(dy, h, g, mean, rstd, zc, dh_in=up)
+    U, K = 2.0**-24, 128.0
+    gs, bs = st(g.cpu()), st(b.cpu())
+    for r0, n in row_blocks(T, seed=7):
+        sl = slice(r0, r0 + n)
+        oh, oy, oy64, omag, omean, orstd = oracle.add_layer_norm_fwd("bf16", st(x[sl].cpu()), st(r[sl].cpu()), "bf16",
+                                                                     gs, bs, eps, zc)
+        assert np.array_equal(st(h[sl]), oh), f"h rows {r0}: differs from the oracle's"
+        fy = assert_close_bounded(st(y[sl]), oy, oy64, K * U * omag, "bf16", f"add_ln y rows {r0}")
+        er = np.abs(rstd[sl].cpu().double().numpy() - orstd) / orstd
+        assert er.max() <= K * U, f"rstd rows {r0}"
+        odx, odx64, omag, _, _, _ = oracle.add_layer_norm_bwd("bf16", st(dy[sl].cpu()), oh, gs, eps, zc,
+                                                              dh_in=st(up[sl].cpu()), want_dres=False)
+        fx = assert_close_bounded(st(dx[sl]), odx, odx64, K * U * omag, "bf16", f"add_ln dx rows {r0}")
+        say(f"add_ln rows {r0}+{n}: y {fy} dx {fx}")
+    hd = h.double()
+    var, mu = torch.var_mean(hd, dim=1, unbiased=False, keepdim=True)
+    xhat = (hd - mu) / torch.sqrt(var + float(np.float32(eps)))
+    dyd = dy.double()
+    ref_g = (dyd * xhat).sum(0)
+    ref_b = dyd.sum(0)
+    # fp32 sums of T terms in a fixed order: |error| <= T * 2^-24 * sum |terms|
+    for name, got, ref, mag in (("dgamma", dg, ref_g, (dyd * xhat).abs().sum(0)), ("dbeta", db, ref_b, dyd.abs().sum(0))):
+        err = (got.double() - ref).abs()
+        bound = T * U * mag + 1e-30
+        worst = float((err / bound).max())
+        say(f"add_ln {name}: worst error / bound {worst:.3g}, max abs error {float(err.max()):.3g}")
+        assert worst <= 1.0, name
+    dx2, _, dg2, db2 = mb.mb_add_layer_norm_bwd(dy, h, g, mean, rstd, zc, dh_in=up)
+    assert torch.equal(dx.view(torch.int16), dx2.view(torch.int16))
+    assert torch.equal(dg.view(torch.int32), dg2.view(torch.int32))
+    assert torch.equal(db.view(torch.int32), db2.view(torch.int32))
