@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
             L.orc_bias_glu_bwd.argtypes = [I, I, P, P, P, P, I, P, P, P, P, P, I64, I64]
             L.orc_add_layer_norm_fwd.argtypes = [I, P, P, I, P, P, I, F, P, P, P, P, P, P, I64, I64]
             L.orc_add_layer_norm_bwd.argtypes = [I, P, P, P, I, F, P, I, P, P, P, P, P, P, I64, I64]
+            L.orc_weighted_squared_relu_fwd.argtypes = [I, P, P, I, P, P, I64, I64]
+            L.orc_weighted_squared_relu_bwd.argtypes = [I, P, P, P, I, P, P, P, I64, I64]
             L.orc_philox4x32_10.argtypes = [P, P, P]
             L.orc_philox4x32_10.restype = None
             for name in ("orc_gelu_tanh", "orc_gelu_tanh_grad", "orc_gelu_erf", "orc_gelu_erf_grad",
@@ -272,6 +274,34 @@ def add_layer_norm_bwd(dt, dy, h, gamma, eps=1e-5, zero_centered=False, dh_in=No
                                      float(eps), _ptr(dh_in), DTYPES[res_dt], _ptr(dx), _ptr(dx64), _ptr(mag),
                                      _ptr(dres), _ptr(dgamma), _ptr(dbeta), T, H))
     return dx, dx64, mag, dres, dgamma, dbeta
+
+
+def weighted_squared_relu_fwd(dt, x, weights=None, w_dt=None):
+    """Returns out (dt storage), out64."""
+    T, H = x.shape
+    w_dt = w_dt or dt
+    x = _check_in(x, dt, name="x")
+    weights = _check_in(weights, w_dt, (T,), "weights")
+    out = np.empty((T, H), _storage(dt))
+    out64 = np.empty((T, H), np.float64)
+    _ok(lib().orc_weighted_squared_relu_fwd(DTYPES[dt], _ptr(x), _ptr(weights), DTYPES[w_dt], _ptr(out), _ptr(out64),
+                                            T, H))
+    return out, out64
+
+
+def weighted_squared_relu_bwd(dt, g, x, weights=None, w_dt=None):
+    """Returns dx (dt storage), dx64, dweights64 [T] (None without weights)."""
+    T, H = x.shape
+    w_dt = w_dt or dt
+    g = _check_in(g, dt, (T, H), "g")
+    x = _check_in(x, dt, name="x")
+    weights = _check_in(weights, w_dt, (T,), "weights")
+    dx = np.empty((T, H), _storage(dt))
+    dx64 = np.empty((T, H), np.float64)
+    dw = np.empty((T,), np.float64) if weights is not None else None
+    _ok(lib().orc_weighted_squared_relu_bwd(DTYPES[dt], _ptr(g), _ptr(x), _ptr(weights), DTYPES[w_dt], _ptr(dx),
+                                            _ptr(dx64), _ptr(dw), T, H))
+    return dx, dx64, dw
 
 
 def dropout_mask(T, H, p, seed, offset, row0=0):

@@ -19,6 +19,7 @@
  *   §9    weighted SwiGLU equals unweighted SwiGLU times the weights
  *   §5    the fused LayerNorm (eps, zero-centred gamma), here behind a
  *         residual add
+ *   §2/§8 the MoE weighted squared ReLU (named only)
  *
  * Evaluation rules (readings where the pages are silent):
  *   - every input is decoded exactly to double; every formula is evaluated in
@@ -590,6 +591,52 @@ int orc_add_layer_norm_bwd(int dt, const void* dy, const void* h_in, const void*
   }
   free(h);
   free(a);
+  return ORC_OK;
+}
+
+/* Weighted squared ReLU for MoE experts [fusions §2 and §8 name the fused
+ * op and its switch, §9 its unit test; the formula is not printed]. Read as
+ * the weighted-SwiGLU pattern of §9 applied to the squared ReLU:
+ *   out[t, j] = relu(x)^2 * w[t]          (w NULL: 1, the plain squared ReLU)
+ * relu passes NaN through as torch's does (NaN > 0 is false, but NaN is not 0).
+ * Backward:
+ *   dx[t, j]  = g * w[t] * 2 relu(x)
+ *   dw[t]     = sum_j g * relu(x)^2      (double, nullable; needs w)    */
+static double relu(double x) { return x > 0.0 ? x : (isnan(x) ? x : 0.0); }
+
+int orc_weighted_squared_relu_fwd(int dt, const void* x, const void* w, int w_dt, void* out, double* out64,
+                                  int64_t T, int64_t H) {
+  if (!dtype_ok(dt) || (w && !dtype_ok(w_dt)) || T < 0 || H <= 0) return ORC_BAD;
+  for (int64_t t = 0; t < T; ++t) {
+    double wt = w ? load_elem(w_dt, w, t) : 1.0;
+    for (int64_t j = 0; j < H; ++j) {
+      int64_t i = t * H + j;
+      double r = relu(load_elem(dt, x, i));
+      double v = r * r * wt;
+      store_elem(dt, out, i, v);
+      if (out64) out64[i] = v;
+    }
+  }
+  return ORC_OK;
+}
+
+int orc_weighted_squared_relu_bwd(int dt, const void* g, const void* x, const void* w, int w_dt, void* dx,
+                                  double* dx64, double* dw, int64_t T, int64_t H) {
+  if (!dtype_ok(dt) || (w && !dtype_ok(w_dt)) || T < 0 || H <= 0 || (dw && !w)) return ORC_BAD;
+  for (int64_t t = 0; t < T; ++t) {
+    double wt = w ? load_elem(w_dt, w, t) : 1.0;
+    double acc = 0.0;
+    for (int64_t j = 0; j < H; ++j) {
+      int64_t i = t * H + j;
+      double r = relu(load_elem(dt, x, i));
+      double gv = load_elem(dt, g, i);
+      double v = gv * wt * 2.0 * r;
+      store_elem(dt, dx, i, v);
+      if (dx64) dx64[i] = v;
+      acc += gv * r * r;
+    }
+    if (dw) dw[t] = acc;
+  }
   return ORC_OK;
 }
 
