@@ -15,10 +15,10 @@ Inputs are resident in HBM before timing starts. `value` is the algorithmic
 bytes of a step (each tensor read or written once, bias and gradients of the
 bias included, reduction partials excluded) divided by the step time.
 
-The ops beyond the step (the exact erf GeLU at the chain's MLP shape, and
-residual add + LayerNorm at the chain's hidden size) are timed after the step
-loop, the same way, and reported under "next_rows"; they are not part of
-`value`.
+The ops beyond the step (the exact erf GeLU at the chain's MLP shape,
+residual add + LayerNorm at the chain's hidden size, and the MoE weighted
+squared ReLU) are timed after the step loop, the same way, and reported under
+"next_rows"; they are not part of `value`.
 
 Prints one JSON line (see the keys below). `--gpus N` with N > 1 exits: this
 build runs on a single GPU.
@@ -192,6 +192,20 @@ def build_ops(dev):
                                                      dbeta=ldb, ws=lws),
                     T * H * 8 + H * 2 + T * 8 + H * 8, ["ln_bwd", "colsum_chunk", "colsum", "colsum_chunk",
                                                         "colsum"]))
+
+    # -- beyond the step: MoE weighted squared ReLU, bf16 [8192, 14336], fp32 weights
+    w = WORKLOADS["wsrelu_bf16_8192x14336"]
+    sx, sg, sw = (load(w.name, k) for k in ("x", "g", "weights"))
+    T, H = sx.shape
+    so, sdx = torch.empty_like(sx), torch.empty_like(sx)
+    sdw = torch.empty(T, dtype=torch.float32, device=dev)
+    sws = torch.empty(max(1, mb.mb_weighted_squared_relu_bwd_workspace(T, H, sx.dtype)), dtype=torch.uint8,
+                      device=dev)
+    extra.append(Op("weighted_squared_relu_fwd_bf16_8192x14336",
+                    lambda: mb.mb_weighted_squared_relu_fwd(sx, sw, out=so), T * H * 4 + T * 4, ["srelu_fwd"]))
+    extra.append(Op("weighted_squared_relu_bwd_bf16_8192x14336",
+                    lambda: mb.mb_weighted_squared_relu_bwd(sg, sx, sw, dx=sdx, dweights=sdw, ws=sws),
+                    T * H * 6 + T * 8, ["srelu_bwd", "colsum"]))
     return ops, extra, host
 
 

@@ -201,6 +201,35 @@ mb_status_t mb_bias_geglu_bwd(const void* g, const void* in, const void* bias, v
                               int64_t hidden, mb_dtype_t dt, hipStream_t s);
 
 /* ---------------------------------------------------------------------------
+ * Weighted squared ReLU for MoE experts [fusions §2 and §8 name the fused op
+ * and its switch, §9 its unit test; no formula is printed]. Read as the
+ * weighted-SwiGLU pattern of §9 (the unweighted activation times the
+ * per-token weight) applied to the squared ReLU:
+ *   out[t, j] = relu(x)^2 * w[t]
+ * relu passes NaN through. weights [T] of weights_dt (fp32, fp16 or bf16) or
+ * NULL for the plain squared ReLU. x, out [T,H] dt; out may equal x (in
+ * place). Errors as for mb_bias_gelu_fwd; weights must be aligned to their
+ * element size. */
+mb_status_t mb_weighted_squared_relu_fwd(const void* x, const void* weights, mb_dtype_t weights_dt,
+                                         void* out, int64_t tokens, int64_t hidden, mb_dtype_t dt,
+                                         hipStream_t s);
+
+/* Workspace bytes for the weights gradient of mb_weighted_squared_relu_bwd. */
+size_t mb_weighted_squared_relu_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt,
+                                              int with_dweights);
+
+/* Backward:
+ *   dx[t, j]    = g * w[t] * 2 relu(x)              (dtype dt; may equal g or x)
+ *   dweights[t] = sum over j of g * relu(x)^2        (fp32 [T], NULL: skip;
+ *                                                    needs weights)
+ * The weights gradient is deterministic and atomic-free: per-strip row
+ * partials in ws, then an ordered sum over the strips. */
+mb_status_t mb_weighted_squared_relu_bwd(const void* g, const void* x, const void* weights,
+                                         mb_dtype_t weights_dt, void* dx, float* dweights, void* ws,
+                                         size_t ws_bytes, int64_t tokens, int64_t hidden,
+                                         mb_dtype_t dt, hipStream_t s);
+
+/* ---------------------------------------------------------------------------
  * Residual add + LayerNorm [fusions §5.1-§5.4: the fused LayerNorm that
  * Megatron-LM wraps, its eps (default 1e-5) in the denominator, and the
  * zero-centred gamma applied as weight + 1], fused with the residual add that

@@ -145,3 +145,19 @@ def test_layer_norm_validation():
     assert bw(A, B, C, D, E, 0, None, BF16, A + 16, None, None, None, None, 0, 1024, 8192, BF16, None) == ALIAS
     assert bw(A, B, C, D, E, 0, None, BF16, A, B, None, None, None, 0, 0, 8192, BF16, None) == OK  # dx = dy, dres = h
     assert bw(A, B, C, D, E, 0, None, F32, A, B, None, None, None, 0, 4, 8192, BF16, None) == ALIAS
+
+
+def test_squared_relu_validation():
+    fw, bw, wsf = (L().mb_weighted_squared_relu_fwd, L().mb_weighted_squared_relu_bwd,
+                   L().mb_weighted_squared_relu_bwd_workspace)
+    assert fw(A, None, F32, B, 4, 60, BF16, None) == SHAPE
+    assert fw(A, C, 7, B, 4, 64, BF16, None) == DTYPE
+    assert fw(A, C + 2, F32, B, 4, 64, BF16, None) == ALIGN       # fp32 weights need 4-byte alignment
+    assert fw(A, None, F32, A + 16, 4, 64, BF16, None) == ALIAS
+    assert fw(A, None, F32, A, 0, 64, BF16, None) == OK           # in place, empty
+    ws = wsf(64, 512, BF16, 1)
+    assert ws > 0 and wsf(64, 512, BF16, 0) == 0
+    assert bw(A, B, None, F32, C, D, E, ws, 64, 512, BF16, None) == NULL        # dweights needs weights
+    assert bw(A, B, E, F32, C, D, None, 0, 64, 512, BF16, None) == WORKSPACE
+    assert bw(A, B, None, F32, A, None, None, 0, 0, 512, BF16, None) == OK      # dx over g, empty
+    assert bw(A, B, None, F32, A + 16, None, None, 0, 4, 512, BF16, None) == ALIAS

@@ -24,6 +24,7 @@ __all__ = [
     "mb_bias_swiglu_fwd", "mb_bias_swiglu_bwd", "mb_bias_geglu_fwd", "mb_bias_geglu_bwd",
     "mb_bias_glu_bwd_workspace",
     "mb_add_layer_norm_fwd", "mb_add_layer_norm_bwd", "mb_add_layer_norm_bwd_workspace",
+    "mb_weighted_squared_relu_fwd", "mb_weighted_squared_relu_bwd", "mb_weighted_squared_relu_bwd_workspace",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmb.so")
@@ -72,6 +73,9 @@ def lib() -> ctypes.CDLL:
                 "mb_bias_geglu_bwd": ([P, P, P, P, P, P, SZ, I64, I64, I, P], I),
                 "mb_add_layer_norm_fwd": ([P, P, I, P, P, F, I, P, P, P, P, I64, I64, I, P], I),
                 "mb_add_layer_norm_bwd_workspace": ([I64, I64, I, I, I], SZ),
+                "mb_weighted_squared_relu_fwd": ([P, P, I, P, I64, I64, I, P], I),
+                "mb_weighted_squared_relu_bwd_workspace": ([I64, I64, I, I], SZ),
+                "mb_weighted_squared_relu_bwd": ([P, P, P, I, P, P, P, SZ, I64, I64, I, P], I),
                 "mb_add_layer_norm_bwd": ([P, P, P, P, P, I, P, I, P, P, P, P, P, SZ, I64, I64, I, P], I),
             }
             for name, (args, res) in sig.items():
@@ -374,3 +378,39 @@ def mb_add_layer_norm_bwd(dy, h, gamma, mean, rstd, zero_centered_gamma=False, d
         _p(dx), _p(dresidual), _p(dgamma), _p(dbeta), _p(ws), ws.numel() if ws is not None else 0, T, H,
         _dt(h), _stream(h, stream)))
     return dx, dresidual, dgamma, dbeta
+
+
+# ------------------------------------------------------------------ weighted squared ReLU
+
+def mb_weighted_squared_relu_fwd(x, weights=None, out=None, stream=None):
+    """relu(x)^2 * weights[t] (weights None: the plain squared ReLU); out=x runs in place."""
+    T, H = _rows(x, "x")
+    _vec(weights, T, "weights")
+    out = torch.empty_like(x) if out is None else out
+    wdt = _dt(weights) if weights is not None else 0
+    _check("mb_weighted_squared_relu_fwd", lib().mb_weighted_squared_relu_fwd(
+        _p(x), _p(weights), wdt, _p(out), T, H, _dt(x), _stream(x, stream)))
+    return out
+
+
+def mb_weighted_squared_relu_bwd_workspace(tokens, hidden, dtype, with_dweights=True) -> int:
+    return int(lib().mb_weighted_squared_relu_bwd_workspace(tokens, hidden, DTYPES[dtype], int(bool(with_dweights))))
+
+
+def mb_weighted_squared_relu_bwd(g, x, weights=None, dx=None, dweights=None, ws=None, stream=None):
+    """Returns (dx, dweights or None); dweights defaults to True when weights are given."""
+    T, H = _rows(x, "x")
+    _rows(g, "g", H)
+    _vec(weights, T, "weights")
+    if dweights is None:
+        dweights = weights is not None
+    dx = torch.empty_like(x) if dx is None else dx
+    dweights = _grad_out(dweights, T, x.device)
+    nws = mb_weighted_squared_relu_bwd_workspace(T, H, x.dtype, dweights is not None)
+    if ws is None and nws:
+        ws = torch.empty(nws, dtype=torch.uint8, device=x.device)
+    wdt = _dt(weights) if weights is not None else 0
+    _check("mb_weighted_squared_relu_bwd", lib().mb_weighted_squared_relu_bwd(
+        _p(g), _p(x), _p(weights), wdt, _p(dx), _p(dweights), _p(ws), ws.numel() if ws is not None else 0, T, H,
+        _dt(x), _stream(x, stream)))
+    return dx, dweights

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "libmb")
 LIB = os.path.join(PKG, "libmb.so")
 
-SOURCES = ["mb_gelu.hip", "mb_bda.hip", "mb_glu.hip", "mb_reduce.hip", "mb_ln.hip", "mb_abi.cpp"]
+SOURCES = ["mb_gelu.hip", "mb_bda.hip", "mb_glu.hip", "mb_reduce.hip", "mb_ln.hip", "mb_sqrelu.hip", "mb_abi.cpp"]
 ARCH = "gfx950"
 
 

@@ -412,6 +412,59 @@ mb_status_t mb_bias_geglu_bwd(const void* g, const void* in, const void* bias, v
                         s);
 }
 
+// ------------------------------------------------------------------ weighted squared ReLU
+
+mb_status_t mb_weighted_squared_relu_fwd(const void* x, const void* weights, mb_dtype_t weights_dt, void* out,
+                                         int64_t tokens, int64_t hidden, mb_dtype_t dt, hipStream_t s) {
+  if (!dt_ok(dt) || (weights && !dt_ok(weights_dt))) return MB_ERR_DTYPE;
+  if (mb_status_t st = check_shape(tokens, hidden, dt)) return st;
+  const size_t tb = static_cast<size_t>(tokens) * hidden * esize(dt);
+  const size_t wb = weights ? static_cast<size_t>(tokens) * esize(weights_dt) : 0;
+  if (!need(x, tb) || !need(out, tb)) return MB_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(out, 16) || (weights && !aligned(weights, esize(weights_dt)))) return MB_ERR_ALIGN;
+  if (!aliasing_ok({{out, tb}}, {{x, tb}, {weights, wb}}, {{0, 0}})) return MB_ERR_ALIAS;
+  if (tokens == 0) return MB_OK;
+  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_SRELU_FWD_BLOCKS);
+  if (hipError_t e = mb::launch_srelu_fwd(dt, weights_dt, x, weights, out, t, s)) return hip_status(e);
+  return finish();
+}
+
+static mb::Tiling srelu_bwd_tiling(int64_t tokens, int64_t hidden, mb_dtype_t dt) {
+  return mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_SRELU_BWD_BLOCKS);
+}
+
+size_t mb_weighted_squared_relu_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dweights) {
+  if (!with_dweights || !dt_ok(dt) || check_shape(tokens, hidden, dt) != MB_OK || tokens == 0) return 0;
+  const mb::Tiling t = srelu_bwd_tiling(tokens, hidden, dt);
+  return static_cast<size_t>(t.strips) * tokens * 4;
+}
+
+mb_status_t mb_weighted_squared_relu_bwd(const void* g, const void* x, const void* weights, mb_dtype_t weights_dt,
+                                         void* dx, float* dweights, void* ws, size_t ws_bytes, int64_t tokens,
+                                         int64_t hidden, mb_dtype_t dt, hipStream_t s) {
+  if (!dt_ok(dt) || (weights && !dt_ok(weights_dt))) return MB_ERR_DTYPE;
+  if (mb_status_t st = check_shape(tokens, hidden, dt)) return st;
+  if (dweights && !weights) return MB_ERR_NULL;
+  const size_t tb = static_cast<size_t>(tokens) * hidden * esize(dt);
+  const size_t wb = weights ? static_cast<size_t>(tokens) * esize(weights_dt) : 0;
+  if (!need(g, tb) || !need(x, tb) || !need(dx, tb)) return MB_ERR_NULL;
+  if (!aligned(g, 16) || !aligned(x, 16) || !aligned(dx, 16) || (weights && !aligned(weights, esize(weights_dt))) ||
+      !aligned(dweights, 4) || !aligned(ws, 16))
+    return MB_ERR_ALIGN;
+  const size_t need_ws = dweights ? mb_weighted_squared_relu_bwd_workspace(tokens, hidden, dt, 1) : 0;
+  if (need_ws && (!ws || ws_bytes < need_ws)) return MB_ERR_WORKSPACE;
+  if (!aliasing_ok({{dx, tb}, {dweights, dweights ? static_cast<size_t>(tokens) * 4 : 0}, {ws, need_ws}},
+                   {{g, tb}, {x, tb}, {weights, wb}}, {{0, 0}, {0, 1}}))
+    return MB_ERR_ALIAS;
+  if (tokens == 0) return MB_OK;
+  const mb::Tiling t = srelu_bwd_tiling(tokens, hidden, dt);
+  float* wpart = dweights ? static_cast<float*>(ws) : nullptr;
+  if (hipError_t e = mb::launch_srelu_bwd(dt, weights_dt, g, x, weights, dx, wpart, t, s)) return hip_status(e);
+  if (dweights)
+    if (hipError_t e = mb::launch_colsum(wpart, t.strips, tokens, dweights, s)) return hip_status(e);
+  return finish();
+}
+
 // ------------------------------------------------------------------ residual add + LayerNorm
 
 static bool ln_dtypes_ok(mb_dtype_t dt, mb_dtype_t rdt) { return dt_ok(dt) && (rdt == dt || rdt == MB_F32); }

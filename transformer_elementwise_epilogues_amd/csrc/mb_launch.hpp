@@ -60,6 +60,18 @@ struct Tiling {
 #endif
 
 // The tiling every kernel of one call uses; also sizes the workspaces.
+#ifndef MB_SRELU_FWD_BLOCKS
+#define MB_SRELU_FWD_BLOCKS 768
+#endif
+#ifndef MB_SRELU_FWD_UNROLL
+#define MB_SRELU_FWD_UNROLL 2
+#endif
+#ifndef MB_SRELU_BWD_BLOCKS
+#define MB_SRELU_BWD_BLOCKS 512
+#endif
+#ifndef MB_SRELU_BWD_UNROLL
+#define MB_SRELU_BWD_UNROLL 2
+#endif
 #ifndef MB_LN_FWD_BLOCKS
 #define MB_LN_FWD_BLOCKS 2048
 #endif
@@ -124,6 +136,13 @@ hipError_t launch_glu_fwd(int act, int dt, const void* in, const void* bias, con
 hipError_t launch_glu_bwd(int act, int dt, const void* g, const void* in, const void* bias,
                           const void* w, int w_dt, void* din, float* bias_partials,
                           float* w_partials, int64_t H, const Tiling& t, hipStream_t s);
+
+// ---- weighted squared ReLU. w: per-token weights of dtype wdt, or nullptr;
+// wpart: [strips, T] fp32 row partials of the weights gradient, or nullptr.
+hipError_t launch_srelu_fwd(int dt, int wdt, const void* x, const void* w, void* out, const Tiling& t,
+                            hipStream_t s);
+hipError_t launch_srelu_bwd(int dt, int wdt, const void* g, const void* x, const void* w, void* dx, float* wpart,
+                            const Tiling& t, hipStream_t s);
 
 // ---- residual add + LayerNorm
 struct LnArgs {

@@ -126,4 +126,11 @@ WORKLOADS = {
         "dy": Tensor(4, (16384, 8192), "bf16"),
         "dh_in": Tensor(5, (16384, 8192), "bf16"),
     }, eps=1e-5, zero_centered_gamma=True),
+    # MoE expert activation: weighted squared ReLU of the first expert GEMM's
+    # output, per-token routing weights in fp32
+    "wsrelu_bf16_8192x14336": _w(7, "wsrelu_bf16_8192x14336", {
+        "x": Tensor(0, (8192, 14336), "bf16"),
+        "g": Tensor(1, (8192, 14336), "bf16"),
+        "weights": Tensor(2, (8192,), "f32", dist="uniform"),
+    }),
 }
