@@ -96,7 +96,9 @@ bool prob_ok(float p) { return !std::isnan(p) && p >= 0.0f && p <= 1.0f; }
 mb::DropoutArgs dropout_args(float p, uint64_t seed, uint64_t offset) {
   mb::DropoutArgs d;
   const double t = std::floor(static_cast<double>(p) * 4294967296.0);
-  d.theta = t >= 4294967296.0 ? (uint64_t{1} << 32) : (t <= 0.0 ? 0 : static_cast<uint64_t>(t));
+  const uint64_t theta = t >= 4294967296.0 ? (uint64_t{1} << 32) : (t <= 0.0 ? 0 : static_cast<uint64_t>(t));
+  d.drop_all = theta == (uint64_t{1} << 32) ? 1u : 0u;
+  d.theta32 = d.drop_all ? 0u : static_cast<uint32_t>(theta);
   d.scale = p < 1.0f ? static_cast<float>(1.0 / (1.0 - static_cast<double>(p))) : 0.0f;
   d.k0 = static_cast<uint32_t>(seed);
   d.k1 = static_cast<uint32_t>(seed >> 32);

@@ -37,7 +37,7 @@ constexpr int epl() {
 template <int N>
 __device__ __forceinline__ void keep_n(uint64_t i0, const DropoutArgs& d, bool* keep) {
 #pragma unroll
-  for (int q = 0; q < N / 4; ++q) keep4((i0 >> 2) + q, d.o0, d.o1, d.k0, d.k1, d.theta, keep + 4 * q);
+  for (int q = 0; q < N / 4; ++q) keep4((i0 >> 2) + q, d.o0, d.o1, d.k0, d.k1, d.theta32, d.drop_all, keep + 4 * q);
 }
 
 // Forward. The U rows' loads are issued before any of their stores.
@@ -153,8 +153,8 @@ __global__ __launch_bounds__(256) void mask_kernel(uint8_t* bits, int64_t n, Dro
   if (byte >= nbytes) return;
   const int64_t i0 = byte * 8;
   bool keep[8] = {false, false, false, false, false, false, false, false};
-  keep4(static_cast<uint64_t>(i0) >> 2, d.o0, d.o1, d.k0, d.k1, d.theta, keep);
-  if (i0 + 4 < n) keep4((static_cast<uint64_t>(i0) >> 2) + 1, d.o0, d.o1, d.k0, d.k1, d.theta, keep + 4);
+  keep4(static_cast<uint64_t>(i0) >> 2, d.o0, d.o1, d.k0, d.k1, d.theta32, d.drop_all, keep);
+  if (i0 + 4 < n) keep4((static_cast<uint64_t>(i0) >> 2) + 1, d.o0, d.o1, d.k0, d.k1, d.theta32, d.drop_all, keep + 4);
   unsigned v = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) v |= (keep[k] ? 1u : 0u) << k;

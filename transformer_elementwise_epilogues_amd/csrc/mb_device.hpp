@@ -187,14 +187,18 @@ template <> __device__ __forceinline__ float round_to<DT::F16>(float x) {
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
 // 32x32->64-bit products and an xor with the round key; the key advances by
 // the Weyl increments after every round. On gfx950 each product is a single
-// v_mad_u64_u32; the key lives in scalar registers.
+// v_mad_u64_u32 and each three-way xor a single v_bitop3_b32 (truth table
+// 0x96 = a ^ b ^ c, new in CDNA4); the key lives in scalar registers.
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
 __device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     const uint64_t m0 = static_cast<uint64_t>(0xD2511F53u) * c[0];
     const uint64_t m1 = static_cast<uint64_t>(0xCD9E8D57u) * c[2];
-    const uint32_t n0 = static_cast<uint32_t>(m1 >> 32) ^ c[1] ^ k0;
-    const uint32_t n2 = static_cast<uint32_t>(m0 >> 32) ^ c[3] ^ k1;
+    const uint32_t n0 = xor3(static_cast<uint32_t>(m1 >> 32), c[1], k0);
+    const uint32_t n2 = xor3(static_cast<uint32_t>(m0 >> 32), c[3], k1);
     c[1] = static_cast<uint32_t>(m1);
     c[3] = static_cast<uint32_t>(m0);
     c[0] = n0;
@@ -205,13 +209,14 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32
 }
 
 // Keep flags of the 4 consecutive elements 4q .. 4q+3: counter (q, offset),
-// key seed; element 4q+k keeps iff word k >= theta (theta <= 2^32).
+// key seed; element 4q+k keeps iff word k >= theta, given as a 32-bit
+// threshold and a drop-everything flag (theta = 2^32).
 __device__ __forceinline__ void keep4(uint64_t q, uint32_t o0, uint32_t o1, uint32_t k0, uint32_t k1,
-                                      uint64_t theta, bool* keep) {
+                                      uint32_t theta32, uint32_t drop_all, bool* keep) {
   uint32_t c[4] = {static_cast<uint32_t>(q), static_cast<uint32_t>(q >> 32), o0, o1};
   philox4x32_10(c, k0, k1);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) keep[k] = static_cast<uint64_t>(c[k]) >= theta;
+  for (int k = 0; k < 4; ++k) keep[k] = c[k] >= theta32 && !drop_all;
 }
 
 // ---------------------------------------------------------------- activations

@@ -112,7 +112,11 @@ hipError_t launch_gelu_bwd(int dt, bool exact, const void* g, const void* y, con
                            float* partials, const Tiling& t, hipStream_t s);
 
 struct DropoutArgs {
-  uint64_t theta;  // keep iff word >= theta
+  // keep iff word >= theta, theta in [0, 2^32]: theta32 = theta and
+  // drop_all = 0, or drop_all = 1 for theta = 2^32 (p = 1), so that the
+  // kernels compare in 32 bits
+  uint32_t theta32;
+  uint32_t drop_all;
   float scale;     // survivor scale
   uint32_t k0, k1; // key = seed
   uint32_t o0, o1; // counter high words = offset
