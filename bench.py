@@ -242,7 +242,9 @@ def source_hash(files):
 
 TRAFFIC_SOURCES = ["transformer_elementwise_epilogues_amd/csrc/mb_gelu.hip",
                    "transformer_elementwise_epilogues_amd/csrc/mb_device.hpp",
-                   "transformer_elementwise_epilogues_amd/csrc/mb_reduce.hip"]
+                   "transformer_elementwise_epilogues_amd/csrc/mb_reduce.hip",
+                   "transformer_elementwise_epilogues_amd/csrc/mb_launch.hpp",
+                   "transformer_elementwise_epilogues_amd/csrc/mb_abi.cpp"]
 
 
 def measured_traffic():

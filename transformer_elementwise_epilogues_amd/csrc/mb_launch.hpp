@@ -20,10 +20,12 @@ struct Tiling {
 
 // Launch shape per kernel family: blocks of 256 threads to aim for (row groups
 // are rounded down so the grid never exceeds it by a partial wave of blocks)
-// and rows in flight per wave. Measured on MI355X (rocprofv3 + bench.py): the
-// write path saturates with 1-2 resident blocks per CU, not with more.
+// and rows in flight per wave, measured on MI355X (bench-order sweeps). The
+// forward kernels without reductions stream best as many short-lived blocks
+// (one to four rows per wave); the backward kernels that keep bias-gradient
+// sums per lane do best with few resident blocks and more rows in flight.
 #ifndef MB_GELU_FWD_BLOCKS
-#define MB_GELU_FWD_BLOCKS 768
+#define MB_GELU_FWD_BLOCKS 65536
 #endif
 #ifndef MB_GELU_FWD_UNROLL
 #define MB_GELU_FWD_UNROLL 2
@@ -35,10 +37,16 @@ struct Tiling {
 #define MB_GELU_BWD_UNROLL 8
 #endif
 #ifndef MB_BDA_BLOCKS
-#define MB_BDA_BLOCKS 512
+#define MB_BDA_BLOCKS 65536
 #endif
 #ifndef MB_BDA_UNROLL
-#define MB_BDA_UNROLL 2
+#define MB_BDA_UNROLL 1
+#endif
+#ifndef MB_BDA_MIXED_BLOCKS
+#define MB_BDA_MIXED_BLOCKS 512
+#endif
+#ifndef MB_BDA_MIXED_UNROLL
+#define MB_BDA_MIXED_UNROLL 2
 #endif
 #ifndef MB_BDA_BWD_BLOCKS
 #define MB_BDA_BWD_BLOCKS 768
@@ -47,10 +55,10 @@ struct Tiling {
 #define MB_BDA_BWD_UNROLL 2
 #endif
 #ifndef MB_GLU_FWD_BLOCKS
-#define MB_GLU_FWD_BLOCKS 512
+#define MB_GLU_FWD_BLOCKS 65536
 #endif
 #ifndef MB_GLU_FWD_UNROLL
-#define MB_GLU_FWD_UNROLL 2
+#define MB_GLU_FWD_UNROLL 1
 #endif
 #ifndef MB_GLU_BWD_BLOCKS
 #define MB_GLU_BWD_BLOCKS 512
@@ -61,16 +69,16 @@ struct Tiling {
 
 // The tiling every kernel of one call uses; also sizes the workspaces.
 #ifndef MB_SRELU_FWD_BLOCKS
-#define MB_SRELU_FWD_BLOCKS 768
+#define MB_SRELU_FWD_BLOCKS 65536
 #endif
 #ifndef MB_SRELU_FWD_UNROLL
-#define MB_SRELU_FWD_UNROLL 2
+#define MB_SRELU_FWD_UNROLL 1
 #endif
 #ifndef MB_SRELU_BWD_BLOCKS
-#define MB_SRELU_BWD_BLOCKS 512
+#define MB_SRELU_BWD_BLOCKS 16384
 #endif
 #ifndef MB_SRELU_BWD_UNROLL
-#define MB_SRELU_BWD_UNROLL 2
+#define MB_SRELU_BWD_UNROLL 1
 #endif
 #ifndef MB_LN_FWD_BLOCKS
 #define MB_LN_FWD_BLOCKS 2048
