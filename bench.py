@@ -169,11 +169,13 @@ def build_ops(dev):
                   bwd5, ["bda_bwd", "colsum"]))
 
     # -- beyond the step: the exact (erf) GeLU on the chain's MLP activation
+    wse = torch.empty(max(1, mb.mb_bias_gelu_erf_bwd_workspace(T, H, gy.dtype, True)), dtype=torch.uint8,
+                      device=dev)
     extra = [Op("erf_gelu_fwd_bf16_16384x32768", lambda: mb.mb_bias_gelu_erf_fwd(gy, gb, out=gout),
                 T * H * 4 + H * 2, ["gelu_fwd"]),
              Op("erf_gelu_bwd_bf16_16384x32768",
-                lambda: mb.mb_bias_gelu_erf_bwd(gg, gy, gb, dgrad=dgr, dbias=dbg, ws=wsg),
-                T * H * 6 + H * 2 + H * 4, ["gelu_bwd", "colsum"])]
+                lambda: mb.mb_bias_gelu_erf_bwd(gg, gy, gb, dgrad=dgr, dbias=dbg, ws=wse),
+                T * H * 6 + H * 2 + H * 4, ["gelu_bwd", "colsum_chunk", "colsum"])]
 
     # -- beyond the step: residual add + LayerNorm, bf16 [16384, 8192]
     w = WORKLOADS["add_ln_bf16_16384x8192"]

@@ -96,10 +96,14 @@ mb_status_t mb_bias_gelu_bwd(const void* g, const void* y, const void* bias, voi
 mb_status_t mb_bias_gelu_erf_fwd(const void* y, const void* bias, void* out, int64_t tokens,
                                  int64_t hidden, mb_dtype_t dt, hipStream_t s);
 
+/* Workspace bytes for mb_bias_gelu_erf_bwd (its own launch shape). */
+size_t mb_bias_gelu_erf_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt,
+                                      int with_dbias);
+
 /* Backward of the exact GeLU:
  *   dgrad = g * (0.5 (1 + erf(0.70710678 z)) + z * 0.3989423 * exp(-z^2 / 2)),
  *   dbias as for mb_bias_gelu_bwd; the workspace is sized by
- *   mb_bias_gelu_bwd_workspace (same tiling). */
+ *   mb_bias_gelu_erf_bwd_workspace. */
 mb_status_t mb_bias_gelu_erf_bwd(const void* g, const void* y, const void* bias, void* dgrad,
                                  float* dbias, void* ws, size_t ws_bytes, int64_t tokens,
                                  int64_t hidden, mb_dtype_t dt, hipStream_t s);

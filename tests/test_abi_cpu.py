@@ -77,6 +77,12 @@ def test_gelu_bwd_validation():
     assert f(A, B, None, C, C + 64, E, ws, 1024, 4096, BF16, None) == ALIAS   # dbias inside dgrad
     assert f(A, B, None, C, D, C, ws, 1024, 4096, BF16, None) == ALIAS        # ws over dgrad
     assert f(A, B, None, B + 16, None, None, 0, 1024, 4096, BF16, None) == ALIAS
+    # the exact form has its own launch shape and workspace query
+    wse = L().mb_bias_gelu_erf_bwd_workspace(1024, 4096, BF16, 1)
+    assert wse > 0 and L().mb_bias_gelu_erf_bwd_workspace(1024, 4096, BF16, 0) == 0
+    fe = L().mb_bias_gelu_erf_bwd
+    assert fe(A, B, None, C, D, E, wse - 1, 1024, 4096, BF16, None) == WORKSPACE
+    assert fe(A, B, None, C, D, None, 0, 1024, 4096, BF16, None) == WORKSPACE
 
 
 def test_bda_validation():

@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "MBError", "lib", "abi_version",
     "mb_bias_gelu_fwd", "mb_bias_gelu_bwd", "mb_bias_gelu_bwd_workspace",
-    "mb_bias_gelu_erf_fwd", "mb_bias_gelu_erf_bwd",
+    "mb_bias_gelu_erf_fwd", "mb_bias_gelu_erf_bwd", "mb_bias_gelu_erf_bwd_workspace",
     "mb_bias_dropout_add_train", "mb_bias_dropout_add_infer", "mb_dropout_mask",
     "mb_bias_dropout_add_bwd", "mb_bias_dropout_add_bwd_workspace",
     "mb_bias_swiglu_fwd", "mb_bias_swiglu_bwd", "mb_bias_geglu_fwd", "mb_bias_geglu_bwd",
@@ -61,6 +61,7 @@ def lib() -> ctypes.CDLL:
                 "mb_bias_gelu_bwd": ([P, P, P, P, P, P, SZ, I64, I64, I, P], I),
                 "mb_bias_gelu_erf_fwd": ([P, P, P, I64, I64, I, P], I),
                 "mb_bias_gelu_erf_bwd": ([P, P, P, P, P, P, SZ, I64, I64, I, P], I),
+                "mb_bias_gelu_erf_bwd_workspace": ([I64, I64, I, I], SZ),
                 "mb_bias_dropout_add_train": ([P, P, P, I, P, I64, I64, I, F, U64, U64, P], I),
                 "mb_bias_dropout_add_infer": ([P, P, P, I, P, I64, I64, I, P], I),
                 "mb_dropout_mask": ([P, I64, I64, F, U64, U64, P], I),
@@ -152,13 +153,18 @@ def mb_bias_gelu_bwd_workspace(tokens, hidden, dtype, with_dbias=True) -> int:
     return int(lib().mb_bias_gelu_bwd_workspace(tokens, hidden, DTYPES[dtype], int(bool(with_dbias))))
 
 
+def mb_bias_gelu_erf_bwd_workspace(tokens, hidden, dtype, with_dbias=True) -> int:
+    return int(lib().mb_bias_gelu_erf_bwd_workspace(tokens, hidden, DTYPES[dtype], int(bool(with_dbias))))
+
+
 def _gelu_bwd(fn, g, y, bias, dgrad, dbias, ws, stream):
     T, H = _rows(y, "y")
     _rows(g, "g", H)
     _vec(bias, H, "bias")
     dgrad = torch.empty_like(y) if dgrad is None else dgrad
     dbias = _grad_out(dbias, H, y.device)
-    nws = mb_bias_gelu_bwd_workspace(T, H, y.dtype, dbias is not None)
+    wsf = mb_bias_gelu_erf_bwd_workspace if fn == "mb_bias_gelu_erf_bwd" else mb_bias_gelu_bwd_workspace
+    nws = wsf(T, H, y.dtype, dbias is not None)
     if ws is None and nws:
         ws = torch.empty(nws, dtype=torch.uint8, device=y.device)
     _check(fn, getattr(lib(), fn)(_p(g), _p(y), _p(bias), _p(dgrad), _p(dbias), _p(ws),

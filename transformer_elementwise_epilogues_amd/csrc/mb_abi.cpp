@@ -162,9 +162,27 @@ mb_status_t mb_bias_gelu_erf_fwd(const void* y, const void* bias, void* out, int
   return gelu_fwd_common(true, y, bias, out, tokens, hidden, dt, s);
 }
 
-size_t mb_bias_gelu_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias) {
+// The tanh and the exact forms have their own launch shapes (the exact form,
+// heavier on the ALU, runs many more row groups), so each has its workspace
+// query: the partial rows, then (for more than 32 of them) the chunk sums of
+// the ordered two-level column sum.
+static mb::Tiling gelu_bwd_tiling(bool exact, int64_t tokens, int64_t hidden, mb_dtype_t dt) {
+  return mb::plan_tiling(tokens, nvec_of(hidden, dt), exact ? MB_GELU_ERF_BWD_BLOCKS : MB_GELU_BWD_BLOCKS);
+}
+
+static size_t gelu_bwd_ws(bool exact, int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias) {
   if (!with_dbias || !dt_ok(dt) || check_shape(tokens, hidden, dt) != MB_OK || tokens == 0) return 0;
-  return col_partials_bytes(mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GELU_BWD_BLOCKS), hidden);
+  const mb::Tiling t = gelu_bwd_tiling(exact, tokens, hidden, dt);
+  return round_up(col_partials_bytes(t, hidden), 256) +
+         static_cast<size_t>(mb::colsum_tall_tmp_floats(t.G, hidden)) * 4;
+}
+
+size_t mb_bias_gelu_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias) {
+  return gelu_bwd_ws(false, tokens, hidden, dt, with_dbias);
+}
+
+size_t mb_bias_gelu_erf_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias) {
+  return gelu_bwd_ws(true, tokens, hidden, dt, with_dbias);
 }
 
 static mb_status_t gelu_bwd_common(bool exact, const void* g, const void* y, const void* bias, void* dgrad,
@@ -174,7 +192,7 @@ static mb_status_t gelu_bwd_common(bool exact, const void* g, const void* y, con
   if (mb_status_t st = check_shape(tokens, hidden, dt)) return st;
   const size_t tb = static_cast<size_t>(tokens) * hidden * esize(dt), bb = hidden * esize(dt);
   if (!need(g, tb) || !need(y, tb) || !need(dgrad, tb)) return MB_ERR_NULL;
-  const size_t need_ws = mb_bias_gelu_bwd_workspace(tokens, hidden, dt, dbias != nullptr);
+  const size_t need_ws = gelu_bwd_ws(exact, tokens, hidden, dt, dbias != nullptr);
   if (!aligned(g, 16) || !aligned(y, 16) || !aligned(dgrad, 16) || !aligned(bias, 16) || !aligned(dbias, 4) ||
       (need_ws && !aligned(ws, 16)))
     return MB_ERR_ALIGN;
@@ -188,11 +206,13 @@ static mb_status_t gelu_bwd_common(bool exact, const void* g, const void* y, con
     if (hipError_t e = mb::launch_fill_zero(dbias, hidden, s)) return hip_status(e);
     return finish();
   }
-  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GELU_BWD_BLOCKS);
+  const mb::Tiling t = gelu_bwd_tiling(exact, tokens, hidden, dt);
   float* partials = dbias ? static_cast<float*>(ws) : nullptr;
   if (hipError_t e = mb::launch_gelu_bwd(dt, exact, g, y, bias, dgrad, partials, t, s)) return hip_status(e);
-  if (dbias)
-    if (hipError_t e = reduce_columns(partials, t, hidden, dbias, s)) return hip_status(e);
+  if (dbias) {
+    float* tmp = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(col_partials_bytes(t, hidden), 256));
+    if (hipError_t e = mb::launch_colsum_tall(partials, t.G, hidden, tmp, dbias, s)) return hip_status(e);
+  }
   return finish();
 }
 
@@ -244,17 +264,21 @@ mb_status_t mb_bias_dropout_add_infer(const void* x, const void* bias, const voi
   return bda_common(x, bias, residual, residual_dt, out, tokens, hidden, dt, false, 0.0f, 0, 0, s);
 }
 
-// Row groups of the dropout-add backward. The lane count depends on the
-// residual dtype; the workspace is sized for the wider lanes (fewer strips,
-// so more row groups), which covers both.
+// Row groups of the dropout-add backward. The lane layout and the launch
+// shape depend on the residual dtype (fp32 beside bf16/fp16 or not), which the
+// workspace query does not take: it returns the larger of the two layouts'
+// partial rows.
 static mb::Tiling bda_bwd_tiling(int64_t tokens, int64_t hidden, mb_dtype_t dt, mb_dtype_t residual_dt) {
   const int lanes = static_cast<int>(hidden / mb::bda_elems_per_lane(dt, residual_dt));
-  return mb::plan_tiling(tokens, lanes, MB_BDA_BWD_BLOCKS);
+  const bool mixed = residual_dt == MB_F32 && dt != MB_F32;
+  return mb::plan_tiling(tokens, lanes, mixed ? MB_BDA_BWD_MIXED_BLOCKS : MB_BDA_BWD_BLOCKS);
 }
 
 size_t mb_bias_dropout_add_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias) {
   if (!with_dbias || !dt_ok(dt) || check_shape(tokens, hidden, dt) != MB_OK || tokens == 0) return 0;
-  return col_partials_bytes(bda_bwd_tiling(tokens, hidden, dt, dt), hidden);
+  const size_t same = col_partials_bytes(bda_bwd_tiling(tokens, hidden, dt, dt), hidden);
+  const size_t mixed = col_partials_bytes(bda_bwd_tiling(tokens, hidden, dt, MB_F32), hidden);
+  return same > mixed ? same : mixed;
 }
 
 mb_status_t mb_bias_dropout_add_bwd(const void* g, void* dx, void* dresidual, mb_dtype_t residual_dt, float* dbias,

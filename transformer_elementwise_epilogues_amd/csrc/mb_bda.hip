@@ -185,7 +185,7 @@ hipError_t bda_bwd_dispatch(const void* g, void* dx, void* dres, float* partials
   auto gp = static_cast<const char*>(g);
   auto xp = static_cast<char*>(dx);
   auto rp = static_cast<char*>(dres);
-  constexpr int U = MB_BDA_BWD_UNROLL;
+  constexpr int U = (R == DT::F32 && D != DT::F32) ? MB_BDA_BWD_MIXED_UNROLL : MB_BDA_BWD_UNROLL;
   if (partials && dres)
     hipLaunchKernelGGL((bda_bwd_kernel<D, R, U, true, true>), grid, dim3(kThreads), 0, s, gp, xp, rp, partials, t.T, t.nvec, H, d);
   else if (partials)

@@ -21,7 +21,8 @@ namespace mb {
 namespace {
 
 constexpr int kUnrollFwd = MB_GELU_FWD_UNROLL;
-constexpr int kUnrollBwd = MB_GELU_BWD_UNROLL;
+// the exact form is heavier on the ALU and prefers more waves (its own shape)
+template <int KIND> constexpr int unroll_bwd() { return KIND == 0 ? MB_GELU_BWD_UNROLL : MB_GELU_ERF_BWD_UNROLL; }
 
 template <DT D>
 __device__ __forceinline__ void load_bias(const char* bias, int cv, float* b) {
@@ -149,10 +150,10 @@ hipError_t gelu_bwd_dispatch(const void* g, const void* y, const void* bias, voi
   auto bp = static_cast<const char*>(bias);
   auto dp = static_cast<char*>(dgrad);
   if (partials)
-    hipLaunchKernelGGL((gelu_bwd_kernel<D, KIND, kUnrollBwd, true>), grid, dim3(kThreads), 0, s, gp, yp, bp, dp, partials,
+    hipLaunchKernelGGL((gelu_bwd_kernel<D, KIND, unroll_bwd<KIND>(), true>), grid, dim3(kThreads), 0, s, gp, yp, bp, dp, partials,
                        t.T, t.nvec);
   else
-    hipLaunchKernelGGL((gelu_bwd_kernel<D, KIND, kUnrollBwd, false>), grid, dim3(kThreads), 0, s, gp, yp, bp, dp, partials,
+    hipLaunchKernelGGL((gelu_bwd_kernel<D, KIND, unroll_bwd<KIND>(), false>), grid, dim3(kThreads), 0, s, gp, yp, bp, dp, partials,
                        t.T, t.nvec);
   return hipGetLastError();
 }

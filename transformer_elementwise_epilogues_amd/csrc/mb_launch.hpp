@@ -36,6 +36,12 @@ struct Tiling {
 #ifndef MB_GELU_BWD_UNROLL
 #define MB_GELU_BWD_UNROLL 8
 #endif
+#ifndef MB_GELU_ERF_BWD_BLOCKS
+#define MB_GELU_ERF_BWD_BLOCKS 32768
+#endif
+#ifndef MB_GELU_ERF_BWD_UNROLL
+#define MB_GELU_ERF_BWD_UNROLL 1
+#endif
 #ifndef MB_BDA_BLOCKS
 #define MB_BDA_BLOCKS 65536
 #endif
@@ -53,6 +59,12 @@ struct Tiling {
 #endif
 #ifndef MB_BDA_BWD_UNROLL
 #define MB_BDA_BWD_UNROLL 2
+#endif
+#ifndef MB_BDA_BWD_MIXED_BLOCKS
+#define MB_BDA_BWD_MIXED_BLOCKS 768
+#endif
+#ifndef MB_BDA_BWD_MIXED_UNROLL
+#define MB_BDA_BWD_MIXED_UNROLL 2
 #endif
 #ifndef MB_GLU_FWD_BLOCKS
 #define MB_GLU_FWD_BLOCKS 65536
