@@ -13,7 +13,10 @@ One step = one pass of every fused op at its full synthetic workload:
       backward regenerates the mask; the residual gradient is g itself)
 Inputs are resident in HBM before timing starts. `value` is the algorithmic
 bytes of a step (each tensor read or written once, bias and gradients of the
-bias included, reduction partials excluded) divided by the step time.
+bias included, reduction partials excluded) divided by the step time. The
+timed steps replay the step captured once into a HIP graph (`--eager` times
+eager launches instead); per-op durations come from a separate eager loop
+with HIP events around every op, which also gives `ms_per_step_eager`.
 
 The ops beyond the step (the exact erf GeLU at the chain's MLP shape,
 residual add + LayerNorm at the chain's hidden size, and the MoE weighted
@@ -51,6 +54,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the step as eager launches instead of one HIP graph replay per step")
     return ap.parse_args()
 
 
@@ -380,8 +385,37 @@ def main():
     for s in range(args.steps):
         for op, (e0, e1) in zip(ops, events[s]):
             op.ms.append(e0.elapsed_time(e1))
-    ms_per_step = total_ms / args.steps
+    ms_per_step_eager = total_ms / args.steps
     step_bytes = sum(op.nbytes for op in ops)
+    launch = "eager"
+    ms_per_step = ms_per_step_eager
+    if not args.eager:
+        # the step captured once into a HIP graph (every entry point issues only
+        # kernel launches, so it is capturable) and replayed: the same kernels
+        # and bytes, without the per-launch host and queue gaps
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for op in ops:
+                op.fn()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            for op in ops:
+                op.fn()
+        for _ in range(max(1, args.warmup)):
+            graph.replay()
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        step0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        step1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        ms_per_step = step0.elapsed_time(step1) / args.steps
+        launch = "hip_graph"
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     # the ops beyond the step, after it, in a loop of their own
     for _ in range(args.warmup):
@@ -435,7 +469,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded numpy normal/uniform, cast to bf16; resident in HBM before timing)",
         "config": {"workload": WORKLOAD, "storage": "bf16 (fp32 residual in the 8192x4096 dropout-add)",
-                   "step_bytes": step_bytes, "frac_peak": round(value / PEAK_HBM_GBS, 4),
+                   "step_bytes": step_bytes, "frac_peak": round(value / PEAK_HBM_GBS, 4), "launch": launch,
+                   "ms_per_step_eager": round(ms_per_step_eager, 4),
                    "copy_ceiling_gbs": round(ceiling["gbs"], 1)},
         "per_op": per_op,
         "next_rows": next_rows,
