@@ -112,9 +112,8 @@ __global__ __launch_bounds__(kThreads) void bda_bwd_kernel(const char* g, char* 
   const TileIdx ti = tile_idx();
   const int cv = ti.strip * kStrip + lane;
   const bool active = cv < lanes;
-  float acc[N];
-#pragma unroll
-  for (int k = 0; k < N; ++k) acc[k] = 0.0f;
+  ColAcc<N> ca;
+  ca.init();
   if (active) {
     const size_t px = static_cast<size_t>(lanes) * XB, pr = static_cast<size_t>(lanes) * RB;
     const size_t cx = static_cast<size_t>(cv) * XB, cr = static_cast<size_t>(cv) * RB;
@@ -137,12 +136,15 @@ __global__ __launch_bounds__(kThreads) void bda_bwd_kernel(const char* g, char* 
 #pragma unroll
         for (int k = 0; k < N; ++k) {
           f[k] = keep[k] ? gv[u][k] * d.scale : 0.0f;
-          acc[k] += f[k];
+          ca.lo[k] += f[k];
         }
         st_elems<D, N>(dx + tt * px + cx, f);
       }
+      if constexpr (DBIAS) ca.tick(U);
     }
   }
+  float acc[N];
+  ca.total(acc);
   if constexpr (DBIAS)
     block_column_partials<N>(acc, wave, lane, active,
                              partials + static_cast<size_t>(ti.rg) * lanes * N + static_cast<size_t>(cv) * N);

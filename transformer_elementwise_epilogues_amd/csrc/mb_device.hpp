@@ -406,6 +406,40 @@ __device__ __forceinline__ void block_column_partials(const float* acc, int wave
   }
 }
 
+// Two-level fp32 column sums for a lane that visits many rows: the terms go
+// into `lo`, which is added into `hi` and cleared every kFlushRows rows, so
+// the rounding error of the lane's sum grows with kFlushRows + rows /
+// kFlushRows instead of with the number of rows (2^14 rows per lane at 2^24
+// tokens). The row count is the same in every lane of a wave.
+#ifndef MB_COL_FLUSH_ROWS
+#define MB_COL_FLUSH_ROWS 64
+#endif
+constexpr int kFlushRows = MB_COL_FLUSH_ROWS;
+template <int N> struct ColAcc {
+  float hi[N], lo[N];
+  int rows;
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int k = 0; k < N; ++k) hi[k] = lo[k] = 0.0f;
+    rows = 0;
+  }
+  __device__ __forceinline__ void tick(int r) {
+    rows += r;
+    if (rows >= kFlushRows) {
+#pragma unroll
+      for (int k = 0; k < N; ++k) {
+        hi[k] += lo[k];
+        lo[k] = 0.0f;
+      }
+      rows = 0;
+    }
+  }
+  __device__ __forceinline__ void total(float* out) const {
+#pragma unroll
+    for (int k = 0; k < N; ++k) out[k] = hi[k] + lo[k];
+  }
+};
+
 // Sum over the 64 lanes of a wave, in a fixed butterfly order (deterministic).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

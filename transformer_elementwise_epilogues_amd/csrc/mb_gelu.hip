@@ -101,9 +101,8 @@ __global__ __launch_bounds__(kThreads) void gelu_bwd_kernel(const char* g, const
   const TileIdx ti = tile_idx();
   const int cv = ti.strip * kStrip + lane;
   const bool active = cv < nvec;
-  float acc[V];
-#pragma unroll
-  for (int k = 0; k < V; ++k) acc[k] = 0.0f;
+  ColAcc<V> ca;
+  ca.init();
   if (active) {
     float b[V];
     load_bias<D>(bias, cv, b);
@@ -120,13 +119,17 @@ __global__ __launch_bounds__(kThreads) void gelu_bwd_kernel(const char* g, const
         yv[u] = ld_stream(y + o);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) st_stream(dgrad + (t + u * S) * pitch + col, gelu_grad_vec<D, KIND>(gv[u], yv[u], b, acc));
+      for (int u = 0; u < U; ++u) st_stream(dgrad + (t + u * S) * pitch + col, gelu_grad_vec<D, KIND>(gv[u], yv[u], b, ca.lo));
+      if constexpr (DBIAS) ca.tick(U);
     }
     for (; t < T; t += S) {
       const size_t o = t * pitch + col;
-      st_stream(dgrad + o, gelu_grad_vec<D, KIND>(ld_stream(g + o), ld_stream(y + o), b, acc));
+      st_stream(dgrad + o, gelu_grad_vec<D, KIND>(ld_stream(g + o), ld_stream(y + o), b, ca.lo));
+      if constexpr (DBIAS) ca.tick(1);
     }
   }
+  float acc[V];
+  ca.total(acc);
   if constexpr (DBIAS)
     block_column_partials<V>(acc, wave, lane, active,
                              partials + static_cast<size_t>(ti.rg) * nvec * V + static_cast<size_t>(cv) * V);

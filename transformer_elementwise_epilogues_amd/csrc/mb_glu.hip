@@ -25,16 +25,18 @@ namespace {
 constexpr int kUnrollFwd = MB_GLU_FWD_UNROLL;
 constexpr int kUnrollBwd = MB_GLU_BWD_UNROLL;
 
+// The bias halves of column vector cv (zero bits, i.e. +0, without a bias).
+// The raw vectors are selected before unpacking: selecting unpacked arrays
+// made the compiler keep two of their values in scratch memory.
 template <DT D>
 __device__ __forceinline__ void load_bias_pair(const char* bias, int cv, int nvec, float* ba, float* bb) {
-  constexpr int V = Vec<D>::N;
+  u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
   if (bias) {
-    unpack<D>(ld_keep(bias + static_cast<size_t>(cv) * 16), ba);
-    unpack<D>(ld_keep(bias + static_cast<size_t>(nvec + cv) * 16), bb);
-  } else {
-#pragma unroll
-    for (int k = 0; k < V; ++k) ba[k] = bb[k] = 0.0f;
+    va = ld_keep(bias + static_cast<size_t>(cv) * 16);
+    vb = ld_keep(bias + static_cast<size_t>(nvec + cv) * 16);
   }
+  unpack<D>(va, ba);
+  unpack<D>(vb, bb);
 }
 
 // Per-token weight of row t, or 1 for the unweighted op. The weighted and
@@ -156,9 +158,11 @@ __global__ __launch_bounds__(kThreads) void glu_bwd_kernel(const char* g, const 
   const TileIdx ti = tile_idx();
   const int cv = ti.strip * kStrip + lane;
   const bool active = cv < nvec;
-  float acc_a[V], acc_b[V];
-#pragma unroll
-  for (int k = 0; k < V; ++k) acc_a[k] = acc_b[k] = 0.0f;
+  ColAcc<V> ca_a, ca_b;
+  ca_a.init();
+  ca_b.init();
+  float* acc_a = ca_a.lo;
+  float* acc_b = ca_b.lo;
   float ba[V], bb[V];
   if (active) {
     load_bias_pair<D>(bias, cv, nvec, ba, bb);
@@ -202,6 +206,10 @@ __global__ __launch_bounds__(kThreads) void glu_bwd_kernel(const char* g, const 
         if (lane == 0) wpart[static_cast<size_t>(ti.strip) * T + tt] = rs;
       }
     }
+    if constexpr (DBIAS) {
+      ca_a.tick(U);
+      ca_b.tick(U);
+    }
   }
   for (; t < T; t += S) {
     u32x4 gv = {0, 0, 0, 0}, av = {0, 0, 0, 0}, bv = {0, 0, 0, 0};
@@ -220,13 +228,20 @@ __global__ __launch_bounds__(kThreads) void glu_bwd_kernel(const char* g, const 
       rs = wave_sum(active ? rs : 0.0f);
       if (lane == 0) wpart[static_cast<size_t>(ti.strip) * T + t] = rs;
     }
+    if constexpr (DBIAS) {
+      ca_a.tick(1);
+      ca_b.tick(1);
+    }
   }
   if constexpr (DBIAS) {
+    float sa_[V], sb_[V];
+    ca_a.total(sa_);
+    ca_b.total(sb_);
     __shared__ float red[kWaves][2 * V][64];
 #pragma unroll
     for (int k = 0; k < V; ++k) {
-      red[wave][k][lane] = acc_a[k];
-      red[wave][V + k][lane] = acc_b[k];
+      red[wave][k][lane] = sa_[k];
+      red[wave][V + k][lane] = sb_[k];
     }
     __syncthreads();
     if (wave == 0 && active) {

@@ -314,16 +314,27 @@ __global__ __launch_bounds__(TPR* RPB) void ln_bwd_kernel(const char* __restrict
   }
   // parameter-gradient sums: in registers, or (ACC_LDS) in this block's LDS,
   // [2][H] floats of which each thread touches only its own columns (so no
-  // barrier is needed), to leave the registers to the next row's prefetch
+  // barrier is needed), to leave the registers to the next row's prefetch.
+  // The register sums are added every kFlushRows rows into a second level in
+  // LDS ([RPB][2][H], again touched by the owning thread only), so their
+  // rounding error does not grow with the rows a block visits.
   constexpr bool ACC_LDS = acc_in_lds(TPR, NV);
   constexpr bool REG = DGB && !ACC_LDS;
   extern __shared__ float lds_acc[];
   float ag[REG ? NV : 1][E], ab[REG ? NV : 1][E];
+  float* hig = lds_acc + static_cast<size_t>(sub) * 2 * H;
+  float* hib = hig + H;
+  int nrows = 0;
   if constexpr (REG) {
 #pragma unroll
     for (int k = 0; k < NV; ++k)
 #pragma unroll
       for (int e = 0; e < E; ++e) ag[k][e] = ab[k][e] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+      if (ok[k])
+#pragma unroll
+        for (int e = 0; e < E; ++e) hig[vc[k] * E + e] = hib[vc[k] * E + e] = 0.0f;
   }
   if constexpr (DGB && ACC_LDS) {
 #pragma unroll
@@ -444,11 +455,38 @@ __global__ __launch_bounds__(TPR* RPB) void ln_bwd_kernel(const char* __restrict
       pk_store<D, E>(dx + xo + static_cast<size_t>(vc[k]) * XB, pk_pack<D, E>(gv));
       if (dres) pk_store<R, E>(dres + ro + static_cast<size_t>(vc[k]) * RB, pk_pack<R, E>(gv));
     }
+    if constexpr (REG) {
+      if (++nrows == kFlushRows) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+          if (ok[k]) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              hig[vc[k] * E + e] += ag[k][e];
+              hib[vc[k] * E + e] += ab[k][e];
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < E; ++e) ag[k][e] = ab[k][e] = 0.0f;
+        }
+        nrows = 0;
+      }
+    }
     if constexpr (!prefetch<TPR, NV>()) {
       if (row + step < T) fetch(row + step);
     }
   }
 
+  if constexpr (REG) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+      if (ok[k])
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          ag[k][e] += hig[vc[k] * E + e];
+          ab[k][e] += hib[vc[k] * E + e];
+        }
+  }
   if constexpr (DGB) {
     // one partial row per block: the RPB rows in flight combined in order
     float* rowg = pg + static_cast<size_t>(blockIdx.x) * H;
@@ -516,9 +554,9 @@ __global__ __launch_bounds__(kThreads) void ln_dgb_kernel(const char* __restrict
   const int cv = ti.strip * kStrip + lane;
   const bool active = cv < nvec;
   const size_t pitch = static_cast<size_t>(nvec) * 16, col = static_cast<size_t>(cv) * 16;
-  float ag[V], ab[V];
-#pragma unroll
-  for (int e = 0; e < V; ++e) ag[e] = ab[e] = 0.0f;
+  ColAcc<V> cg, cb;
+  cg.init();
+  cb.init();
   if (active) {
     for (int64_t t = static_cast<int64_t>(ti.rg) * kWaves + w; t < T; t += static_cast<int64_t>(kWaves) * ti.G) {
       float g[V], x[V];
@@ -527,11 +565,16 @@ __global__ __launch_bounds__(kThreads) void ln_dgb_kernel(const char* __restrict
       const float mu = mean[t], rs = rstd[t];
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        ag[e] = __builtin_fmaf(g[e], (x[e] - mu) * rs, ag[e]);
-        ab[e] += g[e];
+        cg.lo[e] = __builtin_fmaf(g[e], (x[e] - mu) * rs, cg.lo[e]);
+        cb.lo[e] += g[e];
       }
+      cg.tick(1);
+      cb.tick(1);
     }
   }
+  float ag[V], ab[V];
+  cg.total(ag);
+  cb.total(ab);
   __shared__ float red[kWaves][2 * V][64];
 #pragma unroll
   for (int e = 0; e < V; ++e) {
@@ -603,7 +646,7 @@ hipError_t bwd_shape(const LnArgs& a, const LnPlan& p, hipStream_t s) {
     hipLaunchKernelGGL((ln_bwd_kernel<D, R, sh.tpr, sh.nv, sh.rpb, false>), grid, block, 0, s, dy, h, gamma, a.cmean,
                        a.crstd, dh_in, dx, dres, nullptr, nullptr, a.T, H, a.gshift);
   } else if (a.pg) {
-    const size_t shm = acc_in_lds(sh.tpr, sh.nv) ? 2 * static_cast<size_t>(H) * sizeof(float) : 0;
+    const size_t shm = (acc_in_lds(sh.tpr, sh.nv) ? 1 : sh.rpb) * 2 * static_cast<size_t>(H) * sizeof(float);
     hipLaunchKernelGGL((ln_bwd_kernel<D, R, sh.tpr, sh.nv, sh.rpb, true>), grid, block, shm, s, dy, h, gamma,
                        a.cmean, a.crstd, dh_in, dx, dres, a.pg, a.pb, a.T, H, a.gshift);
   } else {
