@@ -23,8 +23,8 @@ residual add + LayerNorm at the chain's hidden size, and the MoE weighted
 squared ReLU) are timed after the step loop, the same way, and reported under
 "next_rows"; they are not part of `value`.
 
-Prints one JSON line (see the keys below). `--gpus N` with N > 1 exits: this
-build runs on a single GPU.
+Prints one JSON line (see the keys below). `--gpus N` with N > 1 exits: the
+benchmark runs on a single GPU.
 """
 from __future__ import annotations
 
@@ -347,7 +347,7 @@ def cpu_baseline(host, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
               "the fused epilogues are per-token and would shard by rows with a dbias all-reduce, "
               "which is not built here.", file=sys.stderr)
         sys.exit(2)
