@@ -19,7 +19,8 @@
  *           even. Bias and weight gradients are always fp32.
  * Shapes:   T >= 0; H > 0; H * sizeof(dt) must be a multiple of 16 bytes
  *           (H % 8 == 0 for bf16/fp16, H % 4 == 0 for fp32), because every
- *           lane moves whole 16-byte vectors.
+ *           lane moves whole 16-byte vectors (residual add + LayerNorm states
+ *           its own rule).
  * Alignment: tensor and bias pointers must be 16-byte aligned; fp32 gradient
  *           outputs 4-byte aligned; workspaces 16-byte aligned.
  * Aliasing: only the exact aliases listed per entry point are allowed; any
@@ -52,7 +53,7 @@ typedef enum {
   MB_ERR_DTYPE = 3,     /* unknown or unsupported dtype combination */
   MB_ERR_ALIGN = 4,     /* a pointer is not aligned as required */
   MB_ERR_ALIAS = 5,     /* two buffers overlap in a way the entry point forbids */
-  MB_ERR_PROB = 6,      /* dropout probability is NaN or outside [0, 1] */
+  MB_ERR_PROB = 6,      /* dropout probability NaN or outside [0, 1]; LayerNorm eps not finite or < 0 */
   MB_ERR_WORKSPACE = 7, /* workspace missing or smaller than the query returned */
   MB_ERR_HIP = 8        /* the HIP runtime reported an error for the launches */
 } mb_status_t;
@@ -73,8 +74,8 @@ int mb_abi_version(void);
 mb_status_t mb_bias_gelu_fwd(const void* y, const void* bias, void* out, int64_t tokens,
                              int64_t hidden, mb_dtype_t dt, hipStream_t s);
 
-/* Bytes of workspace mb_bias_gelu_bwd needs (0 when no bias gradient is asked for
- * is also accepted: pass with_dbias = 0). */
+/* Bytes of workspace mb_bias_gelu_bwd needs for the bias gradient (0 when
+ * with_dbias = 0 or tokens = 0). */
 size_t mb_bias_gelu_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias);
 
 /* Backward of bias + GeLU [fusions §4.2, §4.3]:
