@@ -152,12 +152,13 @@ hipError_t gelu_bwd_dispatch(const void* g, const void* y, const void* bias, voi
   auto yp = static_cast<const char*>(y);
   auto bp = static_cast<const char*>(bias);
   auto dp = static_cast<char*>(dgrad);
+  const size_t pad = KIND == kTanh ? MB_GELU_BWD_LDS_PAD : 0;
   if (partials)
-    hipLaunchKernelGGL((gelu_bwd_kernel<D, KIND, unroll_bwd<KIND>(), true>), grid, dim3(kThreads), 0, s, gp, yp, bp, dp, partials,
-                       t.T, t.nvec);
+    hipLaunchKernelGGL((gelu_bwd_kernel<D, KIND, unroll_bwd<KIND>(), true>), grid, dim3(kThreads), pad, s, gp, yp, bp, dp,
+                       partials, t.T, t.nvec);
   else
-    hipLaunchKernelGGL((gelu_bwd_kernel<D, KIND, unroll_bwd<KIND>(), false>), grid, dim3(kThreads), 0, s, gp, yp, bp, dp, partials,
-                       t.T, t.nvec);
+    hipLaunchKernelGGL((gelu_bwd_kernel<D, KIND, unroll_bwd<KIND>(), false>), grid, dim3(kThreads), pad, s, gp, yp, bp, dp,
+                       partials, t.T, t.nvec);
   return hipGetLastError();
 }
 
