@@ -37,6 +37,11 @@ __device__ __forceinline__ void load_bias(const char* bias, int cv, float* b) {
 
 enum Kind { kTanh = 0, kErf = 1 };
 
+#ifndef MB_GELU_BWD_PIPELINE
+#define MB_GELU_BWD_PIPELINE 1
+#endif
+constexpr bool kPipelineBwd = MB_GELU_BWD_PIPELINE;
+
 template <DT D, int KIND>
 __device__ __forceinline__ u32x4 gelu_vec(u32x4 yv, const float* b) {
   constexpr int V = Vec<D>::N;
@@ -110,17 +115,63 @@ __global__ __launch_bounds__(kThreads) void gelu_bwd_kernel(const char* g, const
     const int64_t S = static_cast<int64_t>(ti.G) * kWaves;
     const size_t col = static_cast<size_t>(cv) * 16;
     int64_t t = static_cast<int64_t>(ti.rg) * kWaves + wave;
-    for (; t + (U - 1) * S < T; t += U * S) {
-      u32x4 gv[U], yv[U];
+    if constexpr (kPipelineBwd) {
+      // software pipeline: the next U rows' loads are issued before this U
+      // rows' arithmetic, so a wave (often the only one on its SIMD) keeps
+      // memory busy while it computes. The steady-state branch always issues
+      // them, so the waits before the arithmetic cover only the current rows.
+      if (t + (U - 1) * S < T) {
+        u32x4 gv[U], yv[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const size_t o = (t + u * S) * pitch + col;
-        gv[u] = ld_stream(g + o);
-        yv[u] = ld_stream(y + o);
+        for (int u = 0; u < U; ++u) {
+          const size_t o = (t + u * S) * pitch + col;
+          gv[u] = ld_stream(g + o);
+          yv[u] = ld_stream(y + o);
+        }
+        for (;;) {
+          const int64_t tn = t + U * S;
+          if (tn + (U - 1) * S < T) {
+            u32x4 gn[U], yn[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+              const size_t o = (tn + u * S) * pitch + col;
+              gn[u] = ld_stream(g + o);
+              yn[u] = ld_stream(y + o);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+              st_stream(dgrad + (t + u * S) * pitch + col, gelu_grad_vec<D, KIND>(gv[u], yv[u], b, ca.lo));
+            if constexpr (DBIAS) ca.tick(U);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+              gv[u] = gn[u];
+              yv[u] = yn[u];
+            }
+            t = tn;
+          } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+              st_stream(dgrad + (t + u * S) * pitch + col, gelu_grad_vec<D, KIND>(gv[u], yv[u], b, ca.lo));
+            if constexpr (DBIAS) ca.tick(U);
+            t = tn;
+            break;
+          }
+        }
       }
+    } else {
+      for (; t + (U - 1) * S < T; t += U * S) {
+        u32x4 gv[U], yv[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) st_stream(dgrad + (t + u * S) * pitch + col, gelu_grad_vec<D, KIND>(gv[u], yv[u], b, ca.lo));
-      if constexpr (DBIAS) ca.tick(U);
+        for (int u = 0; u < U; ++u) {
+          const size_t o = (t + u * S) * pitch + col;
+          gv[u] = ld_stream(g + o);
+          yv[u] = ld_stream(y + o);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          st_stream(dgrad + (t + u * S) * pitch + col, gelu_grad_vec<D, KIND>(gv[u], yv[u], b, ca.lo));
+        if constexpr (DBIAS) ca.tick(U);
+      }
     }
     for (; t < T; t += S) {
       const size_t o = t * pitch + col;

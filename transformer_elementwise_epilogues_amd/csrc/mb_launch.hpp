@@ -34,7 +34,7 @@ struct Tiling {
 #define MB_GELU_BWD_BLOCKS 256
 #endif
 #ifndef MB_GELU_BWD_UNROLL
-#define MB_GELU_BWD_UNROLL 8
+#define MB_GELU_BWD_UNROLL 6
 #endif
 // The tanh GeLU backward runs one block per CU (256 blocks); an unused
 // 96 KiB of dynamic LDS per block makes a second block on one CU impossible,
