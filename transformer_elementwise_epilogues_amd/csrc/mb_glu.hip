@@ -24,6 +24,9 @@ namespace {
 
 constexpr int kUnrollFwd = MB_GLU_FWD_UNROLL;
 constexpr int kUnrollBwd = MB_GLU_BWD_UNROLL;
+#ifndef MB_GLU_BWD_PIPELINE
+#define MB_GLU_BWD_PIPELINE 1
+#endif
 
 // The bias halves of column vector cv (zero bits, i.e. +0, without a bias).
 // The raw vectors are selected before unpacking: selecting unpacked arrays
@@ -176,27 +179,29 @@ __global__ __launch_bounds__(kThreads) void glu_bwd_kernel(const char* g, const 
   const int64_t S = static_cast<int64_t>(ti.G) * kWaves;
   int64_t t = static_cast<int64_t>(ti.rg) * kWaves + wave;
   // Row loop is uniform across the wave (t depends on the wave only), so the
-  // weights-gradient butterfly below sees every lane.
-  for (; t + (U - 1) * S < T; t += U * S) {
-    u32x4 gv[U], av[U], bv[U];
-    float wt[U];
+  // weights-gradient butterfly below sees every lane. Lanes past the last
+  // column vector load a valid vector (clamped) and zero it, so that the
+  // loads need no branch and the next rows' loads can be issued before this
+  // rows' arithmetic (software pipeline).
+  const size_t colc = active ? col : 0;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  auto fetch = [&](int64_t t0, u32x4* gv, u32x4* av, u32x4* bv, float* wt) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t tt = t + u * S;
-      if (active) {
-        gv[u] = ld_stream(g + tt * po + col);
-        av[u] = ld_stream(in + tt * pi + col);
-        bv[u] = ld_stream(in + tt * pi + po + col);
-      } else {
-        gv[u] = av[u] = bv[u] = u32x4{0, 0, 0, 0};
-      }
+      const int64_t tt = t0 + u * S;
+      gv[u] = ld_stream(g + tt * po + colc);
+      av[u] = ld_stream(in + tt * pi + colc);
+      bv[u] = ld_stream(in + tt * pi + po + colc);
       wt[u] = load_weight<WEIGHTED, W>(w, tt);
     }
+  };
+  auto compute = [&](int64_t t0, u32x4* gv, u32x4* av, u32x4* bv, const float* wt) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t tt = t + u * S;
+      const int64_t tt = t0 + u * S;
       u32x4 dav, dbv;
-      float rs = glu_grad_vec<D, ACT, DW>(gv[u], av[u], bv[u], ba, bb, wt[u], acc_a, acc_b, &dav, &dbv);
+      float rs = glu_grad_vec<D, ACT, DW>(active ? gv[u] : zero, active ? av[u] : zero, active ? bv[u] : zero, ba, bb,
+                                          wt[u], acc_a, acc_b, &dav, &dbv);
       if (active) {
         st_stream(din + tt * pi + col, dav);
         st_stream(din + tt * pi + po + col, dbv);
@@ -209,6 +214,37 @@ __global__ __launch_bounds__(kThreads) void glu_bwd_kernel(const char* g, const 
     if constexpr (DBIAS) {
       ca_a.tick(U);
       ca_b.tick(U);
+    }
+  };
+  if (t + (U - 1) * S < T) {
+    u32x4 gv[U], av[U], bv[U];
+    float wt[U];
+    fetch(t, gv, av, bv, wt);
+    for (;;) {
+      const int64_t tn = t + U * S;
+      if (tn + (U - 1) * S < T) {
+        u32x4 gn[U], an[U], bn[U];
+        float wn[U];
+        if constexpr (MB_GLU_BWD_PIPELINE) {
+          fetch(tn, gn, an, bn, wn);
+          compute(t, gv, av, bv, wt);
+        } else {
+          compute(t, gv, av, bv, wt);
+          fetch(tn, gn, an, bn, wn);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          gv[u] = gn[u];
+          av[u] = an[u];
+          bv[u] = bn[u];
+          wt[u] = wn[u];
+        }
+        t = tn;
+      } else {
+        compute(t, gv, av, bv, wt);
+        t = tn;
+        break;
+      }
     }
   }
   for (; t < T; t += S) {
