@@ -19,6 +19,8 @@
 // contiguous 512 B / 1 KiB span. (With 8 elements per lane the fp32 tensor
 // would be stored 16 B per lane at a 32 B stride: half-line non-temporal
 // stores, measured at under 3 TB/s.)
+#include <type_traits>
+
 #include "mb_device.hpp"
 #include "mb_launch.hpp"
 
@@ -33,6 +35,28 @@ template <DT D, DT R> constexpr int unroll() { return (R == DT::F32 && D != DT::
 template <DT D, DT R>
 constexpr int epl() {
   return (R == DT::F32 && D != DT::F32) ? 4 : Vec<D>::N;
+}
+
+#ifndef MB_BDA_BWD_PIPELINE
+#define MB_BDA_BWD_PIPELINE 1
+#endif
+
+// Non-temporal load of a packed 8- or 16-byte piece, and its unpacking into
+// N elements of D (4 bf16/fp16 in 8 bytes, or a full 16-byte vector).
+template <typename Raw> __device__ __forceinline__ Raw ld_raw(const char* p) {
+  if constexpr (MB_NT_LOAD) return __builtin_nontemporal_load(reinterpret_cast<const Raw*>(p));
+  return *reinterpret_cast<const Raw*>(p);
+}
+__device__ __forceinline__ u32x4 widen(u32x4 v) { return v; }
+__device__ __forceinline__ u32x4 widen(u32x2 v) {
+  const unsigned a = v.x, b = v.y;
+  return u32x4{a, b, 0u, 0u};
+}
+template <DT D, int N, typename Raw> __device__ __forceinline__ void unpack_raw(Raw v, float* f) {
+  float t[Vec<D>::N];
+  unpack<D>(widen(v), t);
+#pragma unroll
+  for (int k = 0; k < N; ++k) f[k] = t[k];
 }
 
 // Keep flags of N consecutive elements starting at i0 (a multiple of 4).
@@ -120,27 +144,63 @@ __global__ __launch_bounds__(kThreads) void bda_bwd_kernel(const char* g, char* 
     const int64_t S = static_cast<int64_t>(ti.G) * kWaves;
     const uint64_t j0 = static_cast<uint64_t>(cv) * N;
     int64_t t = static_cast<int64_t>(ti.rg) * kWaves + wave;
-    for (; t < T; t += U * S) {
-      float gv[U][N];
+    // raw (packed) g of U rows; the next U rows are loaded before this U rows'
+    // mask and arithmetic (software pipeline), so memory stays busy while the
+    // Philox rounds run
+    using Raw = typename std::conditional<N * Vec<D>::BYTES == 16, u32x4, u32x2>::type;
+    auto fetch = [&](int64_t t0, Raw* gr) {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (t + u * S < T) ld_elems<D, N>(g + (t + u * S) * px + cx, gv[u]);
+      for (int u = 0; u < U; ++u) gr[u] = ld_raw<Raw>(g + (t0 + u * S) * px + cx);
+    };
+    auto row = [&](int64_t tt, Raw graw) {
+      float gv[N];
+      unpack_raw<D, N>(graw, gv);
+      if constexpr (DRES) st_elems<R, N>(dres + tt * pr + cr, gv);  // exact: g widened or copied
+      bool keep[N];
+      keep_n<N>(static_cast<uint64_t>(tt) * static_cast<uint64_t>(H) + j0, d, keep);
+      float f[N];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t tt = t + u * S;
-        if (tt >= T) break;
-        if constexpr (DRES) st_elems<R, N>(dres + tt * pr + cr, gv[u]);  // exact: g widened or copied
-        bool keep[N];
-        keep_n<N>(static_cast<uint64_t>(tt) * static_cast<uint64_t>(H) + j0, d, keep);
-        float f[N];
-#pragma unroll
-        for (int k = 0; k < N; ++k) {
-          f[k] = keep[k] ? gv[u][k] * d.scale : 0.0f;
-          ca.lo[k] += f[k];
-        }
-        st_elems<D, N>(dx + tt * px + cx, f);
+      for (int k = 0; k < N; ++k) {
+        f[k] = keep[k] ? gv[k] * d.scale : 0.0f;
+        ca.lo[k] += f[k];
       }
+      st_elems<D, N>(dx + tt * px + cx, f);
+    };
+    auto rows = [&](int64_t t0, const Raw* gr) {
+      row(t0, gr[0]);
+      if constexpr (U > 1) row(t0 + S, gr[1]);
+      if constexpr (U > 2) row(t0 + 2 * S, gr[2]);
+      if constexpr (U > 3) row(t0 + 3 * S, gr[3]);
       if constexpr (DBIAS) ca.tick(U);
+    };
+    static_assert(U >= 1 && U <= 4, "1 to 4 rows in flight");
+    if (t + (U - 1) * S < T) {
+      Raw gr[U];
+      fetch(t, gr);
+      for (;;) {
+        const int64_t tn = t + U * S;
+        if (tn + (U - 1) * S < T) {  // steady state: the next rows' loads always go first
+          Raw gn[U];
+          if constexpr (MB_BDA_BWD_PIPELINE) {
+            fetch(tn, gn);
+            rows(t, gr);
+          } else {
+            rows(t, gr);
+            fetch(tn, gn);
+          }
+#pragma unroll
+          for (int u = 0; u < U; ++u) gr[u] = gn[u];
+          t = tn;
+        } else {
+          rows(t, gr);
+          t = tn;
+          break;
+        }
+      }
+    }
+    for (; t < T; t += S) {
+      row(t, ld_raw<Raw>(g + t * px + cx));
+      if constexpr (DBIAS) ca.tick(1);
     }
   }
   float acc[N];
