@@ -219,29 +219,39 @@ __device__ __forceinline__ void keep4(uint64_t q, uint32_t o0, uint32_t o1, uint
   for (int k = 0; k < 4; ++k) keep[k] = c[k] >= theta32 && !drop_all;
 }
 
+// Scheduling fence after a software pipeline's prefetch (emits no code): the
+// compiler may not move instructions across it, so the next rows' loads all
+// issue before this rows' arithmetic instead of being spread through it.
+#ifndef MB_PREFETCH_FENCE
+#define MB_PREFETCH_FENCE 1
+#endif
+__device__ __forceinline__ void prefetch_fence() {
+  if constexpr (MB_PREFETCH_FENCE) __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---------------------------------------------------------------- activations
 
-// Logistic function sigma(t) for an argument given in base-2 units,
-// x = t * log2(e). With e = 2^-|x| and r = 1 / (1 + e):
-//   sigma(t)  = x >= 0 ? r     : e * r
-//   sigma(-t) = x >= 0 ? e * r : r
+// Logistic function sigma(t) from w = 32 - |x|, where x = t log2(e) is the
+// argument in base-2 units, and the sign of t. With e = 2^-|x| and
+// r = 1 / (1 + e):
+//   sigma(t) = t >= 0 ? r : e r,    sigma(t) (1 - sigma(t)) = e r^2
 // so neither 1 - sigma nor exp of a large positive number is ever formed.
-// `es` is e pre-scaled by 2^32 (valid down to |x| = 158), so that products
-// that end in the subnormal range keep their precision; callers multiply by
-// the deferred scale `sc` (1 or 2^-32) last.
+// The exponential is taken as 2^w = 2^32 e, which stays in the normal range
+// down to |x| = 158 (the hardware exp2 flushes subnormal results); e r is then
+// scaled down with a single rounding, so products that end in the subnormal
+// range carry an absolute error near 2^-150, far below any bf16 spacing.
 struct Logistic {
   float r;   // 1 / (1 + e)
-  float e;   // 2^-|x|
-  float es;  // 2^(32 - |x|)
-  bool pos;  // x >= 0
+  float er;  // e r
+  float s;   // sigma(t)
 };
 
-__device__ __forceinline__ Logistic logistic_b2(float x) {
+__device__ __forceinline__ Logistic logistic_w(float w, bool pos) {
   Logistic L;
-  L.es = __builtin_amdgcn_exp2f(32.0f - __builtin_fabsf(x));
-  L.e = L.es * 0x1p-32f;
-  L.r = __builtin_amdgcn_rcpf(1.0f + L.e);
-  L.pos = x >= 0.0f;
+  const float es = __builtin_amdgcn_exp2f(w);
+  L.r = __builtin_amdgcn_rcpf(__builtin_fmaf(es, 0x1p-32f, 1.0f));
+  L.er = (es * L.r) * 0x1p-32f;
+  L.s = pos ? L.r : L.er;
   return L;
 }
 
@@ -252,82 +262,111 @@ constexpr double kGeluK = 0.79788456;
 constexpr double kGeluC = 0.044715;
 constexpr double kGeluKD = 0.1070322243;
 // 0.5 (1 + tanh(u)) = sigma(2u): the logistic argument in base-2 units is
-// x = z * (A0 + A1 z^2) with A0 = 2 k log2(e), A1 = 2 k c log2(e).
+// x = z * (A0 + A1 z^2) with A0 = 2 k log2(e), A1 = 2 k c log2(e); the factor
+// A0 + A1 z^2 is positive, so |x| = |z| (A0 + A1 z^2) and x has the sign of z.
 constexpr float kGeluA0 = static_cast<float>(2.0 * kGeluK * kLog2e);
 constexpr float kGeluA1 = static_cast<float>(2.0 * kGeluK * kGeluC * kLog2e);
 constexpr float kSiluA = static_cast<float>(kLog2e);
-constexpr float kScaleDown = 0x1p-32f;
 
-// gelu_tanh(z) = 0.5 z (1 + tanh u) = z * sigma(2u)
-//   value = (z * r * (pos ? 1 : es)) * sc
-struct GeluF {
-  float v;   // scaled value
-  float sc;  // deferred scale
-};
-__device__ __forceinline__ GeluF gelu_tanh_fwd(float z) {
+__device__ __forceinline__ Logistic gelu_logistic(float z, float z2) {
+  return logistic_w(__builtin_fmaf(-__builtin_fabsf(z), __builtin_fmaf(z2, kGeluA1, kGeluA0), 32.0f), z >= 0.0f);
+}
+
+// gelu_tanh(z) = 0.5 z (1 + tanh u) = z * sigma(2u), forward only: z r, or in
+// the tail (z r) 2^32 e scaled down with one rounding. The same value as z s
+// of the logistic form, but in this order the forward kernels streamed 1-3 %
+// faster on MI355X. For z = +-inf or NaN the products give what the formula
+// gives (inf, NaN, NaN).
+__device__ __forceinline__ float gelu_tanh(float z) {
   const float x = z * __builtin_fmaf(z * z, kGeluA1, kGeluA0);
-  const Logistic L = logistic_b2(x);
-  const float zr = z * L.r;
-  GeluF o;
-  o.v = L.pos ? zr : zr * L.es;
-  o.sc = L.pos ? 1.0f : kScaleDown;
-  return o;
+  const float es = __builtin_amdgcn_exp2f(32.0f - __builtin_fabsf(x));
+  const float zr = z * __builtin_amdgcn_rcpf(__builtin_fmaf(es, 0x1p-32f, 1.0f));
+  return x >= 0.0f ? zr : (zr * es) * 0x1p-32f;
 }
 
 // gelu_tanh and its derivative. With s = sigma(2u), 1 - t^2 = 4 s (1 - s) and
 // s (1 - s) = e r^2, the derivative 0.5 (1+t) + 0.5 z (1-t^2)(k + k' z^2) is
-//   x >= 0:  r (1 + e q)        x < 0:  e r (1 + q)      with q = 2 z r (k + k' z^2).
-// Both branches carry the same deferred scale as the forward value. The
-// derivative is evaluated at z clamped to +-1e4 (where it is exactly 1 or 0 in
-// fp32) so that no 0 * inf arises; z - z restores NaN for NaN / inf inputs.
+//   d = s + q e r,    q = 2 z r (k + k' z^2)
+// evaluated at z clamped to +-1e4, where sigma is exactly 1 or 0 in fp32, so
+// that no 0 * inf arises; the value z s takes the unclamped z and is exact
+// there too. `nan` is z - z (+0, or NaN for a NaN or infinite z, where the
+// formula's 0 * inf gives NaN): callers add it to their product with d.
 struct GeluB {
-  float v;   // scaled gelu_tanh(z)
-  float d;   // scaled gelu_tanh'(z)
-  float sc;  // deferred scale of both
+  float v;    // gelu_tanh(z)
+  float d;    // gelu_tanh'(z), finite for every input
+  float nan;  // +0 or NaN
 };
 __device__ __forceinline__ GeluB gelu_tanh_fwd_bwd(float z) {
   const float zc = __builtin_amdgcn_fmed3f(z, -1e4f, 1e4f);
   const float z2 = zc * zc;
-  const float x = zc * __builtin_fmaf(z2, kGeluA1, kGeluA0);
-  const Logistic L = logistic_b2(x);
-  const float P = __builtin_fmaf(z2, static_cast<float>(kGeluKD), static_cast<float>(kGeluK));
-  const float zr = zc * L.r;
-  const float q = 2.0f * zr * P;
+  const Logistic L = gelu_logistic(zc, z2);
+  const float q = (zc * L.r) * __builtin_fmaf(z2, static_cast<float>(2.0 * kGeluKD), static_cast<float>(2.0 * kGeluK));
   GeluB o;
-  const float A = L.pos ? L.r : L.es * L.r;
-  const float B = L.pos ? __builtin_fmaf(L.e, q, 1.0f) : 1.0f + q;
-  const float nanfix = z - z;  // +0 for finite z, NaN for NaN or inf
-  o.d = A * B + nanfix;
-  o.v = (L.pos ? zr : zr * L.es) + nanfix;
-  o.sc = L.pos ? 1.0f : kScaleDown;
-  // the clamped z only changes the value for |z| > 1e4, where gelu(z) is z,
-  // or z * 0 (-0, and NaN for -inf as the formula gives) with the scale 2^-32
-  if (__builtin_fabsf(z) > 1e4f) o.v = z > 0.0f ? z : z * 0.0f;
+  o.v = z * L.s;
+  o.d = __builtin_fmaf(q, L.er, L.s);
+  o.nan = z - z;
   return o;
 }
 
-// silu(a) = a * sigma(a); silu'(a) = sigma(a) (1 + a sigma(-a)):
-//   a >= 0:  r (1 + a e r)      a < 0:  e r (1 + a r)      (deferred scale as above)
+// Value with a deferred scale: the product of `v` and `sc` (1 or a power of
+// two below 1), applied last by the caller so that results in the subnormal
+// range are rounded only once.
+struct ScaledF {
+  float v;
+  float sc;
+};
+
+// gelu_tanh'(z) in a longer form, as two branch products:
+//   x >= 0:  r (1 + e q)          x < 0:  (2^32 e) r (1 + q), scale 2^-32
+// with q as above; the same value as d of gelu_tanh_fwd_bwd up to rounding.
+// The GeLU backward kernel uses this form: it runs one wave per SIMD, and with
+// the short form it streamed up to 20 % slower on MI355X under some allocation
+// layouts of its three tensors (never faster under the layout the full step
+// uses), while the gated kernels, which keep more waves resident, gained 3-9 %
+// from the short form.
+__device__ __forceinline__ ScaledF gelu_tanh_grad_scaled(float z) {
+  const float zc = __builtin_amdgcn_fmed3f(z, -1e4f, 1e4f);
+  const float z2 = zc * zc;
+  const float x = zc * __builtin_fmaf(z2, kGeluA1, kGeluA0);
+  const float es = __builtin_amdgcn_exp2f(32.0f - __builtin_fabsf(x));
+  const float e = es * 0x1p-32f;
+  const float r = __builtin_amdgcn_rcpf(1.0f + e);
+  const bool pos = x >= 0.0f;
+  const float P = __builtin_fmaf(z2, static_cast<float>(kGeluKD), static_cast<float>(kGeluK));
+  const float zr = zc * r;
+  const float q = 2.0f * zr * P;
+  const float A = pos ? r : es * r;
+  const float B = pos ? __builtin_fmaf(e, q, 1.0f) : 1.0f + q;
+  const float nanfix = z - z;
+  ScaledF o;
+  o.v = A * B + nanfix;
+  o.sc = pos ? 1.0f : 0x1p-32f;
+  return o;
+}
+
+// silu(a) = a s with s = sigma(a); silu'(a) = s (1 + a (1 - s)) = s + (a r) (e r).
+// For a = +-inf or NaN both give what the formula gives.
 struct SiluB {
   float v;
   float d;
-  float sc;
 };
+__device__ __forceinline__ Logistic silu_logistic(float a) {
+  return logistic_w(__builtin_fmaf(-__builtin_fabsf(a), kSiluA, 32.0f), a >= 0.0f);
+}
 __device__ __forceinline__ SiluB silu_fwd_bwd(float a) {
-  const Logistic L = logistic_b2(a * kSiluA);
-  const float ar = a * L.r;
+  const Logistic L = silu_logistic(a);
   SiluB o;
-  o.v = L.pos ? ar : ar * L.es;
-  o.d = L.pos ? L.r * __builtin_fmaf(ar, L.e, 1.0f) : (L.es * L.r) * (1.0f + ar);
-  o.sc = L.pos ? 1.0f : kScaleDown;
+  o.v = a * L.s;
+  o.d = __builtin_fmaf(a * L.r, L.er, L.s);
   return o;
 }
 
-__device__ __forceinline__ float silu_fwd(float a, float* sc) {
-  const Logistic L = logistic_b2(a * kSiluA);
-  const float ar = a * L.r;
-  *sc = L.pos ? 1.0f : kScaleDown;
-  return L.pos ? ar : ar * L.es;
+// forward only, in the order of gelu_tanh above
+__device__ __forceinline__ float silu(float a) {
+  const float x = a * kSiluA;
+  const float es = __builtin_amdgcn_exp2f(32.0f - __builtin_fabsf(x));
+  const float ar = a * __builtin_amdgcn_rcpf(__builtin_fmaf(es, 0x1p-32f, 1.0f));
+  return x >= 0.0f ? ar : (ar * es) * 0x1p-32f;
 }
 
 // Exact GeLU, 0.5 z (1 + erf(k z)) = z Phi(z), with the constants printed with
@@ -341,7 +380,10 @@ __device__ __forceinline__ float silu_fwd(float a, float* sc) {
 //   z >= 0:  Phi = 1 - erfc(x) / 2        z < 0:  Phi = erfc(x) / 2
 // so the negative tail is a product, never a difference. Below z = -12 the
 // exponent is shifted by 64 (results are subnormal there) and the caller
-// multiplies by the deferred scale 2^-64 last, like the tanh form.
+// multiplies by the deferred scale 2^-64 last. (Unlike the logistic forms,
+// whose exponent is shifted by a constant, the shift here depends on z: a
+// constant shift of 64 would round the exponent's argument near 63, a relative
+// error up to 1.3e-6 in erfc near z = 0, too close to the fp32 tolerance.)
 constexpr float kErfK = 0.70710678f;
 constexpr float kErfPdf = 0.3989423f;
 constexpr float kErfcP[10] = {-1.26551223f, 1.00002368f, 0.37409196f, 0.09678418f, -0.18628806f,
@@ -361,26 +403,26 @@ __device__ __forceinline__ float half_erfc_abs(float z, float shift) {
   return t * __builtin_amdgcn_exp2f(__builtin_fmaf(a, static_cast<float>(kLog2e), shift - 1.0f));
 }
 
-__device__ __forceinline__ GeluF gelu_erf_fwd(float z) {
+// value and derivative below z = -12 carry the deferred scale 2^-64
+__device__ __forceinline__ ScaledF gelu_erf_fwd(float z) {
   const bool tail = z < kErfTail;
   const float h = half_erfc_abs(z, tail ? kErfShift : 0.0f);
-  GeluF o;
+  ScaledF o;
   o.v = z * (z < 0.0f ? h : 1.0f - h);  // not z - z h: inf * 0 at z = inf
   o.sc = tail ? kErfScaleDown : 1.0f;
   return o;
 }
 
 // gelu_erf'(z) = Phi(z) + z * 0.3989423 * exp(-z^2 / 2), both terms carrying the
-// same deferred scale (only `d` and `sc` are set)
-__device__ __forceinline__ GeluB gelu_erf_fwd_bwd(float z) {
+// same deferred scale
+__device__ __forceinline__ ScaledF gelu_erf_grad(float z) {
   const bool tail = z < kErfTail;
   const float shift = tail ? kErfShift : 0.0f;
   const float h = half_erfc_abs(z, shift);
   const float zphi = (z * kErfPdf) *
                      __builtin_amdgcn_exp2f(__builtin_fmaf(z * z, static_cast<float>(-0.5 * kLog2e), shift));
-  GeluB o;
-  o.v = 0.0f;
-  o.d = (z < 0.0f ? h : 1.0f - h) + zphi;
+  ScaledF o;
+  o.v = (z < 0.0f ? h : 1.0f - h) + zphi;
   o.sc = tail ? kErfScaleDown : 1.0f;
   return o;
 }

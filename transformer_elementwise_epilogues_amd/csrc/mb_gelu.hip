@@ -49,8 +49,12 @@ __device__ __forceinline__ u32x4 gelu_vec(u32x4 yv, const float* b) {
   unpack<D>(yv, f);
 #pragma unroll
   for (int k = 0; k < V; ++k) {
-    const GeluF r = KIND == kTanh ? gelu_tanh_fwd(f[k] + b[k]) : gelu_erf_fwd(f[k] + b[k]);
-    f[k] = r.v * r.sc;
+    if constexpr (KIND == kTanh) {
+      f[k] = gelu_tanh(f[k] + b[k]);
+    } else {
+      const ScaledF r = gelu_erf_fwd(f[k] + b[k]);
+      f[k] = r.v * r.sc;
+    }
   }
   return pack<D>(f);
 }
@@ -88,8 +92,8 @@ __device__ __forceinline__ u32x4 gelu_grad_vec(u32x4 gv, u32x4 yv, const float* 
   unpack<D>(yv, f);
 #pragma unroll
   for (int k = 0; k < V; ++k) {
-    const GeluB r = KIND == kTanh ? gelu_tanh_fwd_bwd(f[k] + b[k]) : gelu_erf_fwd_bwd(f[k] + b[k]);
-    const float d = (g[k] * r.d) * r.sc;
+    const ScaledF r = KIND == kTanh ? gelu_tanh_grad_scaled(f[k] + b[k]) : gelu_erf_grad(f[k] + b[k]);
+    const float d = (g[k] * r.v) * r.sc;
     acc[k] += d;
     f[k] = d;
   }
@@ -138,6 +142,7 @@ __global__ __launch_bounds__(kThreads) void gelu_bwd_kernel(const char* g, const
               gn[u] = ld_stream(g + o);
               yn[u] = ld_stream(y + o);
             }
+            prefetch_fence();
 #pragma unroll
             for (int u = 0; u < U; ++u)
               st_stream(dgrad + (t + u * S) * pitch + col, gelu_grad_vec<D, KIND>(gv[u], yv[u], b, ca.lo));

@@ -67,14 +67,10 @@ __device__ __forceinline__ u32x4 glu_vec(u32x4 av, u32x4 bv, const float* ba, co
   for (int k = 0; k < V; ++k) {
     const float x = a[k] + ba[k];
     const float y = b[k] + bb[k];
-    if constexpr (ACT == kSwiGLU) {
-      float sc;
-      const float sv = silu_fwd(x, &sc);
-      a[k] = ((sv * y) * w) * sc;
-    } else {
-      const GeluF r = gelu_tanh_fwd(x);
-      a[k] = (r.v * y) * r.sc;
-    }
+    if constexpr (ACT == kSwiGLU)
+      a[k] = (silu(x) * y) * w;
+    else
+      a[k] = gelu_tanh(x) * y;
   }
   return pack<D>(a);
 }
@@ -133,13 +129,13 @@ __device__ __forceinline__ float glu_grad_vec(u32x4 gv, u32x4 av, u32x4 bv, cons
     if constexpr (ACT == kSwiGLU) {
       const SiluB s = silu_fwd_bwd(x);
       const float gw = g[k] * w;
-      da = ((gw * y) * s.d) * s.sc;
-      db = (gw * s.v) * s.sc;
-      if constexpr (DW) rowsum += ((g[k] * s.v) * y) * s.sc;
+      da = (gw * y) * s.d;
+      db = gw * s.v;
+      if constexpr (DW) rowsum += (g[k] * s.v) * y;
     } else {
       const GeluB r = gelu_tanh_fwd_bwd(x);
-      da = ((g[k] * y) * r.d) * r.sc;
-      db = (g[k] * r.v) * r.sc;
+      da = __builtin_fmaf(g[k] * y, r.d, r.nan);
+      db = g[k] * r.v;
     }
     acc_a[k] += da;
     acc_b[k] += db;
@@ -227,6 +223,7 @@ __global__ __launch_bounds__(kThreads) void glu_bwd_kernel(const char* g, const 
         float wn[U];
         if constexpr (MB_GLU_BWD_PIPELINE) {
           fetch(tn, gn, an, bn, wn);
+          prefetch_fence();
           compute(t, gv, av, bv, wt);
         } else {
           compute(t, gv, av, bv, wt);
