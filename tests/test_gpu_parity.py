@@ -323,6 +323,51 @@ def test_glu_tail_inputs():
         assert_close(st(din), d, d64, mag, "bf16", f"{act} tail bwd")
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_glu_extreme_values(dt, weighted):
+    """Gate values at the infinities, NaN, huge finite values, the SiLU tail
+    where sigma(a) is subnormal in fp32 (a < -87), the GeLU tail and the roots
+    of both derivatives, against up values from tiny to huge (1e20), in both
+    gated activations, forward and backward (NaN and inf follow the formulas).
+    The deepest SiLU gate is -109: below |a| log2(e) = 158 the kernels flush
+    the activation to zero, which is exact to tolerance only while the up
+    value and gradient stay below about 2^16. Up values stay finite in each
+    dtype (6e4 in fp16): an infinite one times an activation that is nonzero
+    in fp64 but below fp32's range (gelu(-20) is about -1e-261) is inf in the
+    fp64 oracle and 0 * inf = NaN in any fp32 evaluation. Weights are >= 1
+    here: the kernels form products in fp32, and a weight below 1 would bring
+    an intermediate that overflowed fp32 (silu(3e38) * 7) back into range in
+    the fp64 oracle (zero and small weights are in the regular tests)."""
+    gate = np.array([0.0, -0.0, 1e-30, -1e-30, -0.7525, -1.2785, -6.0, -10.3, -14.0, -20.0, -80.0, -87.0, -87.5,
+                     -90.0, -95.0, -100.0, -104.0, -109.0, 3.0, 20.0, 90.0, 1e4, -1e4, 2e4, -2e4, 1e20, -1e20,
+                     3e38, -3e38, np.inf, -np.inf, np.nan], np.float32)
+    up = np.array([1.0, -2.5, 1e-3, 7.0, 6e4 if dt == "f16" else 1e20, -1e-20, 0.0, 300.0], np.float32)
+    T, H = 8, 32
+    a = np.stack([np.roll(gate, 3 * r) for r in range(T)])
+    b = np.resize(up, (T, H))
+    x32 = np.concatenate([a, b], axis=1)
+    g32 = np.linspace(-2, 2, T * H, dtype=np.float32).reshape(T, H)
+    x = torch.from_numpy(x32).to(TD[dt])
+    g = torch.from_numpy(g32).to(TD[dt])
+    w = torch.tensor([1.0, 1.5, 2.0, 3.0, 1.25, 4.0, 1.0, 2.5], dtype=TD[dt]) if weighted else None
+    for act in ("swiglu", "geglu"):
+        if act == "geglu" and weighted:
+            continue
+        if act == "swiglu":
+            out = mb.mb_bias_swiglu_fwd(x.to(DEV), None, None if w is None else w.to(DEV))
+            din, _, _ = mb.mb_bias_swiglu_bwd(g.to(DEV), x.to(DEV), None, None if w is None else w.to(DEV),
+                                              dbias=False, dweights=False)
+        else:
+            out = mb.mb_bias_geglu_fwd(x.to(DEV))
+            din, _ = mb.mb_bias_geglu_bwd(g.to(DEV), x.to(DEV), dbias=False)
+        ws = None if w is None else st(w)
+        o, o64 = oracle.bias_glu_fwd(act, dt, st(x), None, ws, dt if weighted else None)
+        log(f"{act} extremes fwd {dt} w={weighted}", assert_close(st(out), o, o64, None, dt, f"{act} extremes fwd"))
+        d, d64, mag, _, _ = oracle.bias_glu_bwd(act, dt, st(g), st(x), None, ws, dt if weighted else None)
+        log(f"{act} extremes bwd {dt} w={weighted}", assert_close(st(din), d, d64, mag, dt, f"{act} extremes bwd"))
+
+
 def test_glu_empty_tokens():
     x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
     g = torch.empty((0, 32), dtype=torch.bfloat16, device=DEV)

@@ -231,27 +231,40 @@ __device__ __forceinline__ void prefetch_fence() {
 
 // ---------------------------------------------------------------- activations
 
-// Logistic function sigma(t) from w = 32 - |x|, where x = t log2(e) is the
-// argument in base-2 units, and the sign of t. With e = 2^-|x| and
-// r = 1 / (1 + e):
-//   sigma(t) = t >= 0 ? r : e r,    sigma(t) (1 - sigma(t)) = e r^2
-// so neither 1 - sigma nor exp of a large positive number is ever formed.
-// The exponential is taken as 2^w = 2^32 e, which stays in the normal range
-// down to |x| = 158 (the hardware exp2 flushes subnormal results); e r is then
-// scaled down with a single rounding, so products that end in the subnormal
-// range carry an absolute error near 2^-150, far below any bf16 spacing.
-struct Logistic {
-  float r;   // 1 / (1 + e)
-  float er;  // e r
-  float s;   // sigma(t)
+// Value with a deferred scale: the product of `v` and `sc` (1 or a power of
+// two below 1), applied by the caller to its final product, so that results
+// in the fp32 subnormal range are rounded only once however large the factors
+// they are multiplied by (the up half, the gradient, the router weight).
+struct ScaledF {
+  float v;
+  float sc;
 };
 
-__device__ __forceinline__ Logistic logistic_w(float w, bool pos) {
-  Logistic L;
+// The logistic function sigma(t) goes through e = 2^-|x|, x = t log2(e) the
+// argument in base-2 units, and r = 1 / (1 + e):
+//   sigma(t) = t >= 0 ? r : e r,    sigma(t) (1 - sigma(t)) = e r^2
+// so neither 1 - sigma nor exp of a large positive number is ever formed. The
+// hardware exp2 flushes subnormal results, so it is taken as 2^(32 - |x|) =
+// 2^32 e, which stays normal down to |x| = 158, and quantities that carry the
+// factor e for t < 0 are kept scaled by 2^32, with the deferred scale
+// sc = 2^-32 (1 for t >= 0). Below |x| = 158 they are flushed to zero; the
+// activation there is below 2^-158 |t|.
+struct Logistic {
+  float r;   // 1 / (1 + e)
+  float s;   // sigma(t) / sc
+  float er;  // e r / sc
+  float sc;  // 1 or 2^-32
+};
+
+// w = 32 - |x|
+__device__ __forceinline__ Logistic logistic_scaled(float w, bool pos) {
   const float es = __builtin_amdgcn_exp2f(w);
+  Logistic L;
   L.r = __builtin_amdgcn_rcpf(__builtin_fmaf(es, 0x1p-32f, 1.0f));
-  L.er = (es * L.r) * 0x1p-32f;
-  L.s = pos ? L.r : L.er;
+  const float esr = es * L.r;
+  L.s = pos ? L.r : esr;
+  L.er = pos ? esr * 0x1p-32f : esr;
+  L.sc = pos ? 1.0f : 0x1p-32f;
   return L;
 }
 
@@ -268,62 +281,67 @@ constexpr float kGeluA0 = static_cast<float>(2.0 * kGeluK * kLog2e);
 constexpr float kGeluA1 = static_cast<float>(2.0 * kGeluK * kGeluC * kLog2e);
 constexpr float kSiluA = static_cast<float>(kLog2e);
 
-__device__ __forceinline__ Logistic gelu_logistic(float z, float z2) {
-  return logistic_w(__builtin_fmaf(-__builtin_fabsf(z), __builtin_fmaf(z2, kGeluA1, kGeluA0), 32.0f), z >= 0.0f);
-}
-
-// gelu_tanh(z) = 0.5 z (1 + tanh u) = z * sigma(2u), forward only: z r, or in
-// the tail (z r) 2^32 e scaled down with one rounding. The same value as z s
-// of the logistic form, but in this order the forward kernels streamed 1-3 %
-// faster on MI355X. For z = +-inf or NaN the products give what the formula
-// gives (inf, NaN, NaN).
-__device__ __forceinline__ float gelu_tanh(float z) {
+// Forward only: gelu_tanh(z) = 0.5 z (1 + tanh u) = z sigma(2u) as z r, or
+// (z r 2^32 e) with the scale 2^-32 below zero. For z = +-inf or NaN the
+// products give what the formula gives (inf, NaN, NaN).
+__device__ __forceinline__ ScaledF gelu_tanh_scaled(float z) {
   const float x = z * __builtin_fmaf(z * z, kGeluA1, kGeluA0);
   const float es = __builtin_amdgcn_exp2f(32.0f - __builtin_fabsf(x));
   const float zr = z * __builtin_amdgcn_rcpf(__builtin_fmaf(es, 0x1p-32f, 1.0f));
-  return x >= 0.0f ? zr : (zr * es) * 0x1p-32f;
+  ScaledF o;
+  o.v = x >= 0.0f ? zr : zr * es;
+  o.sc = x >= 0.0f ? 1.0f : 0x1p-32f;
+  return o;
 }
 
-// gelu_tanh and its derivative. With s = sigma(2u), 1 - t^2 = 4 s (1 - s) and
-// s (1 - s) = e r^2, the derivative 0.5 (1+t) + 0.5 z (1-t^2)(k + k' z^2) is
+// Forward only, silu(a) = a sigma(a), in the same form.
+__device__ __forceinline__ ScaledF silu_scaled(float a) {
+  const float x = a * kSiluA;
+  const float es = __builtin_amdgcn_exp2f(32.0f - __builtin_fabsf(x));
+  const float ar = a * __builtin_amdgcn_rcpf(__builtin_fmaf(es, 0x1p-32f, 1.0f));
+  ScaledF o;
+  o.v = x >= 0.0f ? ar : ar * es;
+  o.sc = x >= 0.0f ? 1.0f : 0x1p-32f;
+  return o;
+}
+
+// gelu_tanh and its derivative (gated backward kernels). With s = sigma(2u),
+// 1 - t^2 = 4 s (1 - s) and s (1 - s) = e r^2, the derivative
+// 0.5 (1+t) + 0.5 z (1-t^2)(k + k' z^2) is
 //   d = s + q e r,    q = 2 z r (k + k' z^2)
 // evaluated at z clamped to +-1e4, where sigma is exactly 1 or 0 in fp32, so
 // that no 0 * inf arises; the value z s takes the unclamped z and is exact
-// there too. `nan` is z - z (+0, or NaN for a NaN or infinite z, where the
-// formula's 0 * inf gives NaN): callers add it to their product with d.
+// there too. v and d carry the deferred scale sc. `nan` is z - z (+0, or NaN
+// for a NaN or infinite z, where the formula's 0 * inf gives NaN): callers
+// add it to their scaled product with d.
 struct GeluB {
-  float v;    // gelu_tanh(z)
-  float d;    // gelu_tanh'(z), finite for every input
+  float v;    // gelu_tanh(z) / sc
+  float d;    // gelu_tanh'(z) / sc, finite for every input
   float nan;  // +0 or NaN
+  float sc;
 };
 __device__ __forceinline__ GeluB gelu_tanh_fwd_bwd(float z) {
   const float zc = __builtin_amdgcn_fmed3f(z, -1e4f, 1e4f);
   const float z2 = zc * zc;
-  const Logistic L = gelu_logistic(zc, z2);
+  const Logistic L = logistic_scaled(
+      __builtin_fmaf(-__builtin_fabsf(zc), __builtin_fmaf(z2, kGeluA1, kGeluA0), 32.0f), zc >= 0.0f);
   const float q = (zc * L.r) * __builtin_fmaf(z2, static_cast<float>(2.0 * kGeluKD), static_cast<float>(2.0 * kGeluK));
   GeluB o;
   o.v = z * L.s;
   o.d = __builtin_fmaf(q, L.er, L.s);
   o.nan = z - z;
+  o.sc = L.sc;
   return o;
 }
 
-// Value with a deferred scale: the product of `v` and `sc` (1 or a power of
-// two below 1), applied last by the caller so that results in the subnormal
-// range are rounded only once.
-struct ScaledF {
-  float v;
-  float sc;
-};
-
-// gelu_tanh'(z) in a longer form, as two branch products:
+// gelu_tanh'(z) in the longer form of two branch products:
 //   x >= 0:  r (1 + e q)          x < 0:  (2^32 e) r (1 + q), scale 2^-32
 // with q as above; the same value as d of gelu_tanh_fwd_bwd up to rounding.
 // The GeLU backward kernel uses this form: it runs one wave per SIMD, and with
 // the short form it streamed up to 20 % slower on MI355X under some allocation
 // layouts of its three tensors (never faster under the layout the full step
-// uses), while the gated kernels, which keep more waves resident, gained 3-9 %
-// from the short form.
+// uses), while the gated kernels, which keep more waves resident, gained from
+// the short form.
 __device__ __forceinline__ ScaledF gelu_tanh_grad_scaled(float z) {
   const float zc = __builtin_amdgcn_fmed3f(z, -1e4f, 1e4f);
   const float z2 = zc * zc;
@@ -344,29 +362,21 @@ __device__ __forceinline__ ScaledF gelu_tanh_grad_scaled(float z) {
   return o;
 }
 
-// silu(a) = a s with s = sigma(a); silu'(a) = s (1 + a (1 - s)) = s + (a r) (e r).
-// For a = +-inf or NaN both give what the formula gives.
+// silu(a) = a s with s = sigma(a); silu'(a) = s (1 + a (1 - s)) = s + (a r) (e r),
+// both carrying the deferred scale sc. For a = +-inf or NaN both give what
+// the formula gives.
 struct SiluB {
-  float v;
-  float d;
+  float v;  // silu(a) / sc
+  float d;  // silu'(a) / sc
+  float sc;
 };
-__device__ __forceinline__ Logistic silu_logistic(float a) {
-  return logistic_w(__builtin_fmaf(-__builtin_fabsf(a), kSiluA, 32.0f), a >= 0.0f);
-}
 __device__ __forceinline__ SiluB silu_fwd_bwd(float a) {
-  const Logistic L = silu_logistic(a);
+  const Logistic L = logistic_scaled(__builtin_fmaf(-__builtin_fabsf(a), kSiluA, 32.0f), a >= 0.0f);
   SiluB o;
   o.v = a * L.s;
   o.d = __builtin_fmaf(a * L.r, L.er, L.s);
+  o.sc = L.sc;
   return o;
-}
-
-// forward only, in the order of gelu_tanh above
-__device__ __forceinline__ float silu(float a) {
-  const float x = a * kSiluA;
-  const float es = __builtin_amdgcn_exp2f(32.0f - __builtin_fabsf(x));
-  const float ar = a * __builtin_amdgcn_rcpf(__builtin_fmaf(es, 0x1p-32f, 1.0f));
-  return x >= 0.0f ? ar : (ar * es) * 0x1p-32f;
 }
 
 // Exact GeLU, 0.5 z (1 + erf(k z)) = z Phi(z), with the constants printed with

@@ -67,10 +67,13 @@ __device__ __forceinline__ u32x4 glu_vec(u32x4 av, u32x4 bv, const float* ba, co
   for (int k = 0; k < V; ++k) {
     const float x = a[k] + ba[k];
     const float y = b[k] + bb[k];
-    if constexpr (ACT == kSwiGLU)
-      a[k] = (silu(x) * y) * w;
-    else
-      a[k] = gelu_tanh(x) * y;
+    if constexpr (ACT == kSwiGLU) {
+      const ScaledF r = silu_scaled(x);
+      a[k] = ((r.v * y) * w) * r.sc;
+    } else {
+      const ScaledF r = gelu_tanh_scaled(x);
+      a[k] = (r.v * y) * r.sc;
+    }
   }
   return pack<D>(a);
 }
@@ -129,13 +132,13 @@ __device__ __forceinline__ float glu_grad_vec(u32x4 gv, u32x4 av, u32x4 bv, cons
     if constexpr (ACT == kSwiGLU) {
       const SiluB s = silu_fwd_bwd(x);
       const float gw = g[k] * w;
-      da = (gw * y) * s.d;
-      db = gw * s.v;
-      if constexpr (DW) rowsum += (g[k] * s.v) * y;
+      da = ((gw * y) * s.d) * s.sc;
+      db = (gw * s.v) * s.sc;
+      if constexpr (DW) rowsum += ((g[k] * s.v) * y) * s.sc;
     } else {
       const GeluB r = gelu_tanh_fwd_bwd(x);
-      da = __builtin_fmaf(g[k] * y, r.d, r.nan);
-      db = g[k] * r.v;
+      da = __builtin_fmaf((g[k] * y) * r.d, r.sc, r.nan);
+      db = (g[k] * r.v) * r.sc;
     }
     acc_a[k] += da;
     acc_b[k] += db;
