@@ -124,6 +124,16 @@ __global__ __launch_bounds__(kThreads) void bda_kernel(const char* x, const char
 // Backward: dx = keep ? g * s : 0 with the keep decisions regenerated from
 // (seed, offset, element index); dresidual = g in the residual's dtype; the
 // fp32 dx values are summed per column into one partial row per row group.
+// Row order of the backward: strided (a wave's U rows in flight are S apart,
+// so the grid sweeps one band of rows) or banded (the U rows come from U
+// equal bands of the tensor, so U bands are swept at once). Banded streamed
+// 3 % faster for the same-dtype backward at [16384, 8192] and 3 % slower for
+// the fp32-residual one at [8192, 4096] (MI355X, two allocation layouts).
+#ifndef MB_BDA_BWD_BANDED
+#define MB_BDA_BWD_BANDED 1
+#endif
+template <DT D, DT R> constexpr bool banded_bwd() { return MB_BDA_BWD_BANDED && !(R == DT::F32 && D != DT::F32); }
+
 template <DT D, DT R, int U, bool DBIAS, bool DRES>
 __global__ __launch_bounds__(kThreads) void bda_bwd_kernel(const char* g, char* dx, char* dres, float* partials,
                                                            int64_t T, int lanes, int64_t H, DropoutArgs d) {
@@ -174,33 +184,77 @@ __global__ __launch_bounds__(kThreads) void bda_bwd_kernel(const char* g, char* 
       if constexpr (DBIAS) ca.tick(U);
     };
     static_assert(U >= 1 && U <= 4, "1 to 4 rows in flight");
-    if (t + (U - 1) * S < T) {
-      Raw gr[U];
-      fetch(t, gr);
-      for (;;) {
-        const int64_t tn = t + U * S;
-        if (tn + (U - 1) * S < T) {  // steady state: the next rows' loads always go first
-          Raw gn[U];
-          if constexpr (MB_BDA_BWD_PIPELINE) {
-            fetch(tn, gn);
-            rows(t, gr);
-          } else {
-            rows(t, gr);
-            fetch(tn, gn);
-          }
+    if constexpr (banded_bwd<D, R>()) {
+      // the U rows in flight come from U bands of TB rows: slot u of base j
+      // is row u TB + j (the last band may be shorter)
+      const int64_t TB = (T + U - 1) / U;
+      auto fetch_b = [&](int64_t j, Raw* gr) {
 #pragma unroll
-          for (int u = 0; u < U; ++u) gr[u] = gn[u];
-          t = tn;
-        } else {
-          rows(t, gr);
-          t = tn;
-          break;
+        for (int u = 0; u < U; ++u) gr[u] = ld_raw<Raw>(g + (u * TB + j) * px + cx);
+      };
+      auto rows_b = [&](int64_t j, const Raw* gr) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) row(u * TB + j, gr[u]);
+        if constexpr (DBIAS) ca.tick(U);
+      };
+      int64_t j = t;
+      if (j < TB && (U - 1) * TB + j < T) {
+        Raw gr[U];
+        fetch_b(j, gr);
+        for (;;) {
+          const int64_t jn = j + S;
+          if (jn < TB && (U - 1) * TB + jn < T) {
+            Raw gn[U];
+            fetch_b(jn, gn);
+            rows_b(j, gr);
+#pragma unroll
+            for (int u = 0; u < U; ++u) gr[u] = gn[u];
+            j = jn;
+          } else {
+            rows_b(j, gr);
+            j = jn;
+            break;
+          }
         }
       }
-    }
-    for (; t < T; t += S) {
-      row(t, ld_raw<Raw>(g + t * px + cx));
-      if constexpr (DBIAS) ca.tick(1);
+      for (; j < TB; j += S) {
+        for (int u = 0; u < U; ++u) {
+          const int64_t tt = u * TB + j;
+          if (tt < T) {
+            row(tt, ld_raw<Raw>(g + tt * px + cx));
+            if constexpr (DBIAS) ca.tick(1);
+          }
+        }
+      }
+    } else {
+      if (t + (U - 1) * S < T) {
+        Raw gr[U];
+        fetch(t, gr);
+        for (;;) {
+          const int64_t tn = t + U * S;
+          if (tn + (U - 1) * S < T) {  // steady state: the next rows' loads always go first
+            Raw gn[U];
+            if constexpr (MB_BDA_BWD_PIPELINE) {
+              fetch(tn, gn);
+              rows(t, gr);
+            } else {
+              rows(t, gr);
+              fetch(tn, gn);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) gr[u] = gn[u];
+            t = tn;
+          } else {
+            rows(t, gr);
+            t = tn;
+            break;
+          }
+        }
+      }
+      for (; t < T; t += S) {
+        row(t, ld_raw<Raw>(g + t * px + cx));
+        if constexpr (DBIAS) ca.tick(1);
+      }
     }
   }
   float acc[N];
