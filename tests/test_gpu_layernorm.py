@@ -19,7 +19,7 @@ import torch
 import oracle
 import transformer_elementwise_epilogues_amd as mb
 from transformer_elementwise_epilogues_amd import synthetic
-from tolerances import assert_close_bounded, assert_reduction_close, to_storage as st
+from tolerances import assert_close_bounded, assert_reduction_close, to_storage as st, values as values_of
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -178,6 +178,57 @@ def test_ln_edge_cases():
     dx0, _, dg0, db0 = mb.mb_add_layer_norm_bwd(e, e, ge, m0, s0)
     torch.cuda.synchronize()
     assert dx0.shape == (0, 64) and torch.count_nonzero(dg0).item() == 0 and torch.count_nonzero(db0).item() == 0
+
+
+@pytest.mark.parametrize("dt,rdt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")])
+def test_ln_non_finite_and_extreme_magnitude_rows(dt, rdt):
+    """Rows holding a NaN, a +inf or a -inf (the whole row is NaN, as in the
+    oracle: the mean is NaN or +-inf and the variance NaN), rows scaled to
+    1e15 and to 1e-30 (the variance 1e30 and 1e-60, the latter far below eps),
+    a row at 3 with a spread of 1e-3, and an ordinary row. The finite rows also go through the backward. Rows
+    stay below 1e19: beyond it (x - mean)^2 overflows fp32 while the oracle's
+    fp64 variance stays finite."""
+    T, H = 7, 1024
+    x, r, g, b = inputs(dt, rdt, T, H, 61)
+    xf, rf = x.float(), r.float()
+    xf[1, 17], xf[2, 300], xf[3, 1023] = float("nan"), float("inf"), float("-inf")
+    xf[4] *= 1e15
+    rf[4] *= 1e15
+    xf[5] *= 1e-30
+    rf[5] *= 1e-30
+    xf[6] = 3.0 + xf[6] * 1e-3  # a mean far from zero against the spread:
+    rf[6] *= 1e-3  # the two-pass variance keeps it
+    x, r = xf.to(TD[dt]), rf.to(TD[rdt])
+    y, h, mean, rstd = mb.mb_add_layer_norm_fwd(x.to(DEV), r.to(DEV), g.to(DEV), b.to(DEV), eps=1e-5)
+    oh, oy, oy64, omag, omean, orstd = oracle.add_layer_norm_fwd(dt, st(x), st(r), rdt, st(g), st(b), 1e-5, False)
+    ky, kh = y.cpu().float().numpy(), h.cpu().float().numpy()
+    bad = [1, 2, 3]
+    for i in bad:
+        assert np.isnan(ky[i]).all() and np.isnan(oy64[i]).all(), f"row {i}: y not all NaN"
+        assert np.isnan(rstd[i].item()) and np.isnan(orstd[i]), f"row {i}: rstd"
+        km, om = mean[i].item(), omean[i]
+        assert (np.isnan(km) and np.isnan(om)) or km == om, f"row {i}: mean {km} vs {om}"
+    hv = st(h)
+    same = (hv == oh) | (np.isnan(kh) & np.isnan(values_of(oh, dt)))
+    assert same.all(), "h differs from the oracle's"
+    good = [0, 4, 5, 6]
+    sel = np.array(good)
+    s1 = assert_close_bounded(st(y)[sel], oy[sel], oy64[sel], (K * U * omag)[sel], dt, "extreme rows y")
+    mean_abs = h.double().abs().mean(1).cpu().numpy()[sel]
+    em = np.abs(mean.cpu().double().numpy()[sel] - omean[sel])
+    assert np.all(em <= K * U * mean_abs + 1e-300), "extreme rows mean"
+    er = np.abs(rstd.cpu().double().numpy()[sel] - orstd[sel]) / orstd[sel]
+    assert np.all(er <= K * U), f"extreme rows rstd: worst relative {float(er.max())}"
+    say(f"extreme rows {dt}/{rdt} fwd: {s1}")
+    hg, mg, rg_ = h[sel].contiguous(), mean[sel].contiguous(), rstd[sel].contiguous()
+    dy = synthetic.draw(62, (len(good), H), "normal", 1.0, dt).to(DEV)
+    dx, _, dgam, dbet = mb.mb_add_layer_norm_bwd(dy, hg, g.to(DEV), mg, rg_, residual_dtype=TD[rdt])
+    odx, odx64, omag2, _, odg, odb = oracle.add_layer_norm_bwd(dt, st(dy), oh[sel], st(g), 1e-5, False, res_dt=rdt,
+                                                               want_dres=False)
+    s2 = assert_close_bounded(st(dx), odx, odx64, K * U * omag2, dt, "extreme rows dx")
+    assert_reduction_close(dgam.cpu().numpy(), odg, "extreme rows dgamma")
+    assert_reduction_close(dbet.cpu().numpy(), odb, "extreme rows dbeta")
+    say(f"extreme rows {dt}/{rdt} bwd: {s2}")
 
 
 def test_ln_errors_on_device_tensors():
