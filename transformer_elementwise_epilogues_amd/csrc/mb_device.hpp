@@ -398,41 +398,48 @@ __device__ __forceinline__ SiluB silu_fwd_bwd(float a) {
 // Megatron-LM's fusions: k = 0.70710678 (1/sqrt 2) and 0.3989423 (1/sqrt(2 pi)).
 // 1 + erf(k z) = erfc(-k z), and for x = k |z| >= 0 the complementary error
 // function is evaluated branch-free as
-//   erfc(x) = t exp(-x^2 + P(t)),   t = 1 / (1 + x / 2),
-// with the degree-9 Chebyshev-fitted P of the erfcc routine in Numerical
-// Recipes (Press, Teukolsky, Vetterling, Flannery, 2nd ed., section 6.2),
-// whose fractional error is below 1.2e-7 for every x >= 0. Then
-//   z >= 0:  Phi = 1 - erfc(x) / 2        z < 0:  Phi = erfc(x) / 2
+//   0.5 erfc(x) = t Q(t) exp(-z^2 / 2),   t = 1 / (1 + x / 2),
+// with Q a degree-8 polynomial fitted for relative error (fit_erfc.py beside
+// this file: least squares on t in [1/8, 1], i.e. x <= 14; the fp32 Horner
+// evaluation is within 1.9e-7 relative of 0.5 erfc(x) exp(z^2/2) / t, and the
+// small difference between k^2 and 1/2 is part of the fitted function). The
+// factor exp(-z^2/2) is the Gaussian of the derivative too, so the backward
+// needs one exponential. Then
+//   z >= 0:  Phi = 1 - 0.5 erfc(x)        z < 0:  Phi = 0.5 erfc(x)
 // so the negative tail is a product, never a difference. Below z = -12 the
 // exponent is shifted by 64 (results are subnormal there) and the caller
 // multiplies by the deferred scale 2^-64 last. (Unlike the logistic forms,
 // whose exponent is shifted by a constant, the shift here depends on z: a
 // constant shift of 64 would round the exponent's argument near 63, a relative
-// error up to 1.3e-6 in erfc near z = 0, too close to the fp32 tolerance.)
+// error up to 1.3e-6 near z = 0, too close to the fp32 tolerance.)
 constexpr float kErfK = 0.70710678f;
 constexpr float kErfPdf = 0.3989423f;
-constexpr float kErfcP[10] = {-1.26551223f, 1.00002368f, 0.37409196f, 0.09678418f, -0.18628806f,
-                              0.27886807f,  -1.13520398f, 1.48851587f, -0.82215223f, 0.17087277f};
+constexpr float kErfQ[9] = {1.410423517e-01f, 1.412065774e-01f, 1.213941872e-01f, 1.020300612e-01f, -1.505985670e-02f,
+                            1.417247653e-01f, -2.460705340e-01f, 1.435308009e-01f, -2.979838476e-02f};
 constexpr float kErfTail = -12.0f;
 constexpr float kErfShift = 64.0f;
 constexpr float kErfScaleDown = 0x1p-64f;
 
-// 0.5 erfc(k |z|) times 2^shift; the 1/2 is the -1 in the exponent; k is
-// kErfK, passed in so that the forward can hold it in a VGPR
-__device__ __forceinline__ float half_erfc_abs(float z, float shift, float k) {
+// t Q(t) for x = k |z|; k is kErfK, passed in so that the forward can hold it
+// in a VGPR
+__device__ __forceinline__ float erf_tq(float z, float k) {
   const float x = __builtin_fabsf(z) * k;
   const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, x, 1.0f));
-  float p = kErfcP[9];
+  float q = kErfQ[8];
 #pragma unroll
-  for (int k = 8; k >= 0; --k) p = __builtin_fmaf(p, t, kErfcP[k]);
-  const float a = __builtin_fmaf(-x, x, p);  // -x^2 + P(t), rounded once
-  return t * __builtin_amdgcn_exp2f(__builtin_fmaf(a, static_cast<float>(kLog2e), shift - 1.0f));
+  for (int j = 7; j >= 0; --j) q = __builtin_fmaf(q, t, kErfQ[j]);
+  return t * q;
+}
+
+// exp(-z^2 / 2) times 2^shift
+__device__ __forceinline__ float gauss_scaled(float z, float shift) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(z * z, static_cast<float>(-0.5 * kLog2e), shift));
 }
 
 // value and derivative below z = -12 carry the deferred scale 2^-64
 __device__ __forceinline__ ScaledF gelu_erf_fwd(float z) {
   const bool tail = z < kErfTail;
-  const float h = half_erfc_abs(z, tail ? kErfShift : 0.0f, vconst(kErfK));
+  const float h = erf_tq(z, vconst(kErfK)) * gauss_scaled(z, tail ? kErfShift : 0.0f);
   ScaledF o;
   o.v = z * (z < 0.0f ? h : 1.0f - h);  // not z - z h: inf * 0 at z = inf
   o.sc = tail ? kErfScaleDown : 1.0f;
@@ -443,12 +450,10 @@ __device__ __forceinline__ ScaledF gelu_erf_fwd(float z) {
 // same deferred scale
 __device__ __forceinline__ ScaledF gelu_erf_grad(float z) {
   const bool tail = z < kErfTail;
-  const float shift = tail ? kErfShift : 0.0f;
-  const float h = half_erfc_abs(z, shift, kErfK);
-  const float zphi = (z * kErfPdf) *
-                     __builtin_amdgcn_exp2f(__builtin_fmaf(z * z, static_cast<float>(-0.5 * kLog2e), shift));
+  const float E = gauss_scaled(z, tail ? kErfShift : 0.0f);
+  const float h = erf_tq(z, kErfK) * E;
   ScaledF o;
-  o.v = (z < 0.0f ? h : 1.0f - h) + zphi;
+  o.v = (z < 0.0f ? h : 1.0f - h) + (z * kErfPdf) * E;
   o.sc = tail ? kErfScaleDown : 1.0f;
   return o;
 }
