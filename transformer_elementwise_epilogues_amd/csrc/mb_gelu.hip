@@ -37,6 +37,26 @@ __device__ __forceinline__ void load_bias(const char* bias, int cv, float* b) {
 
 enum Kind { kTanh = 0, kErf = 1 };
 
+// Cache policy of the streaming stores per kind (st_row: -1 global nt,
+// 2 buffer nt, 18 buffer nt sc1), by measurement: buffer nt sc1 stores made
+// the tanh forward 4-5 % and the exact backward 1.8 % faster; the exact
+// forward did not change and the tanh backward varied with the allocation
+// layout.
+#ifndef MB_GELU_FWD_ST
+#define MB_GELU_FWD_ST 18
+#endif
+#ifndef MB_GELU_ERF_FWD_ST
+#define MB_GELU_ERF_FWD_ST -1
+#endif
+#ifndef MB_GELU_BWD_ST
+#define MB_GELU_BWD_ST -1
+#endif
+#ifndef MB_GELU_ERF_BWD_ST
+#define MB_GELU_ERF_BWD_ST 18
+#endif
+template <int KIND> constexpr int st_fwd() { return KIND == kTanh ? MB_GELU_FWD_ST : MB_GELU_ERF_FWD_ST; }
+template <int KIND> constexpr int st_bwd() { return KIND == kTanh ? MB_GELU_BWD_ST : MB_GELU_ERF_BWD_ST; }
+
 #ifndef MB_GELU_BWD_PIPELINE
 #define MB_GELU_BWD_PIPELINE 1
 #endif
@@ -59,7 +79,7 @@ template <DT D, int KIND, int U>
 __global__ __launch_bounds__(kThreads) void gelu_fwd_kernel(const char* y, const char* bias, char* out,
                                                             int64_t T, int nvec) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_index<(st_fwd<KIND>() >= 0)>();
   const TileIdx ti = tile_idx();
   const int cv = ti.strip * kStrip + lane;
   if (cv >= nvec) return;
@@ -75,9 +95,11 @@ __global__ __launch_bounds__(kThreads) void gelu_fwd_kernel(const char* y, const
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] = ld_stream(yp + (t + u * S) * pitch);
 #pragma unroll
-    for (int u = 0; u < U; ++u) st_stream(op + (t + u * S) * pitch, gelu_vec<D, KIND>(v[u], b));
+    for (int u = 0; u < U; ++u)
+      st_row<st_fwd<KIND>()>(op + (t + u * S) * pitch, out + (t + u * S) * pitch, static_cast<uint32_t>(cv) * 16, gelu_vec<D, KIND>(v[u], b));
   }
-  for (; t < T; t += S) st_stream(op + t * pitch, gelu_vec<D, KIND>(ld_stream(yp + t * pitch), b));
+  for (; t < T; t += S)
+    st_row<st_fwd<KIND>()>(op + t * pitch, out + t * pitch, static_cast<uint32_t>(cv) * 16, gelu_vec<D, KIND>(ld_stream(yp + t * pitch), b));
 }
 
 template <DT D, int KIND>
@@ -102,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void gelu_bwd_kernel(const char* g, const
                                                             int nvec) {
   constexpr int V = Vec<D>::N;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_index<(st_bwd<KIND>() >= 0)>();
   const TileIdx ti = tile_idx();
   const int cv = ti.strip * kStrip + lane;
   const bool active = cv < nvec;
@@ -141,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void gelu_bwd_kernel(const char* g, const
             prefetch_fence();
 #pragma unroll
             for (int u = 0; u < U; ++u)
-              st_stream(dgrad + (t + u * S) * pitch + col, gelu_grad_vec<D, KIND>(gv[u], yv[u], b, ca.lo));
+              st_row<st_bwd<KIND>()>(dgrad + (t + u * S) * pitch + col, dgrad + (t + u * S) * pitch, static_cast<uint32_t>(col), gelu_grad_vec<D, KIND>(gv[u], yv[u], b, ca.lo));
             if constexpr (DBIAS) ca.tick(U);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -152,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void gelu_bwd_kernel(const char* g, const
           } else {
 #pragma unroll
             for (int u = 0; u < U; ++u)
-              st_stream(dgrad + (t + u * S) * pitch + col, gelu_grad_vec<D, KIND>(gv[u], yv[u], b, ca.lo));
+              st_row<st_bwd<KIND>()>(dgrad + (t + u * S) * pitch + col, dgrad + (t + u * S) * pitch, static_cast<uint32_t>(col), gelu_grad_vec<D, KIND>(gv[u], yv[u], b, ca.lo));
             if constexpr (DBIAS) ca.tick(U);
             t = tn;
             break;
@@ -170,13 +192,13 @@ __global__ __launch_bounds__(kThreads) void gelu_bwd_kernel(const char* g, const
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
-          st_stream(dgrad + (t + u * S) * pitch + col, gelu_grad_vec<D, KIND>(gv[u], yv[u], b, ca.lo));
+          st_row<st_bwd<KIND>()>(dgrad + (t + u * S) * pitch + col, dgrad + (t + u * S) * pitch, static_cast<uint32_t>(col), gelu_grad_vec<D, KIND>(gv[u], yv[u], b, ca.lo));
         if constexpr (DBIAS) ca.tick(U);
       }
     }
     for (; t < T; t += S) {
       const size_t o = t * pitch + col;
-      st_stream(dgrad + o, gelu_grad_vec<D, KIND>(ld_stream(g + o), ld_stream(y + o), b, ca.lo));
+      st_row<st_bwd<KIND>()>(dgrad + o, dgrad + t * pitch, static_cast<uint32_t>(col), gelu_grad_vec<D, KIND>(ld_stream(g + o), ld_stream(y + o), b, ca.lo));
       if constexpr (DBIAS) ca.tick(1);
     }
   }

@@ -21,6 +21,13 @@ namespace mb {
 
 namespace {
 
+// Cache policy of the streaming stores (st_row: -1 global nt, 2 buffer nt,
+// 18 buffer nt sc1), by measurement: buffer nt sc1 stores made the forward
+// 1.9 % and the backward 0.5 % faster.
+#ifndef MB_SRELU_ST
+#define MB_SRELU_ST 18
+#endif
+
 constexpr int kUnrollFwd = MB_SRELU_FWD_UNROLL;
 constexpr int kUnrollBwd = MB_SRELU_BWD_UNROLL;
 
@@ -59,7 +66,7 @@ __device__ __forceinline__ u32x4 srelu_vec(u32x4 xv, float w) {
 template <DT D, bool WEIGHTED, DT W, int U>
 __global__ __launch_bounds__(kThreads) void srelu_fwd_kernel(const char* x, const char* w, char* out, int64_t T,
                                                              int nvec) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_index<(MB_SRELU_ST >= 0)>();
   const TileIdx ti = tile_idx();
   const int cv = ti.strip * kStrip + lane;
   if (cv >= nvec) return;
@@ -77,9 +84,10 @@ __global__ __launch_bounds__(kThreads) void srelu_fwd_kernel(const char* x, cons
       wt[u] = row_weight<WEIGHTED, W>(w, t + u * S);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) st_stream(op + (t + u * S) * pitch, srelu_vec<D>(v[u], wt[u]));
+    for (int u = 0; u < U; ++u) st_row<MB_SRELU_ST>(op + (t + u * S) * pitch, out + (t + u * S) * pitch, static_cast<uint32_t>(cv) * 16, srelu_vec<D>(v[u], wt[u]));
   }
-  for (; t < T; t += S) st_stream(op + t * pitch, srelu_vec<D>(ld_stream(xp + t * pitch), row_weight<WEIGHTED, W>(w, t)));
+  for (; t < T; t += S)
+    st_row<MB_SRELU_ST>(op + t * pitch, out + t * pitch, static_cast<uint32_t>(cv) * 16, srelu_vec<D>(ld_stream(xp + t * pitch), row_weight<WEIGHTED, W>(w, t)));
 }
 
 // dx of one vector; returns the lane's part of the row's weights gradient
@@ -103,7 +111,7 @@ __device__ __forceinline__ float srelu_grad_vec(u32x4 gv, u32x4 xv, float w, u32
 template <DT D, bool WEIGHTED, DT W, int U, bool DW>
 __global__ __launch_bounds__(kThreads) void srelu_bwd_kernel(const char* g, const char* x, const char* w, char* dx,
                                                              float* wpart, int64_t T, int nvec) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_index<(MB_SRELU_ST >= 0)>();
   const TileIdx ti = tile_idx();
   const int cv = ti.strip * kStrip + lane;
   const bool active = cv < nvec;
@@ -134,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void srelu_bwd_kernel(const char* g, cons
       const int64_t tt = t + u * S;
       u32x4 d;
       float rs = srelu_grad_vec<D, DW>(gv[u], xv[u], wt[u], &d);
-      if (active) st_stream(dx + tt * pitch + col, d);
+      if (active) st_row<MB_SRELU_ST>(dx + tt * pitch + col, dx + tt * pitch, static_cast<uint32_t>(col), d);
       if constexpr (DW) {
         rs = wave_sum(active ? rs : 0.0f);
         if (lane == 0) wpart[static_cast<size_t>(ti.strip) * T + tt] = rs;
@@ -149,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void srelu_bwd_kernel(const char* g, cons
     }
     u32x4 d;
     float rs = srelu_grad_vec<D, DW>(gv, xv, row_weight<WEIGHTED, W>(w, t), &d);
-    if (active) st_stream(dx + t * pitch + col, d);
+    if (active) st_row<MB_SRELU_ST>(dx + t * pitch + col, dx + t * pitch, static_cast<uint32_t>(col), d);
     if constexpr (DW) {
       rs = wave_sum(active ? rs : 0.0f);
       if (lane == 0) wpart[static_cast<size_t>(ti.strip) * T + t] = rs;
