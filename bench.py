@@ -168,7 +168,7 @@ def build_ops(dev):
                   bwd5, ["bda_bwd", "colsum"]))
     ops.append(Op("chain_gelu_bwd_bf16_16384x32768",
                   lambda: mb.mb_bias_gelu_bwd(gg, gy, gb, dgrad=dgr, dbias=dbg, ws=wsg),
-                  T * H * 6 + H * 2 + H * 4, ["gelu_bwd", "colsum"]))
+                  T * H * 6 + H * 2 + H * 4, ["gelu_bwd", "colsum_chunk", "colsum"]))
     ops.append(Op("chain_attn_bda_bwd_bf16_16384x8192",
                   lambda: mb.mb_bias_dropout_add_bwd(ag, p5, s_attn, off5, dx=adx, dresidual=False, dbias=adb, ws=wsb),
                   bwd5, ["bda_bwd", "colsum"]))

@@ -40,8 +40,8 @@ enum Kind { kTanh = 0, kErf = 1 };
 // Cache policy of the streaming stores per kind (st_row: -1 global nt,
 // 2 buffer nt, 18 buffer nt sc1), by measurement: buffer nt sc1 stores made
 // the tanh forward 4-5 % and the exact backward 1.8 % faster; the exact
-// forward did not change and the tanh backward varied with the allocation
-// layout.
+// forward did not change, and the tanh backward is as fast either way in its
+// many-block grid.
 #ifndef MB_GELU_FWD_ST
 #define MB_GELU_FWD_ST 18
 #endif
@@ -49,7 +49,7 @@ enum Kind { kTanh = 0, kErf = 1 };
 #define MB_GELU_ERF_FWD_ST -1
 #endif
 #ifndef MB_GELU_BWD_ST
-#define MB_GELU_BWD_ST -1
+#define MB_GELU_BWD_ST 18
 #endif
 #ifndef MB_GELU_ERF_BWD_ST
 #define MB_GELU_ERF_BWD_ST 18
@@ -226,12 +226,11 @@ hipError_t gelu_bwd_dispatch(const void* g, const void* y, const void* bias, voi
   auto yp = static_cast<const char*>(y);
   auto bp = static_cast<const char*>(bias);
   auto dp = static_cast<char*>(dgrad);
-  const size_t pad = KIND == kTanh ? MB_GELU_BWD_LDS_PAD : 0;
   if (partials)
-    hipLaunchKernelGGL((gelu_bwd_kernel<D, KIND, unroll_bwd<KIND>(), true>), grid, dim3(kThreads), pad, s, gp, yp, bp, dp,
+    hipLaunchKernelGGL((gelu_bwd_kernel<D, KIND, unroll_bwd<KIND>(), true>), grid, dim3(kThreads), 0, s, gp, yp, bp, dp,
                        partials, t.T, t.nvec);
   else
-    hipLaunchKernelGGL((gelu_bwd_kernel<D, KIND, unroll_bwd<KIND>(), false>), grid, dim3(kThreads), pad, s, gp, yp, bp, dp,
+    hipLaunchKernelGGL((gelu_bwd_kernel<D, KIND, unroll_bwd<KIND>(), false>), grid, dim3(kThreads), 0, s, gp, yp, bp, dp,
                        partials, t.T, t.nvec);
   return hipGetLastError();
 }

@@ -22,8 +22,11 @@ struct Tiling {
 // are rounded down so the grid never exceeds it by a partial wave of blocks)
 // and rows in flight per wave, measured on MI355X (bench-order sweeps). The
 // forward kernels without reductions stream best as many short-lived blocks
-// (one to four rows per wave); the backward kernels that keep bias-gradient
-// sums per lane do best with few resident blocks and more rows in flight.
+// (one to four rows per wave). Of the backward kernels that keep bias-gradient
+// sums per lane, the GeLU pair also runs many blocks (8 rows per wave, 4 in
+// flight): the dispatcher's balancing beat a persistent grid of one block per
+// CU by 3-4 % and removed its slow calls, although the partial rows grow to
+// 1/16 of dgrad's bytes. The others do best with few resident blocks.
 #ifndef MB_GELU_FWD_BLOCKS
 #define MB_GELU_FWD_BLOCKS 65536
 #endif
@@ -31,23 +34,16 @@ struct Tiling {
 #define MB_GELU_FWD_UNROLL 1
 #endif
 #ifndef MB_GELU_BWD_BLOCKS
-#define MB_GELU_BWD_BLOCKS 256
+#define MB_GELU_BWD_BLOCKS 32768
 #endif
 #ifndef MB_GELU_BWD_UNROLL
-#define MB_GELU_BWD_UNROLL 6
-#endif
-// The tanh GeLU backward runs one block per CU (256 blocks); an unused
-// 96 KiB of dynamic LDS per block makes a second block on one CU impossible,
-// so the dispatcher cannot leave a CU idle while another runs two: it removed
-// the slow outliers (worst call 4.2 -> 5.1 TB/s, mean +3 %).
-#ifndef MB_GELU_BWD_LDS_PAD
-#define MB_GELU_BWD_LDS_PAD 98304
+#define MB_GELU_BWD_UNROLL 4
 #endif
 #ifndef MB_GELU_ERF_BWD_BLOCKS
 #define MB_GELU_ERF_BWD_BLOCKS 32768
 #endif
 #ifndef MB_GELU_ERF_BWD_UNROLL
-#define MB_GELU_ERF_BWD_UNROLL 1
+#define MB_GELU_ERF_BWD_UNROLL 4
 #endif
 #ifndef MB_BDA_BLOCKS
 #define MB_BDA_BLOCKS 65536
