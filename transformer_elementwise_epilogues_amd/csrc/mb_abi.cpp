@@ -246,7 +246,8 @@ static mb_status_t bda_common(const void* x, const void* bias, const void* resid
   if (tokens == 0) return MB_OK;
   const int lanes = static_cast<int>(hidden / mb::bda_elems_per_lane(dt, residual_dt));
   const bool mixed = residual_dt == MB_F32 && dt != MB_F32;
-  const mb::Tiling t = mb::plan_tiling(tokens, lanes, mixed ? MB_BDA_MIXED_BLOCKS : MB_BDA_BLOCKS);
+  const mb::Tiling t =
+      mb::plan_tiling(tokens, lanes, !mixed ? MB_BDA_BLOCKS : train ? MB_BDA_MIXED_TRAIN_BLOCKS : MB_BDA_MIXED_BLOCKS);
   const mb::DropoutArgs d = train ? dropout_args(p, seed, offset) : mb::DropoutArgs{};
   if (hipError_t e = mb::launch_bda(dt, residual_dt, train, x, bias, residual, out, hidden, t, d, s))
     return hip_status(e);

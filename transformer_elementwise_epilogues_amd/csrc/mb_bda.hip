@@ -28,9 +28,11 @@ namespace mb {
 
 namespace {
 
-// rows in flight per wave: the fp32-residual layout (4 elements per lane) and
-// the same-dtype layout are tuned apart
-template <DT D, DT R> constexpr int unroll() { return (R == DT::F32 && D != DT::F32) ? MB_BDA_MIXED_UNROLL : MB_BDA_UNROLL; }
+// rows in flight per wave: the fp32-residual layout (4 elements per lane),
+// its training pass and the same-dtype layout are tuned apart
+template <DT D, DT R, bool TRAIN> constexpr int unroll() {
+  return (R == DT::F32 && D != DT::F32) ? (TRAIN ? MB_BDA_MIXED_TRAIN_UNROLL : MB_BDA_MIXED_UNROLL) : MB_BDA_UNROLL;
+}
 
 template <DT D, DT R>
 constexpr int epl() {
@@ -303,9 +305,9 @@ hipError_t bda_dispatch(bool train, const void* x, const void* bias, const void*
   auto rp = static_cast<const char*>(res);
   auto op = static_cast<char*>(out);
   if (train)
-    hipLaunchKernelGGL((bda_kernel<D, R, true, unroll<D, R>()>), grid, dim3(kThreads), 0, s, xp, bp, rp, op, t.T, t.nvec, H, d);
+    hipLaunchKernelGGL((bda_kernel<D, R, true, unroll<D, R, true>()>), grid, dim3(kThreads), 0, s, xp, bp, rp, op, t.T, t.nvec, H, d);
   else
-    hipLaunchKernelGGL((bda_kernel<D, R, false, unroll<D, R>()>), grid, dim3(kThreads), 0, s, xp, bp, rp, op, t.T, t.nvec, H, d);
+    hipLaunchKernelGGL((bda_kernel<D, R, false, unroll<D, R, false>()>), grid, dim3(kThreads), 0, s, xp, bp, rp, op, t.T, t.nvec, H, d);
   return hipGetLastError();
 }
 
