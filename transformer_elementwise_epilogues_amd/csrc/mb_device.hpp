@@ -299,8 +299,7 @@ __device__ __forceinline__ void prefetch_fence() {
 // loop-invariant constants of three-operand instructions in SGPRs. The asm
 // has no side effects, so the compiler hoists the copy out of loops but cannot
 // fold it back into an SGPR. Used only where it costs no occupancy (one VGPR
-// per constant) and measured faster: the tanh GeLU backward (+1 %) and the
-// exact GeLU forward (+4.6 %).
+// per constant) and measured faster: the exact GeLU forward (+4.6 %).
 __device__ __forceinline__ float vconst(float c) {
   float v;
   asm("v_mov_b32 %0, %1" : "=v"(v) : "s"(c));
@@ -381,8 +380,8 @@ __device__ __forceinline__ ScaledF silu_scaled(float a) {
   return o;
 }
 
-// gelu_tanh and its derivative (gated backward kernels). With s = sigma(2u),
-// 1 - t^2 = 4 s (1 - s) and s (1 - s) = e r^2, the derivative
+// gelu_tanh and its derivative (the GeLU and gated backward kernels). With
+// s = sigma(2u), 1 - t^2 = 4 s (1 - s) and s (1 - s) = e r^2, the derivative
 // 0.5 (1+t) + 0.5 z (1-t^2)(k + k' z^2) is
 //   d = s + q e r,    q = 2 z r (k + k' z^2)
 // evaluated at z clamped to +-1e4, where sigma is exactly 1 or 0 in fp32, so
@@ -407,34 +406,6 @@ __device__ __forceinline__ GeluB gelu_tanh_fwd_bwd(float z) {
   o.d = __builtin_fmaf(q, L.er, L.s);
   o.nan = z - z;
   o.sc = L.sc;
-  return o;
-}
-
-// gelu_tanh'(z) in the longer form of two branch products:
-//   x >= 0:  r (1 + e q)          x < 0:  (2^32 e) r (1 + q), scale 2^-32
-// with q as above; the same value as d of gelu_tanh_fwd_bwd up to rounding.
-// The GeLU backward kernel uses this form: it runs one wave per SIMD, and with
-// the short form it streamed up to 20 % slower on MI355X under some allocation
-// layouts of its three tensors (never faster under the layout the full step
-// uses), while the gated kernels, which keep more waves resident, gained from
-// the short form.
-__device__ __forceinline__ ScaledF gelu_tanh_grad_scaled(float z) {
-  const float zc = __builtin_amdgcn_fmed3f(z, vconst(-1e4f), vconst(1e4f));
-  const float z2 = zc * zc;
-  const float x = zc * __builtin_fmaf(z2, kGeluA1, vconst(kGeluA0));
-  const float es = __builtin_amdgcn_exp2f(vconst(32.0f) - __builtin_fabsf(x));
-  const float e = es * 0x1p-32f;
-  const float r = __builtin_amdgcn_rcpf(1.0f + e);
-  const bool pos = x >= 0.0f;
-  const float P = __builtin_fmaf(z2, static_cast<float>(kGeluKD), vconst(static_cast<float>(kGeluK)));
-  const float zr = zc * r;
-  const float q = 2.0f * zr * P;
-  const float A = pos ? r : es * r;
-  const float B = pos ? __builtin_fmaf(e, q, 1.0f) : 1.0f + q;
-  const float nanfix = z - z;
-  ScaledF o;
-  o.v = A * B + nanfix;
-  o.sc = pos ? 1.0f : 0x1p-32f;
   return o;
 }
 

@@ -110,8 +110,14 @@ __device__ __forceinline__ u32x4 gelu_grad_vec(u32x4 gv, u32x4 yv, const float* 
   unpack<D>(yv, f);
 #pragma unroll
   for (int k = 0; k < V; ++k) {
-    const ScaledF r = KIND == kTanh ? gelu_tanh_grad_scaled(f[k] + b[k]) : gelu_erf_grad(f[k] + b[k]);
-    const float d = (g[k] * r.v) * r.sc;
+    float d;
+    if constexpr (KIND == kTanh) {
+      const GeluB q = gelu_tanh_fwd_bwd(f[k] + b[k]);
+      d = __builtin_fmaf(g[k] * q.d, q.sc, q.nan);
+    } else {
+      const ScaledF r = gelu_erf_grad(f[k] + b[k]);
+      d = (g[k] * r.v) * r.sc;
+    }
     acc[k] += d;
     f[k] = d;
   }
