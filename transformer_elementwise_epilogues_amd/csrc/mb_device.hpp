@@ -188,6 +188,21 @@ template <int AUX> __device__ __forceinline__ void st_buf(char* row, uint32_t of
   __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, AUX);
 }
 
+// Streaming loads through a buffer descriptor on a wave-uniform row, with the
+// cache policy AUX (as st_buf), and ld_row: AUX < 0 loads at `at` with the
+// global non-temporal load (at == row + off).
+template <int AUX> __device__ __forceinline__ u32x4 ld_buf(const char* row, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(row), 0, 0x7fffffff, 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+}
+template <int AUX> __device__ __forceinline__ u32x4 ld_row(const char* at, const char* row, uint32_t off) {
+  if constexpr (AUX < 0)
+    return ld_stream(at);
+  else
+    return ld_buf<AUX>(row, off);
+}
+
 template <DT D, int N> __device__ __forceinline__ u32x2 pack4(const float* f) {
   static_assert(N == 4 && Vec<D>::BYTES == 2, "8-byte groups hold 4 bf16/fp16 values");
   const unsigned w0 = D == DT::BF16 ? pk_bf16(f[0], f[1]) : pk_f16(f[0], f[1]);
