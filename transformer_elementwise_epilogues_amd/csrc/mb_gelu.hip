@@ -1,5 +1,5 @@
-// mb_gelu.hip -- bias + GeLU (tanh approximation), forward and backward with
-// the fused bias-gradient column reduction.
+// mb_gelu.hip -- bias + GeLU (tanh approximation and the exact erf form),
+// forward and backward with the fused bias-gradient column reduction.
 //
 // Method: Megatron-LM's bias_gelu / bias_gelu_back as described by the
 // wmrh.cn article on megatron/core/fusions, section 4.2 (formulas and
@@ -21,7 +21,7 @@ namespace mb {
 namespace {
 
 constexpr int kUnrollFwd = MB_GELU_FWD_UNROLL;
-// the exact form is heavier on the ALU and prefers more waves (its own shape)
+// rows in flight per wave in the backward, per form (both 4 at present)
 template <int KIND> constexpr int unroll_bwd() { return KIND == 0 ? MB_GELU_BWD_UNROLL : MB_GELU_ERF_BWD_UNROLL; }
 
 template <DT D>
@@ -55,6 +55,7 @@ enum Kind { kTanh = 0, kErf = 1 };
 #define MB_GELU_ERF_BWD_ST 18
 #endif
 template <int KIND> constexpr int st_fwd() { return KIND == kTanh ? MB_GELU_FWD_ST : MB_GELU_ERF_FWD_ST; }
+template <int KIND> constexpr int st_bwd() { return KIND == kTanh ? MB_GELU_BWD_ST : MB_GELU_ERF_BWD_ST; }
 // Loads likewise (ld_row: -1 global nt, else a buffer load with that cache
 // policy): buffer loads made the tanh backward 1.3 % faster (any of nt, nt sc0,
 // nt sc1, nt sc0 sc1), changed nothing in the tanh forward and cost the exact
@@ -73,7 +74,6 @@ template <int KIND> constexpr int st_fwd() { return KIND == kTanh ? MB_GELU_FWD_
 #endif
 template <int KIND> constexpr int ld_fwd() { return KIND == kTanh ? MB_GELU_FWD_LD : MB_GELU_ERF_FWD_LD; }
 template <int KIND> constexpr int ld_bwd() { return KIND == kTanh ? MB_GELU_BWD_LD : MB_GELU_ERF_BWD_LD; }
-template <int KIND> constexpr int st_bwd() { return KIND == kTanh ? MB_GELU_BWD_ST : MB_GELU_ERF_BWD_ST; }
 
 #ifndef MB_GELU_BWD_PIPELINE
 #define MB_GELU_BWD_PIPELINE 1
