@@ -197,8 +197,7 @@ def build_ops(dev):
     extra.append(Op("add_ln_bwd_bf16_16384x8192",
                     lambda: mb.mb_add_layer_norm_bwd(ldy, lh, lg, lmean, lrstd, zc, dh_in=lup, dx=ldx, dgamma=ldg,
                                                      dbeta=ldb, ws=lws),
-                    T * H * 8 + H * 2 + T * 8 + H * 8, ["ln_bwd", "colsum_chunk", "colsum", "colsum_chunk",
-                                                        "colsum"]))
+                    T * H * 8 + H * 2 + T * 8 + H * 8, ["ln_bwd", "colsum_chunk", "colsum"]))
 
     # -- beyond the step: MoE weighted squared ReLU, bf16 [8192, 14336], fp32 weights
     w = WORKLOADS["wsrelu_bf16_8192x14336"]

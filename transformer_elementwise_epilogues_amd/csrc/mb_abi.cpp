@@ -420,10 +420,15 @@ static mb_status_t glu_bwd_common(int act, const void* g, const void* in, const 
   if (hipError_t e = mb::launch_glu_bwd(act, dt, g, in, bias, weights, weights ? weights_dt : dt, din, bp, wp, hidden,
                                         t, s))
     return hip_status(e);
-  if (dbias)
+  if (dbias && dweights) {
+    if (hipError_t e = mb::launch_colsum2(mb::ColSum{bp, t.G, 2 * hidden, dbias},
+                                          mb::ColSum{wp, t.strips, tokens, dweights}, s))
+      return hip_status(e);
+  } else if (dbias) {
     if (hipError_t e = reduce_columns(bp, t, 2 * hidden, dbias, s)) return hip_status(e);
-  if (dweights)
+  } else if (dweights) {
     if (hipError_t e = mb::launch_colsum(wp, t.strips, tokens, dweights, s)) return hip_status(e);
+  }
   return finish();
 }
 
@@ -631,14 +636,16 @@ mb_status_t mb_add_layer_norm_bwd(const void* dy, const void* h, const void* gam
     a.pb = reinterpret_cast<float*>(w + lay.pb);
   }
   if (hipError_t e = mb::launch_ln_bwd(a, plan, s)) return hip_status(e);
-  if (dgamma)
-    if (hipError_t e = mb::launch_colsum_tall(a.pg, plan.partial_rows, hidden, reinterpret_cast<float*>(w + lay.tg),
-                                              dgamma, s))
+  float* tg = reinterpret_cast<float*>(w + lay.tg);
+  float* tbeta = reinterpret_cast<float*>(w + lay.tb);
+  if (dgamma && dbeta) {
+    if (hipError_t e = mb::launch_colsum_tall2(a.pg, a.pb, plan.partial_rows, hidden, tg, tbeta, dgamma, dbeta, s))
       return hip_status(e);
-  if (dbeta)
-    if (hipError_t e = mb::launch_colsum_tall(a.pb, plan.partial_rows, hidden, reinterpret_cast<float*>(w + lay.tb),
-                                              dbeta, s))
-      return hip_status(e);
+  } else if (dgamma) {
+    if (hipError_t e = mb::launch_colsum_tall(a.pg, plan.partial_rows, hidden, tg, dgamma, s)) return hip_status(e);
+  } else if (dbeta) {
+    if (hipError_t e = mb::launch_colsum_tall(a.pb, plan.partial_rows, hidden, tbeta, dbeta, s)) return hip_status(e);
+  }
   return finish();
 }
 

@@ -130,9 +130,22 @@ struct Tiling {
 Tiling plan_tiling(int64_t T, int nvec, int target_blocks);
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+// One column sum: out[c] = sum over r < R of in[r * C + c], r ascending (fp32).
+struct ColSum {
+  const float* in;
+  int R;
+  int64_t C;
+  float* out;
+};
+// Two independent column sums (any shapes) in one launch.
+hipError_t launch_colsum2(const ColSum& a, const ColSum& b, hipStream_t s);
 // As launch_colsum for many partial rows: rows are first summed in ascending
 // chunks of 32 into tmp ([ceil(R / 32), C]), then the chunk sums in order.
 hipError_t launch_colsum_tall(const float* in, int R, int64_t C, float* tmp, float* out, hipStream_t s);
+// Two such sums of the same shape in the same launches (in0 -> out0 through
+// tmp0, in1 -> out1 through tmp1).
+hipError_t launch_colsum_tall2(const float* in0, const float* in1, int R, int64_t C, float* tmp0, float* tmp1,
+                               float* out0, float* out1, hipStream_t s);
 int64_t colsum_tall_tmp_floats(int R, int64_t C);
 // out[c] = sum over r < R of in[r * C + c], r ascending (fp32).
 hipError_t launch_colsum(const float* in, int R, int64_t C, float* out, hipStream_t s);

@@ -13,11 +13,16 @@ namespace mb {
 
 namespace {
 
-__global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ in, int R, int64_t C,
-                                                     float* __restrict__ out) {
+// Every kernel below sums one of two independent arrays, chosen by
+// blockIdx.z, so that two column sums of one op (dgamma and dbeta; the bias
+// and the weights gradients) share their launches; a single sum passes z = 1.
+__global__ __launch_bounds__(256) void colsum_kernel(ColSum a, ColSum b) {
+  const ColSum& k = blockIdx.z ? b : a;
   const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (c >= C) return;
-  const float* p = in + c;
+  if (c >= k.C) return;
+  const int64_t C = k.C;
+  const int R = k.R;
+  const float* __restrict__ p = k.in + c;
   float s = 0.0f;
   int r = 0;
   for (; r + 4 <= R; r += 4) {
@@ -28,16 +33,18 @@ __global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ i
     s = (((s + v0) + v1) + v2) + v3;
   }
   for (; r < R; ++r) s += p[static_cast<size_t>(r) * C];
-  out[c] = s;
+  k.out[c] = s;
 }
 
 // out[y, c] = sum of in[r, c] for r in [32 y, min(R, 32 y + 32)), ascending
-__global__ __launch_bounds__(256) void colsum_chunk_kernel(const float* __restrict__ in, int R, int64_t C,
-                                                           float* __restrict__ out) {
+__global__ __launch_bounds__(256) void colsum_chunk_kernel(ColSum a, ColSum b) {
+  const ColSum& k = blockIdx.z ? b : a;
   const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (c >= C) return;
-  const int r0 = static_cast<int>(blockIdx.y) * 32, r1 = r0 + 32 < R ? r0 + 32 : R;
-  const float* p = in + c;
+  const int r0 = static_cast<int>(blockIdx.y) * 32;
+  if (c >= k.C || r0 >= k.R) return;
+  const int64_t C = k.C;
+  const int r1 = r0 + 32 < k.R ? r0 + 32 : k.R;
+  const float* __restrict__ p = k.in + c;
   float s = 0.0f;
   int r = r0;
   for (; r + 4 <= r1; r += 4) {
@@ -48,7 +55,7 @@ __global__ __launch_bounds__(256) void colsum_chunk_kernel(const float* __restri
     s = (((s + v0) + v1) + v2) + v3;
   }
   for (; r < r1; ++r) s += p[static_cast<size_t>(r) * C];
-  out[static_cast<size_t>(blockIdx.y) * C + c] = s;
+  k.out[static_cast<size_t>(blockIdx.y) * C + c] = s;
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
@@ -71,22 +78,46 @@ Tiling plan_tiling(int64_t T, int nvec, int target_blocks) {
   return t;
 }
 
+static unsigned col_blocks(int64_t C) { return static_cast<unsigned>((C + 255) / 256); }
+
+hipError_t launch_colsum2(const ColSum& a, const ColSum& b, hipStream_t s) {
+  hipLaunchKernelGGL(colsum_kernel, dim3(std::max(col_blocks(a.C), col_blocks(b.C)), 1, 2), dim3(256), 0, s, a, b);
+  return hipGetLastError();
+}
+
 hipError_t launch_colsum(const float* in, int R, int64_t C, float* out, hipStream_t s) {
-  const int64_t blocks = (C + 255) / 256;
-  hipLaunchKernelGGL(colsum_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, in, R, C, out);
+  const ColSum a{in, R, C, out};
+  hipLaunchKernelGGL(colsum_kernel, dim3(col_blocks(C), 1, 1), dim3(256), 0, s, a, a);
   return hipGetLastError();
 }
 
 int64_t colsum_tall_tmp_floats(int R, int64_t C) { return R <= 32 ? 0 : static_cast<int64_t>((R + 31) / 32) * C; }
 
-hipError_t launch_colsum_tall(const float* in, int R, int64_t C, float* tmp, float* out, hipStream_t s) {
-  if (R <= 32) return launch_colsum(in, R, C, out, s);
-  const int chunks = (R + 31) / 32;
-  const int64_t blocks = (C + 255) / 256;
-  hipLaunchKernelGGL(colsum_chunk_kernel, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(chunks)),
-                     dim3(256), 0, s, in, R, C, tmp);
+// a, b: the partial rows; ta, tb: the same with their chunk-sum buffers as `out`
+static hipError_t colsum_tall_pair(const ColSum& a, const ColSum& b, float* tmp_a, float* tmp_b, unsigned arrays,
+                                   hipStream_t s) {
+  if (arrays == 1 && a.R <= 32) return launch_colsum(a.in, a.R, a.C, a.out, s);
+  if (arrays == 2 && a.R <= 32 && b.R <= 32) return launch_colsum2(a, b, s);
+  const ColSum ca{a.in, a.R, a.C, tmp_a}, cb{b.in, b.R, b.C, tmp_b};
+  const int chunks_a = (a.R + 31) / 32, chunks_b = (b.R + 31) / 32;
+  hipLaunchKernelGGL(colsum_chunk_kernel,
+                     dim3(std::max(col_blocks(a.C), col_blocks(b.C)), static_cast<unsigned>(std::max(chunks_a, chunks_b)),
+                          arrays),
+                     dim3(256), 0, s, ca, cb);
   if (hipError_t e = hipGetLastError()) return e;
-  return launch_colsum(tmp, chunks, C, out, s);
+  const ColSum fa{tmp_a, chunks_a, a.C, a.out}, fb{tmp_b, chunks_b, b.C, b.out};
+  if (arrays == 1) return launch_colsum(fa.in, fa.R, fa.C, fa.out, s);
+  return launch_colsum2(fa, fb, s);
+}
+
+hipError_t launch_colsum_tall(const float* in, int R, int64_t C, float* tmp, float* out, hipStream_t s) {
+  const ColSum a{in, R, C, out};
+  return colsum_tall_pair(a, a, tmp, tmp, 1, s);
+}
+
+hipError_t launch_colsum_tall2(const float* in0, const float* in1, int R, int64_t C, float* tmp0, float* tmp1,
+                               float* out0, float* out1, hipStream_t s) {
+  return colsum_tall_pair(ColSum{in0, R, C, out0}, ColSum{in1, R, C, out1}, tmp0, tmp1, 2, s);
 }
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
