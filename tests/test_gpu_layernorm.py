@@ -243,3 +243,23 @@ def test_ln_errors_on_device_tensors():
     y, h, m, s = mb.mb_add_layer_norm_fwd(x, x, g)
     with pytest.raises(mb.MBError):
         mb.mb_add_layer_norm_bwd(x, h, g, m, s, ws=torch.zeros(4, dtype=torch.uint8, device=DEV))
+
+
+@pytest.mark.parametrize("T,H", [(3000, 512), (40, 2048)])
+def test_ln_bwd_each_param_gradient_alone_matches_both(T, H):
+    """dgamma and dbeta share their column-sum launches when both are asked
+    for; each alone comes out bit for bit the same (3000 rows: more than 32
+    partial rows, the two-level sum)."""
+    dt = "bf16"
+    x = synthetic.draw(501, (T, H), "normal", 1.0, dt).to(DEV)
+    r = synthetic.draw(502, (T, H), "normal", 1.0, dt).to(DEV)
+    g = synthetic.draw(503, (H,), "normal", 0.02, dt).to(DEV)
+    b = synthetic.draw(504, (H,), "normal", 0.02, dt).to(DEV)
+    dy = synthetic.draw(505, (T, H), "normal", 1.0, dt).to(DEV)
+    _, h, mean, rstd = mb.mb_add_layer_norm_fwd(x, r, g, b)
+    _, _, dg_both, dbt_both = mb.mb_add_layer_norm_bwd(dy, h, g, mean, rstd)
+    _, _, dg_only, none_b = mb.mb_add_layer_norm_bwd(dy, h, g, mean, rstd, dbeta=False)
+    _, _, none_g, dbt_only = mb.mb_add_layer_norm_bwd(dy, h, g, mean, rstd, dgamma=False)
+    assert none_b is None and none_g is None
+    assert torch.equal(dg_both.view(torch.int32), dg_only.view(torch.int32))
+    assert torch.equal(dbt_both.view(torch.int32), dbt_only.view(torch.int32))

@@ -447,3 +447,22 @@ def test_bda_bwd_empty_and_errors():
         mb.mb_bias_dropout_add_bwd(g, 1.5, 1)
     with pytest.raises(mb.MBError, match="MB_ERR_ALIAS"):
         mb.mb_bias_dropout_add_bwd(g, 0.1, 1, dx=g, dresidual=g)  # two outputs on one buffer
+
+
+@pytest.mark.parametrize("shape", [(333, 1024), (4000, 64)])
+def test_glu_bwd_each_reduction_alone_matches_both(shape):
+    """dbias and dweights are summed in one launch when both are asked for and
+    in a launch of their own otherwise; either way each comes out bit for bit
+    the same (the (4000, 64) case has more than 32 partial rows of dbias)."""
+    T, H = shape
+    x, b, g, w = _glu_inputs("bf16", "f32", T, H, 311)
+    xd, bd, gd, wd = x.to(DEV), b.to(DEV), g.to(DEV), w.to(DEV)
+    _, db_both, dw_both = mb.mb_bias_swiglu_bwd(gd, xd, bd, wd, dbias=True, dweights=True)
+    _, db_only, none_w = mb.mb_bias_swiglu_bwd(gd, xd, bd, wd, dbias=True, dweights=False)
+    _, none_b, dw_only = mb.mb_bias_swiglu_bwd(gd, xd, bd, wd, dbias=False, dweights=True)
+    assert none_w is None and none_b is None
+    assert torch.equal(db_both.view(torch.int32), db_only.view(torch.int32))
+    assert torch.equal(dw_both.view(torch.int32), dw_only.view(torch.int32))
+    d, d64, mag, db64, dw64 = oracle.bias_glu_bwd("swiglu", "bf16", st(g), st(x), st(b), st(w), "f32")
+    log("swiglu dbias (pair)", assert_reduction_close(db_both.cpu().numpy(), db64, "swiglu dbias"))
+    log("swiglu dweights (pair)", assert_reduction_close(dw_both.cpu().numpy(), dw64, "swiglu dweights"))
