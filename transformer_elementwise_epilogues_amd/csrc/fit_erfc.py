@@ -11,9 +11,12 @@ relative error gives erfc to the same relative error everywhere, tails
 included, and the factor exp(-z^2/2) is the one the derivative's Gaussian
 term needs anyway.
 
-Least squares with relative weights on Chebyshev points, degree 8; prints the
-fp32 coefficients (lowest degree first) and the maximum relative error of the
-fp32 Horner evaluation on a dense grid. Needs numpy and scipy.
+Least squares with relative weights on Chebyshev points, degree 8 (kErfQ, for
+fp32 outputs and every backward) and degree 5 (kErfQ5, for the forward with
+bf16/fp16 outputs, where 3.5e-5 relative is far inside half an output ulp and
+a product z Phi(z) has no cancellation to amplify it); prints the fp32
+coefficients (lowest degree first) and the maximum relative error of the fp32
+Horner evaluation on a dense grid. Needs numpy and scipy.
 
     python fit_erfc.py
 """
@@ -22,6 +25,7 @@ from scipy.special import erfcx
 
 K = 0.70710678
 DEGREE = 8
+DEGREE_HALF = 5
 TMIN = 1.0 / 8.0
 
 
@@ -31,12 +35,13 @@ def target(t):
     return 0.5 * erfcx(x) * np.exp(x * x * (0.5 / (K * K) - 1.0)) / t
 
 
-def fit():
+def fit(degree=None):
+    degree = DEGREE if degree is None else degree
     n = 6000
     j = np.arange(n)
     t = 0.5 * (1 + TMIN) + 0.5 * (1 - TMIN) * np.cos(np.pi * (j + 0.5) / n)
     q = target(t)
-    V = np.vander(t, DEGREE + 1, increasing=True) / q[:, None]
+    V = np.vander(t, degree + 1, increasing=True) / q[:, None]
     c, *_ = np.linalg.lstsq(V, np.ones_like(t), rcond=None)
     return c.astype(np.float32)
 
@@ -50,10 +55,11 @@ def horner32(c32, t):
 
 
 if __name__ == "__main__":
-    c32 = fit()
     dense = np.linspace(TMIN, 1.0, 400001)
-    rel = np.abs(horner32(c32, dense) / target(dense) - 1.0)
-    print("coefficients (t^0 first):")
-    for ck in c32:
-        print(f"  {float(ck):.9e}f  ({np.float32(ck).view(np.uint32):#010x})")
-    print(f"max relative error of the fp32 evaluation on t in [{TMIN}, 1]: {rel.max():.3e}")
+    for name, degree in (("kErfQ", DEGREE), ("kErfQ5", DEGREE_HALF)):
+        c32 = fit(degree)
+        rel = np.abs(horner32(c32, dense) / target(dense) - 1.0)
+        print(f"{name}, degree {degree}, coefficients (t^0 first):")
+        for ck in c32:
+            print(f"  {float(ck):.9e}f  ({np.float32(ck).view(np.uint32):#010x})")
+        print(f"max relative error of the fp32 evaluation on t in [{TMIN}, 1]: {rel.max():.3e}")

@@ -463,18 +463,24 @@ constexpr float kErfK = 0.70710678f;
 constexpr float kErfPdf = 0.3989423f;
 constexpr float kErfQ[9] = {1.410423517e-01f, 1.412065774e-01f, 1.213941872e-01f, 1.020300612e-01f, -1.505985670e-02f,
                             1.417247653e-01f, -2.460705340e-01f, 1.435308009e-01f, -2.979838476e-02f};
+// the degree-5 fit (fit_erfc.py: within 3.5e-5 relative) for the forward
+// with bf16/fp16 outputs, whose half ulp is 2e-3 or 5e-4 relative
+constexpr float kErfQ5[6] = {1.408312619e-01f, 1.445789635e-01f, 1.034489125e-01f,
+                             1.344528794e-01f, 1.098317560e-02f, -3.431227431e-02f};
 constexpr float kErfTail = -12.0f;
 constexpr float kErfShift = 64.0f;
 constexpr float kErfScaleDown = 0x1p-64f;
 
 // t Q(t) for x = k |z|; k is kErfK, passed in so that the forward can hold it
-// in a VGPR
+// in a VGPR. HALF: the degree-5 polynomial.
+template <bool HALF = false>
 __device__ __forceinline__ float erf_tq(float z, float k) {
   const float x = __builtin_fabsf(z) * k;
   const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, x, 1.0f));
-  float q = kErfQ[8];
+  constexpr int n = HALF ? 5 : 8;
+  float q = HALF ? kErfQ5[n] : kErfQ[n];
 #pragma unroll
-  for (int j = 7; j >= 0; --j) q = __builtin_fmaf(q, t, kErfQ[j]);
+  for (int j = n - 1; j >= 0; --j) q = __builtin_fmaf(q, t, HALF ? kErfQ5[j] : kErfQ[j]);
   return t * q;
 }
 
@@ -483,10 +489,12 @@ __device__ __forceinline__ float gauss_scaled(float z, float shift) {
   return __builtin_amdgcn_exp2f(__builtin_fmaf(z * z, static_cast<float>(-0.5 * kLog2e), shift));
 }
 
-// value and derivative below z = -12 carry the deferred scale 2^-64
+// value and derivative below z = -12 carry the deferred scale 2^-64. HALF
+// (bf16/fp16 outputs): erfc from the degree-5 polynomial.
+template <bool HALF = false>
 __device__ __forceinline__ ScaledF gelu_erf_fwd(float z) {
   const bool tail = z < kErfTail;
-  const float h = erf_tq(z, vconst(kErfK)) * gauss_scaled(z, tail ? kErfShift : 0.0f);
+  const float h = erf_tq<HALF>(z, vconst(kErfK)) * gauss_scaled(z, tail ? kErfShift : 0.0f);
   ScaledF o;
   o.v = z * (z < 0.0f ? h : 1.0f - h);  // not z - z h: inf * 0 at z = inf
   o.sc = tail ? kErfScaleDown : 1.0f;

@@ -87,7 +87,7 @@ __device__ __forceinline__ u32x4 gelu_vec(u32x4 yv, const float* b) {
   unpack<D>(yv, f);
 #pragma unroll
   for (int k = 0; k < V; ++k) {
-    const ScaledF r = KIND == kTanh ? gelu_tanh_scaled(f[k] + b[k]) : gelu_erf_fwd(f[k] + b[k]);
+    const ScaledF r = KIND == kTanh ? gelu_tanh_scaled(f[k] + b[k]) : gelu_erf_fwd<(D != DT::F32)>(f[k] + b[k]);
     f[k] = r.v * r.sc;
   }
   return pack<D>(f);
