@@ -466,3 +466,62 @@ def test_glu_bwd_each_reduction_alone_matches_both(shape):
     d, d64, mag, db64, dw64 = oracle.bias_glu_bwd("swiglu", "bf16", st(g), st(x), st(b), st(w), "f32")
     log("swiglu dbias (pair)", assert_reduction_close(db_both.cpu().numpy(), db64, "swiglu dbias"))
     log("swiglu dweights (pair)", assert_reduction_close(dw_both.cpu().numpy(), dw64, "swiglu dweights"))
+
+
+@EXACT
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_gelu_every_half_precision_input(dt, exact):
+    """Every finite bf16 / fp16 value as input (no bias), forward and backward
+    with g = 1 and g = -3 against the oracle: the whole input space of the
+    half-precision kernels, including the degree-5 erfc forward."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    if dt == "bf16":
+        vals = (bits.astype(np.uint32) << 16).view(np.float32)
+        keep = np.isfinite(vals)
+        y = torch.from_numpy(vals[keep].copy()).to(torch.bfloat16)
+    else:
+        vals = bits.view(np.float16)
+        keep = np.isfinite(vals)
+        y = torch.from_numpy(vals[keep].copy())
+    n = (y.numel() // 8) * 8
+    y = y[:n].reshape(-1, 64 if n % 64 == 0 else 8)
+    out = GELU_FWD[exact](y.to(DEV))
+    o, o64 = oracle.bias_gelu_fwd(dt, st(y), None, exact=exact)
+    log(f"gelu fwd every {dt} exact={exact}", assert_close(st(out), o, o64, None, dt, "gelu fwd every input"))
+    for gval in (1.0, -3.0):
+        g = torch.full_like(y, gval)
+        dg, _ = GELU_BWD[exact](g.to(DEV), y.to(DEV), dbias=False)
+        d, d64, mag, _ = oracle.bias_gelu_bwd(dt, st(g), st(y), None, exact=exact)
+        log(f"gelu bwd every {dt} exact={exact} g={gval}", assert_close(st(dg), d, d64, mag, dt, "gelu bwd every input"))
+
+
+@pytest.mark.parametrize("act", ["swiglu", "geglu"])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_glu_every_half_precision_gate(act, dt):
+    """Every finite bf16 / fp16 value as the gate a (up half b = 0.75, no
+    bias), forward and backward with g = -0.5 against the oracle (the up value
+    and g keep every product finite in the output dtype)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    if dt == "bf16":
+        vals = (bits.astype(np.uint32) << 16).view(np.float32)
+        keep = np.isfinite(vals)
+        a = torch.from_numpy(vals[keep].copy()).to(torch.bfloat16)
+    else:
+        vals = bits.view(np.float16)
+        keep = np.isfinite(vals)
+        a = torch.from_numpy(vals[keep].copy())
+    H = 64
+    n = (a.numel() // H) * H
+    a = a[:n].reshape(-1, H)
+    x = torch.cat([a, torch.full_like(a, 0.75)], dim=1).contiguous()
+    g = torch.full_like(a, -0.5)
+    if act == "swiglu":
+        out = mb.mb_bias_swiglu_fwd(x.to(DEV))
+        din, _, _ = mb.mb_bias_swiglu_bwd(g.to(DEV), x.to(DEV), dbias=False)
+    else:
+        out = mb.mb_bias_geglu_fwd(x.to(DEV))
+        din, _ = mb.mb_bias_geglu_bwd(g.to(DEV), x.to(DEV), dbias=False)
+    o, o64 = oracle.bias_glu_fwd(act, dt, st(x), None, None, None)
+    log(f"{act} fwd every {dt} gate", assert_close(st(out), o, o64, None, dt, f"{act} fwd every gate"))
+    d, d64, mag, _, _ = oracle.bias_glu_bwd(act, dt, st(g), st(x), None, None, None)
+    log(f"{act} bwd every {dt} gate", assert_close(st(din), d, d64, mag, dt, f"{act} bwd every gate"))
