@@ -110,3 +110,32 @@ def test_srelu_full_workload():
     mag = (g.double().abs() * torch.relu(x.double()) ** 2).sum(1)
     err = (dw.double() - ref).abs()
     assert bool((err <= H * 2.0**-24 * mag + 1e-30).all())
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_srelu_every_half_precision_input(dt):
+    """Every finite bf16 / fp16 value as x, with fp32 weights 0.5 and g = -0.5,
+    forward and backward against the oracle (relu(x)^2 overflows the output
+    dtype for large x in both, as the formula does)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    if dt == "bf16":
+        vals = (bits.astype(np.uint32) << 16).view(np.float32)
+        keep = np.isfinite(vals)
+        x = torch.from_numpy(vals[keep].copy()).to(torch.bfloat16)
+    else:
+        vals = bits.view(np.float16)
+        keep = np.isfinite(vals)
+        x = torch.from_numpy(vals[keep].copy())
+    H = 64
+    n = (x.numel() // H) * H
+    x = x[:n].reshape(-1, H)
+    T = x.shape[0]
+    w = torch.full((T,), 0.5, dtype=torch.float32)
+    g = torch.full_like(x, -0.5)
+    out = mb.mb_weighted_squared_relu_fwd(x.to(DEV), w.to(DEV))
+    o, o64 = oracle.weighted_squared_relu_fwd(dt, st(x), st(w), "f32")
+    s1 = assert_close(st(out), o, o64, None, dt, f"srelu fwd every {dt}")
+    dx, dw = mb.mb_weighted_squared_relu_bwd(g.to(DEV), x.to(DEV), w.to(DEV))
+    d, d64, _ = oracle.weighted_squared_relu_bwd(dt, st(g), st(x), st(w), "f32")
+    s2 = assert_close(st(dx), d, d64, None, dt, f"srelu bwd every {dt}")
+    say(f"every {dt} input: fwd {s1} bwd {s2}")
