@@ -168,7 +168,7 @@ def build_ops(dev):
                   bwd5, ["bda_bwd", "colsum"]))
     ops.append(Op("chain_gelu_bwd_bf16_16384x32768",
                   lambda: mb.mb_bias_gelu_bwd(gg, gy, gb, dgrad=dgr, dbias=dbg, ws=wsg),
-                  T * H * 6 + H * 2 + H * 4, ["gelu_bwd", "colsum_chunk", "colsum"]))
+                  T * H * 6 + H * 2 + H * 4, ["gelu_bwd", "colsum_fold"]))
     ops.append(Op("chain_attn_bda_bwd_bf16_16384x8192",
                   lambda: mb.mb_bias_dropout_add_bwd(ag, p5, s_attn, off5, dx=adx, dresidual=False, dbias=adb, ws=wsb),
                   bwd5, ["bda_bwd", "colsum"]))
@@ -180,7 +180,7 @@ def build_ops(dev):
                 T * H * 4 + H * 2, ["gelu_fwd"]),
              Op("erf_gelu_bwd_bf16_16384x32768",
                 lambda: mb.mb_bias_gelu_erf_bwd(gg, gy, gb, dgrad=dgr, dbias=dbg, ws=wse),
-                T * H * 6 + H * 2 + H * 4, ["gelu_bwd", "colsum_chunk", "colsum"])]
+                T * H * 6 + H * 2 + H * 4, ["gelu_bwd", "colsum_fold"])]
 
     # -- beyond the step: residual add + LayerNorm, bf16 [16384, 8192]
     w = WORKLOADS["add_ln_bf16_16384x8192"]
@@ -197,7 +197,7 @@ def build_ops(dev):
     extra.append(Op("add_ln_bwd_bf16_16384x8192",
                     lambda: mb.mb_add_layer_norm_bwd(ldy, lh, lg, lmean, lrstd, zc, dh_in=lup, dx=ldx, dgamma=ldg,
                                                      dbeta=ldb, ws=lws),
-                    T * H * 8 + H * 2 + T * 8 + H * 8, ["ln_bwd", "colsum_chunk", "colsum"]))
+                    T * H * 8 + H * 2 + T * 8 + H * 8, ["ln_bwd", "colsum_fold"]))
 
     # -- beyond the step: MoE weighted squared ReLU, bf16 [8192, 14336], fp32 weights
     w = WORKLOADS["wsrelu_bf16_8192x14336"]

@@ -58,6 +58,41 @@ __global__ __launch_bounds__(256) void colsum_chunk_kernel(ColSum a, ColSum b) {
   k.out[static_cast<size_t>(blockIdx.y) * C + c] = s;
 }
 
+// Up to 16 chunks of 32 partial rows in one launch: wave y of a block sums
+// chunk y of 64 columns as colsum_chunk_kernel does, and wave 0 adds the
+// chunk sums in ascending order as colsum_kernel does, so the result is bit
+// for bit that of the two launches.
+constexpr int kFoldChunks = 16;
+__global__ __launch_bounds__(64 * kFoldChunks) void colsum_fold_kernel(ColSum a, ColSum b) {
+  const ColSum& k = blockIdx.z ? b : a;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+  __shared__ float part[kFoldChunks][64];
+  const int r0 = w * 32, r1 = r0 + 32 < k.R ? r0 + 32 : k.R;
+  float s = 0.0f;
+  if (c < k.C && r0 < k.R) {
+    const int64_t C = k.C;
+    const float* __restrict__ p = k.in + c;
+    int r = r0;
+    for (; r + 4 <= r1; r += 4) {
+      const float v0 = p[static_cast<size_t>(r) * C];
+      const float v1 = p[static_cast<size_t>(r + 1) * C];
+      const float v2 = p[static_cast<size_t>(r + 2) * C];
+      const float v3 = p[static_cast<size_t>(r + 3) * C];
+      s = (((s + v0) + v1) + v2) + v3;
+    }
+    for (; r < r1; ++r) s += p[static_cast<size_t>(r) * C];
+  }
+  part[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && c < k.C) {
+    const int chunks = (k.R + 31) / 32;
+    float t = 0.0f;
+    for (int j = 0; j < chunks; ++j) t += part[j][lane];
+    k.out[c] = t;
+  }
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i < n) p[i] = 0.0f;
@@ -98,8 +133,15 @@ static hipError_t colsum_tall_pair(const ColSum& a, const ColSum& b, float* tmp_
                                    hipStream_t s) {
   if (arrays == 1 && a.R <= 32) return launch_colsum(a.in, a.R, a.C, a.out, s);
   if (arrays == 2 && a.R <= 32 && b.R <= 32) return launch_colsum2(a, b, s);
-  const ColSum ca{a.in, a.R, a.C, tmp_a}, cb{b.in, b.R, b.C, tmp_b};
   const int chunks_a = (a.R + 31) / 32, chunks_b = (b.R + 31) / 32;
+  const int chunks = arrays == 2 ? std::max(chunks_a, chunks_b) : chunks_a;
+  if (chunks <= kFoldChunks) {
+    const int64_t cols = arrays == 2 ? std::max(a.C, b.C) : a.C;
+    hipLaunchKernelGGL(colsum_fold_kernel, dim3(static_cast<unsigned>((cols + 63) / 64), 1, arrays),
+                       dim3(64 * chunks), 0, s, a, b);
+    return hipGetLastError();
+  }
+  const ColSum ca{a.in, a.R, a.C, tmp_a}, cb{b.in, b.R, b.C, tmp_b};
   hipLaunchKernelGGL(colsum_chunk_kernel,
                      dim3(std::max(col_blocks(a.C), col_blocks(b.C)), static_cast<unsigned>(std::max(chunks_a, chunks_b)),
                           arrays),
