@@ -343,6 +343,15 @@ def cpu_baseline(host, seconds):
             "per_op_gbs": per}
 
 
+def device_info(dev):
+    """Architecture and compute-unit count of the measured device (the launch
+    shapes assume the whole 256-CU MI355X)."""
+    import torch
+
+    p = torch.cuda.get_device_properties(dev)
+    return {"arch": p.gcnArchName.split(":")[0], "compute_units": p.multi_processor_count}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -470,7 +479,8 @@ def main():
         "config": {"workload": WORKLOAD, "storage": "bf16 (fp32 residual in the 8192x4096 dropout-add)",
                    "step_bytes": step_bytes, "frac_peak": round(value / PEAK_HBM_GBS, 4), "launch": launch,
                    "ms_per_step_eager": round(ms_per_step_eager, 4),
-                   "copy_ceiling_gbs": round(ceiling["gbs"], 1)},
+                   "copy_ceiling_gbs": round(ceiling["gbs"], 1),
+                   "device": device_info(dev)},
         "per_op": per_op,
         "next_rows": next_rows,
         "roofline": roofline,
