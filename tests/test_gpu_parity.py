@@ -525,3 +525,35 @@ def test_glu_every_half_precision_gate(act, dt):
     log(f"{act} fwd every {dt} gate", assert_close(st(out), o, o64, None, dt, f"{act} fwd every gate"))
     d, d64, mag, _, _ = oracle.bias_glu_bwd(act, dt, st(g), st(x), None, None, None)
     log(f"{act} bwd every {dt} gate", assert_close(st(din), d, d64, mag, dt, f"{act} bwd every gate"))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_bda_every_half_precision_input(dt):
+    """Every finite bf16 / fp16 value as x, with a residual of 0.25 and a
+    bias of -0.5, through the training (p = 0.1) and inference passes and
+    the backward (g = x), against the oracle."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    if dt == "bf16":
+        vals = (bits.astype(np.uint32) << 16).view(np.float32)
+        keep = np.isfinite(vals)
+        x = torch.from_numpy(vals[keep].copy()).to(torch.bfloat16)
+    else:
+        vals = bits.view(np.float16)
+        keep = np.isfinite(vals)
+        x = torch.from_numpy(vals[keep].copy())
+    H = 64
+    n = (x.numel() // H) * H
+    x = x[:n].reshape(-1, H)
+    r = torch.full_like(x, 0.25)
+    b = torch.full((H,), -0.5, dtype=x.dtype)
+    p, seed, off = 0.1, 77, 3
+    out = mb.mb_bias_dropout_add_train(x.to(DEV), b.to(DEV), r.to(DEV), p, seed, off)
+    o, o64, mag = oracle.bias_dropout_add(dt, st(x), st(b), st(r), dt, True, p, seed, off)
+    log(f"bda train every {dt}", assert_close(st(out), o, o64, mag, dt, "bda train every input"))
+    inf_out = mb.mb_bias_dropout_add_infer(x.to(DEV), b.to(DEV), r.to(DEV))
+    o, o64, mag = oracle.bias_dropout_add(dt, st(x), st(b), st(r), dt, False)
+    log(f"bda infer every {dt}", assert_close(st(inf_out), o, o64, mag, dt, "bda infer every input"))
+    dx, dres, _ = mb.mb_bias_dropout_add_bwd(x.to(DEV), p, seed, off, dbias=False)
+    odx, odx64, odres, _ = oracle.bias_dropout_add_bwd(dt, st(x), dt, p, seed, off)
+    log(f"bda bwd every {dt}", assert_close(st(dx), odx, odx64, None, dt, "bda bwd every input"))
+    assert np.array_equal(st(dres), odres)
