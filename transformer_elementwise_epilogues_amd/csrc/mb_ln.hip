@@ -608,10 +608,16 @@ constexpr Shape kShapes[] = {{64, 1, 4},  {64, 2, 4},  {64, 4, 4},  {256, 1, 1},
                              {256, 4, 1}, {512, 1, 1}, {512, 2, 1}, {512, 4, 1},  {1024, 1, 1},
                              {1024, 2, 1}, {1024, 4, 1}, {1024, 8, 1}};
 constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
-// dgamma / dbeta come from the column-strip kernel for 1024-thread rows of
-// more than 2 vectors per thread: the per-thread accumulators would not fit
-// beside the row in the 128 registers a thread of such a block has.
-constexpr bool split_shape(int s) { return kShapes[s].tpr == 1024 && kShapes[s].nv > 2; }
+// dgamma / dbeta come from the column-strip kernel (which reads dy and h once
+// more) for 1024-thread rows of 2 or more vectors per thread: beyond 2 the
+// per-thread accumulators would not fit beside the row in the 128 registers
+// a thread of such a block has, and at 2 (rows of 2048 vectors) holding them
+// in LDS (128 KiB per block, one block per CU) ran 22 % slower than the
+// column-strip kernel on MI355X. (MB_LN_SPLIT_MIN_NV 4 restores the LDS sums.)
+#ifndef MB_LN_SPLIT_MIN_NV
+#define MB_LN_SPLIT_MIN_NV 2
+#endif
+constexpr bool split_shape(int s) { return kShapes[s].tpr == 1024 && kShapes[s].nv >= MB_LN_SPLIT_MIN_NV; }
 
 template <DT D, DT R, int S>
 hipError_t fwd_shape(const LnArgs& a, const LnPlan& p, hipStream_t s) {
