@@ -33,8 +33,8 @@ PAIRS = [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"), ("f16", "f16"), ("f1
 def hidden_cases(dt, rdt):
     """(T, H) per row-group shape, for elements-per-vector E."""
     E = 4 if (dt == "f32" or rdt == "f32") else 8
-    # vectors per row; 2048 is the widest row whose parameter-gradient sums
-    # stay in LDS (128 KiB at bf16)
+    # vectors per row; from 2048 on the parameter-gradient sums come from the
+    # column-strip kernel, and the forward of 4096 runs 512 threads of 8
     widths = [33, 128, 255, 512, 1021, 1536, 2048, 4096, 8192]
     rows = {33: 37, 128: 65, 255: 9, 512: 20, 1021: 6, 1536: 5, 2048: 300, 4096: 4, 8192: 3}
     return [(rows[w], w * E) for w in widths]

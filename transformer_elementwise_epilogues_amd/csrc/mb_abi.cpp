@@ -551,7 +551,11 @@ mb_status_t mb_add_layer_norm_fwd(const void* x, const void* residual, mb_dtype_
   a.y = y;
   a.mean = mean;
   a.rstd = rstd;
-  const mb::LnPlan fp = mb::plan_ln(tokens, hidden, dt, residual_dt, MB_LN_FWD_BLOCKS, MB_LN_FWD_NV);
+  mb::LnPlan fp = mb::plan_ln(tokens, hidden, dt, residual_dt, MB_LN_FWD_BLOCKS, MB_LN_FWD_NV);
+  if (MB_LN_FWD_WIDE_HALF && mb::ln_plan_is(fp, 1024, 4)) {
+    const mb::LnPlan half = mb::plan_ln(tokens, hidden, dt, residual_dt, MB_LN_FWD_BLOCKS, 8);
+    if (mb::ln_plan_is(half, 512, 8)) fp = half;
+  }
   if (fp.shape < 0) return MB_ERR_SHAPE;
   if (hipError_t e = mb::launch_ln_fwd(a, fp, s)) return hip_status(e);
   return finish();

@@ -123,6 +123,11 @@ struct Tiling {
 #ifndef MB_LN_FWD_NV
 #define MB_LN_FWD_NV 4
 #endif
+// forward rows of 4096 vectors: 512 threads of 8 (two blocks per CU) instead
+// of 1024 threads of 4 (one)
+#ifndef MB_LN_FWD_WIDE_HALF
+#define MB_LN_FWD_WIDE_HALF 1
+#endif
 #ifndef MB_LN_BWD_NV
 #define MB_LN_BWD_NV 2
 #endif
@@ -229,6 +234,8 @@ struct LnPlan {
 };
 int ln_elems_per_vector(int dt, int rdt);
 LnPlan plan_ln(int64_t T, int64_t H, int dt, int rdt, int target_blocks, int nv_pref);
+// the plan's row group is `tpr` threads of `nv` vectors
+bool ln_plan_is(const LnPlan& p, int tpr, int nv);
 hipError_t launch_ln_fwd(const LnArgs& a, const LnPlan& p, hipStream_t s);
 hipError_t launch_ln_bwd(const LnArgs& a, const LnPlan& p, hipStream_t s);
 

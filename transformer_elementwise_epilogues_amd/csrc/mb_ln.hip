@@ -146,9 +146,10 @@ constexpr bool acc_in_lds(int tpr, int nv) { return tpr == 1024 && nv == 2; }
 #ifndef MB_LN_PREFETCH
 #define MB_LN_PREFETCH 1
 #endif
-// The next row is prefetched into registers, except for 1024-thread rows of
-// 4 or more vectors per thread, which have no registers to spare.
-template <int TPR, int NV> constexpr bool prefetch() { return MB_LN_PREFETCH && !(TPR == 1024 && NV >= 4); }
+// The next row is prefetched into registers, except for rows of 4096 or more
+// vectors (1024 threads of 4 or 8, 512 threads of 8), which have no registers
+// to spare.
+template <int TPR, int NV> constexpr bool prefetch() { return MB_LN_PREFETCH && TPR * NV < 4096; }
 
 // Parameters (gamma, beta) stay packed in registers unless the row slice is
 // the widest one (8 vectors per thread), where they are re-read from cache.
@@ -606,7 +607,7 @@ struct Shape {
 };
 constexpr Shape kShapes[] = {{64, 1, 4},  {64, 2, 4},  {64, 4, 4},  {256, 1, 1},  {256, 2, 1},
                              {256, 4, 1}, {512, 1, 1}, {512, 2, 1}, {512, 4, 1},  {1024, 1, 1},
-                             {1024, 2, 1}, {1024, 4, 1}, {1024, 8, 1}};
+                             {1024, 2, 1}, {1024, 4, 1}, {1024, 8, 1}, {512, 8, 1}};
 constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
 // dgamma / dbeta come from the column-strip kernel (which reads dy and h once
 // more) for 1024-thread rows of 2 or more vectors per thread: beyond 2 the
@@ -617,7 +618,9 @@ constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
 #ifndef MB_LN_SPLIT_MIN_NV
 #define MB_LN_SPLIT_MIN_NV 2
 #endif
-constexpr bool split_shape(int s) { return kShapes[s].tpr == 1024 && kShapes[s].nv >= MB_LN_SPLIT_MIN_NV; }
+constexpr bool split_shape(int s) {
+  return (kShapes[s].tpr == 1024 && kShapes[s].nv >= MB_LN_SPLIT_MIN_NV) || kShapes[s].nv >= 8;
+}
 
 template <DT D, DT R, int S>
 hipError_t fwd_shape(const LnArgs& a, const LnPlan& p, hipStream_t s) {
@@ -713,6 +716,10 @@ LnPlan plan_ln(int64_t T, int64_t H, int dt, int rdt, int target_blocks, int nv_
   p.dgb = plan_tiling(T, v16, MB_LN_DGB_BLOCKS);
   p.partial_rows = p.split ? p.dgb.G : p.grid;
   return p;
+}
+
+bool ln_plan_is(const LnPlan& p, int tpr, int nv) {
+  return p.shape >= 0 && kShapes[p.shape].tpr == tpr && kShapes[p.shape].nv == nv;
 }
 
 hipError_t launch_ln_fwd(const LnArgs& a, const LnPlan& p, hipStream_t s) { return by_dtype<false>(a, p, s); }
