@@ -557,3 +557,24 @@ def test_bda_every_half_precision_input(dt):
     odx, odx64, odres, _ = oracle.bias_dropout_add_bwd(dt, st(x), dt, p, seed, off)
     log(f"bda bwd every {dt}", assert_close(st(dx), odx, odx64, None, dt, "bda bwd every input"))
     assert np.array_equal(st(dres), odres)
+
+
+@EXACT
+@pytest.mark.parametrize("T", [132, 2048, 2052])
+def test_gelu_bwd_dbias_across_column_sum_paths(T, exact):
+    """H = 16384 bf16 (32 column strips): T = 132 gives 33 partial rows (the
+    one-launch fold of 2 chunks), 2048 gives 512 (16 chunks, the most one
+    launch folds), 2052 gives 513 (17 chunks: the two-launch path). dbias on
+    sampled columns against the oracle's fp64 sum over every row, and dgrad on
+    sampled rows."""
+    H = 16384
+    y = gen(601, (T, H), "bf16", sigma=2.0)
+    g = gen(602, (T, H), "bf16")
+    b = gen(603, (H,), "bf16", sigma=0.5)
+    dgrad, dbias = GELU_BWD[exact](g.to(DEV), y.to(DEV), b.to(DEV))
+    cols = np.unique(np.concatenate([np.random.default_rng(T).choice(H, 256, replace=False), [0, H - 1]]))
+    _, _, _, db64 = oracle.bias_gelu_bwd("bf16", st(g[:, cols]), st(y[:, cols]), st(b[cols]), exact=exact)
+    log(f"gelu dbias T={T} exact={exact}", assert_reduction_close(dbias.cpu().numpy()[cols], db64, "gelu dbias"))
+    rows = np.unique(np.concatenate([np.random.default_rng(T + 1).choice(T, 16, replace=False), [0, T - 1]]))
+    d, d64, mag, _ = oracle.bias_gelu_bwd("bf16", st(g[rows]), st(y[rows]), st(b), exact=exact)
+    log(f"gelu dgrad rows T={T}", assert_close(st(dgrad.cpu()[rows]), d, d64, mag, "bf16", "gelu dgrad rows"))
