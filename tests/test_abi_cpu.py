@@ -167,3 +167,4 @@ def test_squared_relu_validation():
     assert bw(A, B, E, F32, C, D, None, 0, 64, 512, BF16, None) == WORKSPACE
     assert bw(A, B, None, F32, A, None, None, 0, 0, 512, BF16, None) == OK      # dx over g, empty
     assert bw(A, B, None, F32, A + 16, None, None, 0, 4, 512, BF16, None) == ALIAS
+

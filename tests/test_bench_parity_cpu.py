@@ -1,0 +1,79 @@
+"""The benchmark's CPU-baseline leg on small inputs, without a GPU: every op
+of the step and of the next rows has an oracle plan, the thread-pool leg
+covers row chunks, and the parity statistics of outputs equal to the
+oracle's report no failures (and do report a planted one)."""
+import numpy as np
+import torch
+
+import bench
+from oracle.tolerances import from_storage
+from transformer_elementwise_epilogues_amd.synthetic import WORKLOADS, draw
+
+ROWS = 6
+
+
+def small_host():
+    host = {}
+    for wn, w in WORKLOADS.items():
+        if wn == "gelu_f32_512x4096":
+            continue
+        for tn, t in w.tensors.items():
+            if tn == "weights":  # per token
+                shape = (ROWS,)
+            elif len(t.shape) == 1:  # per column
+                shape = t.shape
+            else:
+                shape = (ROWS,) + tuple(t.shape[1:])
+            host[(wn, tn)] = draw(1000 * w.c + t.k, shape, t.dist, t.sigma, t.dtype)
+    return host
+
+
+def test_cpu_baseline_and_parity_plumbing():
+    host = small_host()
+    plan = bench.oracle_plan(host)
+    assert len(plan) == 25
+    gpu_rows = {}
+    for name, (f, _, T) in plan.items():
+        assert T == ROWS
+        exp = f(0, ROWS)
+        gpu_rows[name] = {}
+        for k, e in exp.items():
+            if e[0] == "rowsum":
+                gpu_rows[name][k] = torch.from_numpy(e[1].astype(np.float32))
+            else:
+                dt = torch.float32 if e[1].dtype == np.float32 else torch.bfloat16
+                gpu_rows[name][k] = from_storage(e[1], dt)
+    cpu, parity = bench.cpu_baseline(host, gpu_rows, seconds=0.05, max_rows=ROWS, max_threads=2)
+    assert cpu["kind"] == "oracle" and cpu["cores"] >= 1 and cpu["value"] > 0
+    assert cpu["cpu"]["nproc"] >= 1 and cpu["single_core"]["rows"] <= ROWS
+    assert set(parity) == set(plan)
+    for name, outs in parity.items():
+        for out, st in outs.items():
+            assert st["fail"] == 0, (name, out, st)
+    # a planted difference in one output element is counted
+    g = gpu_rows["chain_gelu_fwd_bf16_16384x32768"]["out"]
+    g.view(torch.int16)[0, 0] += 3
+    _, parity = bench.cpu_baseline(host, gpu_rows, seconds=0.05, max_rows=ROWS, max_threads=2)
+    assert parity["chain_gelu_fwd_bf16_16384x32768"]["out"]["fail"] == 1
+
+
+def test_streaming_mix_bounds_are_checked_on_the_host():
+    """The ceiling kernel's pieces stay inside their tensors (host tensors
+    stand in for device buffers: only addresses and sizes are used)."""
+    bf = torch.bfloat16
+    T, H = 16, 1024
+    inp, g, din, out = (torch.zeros(s, dtype=bf) for s in ((T, 2 * H), (T, H), (T, 2 * H), (T, H)))
+    m = bench.glu_bwd_mix(g, inp, din)
+    assert m.bytes == T * H * 2 * 5 and m.lanes == H * 2 // 16
+    assert bench.glu_fwd_mix(inp, out).bytes == T * H * 2 * 3
+    x, r, o = torch.zeros((T, H), dtype=bf), torch.zeros((T, H), dtype=torch.float32), torch.zeros((T, H), dtype=bf)
+    m = bench.Mix([bench.Piece(x, 0, H * 2, 8), bench.Piece(r, 0, H * 4, 16)], [bench.Piece(o, 0, H * 2, 8)], T,
+                  H // 4)
+    assert m.bytes == T * H * 8
+    import pytest
+    with pytest.raises(AssertionError):  # one row too many
+        bench.rows_mix([x], [o], T + 1, H * 2)
+    with pytest.raises(AssertionError):  # an output narrower than half the input row
+        bench.glu_fwd_mix(inp, torch.zeros((T, H // 2), dtype=bf))
+    with pytest.raises(AssertionError):  # 8-byte pieces only in the dropout-add mixes
+        bench.Mix([bench.Piece(x, 0, H * 2, 8)], [bench.Piece(o, 0, H * 2, 8)], T, H // 4)

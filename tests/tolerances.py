@@ -1,139 +1,5 @@
-"""Parity comparators between kernel outputs and the oracle.
-
-Floating point (per element, kernel value k, oracle value o rounded once to
-the output dtype, unrounded oracle value o64):
-  fp32 outputs:       |k - o| <= 1e-6 |o| + 1e-6
-  bf16/fp16 outputs:  |k - o| <= 1 ulp_dt(o)
-  either, at cancellations only: |k - o64| <= 8 * 2^-24 * mag, where mag is
-      the size of the largest term the fp32 evaluation combines (reported
-      separately as "floor" passes; it only matters near roots of the
-      derivatives and where r' + z*s cancels, and for fp32 outputs only when
-      an upstream factor (the gradient, the up half) scales such a root
-      value far above the 1e-6 absolute term)
-  fp32 reductions (dbias, dweights): |k - o| <= 1e-3 |o| + 1e-3 rms(o)
-Integers / bits: exact. Equal bit patterns, both NaN, and +0 vs -0 pass.
-"""
-from __future__ import annotations
-
-import numpy as np
-import torch
-
-FLOOR_FACTOR = 8 * 2.0**-24
-
-
-def to_storage(t: torch.Tensor) -> np.ndarray:
-    """Raw storage of a CPU/GPU tensor in the oracle's convention."""
-    t = t.detach().contiguous().cpu()
-    if t.dtype == torch.float32:
-        return t.numpy()
-    if t.dtype in (torch.bfloat16, torch.float16):
-        return t.view(torch.int16).numpy().view(np.uint16)
-    raise TypeError(t.dtype)
-
-
-def from_storage(a: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
-    if dtype == torch.float32:
-        return torch.from_numpy(np.ascontiguousarray(a, np.float32))
-    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16).copy()).view(dtype)
-
-
-def values(a: np.ndarray, dt: str) -> np.ndarray:
-    if dt == "f32":
-        return a.astype(np.float64)
-    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16).copy()).view(
-        torch.bfloat16 if dt == "bf16" else torch.float16)
-    return t.to(torch.float64).numpy()
-
-
-def ulp(o: np.ndarray, dt: str) -> np.ndarray:
-    """Spacing of the dt grid at |o| (the subnormal spacing below the normal range)."""
-    prec, emin = (8, -126) if dt == "bf16" else (11, -14)
-    a = np.abs(o)
-    with np.errstate(divide="ignore"):
-        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    e = np.maximum(np.where(a > 0, e, emin), emin)
-    return np.ldexp(1.0, (e - (prec - 1)).astype(np.int64))
-
-
-def compare(kernel: np.ndarray, oracle_out: np.ndarray, o64: np.ndarray, mag, dt: str):
-    """Returns (pass mask, stats dict)."""
-    k = values(kernel, dt)
-    o = values(oracle_out, dt)
-    same_bits = kernel.view(np.uint32 if dt == "f32" else np.uint16) == oracle_out.view(
-        np.uint32 if dt == "f32" else np.uint16)
-    both_nan = np.isnan(k) & np.isnan(o)
-    with np.errstate(invalid="ignore"):
-        d = np.abs(k - o)
-        d = np.where(np.isinf(k) & np.isinf(o) & (np.sign(k) == np.sign(o)), 0.0, d)
-        ok = d <= 1e-6 * np.abs(o) + 1e-6 if dt == "f32" else d <= ulp(o, dt)
-        floor_ok = ~ok & (np.abs(k - o64) <= FLOOR_FACTOR * (mag if mag is not None else 0.0))
-    passed = same_bits | both_nan | ok | floor_ok
-    with np.errstate(invalid="ignore", divide="ignore"):
-        rel = np.where(np.abs(o) > 0, d / np.abs(o), 0.0)
-        ulps = d / ulp(o, dt) if dt != "f32" else rel
-    fin = np.isfinite(ulps)
-    stats = {
-        "n": int(k.size),
-        "fail": int((~passed).sum()),
-        "bit_equal": int(same_bits.sum()),
-        "floor_only": int((floor_ok & ~ok & ~same_bits).sum()),
-        "max_ulp_or_rel": float(np.max(ulps[fin])) if fin.any() else 0.0,
-        "max_abs": float(np.nanmax(d)) if d.size else 0.0,
-        "ref_max": float(np.nanmax(np.abs(o))) if o.size else 0.0,
-    }
-    return passed, stats
-
-
-def assert_close(kernel, oracle_out, o64, mag, dt, what=""):
-    passed, stats = compare(kernel, oracle_out, o64, mag, dt)
-    if stats["fail"]:
-        idx = np.flatnonzero(~passed.reshape(-1))[:8]
-        kv, ov = values(kernel, dt).reshape(-1), values(oracle_out, dt).reshape(-1)
-        ex = [(int(i), float(kv[i]), float(ov[i]), float(o64.reshape(-1)[i])) for i in idx]
-        raise AssertionError(f"{what}: {stats['fail']}/{stats['n']} elements out of tolerance; "
-                             f"first (index, kernel, oracle, oracle64): {ex}; stats {stats}")
-    return stats
-
-
-def assert_reduction_close(kernel: np.ndarray, oracle64: np.ndarray, what=""):
-    k = kernel.astype(np.float64)
-    o = oracle64
-    rms = float(np.sqrt(np.mean(o * o))) if o.size else 0.0
-    bad = np.abs(k - o) > 1e-3 * np.abs(o) + 1e-3 * rms
-    if bad.any():
-        i = np.flatnonzero(bad)[:8]
-        raise AssertionError(f"{what}: {int(bad.sum())}/{o.size} out of 1e-3 tolerance; first {list(zip(i, k[i], o[i]))}")
-    worst = float(np.max(np.abs(k - o) / (np.abs(o) + rms + 1e-300))) if o.size else 0.0
-    return {"n": int(o.size), "max_rel_to_rms": worst}
-
-
-def assert_close_bounded(kernel, oracle_out, o64, bound, dt, what=""):
-    """For ops whose fp32 evaluation error has a derived bound per element
-    (row reductions such as LayerNorm): passes when the bits are equal, both
-    are NaN, |k - o| <= 1 ulp of the once-rounded oracle value (bf16/fp16), or
-    |k - o64| <= bound + the output rounding (half an fp32 ulp, one bf16/fp16
-    ulp)."""
-    k = values(kernel, dt)
-    o = values(oracle_out, dt)
-    same_bits = kernel.view(np.uint32 if dt == "f32" else np.uint16) == oracle_out.view(
-        np.uint32 if dt == "f32" else np.uint16)
-    both_nan = np.isnan(k) & np.isnan(o)
-    with np.errstate(invalid="ignore"):
-        if dt == "f32":
-            ok = np.abs(k - o64) <= bound + 2.0**-24 * np.abs(o64)
-        else:
-            ok = (np.abs(k - o) <= ulp(o, dt)) | (np.abs(k - o64) <= bound + ulp(o64, dt))
-    passed = same_bits | both_nan | ok
-    err = np.abs(k - o64)
-    with np.errstate(invalid="ignore", divide="ignore"):
-        ratio = np.where(bound > 0, err / bound, 0.0)
-    stats = {"n": int(k.size), "fail": int((~passed).sum()), "bit_equal": int(same_bits.sum()),
-             "max_err_over_bound": float(np.nanmax(ratio)) if ratio.size else 0.0,
-             "max_abs": float(np.nanmax(err)) if err.size else 0.0}
-    if stats["fail"]:
-        idx = np.flatnonzero(~passed.reshape(-1))[:8]
-        ex = [(int(i), float(k.reshape(-1)[i]), float(o64.reshape(-1)[i]), float(np.reshape(bound, -1)[i]))
-              for i in idx]
-        raise AssertionError(f"{what}: {stats['fail']}/{stats['n']} out of bound; first (index, kernel, oracle64, "
-                             f"bound): {ex}; stats {stats}")
-    return stats
+"""The parity comparators live with the oracle (oracle/tolerances.py), where
+the benchmark's CPU-baseline leg can use them too; the tests import them from
+here."""
+from oracle.tolerances import (FLOOR_FACTOR, assert_close, assert_close_bounded, assert_reduction_close,  # noqa: F401
+                               compare, from_storage, to_storage, ulp, values)

@@ -97,13 +97,8 @@ def _p(t):
 
 def _dt(t: torch.Tensor) -> int:
     if t.dtype not in DTYPES:
-        raise TypeError(f"unsupported dtype {t.dtype}")
+        raise ValueError(f"unsupported dtype {t.dtype}")
     return DTYPES[t.dtype]
-
-
-def _stream(t: torch.Tensor, stream):
-    s = stream if stream is not None else torch.cuda.current_stream(t.device)
-    return ctypes.c_void_p(s.cuda_stream)
 
 
 def _check(fn: str, status: int):
@@ -111,31 +106,113 @@ def _check(fn: str, status: int):
         raise MBError(fn, status, lib().mb_status_string(status).decode())
 
 
-def _rows(t: torch.Tensor, name: str, cols=None):
-    if t.dim() != 2:
-        raise ValueError(f"{name} must be 2-D [tokens, hidden], got {tuple(t.shape)}")
+# Argument checks. The C ABI receives raw pointers and (tokens, hidden) only,
+# so every size, dtype and device rule that a pointer alone cannot carry is
+# enforced here, before any library call: each tensor argument, input or
+# output, must have exactly the shape the entry point reads or writes, an
+# accepted dtype, a contiguous layout, and live on the same GPU as the others
+# (a host address handed to a kernel would fault the device). What the ABI
+# checks itself from the pointers (alignment, overlap, the 16-byte row rule,
+# the workspace size) is left to it.
+
+def _need(t, name: str, shape, dtypes):
+    """Check one tensor argument (not yet its device)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        names = ", ".join(str(d) for d in dtypes)
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {names}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if cols is not None and t.shape[1] != cols:
-        raise ValueError(f"{name} has {t.shape[1]} columns, expected {cols}")
+    return t
+
+
+def _opt(t, name: str, shape, dtypes):
+    return None if t is None else _need(t, name, shape, dtypes)
+
+
+def _rows2d(t, name: str):
+    """[tokens, columns] of the tensor that defines an op's shape."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D [tokens, hidden], got {tuple(t.shape)}")
+    if t.dtype not in DTYPES:
+        raise ValueError(f"{name} has unsupported dtype {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
     return t.shape
 
 
-def _vec(t, n, name):
-    if t is None:
-        return None
-    if t.dim() != 1 or t.shape[0] != n or not t.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous vector of {n} elements")
+def _gpu(stream, *named):
+    """All (name, tensor) pairs (None skipped) on one GPU; `stream`, if given,
+    on that GPU too. Returns the device."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor, got one on {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+    if stream is not None and dev is not None and torch.device(stream.device) != dev:
+        raise ValueError(f"stream is on {stream.device}, the tensors on {dev}")
+    return dev
+
+
+def _stream(dev, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _on(dev, name: str, t):
+    """A caller-supplied output or buffer on the inputs' GPU."""
+    if not t.is_cuda or t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {dev}")
     return t
+
+
+def _out(t, name: str, shape, dtype, dev):
+    """An output: allocated when not given, else checked like an input."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    return _on(dev, name, _need(t, name, shape, (dtype,)))
+
+
+def _grad_out(flag, name: str, n: int, dev):
+    """An optional fp32 gradient vector: True allocates it, False/None skips it."""
+    if flag is True:
+        return torch.empty(n, dtype=torch.float32, device=dev)
+    if flag is False or flag is None:
+        return None
+    return _on(dev, name, _need(flag, name, (n,), (torch.float32,)))
+
+
+def _ws(ws, nbytes: int, dev):
+    """The workspace: allocated when not given (nbytes > 0), else a contiguous
+    tensor on the GPU; its byte size goes to the ABI, which checks it."""
+    if ws is None:
+        return (torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None), nbytes
+    if not isinstance(ws, torch.Tensor) or not ws.is_contiguous():
+        raise ValueError("ws must be a contiguous torch.Tensor")
+    return _on(dev, "ws", ws), ws.numel() * ws.element_size()
+
+
+_FLOAT = tuple(DTYPES)
 
 
 # ------------------------------------------------------------------ GeLU
 
 def _gelu_fwd(fn, y, bias, out, stream):
-    T, H = _rows(y, "y")
-    _vec(bias, H, "bias")
-    out = torch.empty_like(y) if out is None else out
-    _check(fn, getattr(lib(), fn)(_p(y), _p(bias), _p(out), T, H, _dt(y), _stream(y, stream)))
+    T, H = _rows2d(y, "y")
+    _opt(bias, "bias", (H,), (y.dtype,))
+    dev = _gpu(stream, ("y", y), ("bias", bias))
+    out = _out(out, "out", (T, H), y.dtype, dev)
+    _check(fn, getattr(lib(), fn)(_p(y), _p(bias), _p(out), T, H, _dt(y), _stream(dev, stream)))
     return out
 
 
@@ -157,18 +234,20 @@ def mb_bias_gelu_erf_bwd_workspace(tokens, hidden, dtype, with_dbias=True) -> in
     return int(lib().mb_bias_gelu_erf_bwd_workspace(tokens, hidden, DTYPES[dtype], int(bool(with_dbias))))
 
 
+def _gelu_bwd_args(g, y, bias, dgrad, dbias, stream):
+    T, H = _rows2d(y, "y")
+    _need(g, "g", (T, H), (y.dtype,))
+    _opt(bias, "bias", (H,), (y.dtype,))
+    dev = _gpu(stream, ("y", y), ("g", g), ("bias", bias))
+    return T, H, dev, _out(dgrad, "dgrad", (T, H), y.dtype, dev), _grad_out(dbias, "dbias", H, dev)
+
+
 def _gelu_bwd(fn, g, y, bias, dgrad, dbias, ws, stream):
-    T, H = _rows(y, "y")
-    _rows(g, "g", H)
-    _vec(bias, H, "bias")
-    dgrad = torch.empty_like(y) if dgrad is None else dgrad
-    dbias = _grad_out(dbias, H, y.device)
+    T, H, dev, dgrad, dbias = _gelu_bwd_args(g, y, bias, dgrad, dbias, stream)
     wsf = mb_bias_gelu_erf_bwd_workspace if fn == "mb_bias_gelu_erf_bwd" else mb_bias_gelu_bwd_workspace
-    nws = wsf(T, H, y.dtype, dbias is not None)
-    if ws is None and nws:
-        ws = torch.empty(nws, dtype=torch.uint8, device=y.device)
-    _check(fn, getattr(lib(), fn)(_p(g), _p(y), _p(bias), _p(dgrad), _p(dbias), _p(ws),
-                                  ws.numel() if ws is not None else 0, T, H, _dt(y), _stream(y, stream)))
+    ws, nws = _ws(ws, wsf(T, H, y.dtype, dbias is not None), dev)
+    _check(fn, getattr(lib(), fn)(_p(g), _p(y), _p(bias), _p(dgrad), _p(dbias), _p(ws), nws, T, H, _dt(y),
+                                  _stream(dev, stream)))
     return dgrad, dbias
 
 
@@ -184,25 +263,32 @@ def mb_bias_gelu_erf_bwd(g, y, bias=None, dgrad=None, dbias=True, ws=None, strea
 
 # ------------------------------------------------------------------ dropout-add
 
+def _res_dtypes(x):
+    return (x.dtype, torch.float32)
+
+
 def mb_bias_dropout_add_train(x, bias, residual, p, seed, offset=0, out=None, stream=None):
-    T, H = _rows(x, "x")
-    _rows(residual, "residual", H)
-    _vec(bias, H, "bias")
-    out = torch.empty_like(x) if out is None else out
+    """out = residual' + dropout(x + bias) with the Philox keep mask of (p, seed, offset)."""
+    T, H = _rows2d(x, "x")
+    _need(residual, "residual", (T, H), _res_dtypes(x))
+    _opt(bias, "bias", (H,), (x.dtype,))
+    dev = _gpu(stream, ("x", x), ("residual", residual), ("bias", bias))
+    out = _out(out, "out", (T, H), x.dtype, dev)
     _check("mb_bias_dropout_add_train", lib().mb_bias_dropout_add_train(
         _p(x), _p(bias), _p(residual), _dt(residual), _p(out), T, H, _dt(x), float(p), int(seed), int(offset),
-        _stream(x, stream)))
+        _stream(dev, stream)))
     return out
 
 
 def mb_bias_dropout_add_infer(x, bias, residual, out=None, stream=None):
-    """out=x runs in place."""
-    T, H = _rows(x, "x")
-    _rows(residual, "residual", H)
-    _vec(bias, H, "bias")
-    out = torch.empty_like(x) if out is None else out
+    """out = residual' + x + bias; out=x runs in place."""
+    T, H = _rows2d(x, "x")
+    _need(residual, "residual", (T, H), _res_dtypes(x))
+    _opt(bias, "bias", (H,), (x.dtype,))
+    dev = _gpu(stream, ("x", x), ("residual", residual), ("bias", bias))
+    out = _out(out, "out", (T, H), x.dtype, dev)
     _check("mb_bias_dropout_add_infer", lib().mb_bias_dropout_add_infer(
-        _p(x), _p(bias), _p(residual), _dt(residual), _p(out), T, H, _dt(x), _stream(x, stream)))
+        _p(x), _p(bias), _p(residual), _dt(residual), _p(out), T, H, _dt(x), _stream(dev, stream)))
     return out
 
 
@@ -214,57 +300,75 @@ def mb_bias_dropout_add_bwd(g, p, seed, offset=0, residual_dtype=None, dx=None, 
                             ws=None, stream=None):
     """Returns (dx, dresidual or None, dbias or None) for the train forward with (p, seed, offset).
     residual_dtype defaults to g's dtype; dresidual=True allocates it, False skips it."""
-    T, H = _rows(g, "g")
+    T, H = _rows2d(g, "g")
     rdt = residual_dtype or g.dtype
-    dx = torch.empty_like(g) if dx is None else dx
+    if rdt not in _res_dtypes(g):
+        raise ValueError(f"residual_dtype must be {g.dtype} or torch.float32, got {rdt}")
+    dev = _gpu(stream, ("g", g))
+    dx = _out(dx, "dx", (T, H), g.dtype, dev)
     if dresidual is True:
-        dresidual = torch.empty((T, H), dtype=rdt, device=g.device)
-    elif dresidual is False:
+        dresidual = torch.empty((T, H), dtype=rdt, device=dev)
+    elif dresidual is False or dresidual is None:
         dresidual = None
-    dbias = _grad_out(dbias, H, g.device)
-    nws = mb_bias_dropout_add_bwd_workspace(T, H, g.dtype, dbias is not None)
-    if ws is None and nws:
-        ws = torch.empty(nws, dtype=torch.uint8, device=g.device)
+    else:
+        _on(dev, "dresidual", _need(dresidual, "dresidual", (T, H), (rdt,)))
+    dbias = _grad_out(dbias, "dbias", H, dev)
+    ws, nws = _ws(ws, mb_bias_dropout_add_bwd_workspace(T, H, g.dtype, dbias is not None), dev)
     _check("mb_bias_dropout_add_bwd", lib().mb_bias_dropout_add_bwd(
-        _p(g), _p(dx), _p(dresidual), DTYPES[rdt], _p(dbias), _p(ws), ws.numel() if ws is not None else 0, T, H,
-        _dt(g), float(p), int(seed), int(offset), _stream(g, stream)))
+        _p(g), _p(dx), _p(dresidual), DTYPES[rdt], _p(dbias), _p(ws), nws, T, H, _dt(g), float(p), int(seed),
+        int(offset), _stream(dev, stream)))
     return dx, dresidual, dbias
 
 
 def mb_dropout_mask(tokens, hidden, p, seed, offset=0, device="cuda", out=None, stream=None):
+    """The keep bits of (tokens, hidden, p, seed, offset), LSB-first by element index."""
     nbytes = (tokens * hidden + 7) // 8
-    out = torch.empty(nbytes, dtype=torch.uint8, device=device) if out is None else out
+    if out is None:
+        dev = torch.device(device)
+        if dev.type != "cuda":
+            raise ValueError(f"the mask is computed on a GPU, not on {dev}")
+        out = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _need(out, "out", (nbytes,), (torch.uint8,))
+    dev = _gpu(stream, ("out", out))
     _check("mb_dropout_mask", lib().mb_dropout_mask(_p(out), tokens, hidden, float(p), int(seed), int(offset),
-                                                    _stream(out, stream)))
+                                                    _stream(dev, stream)))
     return out
 
 
 # ------------------------------------------------------------------ gated units
 
 def _glu_shapes(inp):
-    T, H2 = _rows(inp, "in")
+    T, H2 = _rows2d(inp, "in")
     if H2 % 2:
         raise ValueError("gated input needs an even number of columns")
     return T, H2 // 2
 
 
+def _weights_dtype(weights, inp):
+    return _dt(weights) if weights is not None else _dt(inp)
+
+
 def mb_bias_swiglu_fwd(inp, bias=None, weights=None, out=None, stream=None):
+    """silu(a) * b (* weights[t]) of the split input row plus bias."""
     T, H = _glu_shapes(inp)
-    _vec(bias, 2 * H, "bias")
-    _vec(weights, T, "weights")
-    out = torch.empty((T, H), dtype=inp.dtype, device=inp.device) if out is None else out
-    wdt = _dt(weights) if weights is not None else _dt(inp)
+    _opt(bias, "bias", (2 * H,), (inp.dtype,))
+    _opt(weights, "weights", (T,), (inp.dtype, torch.float32))
+    dev = _gpu(stream, ("in", inp), ("bias", bias), ("weights", weights))
+    out = _out(out, "out", (T, H), inp.dtype, dev)
     _check("mb_bias_swiglu_fwd", lib().mb_bias_swiglu_fwd(
-        _p(inp), _p(bias), _p(weights), wdt, _p(out), T, H, _dt(inp), _stream(inp, stream)))
+        _p(inp), _p(bias), _p(weights), _weights_dtype(weights, inp), _p(out), T, H, _dt(inp),
+        _stream(dev, stream)))
     return out
 
 
 def mb_bias_geglu_fwd(inp, bias=None, out=None, stream=None):
+    """gelu_tanh(a) * b of the split input row plus bias."""
     T, H = _glu_shapes(inp)
-    _vec(bias, 2 * H, "bias")
-    out = torch.empty((T, H), dtype=inp.dtype, device=inp.device) if out is None else out
+    _opt(bias, "bias", (2 * H,), (inp.dtype,))
+    dev = _gpu(stream, ("in", inp), ("bias", bias))
+    out = _out(out, "out", (T, H), inp.dtype, dev)
     _check("mb_bias_geglu_fwd", lib().mb_bias_geglu_fwd(_p(inp), _p(bias), _p(out), T, H, _dt(inp),
-                                                        _stream(inp, stream)))
+                                                        _stream(dev, stream)))
     return out
 
 
@@ -273,47 +377,37 @@ def mb_bias_glu_bwd_workspace(tokens, hidden, dtype, with_dbias=True, with_dweig
                                                int(bool(with_dweights))))
 
 
-def _grad_out(flag, n, device):
-    if flag is True:
-        return torch.empty(n, dtype=torch.float32, device=device)
-    return None if flag is False or flag is None else flag
-
-
 def mb_bias_swiglu_bwd(g, inp, bias=None, weights=None, din=None, dbias=True, dweights=None, ws=None,
                        stream=None):
     """Returns (din, dbias or None, dweights or None). dweights defaults to True when weights are given."""
     T, H = _glu_shapes(inp)
-    _rows(g, "g", H)
-    _vec(bias, 2 * H, "bias")
-    _vec(weights, T, "weights")
+    _need(g, "g", (T, H), (inp.dtype,))
+    _opt(bias, "bias", (2 * H,), (inp.dtype,))
+    _opt(weights, "weights", (T,), (inp.dtype, torch.float32))
+    dev = _gpu(stream, ("in", inp), ("g", g), ("bias", bias), ("weights", weights))
     if dweights is None:
         dweights = weights is not None
-    din = torch.empty_like(inp) if din is None else din
-    dbias = _grad_out(dbias, 2 * H, inp.device)
-    dweights = _grad_out(dweights, T, inp.device)
-    nws = mb_bias_glu_bwd_workspace(T, H, inp.dtype, dbias is not None, dweights is not None)
-    if ws is None and nws:
-        ws = torch.empty(nws, dtype=torch.uint8, device=inp.device)
-    wdt = _dt(weights) if weights is not None else _dt(inp)
+    din = _out(din, "din", (T, 2 * H), inp.dtype, dev)
+    dbias = _grad_out(dbias, "dbias", 2 * H, dev)
+    dweights = _grad_out(dweights, "dweights", T, dev)
+    ws, nws = _ws(ws, mb_bias_glu_bwd_workspace(T, H, inp.dtype, dbias is not None, dweights is not None), dev)
     _check("mb_bias_swiglu_bwd", lib().mb_bias_swiglu_bwd(
-        _p(g), _p(inp), _p(bias), _p(weights), wdt, _p(din), _p(dbias), _p(dweights), _p(ws),
-        ws.numel() if ws is not None else 0, T, H, _dt(inp), _stream(inp, stream)))
+        _p(g), _p(inp), _p(bias), _p(weights), _weights_dtype(weights, inp), _p(din), _p(dbias), _p(dweights),
+        _p(ws), nws, T, H, _dt(inp), _stream(dev, stream)))
     return din, dbias, dweights
 
 
 def mb_bias_geglu_bwd(g, inp, bias=None, din=None, dbias=True, ws=None, stream=None):
     """Returns (din, dbias or None)."""
     T, H = _glu_shapes(inp)
-    _rows(g, "g", H)
-    _vec(bias, 2 * H, "bias")
-    din = torch.empty_like(inp) if din is None else din
-    dbias = _grad_out(dbias, 2 * H, inp.device)
-    nws = mb_bias_glu_bwd_workspace(T, H, inp.dtype, dbias is not None, False)
-    if ws is None and nws:
-        ws = torch.empty(nws, dtype=torch.uint8, device=inp.device)
+    _need(g, "g", (T, H), (inp.dtype,))
+    _opt(bias, "bias", (2 * H,), (inp.dtype,))
+    dev = _gpu(stream, ("in", inp), ("g", g), ("bias", bias))
+    din = _out(din, "din", (T, 2 * H), inp.dtype, dev)
+    dbias = _grad_out(dbias, "dbias", 2 * H, dev)
+    ws, nws = _ws(ws, mb_bias_glu_bwd_workspace(T, H, inp.dtype, dbias is not None, False), dev)
     _check("mb_bias_geglu_bwd", lib().mb_bias_geglu_bwd(
-        _p(g), _p(inp), _p(bias), _p(din), _p(dbias), _p(ws), ws.numel() if ws is not None else 0, T, H,
-        _dt(inp), _stream(inp, stream)))
+        _p(g), _p(inp), _p(bias), _p(din), _p(dbias), _p(ws), nws, T, H, _dt(inp), _stream(dev, stream)))
     return din, dbias
 
 
@@ -325,28 +419,29 @@ def mb_add_layer_norm_fwd(x, residual, gamma, beta=None, eps=1e-5, zero_centered
     Returns (y, h or None, mean or None, rstd or None). h_out=True allocates h
     (False skips it; a tensor, e.g. x itself, receives it); stats=True
     allocates the fp32 mean / rstd the backward needs (or pass the pair)."""
-    T, H = _rows(x, "x")
-    _rows(residual, "residual", H)
-    if residual.shape[0] != T:
-        raise ValueError("residual must have x's shape")
-    _vec(gamma, H, "gamma")
-    _vec(beta, H, "beta")
+    T, H = _rows2d(x, "x")
+    _need(residual, "residual", (T, H), _res_dtypes(x))
+    _need(gamma, "gamma", (H,), (x.dtype,))
+    _opt(beta, "beta", (H,), (x.dtype,))
+    dev = _gpu(stream, ("x", x), ("residual", residual), ("gamma", gamma), ("beta", beta))
     if h_out is True:
         h_out = torch.empty_like(x)
-    elif h_out is False:
+    elif h_out is False or h_out is None:
         h_out = None
-    y = torch.empty_like(x) if y is None else y
+    else:
+        _out(h_out, "h_out", (T, H), x.dtype, dev)
+    y = _out(y, "y", (T, H), x.dtype, dev)
     mean = rstd = None
     if stats is True:
-        mean = torch.empty(T, dtype=torch.float32, device=x.device)
-        rstd = torch.empty(T, dtype=torch.float32, device=x.device)
+        mean = torch.empty(T, dtype=torch.float32, device=dev)
+        rstd = torch.empty(T, dtype=torch.float32, device=dev)
     elif stats:
         mean, rstd = stats
-        _vec(mean, T, "mean")
-        _vec(rstd, T, "rstd")
+        _grad_out(mean, "mean", T, dev)
+        _grad_out(rstd, "rstd", T, dev)
     _check("mb_add_layer_norm_fwd", lib().mb_add_layer_norm_fwd(
         _p(x), _p(residual), _dt(residual), _p(gamma), _p(beta), float(eps), int(bool(zero_centered_gamma)),
-        _p(h_out), _p(y), _p(mean), _p(rstd), T, H, _dt(x), _stream(x, stream)))
+        _p(h_out), _p(y), _p(mean), _p(rstd), T, H, _dt(x), _stream(dev, stream)))
     return y, h_out, mean, rstd
 
 
@@ -361,28 +456,31 @@ def mb_add_layer_norm_bwd(dy, h, gamma, mean, rstd, zero_centered_gamma=False, d
     """Returns (dx, dresidual or None, dgamma or None, dbeta or None).
     residual_dtype (default: dh_in's dtype, else h's) is the dtype of dh_in and
     dresidual; dresidual=True allocates it."""
-    T, H = _rows(h, "h")
-    _rows(dy, "dy", H)
-    _vec(gamma, H, "gamma")
-    _vec(mean, T, "mean")
-    _vec(rstd, T, "rstd")
-    rdt = residual_dtype or (dh_in.dtype if dh_in is not None else h.dtype)
-    if dh_in is not None:
-        _rows(dh_in, "dh_in", H)
-    dx = torch.empty_like(h) if dx is None else dx
+    T, H = _rows2d(h, "h")
+    _need(dy, "dy", (T, H), (h.dtype,))
+    _need(gamma, "gamma", (H,), (h.dtype,))
+    _need(mean, "mean", (T,), (torch.float32,))
+    _need(rstd, "rstd", (T,), (torch.float32,))
+    rdt = residual_dtype or (dh_in.dtype if isinstance(dh_in, torch.Tensor) else h.dtype)
+    if rdt not in _res_dtypes(h):
+        raise ValueError(f"residual_dtype must be {h.dtype} or torch.float32, got {rdt}")
+    _opt(dh_in, "dh_in", (T, H), (rdt,))
+    dev = _gpu(stream, ("h", h), ("dy", dy), ("gamma", gamma), ("mean", mean), ("rstd", rstd),
+               ("dh_in", dh_in))
+    dx = _out(dx, "dx", (T, H), h.dtype, dev)
     if dresidual is True:
-        dresidual = torch.empty((T, H), dtype=rdt, device=h.device)
-    elif dresidual is False:
+        dresidual = torch.empty((T, H), dtype=rdt, device=dev)
+    elif dresidual is False or dresidual is None:
         dresidual = None
-    dgamma = _grad_out(dgamma, H, h.device)
-    dbeta = _grad_out(dbeta, H, h.device)
-    nws = mb_add_layer_norm_bwd_workspace(T, H, h.dtype, rdt, dgamma is not None or dbeta is not None)
-    if ws is None and nws:
-        ws = torch.empty(nws, dtype=torch.uint8, device=h.device)
+    else:
+        _out(dresidual, "dresidual", (T, H), rdt, dev)
+    dgamma = _grad_out(dgamma, "dgamma", H, dev)
+    dbeta = _grad_out(dbeta, "dbeta", H, dev)
+    ws, nws = _ws(ws, mb_add_layer_norm_bwd_workspace(T, H, h.dtype, rdt, dgamma is not None or dbeta is not None),
+                  dev)
     _check("mb_add_layer_norm_bwd", lib().mb_add_layer_norm_bwd(
         _p(dy), _p(h), _p(gamma), _p(mean), _p(rstd), int(bool(zero_centered_gamma)), _p(dh_in), DTYPES[rdt],
-        _p(dx), _p(dresidual), _p(dgamma), _p(dbeta), _p(ws), ws.numel() if ws is not None else 0, T, H,
-        _dt(h), _stream(h, stream)))
+        _p(dx), _p(dresidual), _p(dgamma), _p(dbeta), _p(ws), nws, T, H, _dt(h), _stream(dev, stream)))
     return dx, dresidual, dgamma, dbeta
 
 
@@ -390,12 +488,13 @@ def mb_add_layer_norm_bwd(dy, h, gamma, mean, rstd, zero_centered_gamma=False, d
 
 def mb_weighted_squared_relu_fwd(x, weights=None, out=None, stream=None):
     """relu(x)^2 * weights[t] (weights None: the plain squared ReLU); out=x runs in place."""
-    T, H = _rows(x, "x")
-    _vec(weights, T, "weights")
-    out = torch.empty_like(x) if out is None else out
+    T, H = _rows2d(x, "x")
+    _opt(weights, "weights", (T,), _FLOAT)
+    dev = _gpu(stream, ("x", x), ("weights", weights))
+    out = _out(out, "out", (T, H), x.dtype, dev)
     wdt = _dt(weights) if weights is not None else 0
     _check("mb_weighted_squared_relu_fwd", lib().mb_weighted_squared_relu_fwd(
-        _p(x), _p(weights), wdt, _p(out), T, H, _dt(x), _stream(x, stream)))
+        _p(x), _p(weights), wdt, _p(out), T, H, _dt(x), _stream(dev, stream)))
     return out
 
 
@@ -405,18 +504,16 @@ def mb_weighted_squared_relu_bwd_workspace(tokens, hidden, dtype, with_dweights=
 
 def mb_weighted_squared_relu_bwd(g, x, weights=None, dx=None, dweights=None, ws=None, stream=None):
     """Returns (dx, dweights or None); dweights defaults to True when weights are given."""
-    T, H = _rows(x, "x")
-    _rows(g, "g", H)
-    _vec(weights, T, "weights")
+    T, H = _rows2d(x, "x")
+    _need(g, "g", (T, H), (x.dtype,))
+    _opt(weights, "weights", (T,), _FLOAT)
+    dev = _gpu(stream, ("x", x), ("g", g), ("weights", weights))
     if dweights is None:
         dweights = weights is not None
-    dx = torch.empty_like(x) if dx is None else dx
-    dweights = _grad_out(dweights, T, x.device)
-    nws = mb_weighted_squared_relu_bwd_workspace(T, H, x.dtype, dweights is not None)
-    if ws is None and nws:
-        ws = torch.empty(nws, dtype=torch.uint8, device=x.device)
+    dx = _out(dx, "dx", (T, H), x.dtype, dev)
+    dweights = _grad_out(dweights, "dweights", T, dev)
+    ws, nws = _ws(ws, mb_weighted_squared_relu_bwd_workspace(T, H, x.dtype, dweights is not None), dev)
     wdt = _dt(weights) if weights is not None else 0
     _check("mb_weighted_squared_relu_bwd", lib().mb_weighted_squared_relu_bwd(
-        _p(g), _p(x), _p(weights), wdt, _p(dx), _p(dweights), _p(ws), ws.numel() if ws is not None else 0, T, H,
-        _dt(x), _stream(x, stream)))
+        _p(g), _p(x), _p(weights), wdt, _p(dx), _p(dweights), _p(ws), nws, T, H, _dt(x), _stream(dev, stream)))
     return dx, dweights

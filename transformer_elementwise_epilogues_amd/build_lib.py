@@ -20,6 +20,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "libmb")
 LIB = os.path.join(PKG, "libmb.so")
+# the benchmark's streaming-ceiling kernel: a library of its own, outside the ABI
+STREAM_SOURCES = ["mb_stream.hip"]
+STREAM_LIB = os.path.join(PKG, "libmb_stream.so")
 
 SOURCES = ["mb_gelu.hip", "mb_bda.hip", "mb_glu.hip", "mb_reduce.hip", "mb_ln.hip", "mb_sqrelu.hip", "mb_abi.cpp"]
 ARCH = "gfx950"
@@ -47,11 +50,11 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra_flags=(), out: str = LIB, verbose: bool = False) -> str:
+def build(extra_flags=(), out: str = LIB, verbose: bool = False, sources=SOURCES) -> str:
     """Compile every source and link libmb.so (always rebuilds)."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra_flags), SOURCES))
+    with ThreadPoolExecutor(len(sources)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, extra_flags), sources))
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -63,5 +66,11 @@ def build(extra_flags=(), out: str = LIB, verbose: bool = False) -> str:
     return out
 
 
+def build_stream(extra_flags=(), verbose: bool = False) -> str:
+    """The benchmark's streaming-ceiling library, libmb_stream.so."""
+    return build(extra_flags, out=STREAM_LIB, verbose=verbose, sources=STREAM_SOURCES)
+
+
 if __name__ == "__main__":
     build(extra_flags=sys.argv[1:], verbose=True)
+    build_stream(extra_flags=sys.argv[1:], verbose=True)

@@ -185,35 +185,56 @@ size_t mb_bias_gelu_erf_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t
   return gelu_bwd_ws(true, tokens, hidden, dt, with_dbias);
 }
 
+// Checks shared by the GeLU backward entry points, apart from the workspace
+// size: dtype, shape, required pointers, alignment and aliasing (wsb: the
+// caller's workspace, or none).
+static mb_status_t gelu_bwd_check(const void* g, const void* y, const void* bias, void* dgrad, float* dbias,
+                                  const Buf& wsb, int64_t tokens, int64_t hidden, mb_dtype_t dt) {
+  if (!dt_ok(dt)) return MB_ERR_DTYPE;
+  if (mb_status_t st = check_shape(tokens, hidden, dt)) return st;
+  const size_t tb = static_cast<size_t>(tokens) * hidden * esize(dt), bb = hidden * esize(dt);
+  if (!need(g, tb) || !need(y, tb) || !need(dgrad, tb)) return MB_ERR_NULL;
+  if (!aligned(g, 16) || !aligned(y, 16) || !aligned(dgrad, 16) || !aligned(bias, 16) || !aligned(dbias, 4) ||
+      (wsb.bytes && !aligned(wsb.p, 16)))
+    return MB_ERR_ALIGN;
+  if (!aliasing_ok({{dgrad, tb}, {dbias, dbias ? static_cast<size_t>(hidden) * 4 : 0}, wsb},
+                   {{g, tb}, {y, tb}, {bias, bias ? bb : 0}}, {{0, 0}, {0, 1}}))
+    return MB_ERR_ALIAS;
+  return MB_OK;
+}
+
+// The launches of a checked GeLU backward with tokens > 0: the fused pass
+// (partial rows into `partials` when dbias is requested), then the ordered
+// column sum (through `tmp` when there are more than 512 partial rows).
+static mb_status_t gelu_bwd_run(bool exact, const void* g, const void* y, const void* bias, void* dgrad,
+                                float* dbias, float* partials, float* tmp, const mb::Tiling& t, int64_t hidden,
+                                mb_dtype_t dt, hipStream_t s) {
+  if (hipError_t e = mb::launch_gelu_bwd(dt, exact, g, y, bias, dgrad, dbias ? partials : nullptr, t, s))
+    return hip_status(e);
+  if (dbias)
+    if (hipError_t e = mb::launch_colsum_tall(partials, t.G, hidden, tmp, dbias, s)) return hip_status(e);
+  return finish();
+}
+
 static mb_status_t gelu_bwd_common(bool exact, const void* g, const void* y, const void* bias, void* dgrad,
                                    float* dbias, void* ws, size_t ws_bytes, int64_t tokens, int64_t hidden,
                                    mb_dtype_t dt, hipStream_t s) {
   if (!dt_ok(dt)) return MB_ERR_DTYPE;
   if (mb_status_t st = check_shape(tokens, hidden, dt)) return st;
-  const size_t tb = static_cast<size_t>(tokens) * hidden * esize(dt), bb = hidden * esize(dt);
-  if (!need(g, tb) || !need(y, tb) || !need(dgrad, tb)) return MB_ERR_NULL;
   const size_t need_ws = gelu_bwd_ws(exact, tokens, hidden, dt, dbias != nullptr);
-  if (!aligned(g, 16) || !aligned(y, 16) || !aligned(dgrad, 16) || !aligned(bias, 16) || !aligned(dbias, 4) ||
-      (need_ws && !aligned(ws, 16)))
-    return MB_ERR_ALIGN;
+  if (mb_status_t st = gelu_bwd_check(g, y, bias, dgrad, dbias, Buf{need_ws ? ws : nullptr, need_ws}, tokens,
+                                      hidden, dt))
+    return st;
   if (need_ws && (!ws || ws_bytes < need_ws)) return MB_ERR_WORKSPACE;
-  const Buf wsb{need_ws ? ws : nullptr, need_ws};
-  if (!aliasing_ok({{dgrad, tb}, {dbias, dbias ? static_cast<size_t>(hidden) * 4 : 0}, wsb},
-                   {{g, tb}, {y, tb}, {bias, bias ? bb : 0}}, {{0, 0}, {0, 1}}))
-    return MB_ERR_ALIAS;
   if (tokens == 0) {
     if (!dbias) return MB_OK;
     if (hipError_t e = mb::launch_fill_zero(dbias, hidden, s)) return hip_status(e);
     return finish();
   }
   const mb::Tiling t = gelu_bwd_tiling(exact, tokens, hidden, dt);
-  float* partials = dbias ? static_cast<float*>(ws) : nullptr;
-  if (hipError_t e = mb::launch_gelu_bwd(dt, exact, g, y, bias, dgrad, partials, t, s)) return hip_status(e);
-  if (dbias) {
-    float* tmp = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(col_partials_bytes(t, hidden), 256));
-    if (hipError_t e = mb::launch_colsum_tall(partials, t.G, hidden, tmp, dbias, s)) return hip_status(e);
-  }
-  return finish();
+  float* partials = static_cast<float*>(ws);
+  float* tmp = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(col_partials_bytes(t, hidden), 256));
+  return gelu_bwd_run(exact, g, y, bias, dgrad, dbias, partials, tmp, t, hidden, dt, s);
 }
 
 mb_status_t mb_bias_gelu_bwd(const void* g, const void* y, const void* bias, void* dgrad, float* dbias, void* ws,

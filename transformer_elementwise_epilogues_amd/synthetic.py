@@ -133,4 +133,21 @@ WORKLOADS = {
         "g": Tensor(1, (8192, 14336), "bf16"),
         "weights": Tensor(2, (8192,), "f32", dist="uniform"),
     }),
+    # the same at the widest hidden sizes of the persistent-kernel list
+    "add_ln_bf16_8192x16384": _w(8, "add_ln_bf16_8192x16384", {
+        "x": Tensor(0, (8192, 16384), "bf16"),
+        "residual": Tensor(1, (8192, 16384), "bf16"),
+        "gamma": Tensor(2, (16384,), "bf16", sigma=0.02),
+        "beta": Tensor(3, (16384,), "bf16", sigma=0.02),
+        "dy": Tensor(4, (8192, 16384), "bf16"),
+        "dh_in": Tensor(5, (8192, 16384), "bf16"),
+    }, eps=1e-5, zero_centered_gamma=True),
+    "add_ln_bf16_2048x65536": _w(9, "add_ln_bf16_2048x65536", {
+        "x": Tensor(0, (2048, 65536), "bf16"),
+        "residual": Tensor(1, (2048, 65536), "bf16"),
+        "gamma": Tensor(2, (65536,), "bf16", sigma=0.02),
+        "beta": Tensor(3, (65536,), "bf16", sigma=0.02),
+        "dy": Tensor(4, (2048, 65536), "bf16"),
+        "dh_in": Tensor(5, (2048, 65536), "bf16"),
+    }, eps=1e-5, zero_centered_gamma=True),
 }
