@@ -55,7 +55,8 @@ typedef enum {
   MB_ERR_ALIAS = 5,     /* two buffers overlap in a way the entry point forbids */
   MB_ERR_PROB = 6,      /* dropout probability NaN or outside [0, 1]; LayerNorm eps not finite or < 0 */
   MB_ERR_WORKSPACE = 7, /* workspace missing or smaller than the query returned */
-  MB_ERR_HIP = 8        /* the HIP runtime reported an error for the launches */
+  MB_ERR_HIP = 8,       /* the HIP runtime reported an error for the launches */
+  MB_ERR_SCRATCH = 9    /* needs more than the static scratch of mb_bias_gelu_bwd_noalloc */
 } mb_status_t;
 
 /* Human-readable name of a status code (static storage). */
@@ -90,6 +91,26 @@ size_t mb_bias_gelu_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt,
 mb_status_t mb_bias_gelu_bwd(const void* g, const void* y, const void* bias, void* dgrad,
                              float* dbias, void* ws, size_t ws_bytes, int64_t tokens,
                              int64_t hidden, mb_dtype_t dt, hipStream_t s);
+
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation): mb_bias_gelu_bwd
+ * without a workspace argument. It calls no allocating routine; the bias
+ * gradient's partial rows go to a static device array of the library, 16 MiB
+ * per GPU, held from the first call on that GPU
+ * until the process ends. Same arguments, results and errors as
+ * mb_bias_gelu_bwd: dgrad is bit for bit the same; dbias is the same column
+ * sum taken over fewer, larger row groups (the scratch bounds them to
+ * min(512, 16 MiB / (4 hidden)) rows), so it can differ in the last bits.
+ * MB_ERR_SCRATCH when dbias != NULL and one fp32 row of hidden values does
+ * not fit the scratch (hidden > 4194304). Limits: every call on one GPU shares
+ * that GPU's scratch, so calls that overlap in time on one GPU (different
+ * streams, or threads) race and must be serialized by the caller; the first
+ * call on each GPU looks up the scratch address and should not be made under
+ * graph capture. The scratch keeps the last call's contents; nothing in it
+ * needs to start at zero. */
+mb_status_t mb_bias_gelu_bwd_noalloc(const void* g, const void* y, const void* bias, void* dgrad,
+                                     float* dbias, int64_t tokens, int64_t hidden, mb_dtype_t dt,
+                                     hipStream_t s);
 
 /* Exact GeLU [fusions §4.2, the erf definition with its printed constants]:
  *   out = 0.5 z (1 + erf(0.70710678 z)),  z = y + bias;

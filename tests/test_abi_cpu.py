@@ -11,7 +11,7 @@ import transformer_elementwise_epilogues_amd as mb
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mb.h")
-OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, PROB, WORKSPACE = range(8)
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, PROB, WORKSPACE, HIP, SCRATCH = range(10)
 F32, F16, BF16 = 0, 1, 2
 
 
@@ -38,8 +38,9 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_status_strings():
     assert mb.abi_version() == 1
     L = mb.lib()
-    for code in range(9):
+    for code in range(10):
         assert L.mb_status_string(code).startswith(b"MB_")
+    assert b"scratch" in L.mb_status_string(SCRATCH)
 
 
 # Fake, 256-byte aligned "device" addresses: validation never touches them.
@@ -168,3 +169,17 @@ def test_squared_relu_validation():
     assert bw(A, B, None, F32, A, None, None, 0, 0, 512, BF16, None) == OK      # dx over g, empty
     assert bw(A, B, None, F32, A + 16, None, None, 0, 4, 512, BF16, None) == ALIAS
 
+
+def test_gelu_bwd_noalloc_validation():
+    """The entry point without a workspace: the same checks as mb_bias_gelu_bwd,
+    and rows too wide for its static scratch refused before any HIP call."""
+    f = L().mb_bias_gelu_bwd_noalloc
+    assert f(A, B, None, C, D, 4, 63, BF16, None) == SHAPE
+    assert f(A, B, None, C, D, 4, 64, 7, None) == DTYPE
+    assert f(None, B, None, C, D, 4, 64, BF16, None) == NULL
+    assert f(A, B, None, C, D + 2, 4, 64, BF16, None) == ALIGN
+    assert f(A, B, None, C, C + 64, 4, 64, BF16, None) == ALIAS      # dbias inside dgrad
+    assert f(A, B, None, B + 16, None, 4, 64, BF16, None) == ALIAS   # dgrad partly over y
+    wide = (16 << 20) // 4 + 8                                      # one fp32 row exceeds 16 MiB
+    assert f(A, B, None, C, D, 1, wide, BF16, None) == SCRATCH
+    assert f(A, B, None, C, D, 0, wide, BF16, None) == SCRATCH

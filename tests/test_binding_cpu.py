@@ -48,6 +48,7 @@ GOOD_CALLS = {
     "gelu_erf_fwd": lambda: mb.mb_bias_gelu_erf_fwd(z(T, H), z(H)),
     "gelu_bwd": lambda: mb.mb_bias_gelu_bwd(z(T, H), z(T, H), z(H)),
     "gelu_erf_bwd": lambda: mb.mb_bias_gelu_erf_bwd(z(T, H), z(T, H), z(H)),
+    "gelu_bwd_noalloc": lambda: mb.mb_bias_gelu_bwd_noalloc(z(T, H), z(T, H), z(H)),
     "bda_train": lambda: mb.mb_bias_dropout_add_train(z(T, H), z(H), z(T, H, dtype=F32), 0.1, 1),
     "bda_infer": lambda: mb.mb_bias_dropout_add_infer(z(T, H), z(H), z(T, H)),
     "bda_bwd": lambda: mb.mb_bias_dropout_add_bwd(z(T, H), 0.1, 1),
@@ -72,7 +73,7 @@ def test_host_tensors_are_refused(name):
 
 def test_every_entry_point_has_a_host_tensor_case():
     covered = {"mb_bias_gelu_fwd", "mb_bias_gelu_erf_fwd", "mb_bias_gelu_bwd", "mb_bias_gelu_erf_bwd",
-               "mb_bias_dropout_add_train", "mb_bias_dropout_add_infer",
+               "mb_bias_gelu_bwd_noalloc", "mb_bias_dropout_add_train", "mb_bias_dropout_add_infer",
                "mb_bias_dropout_add_bwd", "mb_dropout_mask", "mb_bias_swiglu_fwd", "mb_bias_swiglu_bwd",
                "mb_bias_geglu_fwd", "mb_bias_geglu_bwd", "mb_add_layer_norm_fwd", "mb_add_layer_norm_bwd",
                "mb_weighted_squared_relu_fwd", "mb_weighted_squared_relu_bwd"}
@@ -114,6 +115,7 @@ BAD_CALLS = [
     ("gelu dgrad rows", lambda: mb.mb_bias_gelu_bwd(z(T, H), z(T, H), dgrad=z(T - 1, H))),
     ("gelu dbias length", lambda: mb.mb_bias_gelu_bwd(z(T, H), z(T, H), dbias=z(H - 4, dtype=F32))),
     ("gelu dbias dtype", lambda: mb.mb_bias_gelu_bwd(z(T, H), z(T, H), dbias=z(H))),
+    ("noalloc dbias length", lambda: mb.mb_bias_gelu_bwd_noalloc(z(T, H), z(T, H), dbias=z(H + 4, dtype=F32))),
     ("gelu ws not a tensor", lambda: mb.mb_bias_gelu_bwd(z(T, H), z(T, H), ws=bytearray(64))),
     ("bda out dtype", lambda: mb.mb_bias_dropout_add_train(z(T, H), None, z(T, H), 0.1, 1, out=z(T, H, dtype=F32))),
     ("bda bwd dx rows", lambda: mb.mb_bias_dropout_add_bwd(z(T, H), 0.1, 1, dx=z(T + 1, H))),

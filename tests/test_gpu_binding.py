@@ -28,6 +28,7 @@ MIXED = [
     ("gelu bwd host dbias", lambda s: mb.mb_bias_gelu_bwd(d(T, H), d(T, H), dbias=h(H, dtype=F32), stream=s)),
     ("gelu bwd host ws", lambda s: mb.mb_bias_gelu_bwd(d(T, H), d(T, H), ws=h(1 << 20, dtype=torch.uint8),
                                                        stream=s)),
+    ("noalloc host bias", lambda s: mb.mb_bias_gelu_bwd_noalloc(d(T, H), d(T, H), h(H), stream=s)),
     ("bda host residual", lambda s: mb.mb_bias_dropout_add_train(d(T, H), None, h(T, H, dtype=F32), 0.1, 1,
                                                                  stream=s)),
     ("bda infer host bias", lambda s: mb.mb_bias_dropout_add_infer(d(T, H), h(H), d(T, H), stream=s)),

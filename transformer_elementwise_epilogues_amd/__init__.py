@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "MBError", "lib", "abi_version",
-    "mb_bias_gelu_fwd", "mb_bias_gelu_bwd", "mb_bias_gelu_bwd_workspace",
+    "mb_bias_gelu_fwd", "mb_bias_gelu_bwd", "mb_bias_gelu_bwd_workspace", "mb_bias_gelu_bwd_noalloc",
     "mb_bias_gelu_erf_fwd", "mb_bias_gelu_erf_bwd", "mb_bias_gelu_erf_bwd_workspace",
     "mb_bias_dropout_add_train", "mb_bias_dropout_add_infer", "mb_dropout_mask",
     "mb_bias_dropout_add_bwd", "mb_bias_dropout_add_bwd_workspace",
@@ -59,6 +59,7 @@ def lib() -> ctypes.CDLL:
                 "mb_bias_gelu_fwd": ([P, P, P, I64, I64, I, P], I),
                 "mb_bias_gelu_bwd_workspace": ([I64, I64, I, I], SZ),
                 "mb_bias_gelu_bwd": ([P, P, P, P, P, P, SZ, I64, I64, I, P], I),
+                "mb_bias_gelu_bwd_noalloc": ([P, P, P, P, P, I64, I64, I, P], I),
                 "mb_bias_gelu_erf_fwd": ([P, P, P, I64, I64, I, P], I),
                 "mb_bias_gelu_erf_bwd": ([P, P, P, P, P, P, SZ, I64, I64, I, P], I),
                 "mb_bias_gelu_erf_bwd_workspace": ([I64, I64, I, I], SZ),
@@ -259,6 +260,17 @@ def mb_bias_gelu_bwd(g, y, bias=None, dgrad=None, dbias=True, ws=None, stream=No
 def mb_bias_gelu_erf_bwd(g, y, bias=None, dgrad=None, dbias=True, ws=None, stream=None):
     """Backward of the exact (erf) GeLU; returns (dgrad, dbias or None)."""
     return _gelu_bwd("mb_bias_gelu_erf_bwd", g, y, bias, dgrad, dbias, ws, stream)
+
+
+def mb_bias_gelu_bwd_noalloc(g, y, bias=None, dgrad=None, dbias=True, stream=None):
+    """mb_bias_gelu_bwd without a workspace: the library's static device
+    scratch holds the bias gradient's partial rows (the C entry point
+    allocates nothing; outputs not passed here are still allocated by torch).
+    Returns (dgrad, dbias or None)."""
+    T, H, dev, dgrad, dbias = _gelu_bwd_args(g, y, bias, dgrad, dbias, stream)
+    _check("mb_bias_gelu_bwd_noalloc", lib().mb_bias_gelu_bwd_noalloc(
+        _p(g), _p(y), _p(bias), _p(dgrad), _p(dbias), T, H, _dt(y), _stream(dev, stream)))
+    return dgrad, dbias
 
 
 # ------------------------------------------------------------------ dropout-add

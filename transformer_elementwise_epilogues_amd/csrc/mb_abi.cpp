@@ -130,6 +130,8 @@ const char* mb_status_string(mb_status_t status) {
     case MB_ERR_PROB: return "MB_ERR_PROB: dropout probability is NaN or outside [0, 1]";
     case MB_ERR_WORKSPACE: return "MB_ERR_WORKSPACE: workspace missing or too small";
     case MB_ERR_HIP: return "MB_ERR_HIP: the HIP runtime reported an error";
+    case MB_ERR_SCRATCH:
+      return "MB_ERR_SCRATCH: the problem needs more than the static scratch of the no-allocation entry point";
   }
   return "unknown mb_status_t";
 }
@@ -246,6 +248,35 @@ mb_status_t mb_bias_gelu_erf_bwd(const void* g, const void* y, const void* bias,
                                  void* ws, size_t ws_bytes, int64_t tokens, int64_t hidden, mb_dtype_t dt,
                                  hipStream_t s) {
   return gelu_bwd_common(true, g, y, bias, dgrad, dbias, ws, ws_bytes, tokens, hidden, dt, s);
+}
+
+// The variant that allocates nothing: the partial rows go to the library's
+// static device scratch (MB_NOALLOC_SCRATCH_BYTES per device, mb_noalloc.hip).
+// Its launch shape is the tanh backward's, with the row groups capped so that
+// their partial rows fit the scratch and stay within one column-sum launch
+// (at most 512), so no chunk-sum buffer is needed. Nothing in the scratch has
+// to start at zero: the fused pass writes every partial row the column sum
+// reads.
+mb_status_t mb_bias_gelu_bwd_noalloc(const void* g, const void* y, const void* bias, void* dgrad, float* dbias,
+                                     int64_t tokens, int64_t hidden, mb_dtype_t dt, hipStream_t s) {
+  if (mb_status_t st = gelu_bwd_check(g, y, bias, dgrad, dbias, Buf{nullptr, 0}, tokens, hidden, dt)) return st;
+  const int64_t row_bytes = hidden * 4;  // one fp32 partial row
+  const int64_t max_rows = static_cast<int64_t>(MB_NOALLOC_SCRATCH_BYTES) / row_bytes;
+  if (dbias && max_rows < 1) return MB_ERR_SCRATCH;
+  if (tokens == 0) {
+    if (!dbias) return MB_OK;
+    if (hipError_t e = mb::launch_fill_zero(dbias, hidden, s)) return hip_status(e);
+    return finish();
+  }
+  mb::Tiling t = gelu_bwd_tiling(false, tokens, hidden, dt);
+  if (!dbias) return gelu_bwd_run(false, g, y, bias, dgrad, nullptr, nullptr, nullptr, t, hidden, dt, s);
+  int64_t G = t.G;
+  if (G > max_rows) G = max_rows;
+  if (G > 512) G = 512;
+  t.G = static_cast<int>(G);
+  void* scratch = nullptr;
+  if (hipError_t e = mb::noalloc_scratch(s, &scratch)) return hip_status(e);
+  return gelu_bwd_run(false, g, y, bias, dgrad, dbias, static_cast<float*>(scratch), nullptr, t, hidden, dt, s);
 }
 
 // ------------------------------------------------------------------ dropout-add

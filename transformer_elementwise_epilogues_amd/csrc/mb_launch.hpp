@@ -134,6 +134,15 @@ struct Tiling {
 
 Tiling plan_tiling(int64_t T, int nvec, int target_blocks);
 
+// Bytes of the static device scratch that holds the bias gradient's partial
+// rows for the entry point that allocates nothing (one copy per device).
+#ifndef MB_NOALLOC_SCRATCH_BYTES
+#define MB_NOALLOC_SCRATCH_BYTES (16u << 20)
+#endif
+// Device address of that scratch on the device of stream s; looked up once
+// per device (thread-safe), never allocated.
+hipError_t noalloc_scratch(hipStream_t s, void** ptr);
+
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 // One column sum: out[c] = sum over r < R of in[r * C + c], r ascending (fp32).
 struct ColSum {
