@@ -1,0 +1,32 @@
+// Prints launch plans (mb_plan.cpp, host arithmetic only) for queries read
+// from stdin, one per line:
+//   tiling T nvec target_blocks cus min_rows   -> "tiling strips G"
+//   ln T H dt rdt target_blocks nv_pref cus     -> "ln nvec shape tpr nv grid split dgb_G partial_rows"
+#include <cstdio>
+#include <cstring>
+
+#include "mb_plan.hpp"
+
+int main() {
+  char kind[16];
+  while (std::scanf("%15s", kind) == 1) {
+    if (std::strcmp(kind, "tiling") == 0) {
+      long long T;
+      int nvec, target, cus, min_rows;
+      if (std::scanf("%lld %d %d %d %d", &T, &nvec, &target, &cus, &min_rows) != 5) return 2;
+      const mb::Tiling t = mb::plan_tiling(T, nvec, target, cus, min_rows);
+      std::printf("tiling %d %d\n", t.strips, t.G);
+    } else if (std::strcmp(kind, "ln") == 0) {
+      long long T, H;
+      int dt, rdt, target, nv_pref, cus;
+      if (std::scanf("%lld %lld %d %d %d %d %d", &T, &H, &dt, &rdt, &target, &nv_pref, &cus) != 7) return 2;
+      const mb::LnPlan p = mb::plan_ln(T, H, dt, rdt, target, nv_pref, cus);
+      const int tpr = p.shape >= 0 ? mb::kLnShapes[p.shape].tpr : 0, nv = p.shape >= 0 ? mb::kLnShapes[p.shape].nv : 0;
+      std::printf("ln %d %d %d %d %d %d %d %d\n", p.nvec, p.shape, tpr, nv, p.grid, p.split ? 1 : 0, p.dgb.G,
+                  p.partial_rows);
+    } else {
+      return 3;
+    }
+  }
+  return 0;
+}

@@ -25,7 +25,7 @@ STREAM_SOURCES = ["mb_stream.hip"]
 STREAM_LIB = os.path.join(PKG, "libmb_stream.so")
 
 SOURCES = ["mb_gelu.hip", "mb_bda.hip", "mb_glu.hip", "mb_reduce.hip", "mb_ln.hip", "mb_sqrelu.hip", "mb_noalloc.hip",
-           "mb_abi.cpp"]
+           "mb_plan.cpp", "mb_abi.cpp"]
 ARCH = "gfx950"
 
 

@@ -2,6 +2,7 @@
 // the host, before any HIP call), workspace sizing, and the launches.
 #include "mb.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <initializer_list>
@@ -85,6 +86,33 @@ bool need(const void* p, size_t bytes) { return bytes == 0 || p != nullptr; }
 
 mb_status_t hip_status(hipError_t e) { return e == hipSuccess ? MB_OK : MB_ERR_HIP; }
 
+// Compute units of the device that runs the work: the device of stream s
+// (for_stream), else the calling thread's current device (the workspace
+// queries take no stream). Queried once per device; mb::kTunedCUs when no
+// device answers (no GPU: the queries and the host-side checks still work,
+// and the failed query's error is cleared so that no later call reports it).
+int device_cus(hipStream_t s, bool for_stream) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = -1;
+  const hipError_t e = for_stream ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return mb::kTunedCUs;
+  }
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) {
+    (void)hipGetLastError();
+    return mb::kTunedCUs;
+  }
+  cache[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+
+int stream_cus(hipStream_t s) { return device_cus(s, true); }
+int current_cus() { return device_cus(nullptr, false); }
+
 mb_status_t finish() { return hip_status(hipGetLastError()); }
 
 int nvec_of(int64_t H, mb_dtype_t dt) { return static_cast<int>(static_cast<uint64_t>(H) * esize(dt) / 16); }
@@ -149,7 +177,7 @@ static mb_status_t gelu_fwd_common(bool exact, const void* y, const void* bias, 
   if (!aligned(y, 16) || !aligned(out, 16) || !aligned(bias, 16)) return MB_ERR_ALIGN;
   if (!aliasing_ok({{out, tb}}, {{y, tb}, {bias, bias ? bb : 0}}, {{0, 0}})) return MB_ERR_ALIAS;
   if (tokens == 0) return MB_OK;
-  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GELU_FWD_BLOCKS);
+  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GELU_FWD_BLOCKS, stream_cus(s));
   if (hipError_t e = mb::launch_gelu_fwd(dt, exact, y, bias, out, t, s)) return hip_status(e);
   return finish();
 }
@@ -168,23 +196,24 @@ mb_status_t mb_bias_gelu_erf_fwd(const void* y, const void* bias, void* out, int
 // heavier on the ALU, runs many more row groups), so each has its workspace
 // query: the partial rows, then (for more than 32 of them) the chunk sums of
 // the ordered two-level column sum.
-static mb::Tiling gelu_bwd_tiling(bool exact, int64_t tokens, int64_t hidden, mb_dtype_t dt) {
-  return mb::plan_tiling(tokens, nvec_of(hidden, dt), exact ? MB_GELU_ERF_BWD_BLOCKS : MB_GELU_BWD_BLOCKS);
+static mb::Tiling gelu_bwd_tiling(bool exact, int64_t tokens, int64_t hidden, mb_dtype_t dt, int cus) {
+  return mb::plan_tiling(tokens, nvec_of(hidden, dt), exact ? MB_GELU_ERF_BWD_BLOCKS : MB_GELU_BWD_BLOCKS, cus,
+                         exact ? MB_GELU_ERF_BWD_MIN_ROWS : MB_GELU_BWD_MIN_ROWS);
 }
 
-static size_t gelu_bwd_ws(bool exact, int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias) {
+static size_t gelu_bwd_ws(bool exact, int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias, int cus) {
   if (!with_dbias || !dt_ok(dt) || check_shape(tokens, hidden, dt) != MB_OK || tokens == 0) return 0;
-  const mb::Tiling t = gelu_bwd_tiling(exact, tokens, hidden, dt);
+  const mb::Tiling t = gelu_bwd_tiling(exact, tokens, hidden, dt, cus);
   return round_up(col_partials_bytes(t, hidden), 256) +
          static_cast<size_t>(mb::colsum_tall_tmp_floats(t.G, hidden)) * 4;
 }
 
 size_t mb_bias_gelu_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias) {
-  return gelu_bwd_ws(false, tokens, hidden, dt, with_dbias);
+  return gelu_bwd_ws(false, tokens, hidden, dt, with_dbias, current_cus());
 }
 
 size_t mb_bias_gelu_erf_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias) {
-  return gelu_bwd_ws(true, tokens, hidden, dt, with_dbias);
+  return gelu_bwd_ws(true, tokens, hidden, dt, with_dbias, current_cus());
 }
 
 // Checks shared by the GeLU backward entry points, apart from the workspace
@@ -223,7 +252,8 @@ static mb_status_t gelu_bwd_common(bool exact, const void* g, const void* y, con
                                    mb_dtype_t dt, hipStream_t s) {
   if (!dt_ok(dt)) return MB_ERR_DTYPE;
   if (mb_status_t st = check_shape(tokens, hidden, dt)) return st;
-  const size_t need_ws = gelu_bwd_ws(exact, tokens, hidden, dt, dbias != nullptr);
+  const int cus = stream_cus(s);
+  const size_t need_ws = gelu_bwd_ws(exact, tokens, hidden, dt, dbias != nullptr, cus);
   if (mb_status_t st = gelu_bwd_check(g, y, bias, dgrad, dbias, Buf{need_ws ? ws : nullptr, need_ws}, tokens,
                                       hidden, dt))
     return st;
@@ -233,7 +263,7 @@ static mb_status_t gelu_bwd_common(bool exact, const void* g, const void* y, con
     if (hipError_t e = mb::launch_fill_zero(dbias, hidden, s)) return hip_status(e);
     return finish();
   }
-  const mb::Tiling t = gelu_bwd_tiling(exact, tokens, hidden, dt);
+  const mb::Tiling t = gelu_bwd_tiling(exact, tokens, hidden, dt, cus);
   float* partials = static_cast<float*>(ws);
   float* tmp = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(col_partials_bytes(t, hidden), 256));
   return gelu_bwd_run(exact, g, y, bias, dgrad, dbias, partials, tmp, t, hidden, dt, s);
@@ -268,7 +298,7 @@ mb_status_t mb_bias_gelu_bwd_noalloc(const void* g, const void* y, const void* b
     if (hipError_t e = mb::launch_fill_zero(dbias, hidden, s)) return hip_status(e);
     return finish();
   }
-  mb::Tiling t = gelu_bwd_tiling(false, tokens, hidden, dt);
+  mb::Tiling t = gelu_bwd_tiling(false, tokens, hidden, dt, stream_cus(s));
   if (!dbias) return gelu_bwd_run(false, g, y, bias, dgrad, nullptr, nullptr, nullptr, t, hidden, dt, s);
   int64_t G = t.G;
   if (G > max_rows) G = max_rows;
@@ -299,7 +329,8 @@ static mb_status_t bda_common(const void* x, const void* bias, const void* resid
   const int lanes = static_cast<int>(hidden / mb::bda_elems_per_lane(dt, residual_dt));
   const bool mixed = residual_dt == MB_F32 && dt != MB_F32;
   const mb::Tiling t =
-      mb::plan_tiling(tokens, lanes, !mixed ? MB_BDA_BLOCKS : train ? MB_BDA_MIXED_TRAIN_BLOCKS : MB_BDA_MIXED_BLOCKS);
+      mb::plan_tiling(tokens, lanes, !mixed ? MB_BDA_BLOCKS : train ? MB_BDA_MIXED_TRAIN_BLOCKS : MB_BDA_MIXED_BLOCKS,
+                      stream_cus(s));
   const mb::DropoutArgs d = train ? dropout_args(p, seed, offset) : mb::DropoutArgs{};
   if (hipError_t e = mb::launch_bda(dt, residual_dt, train, x, bias, residual, out, hidden, t, d, s))
     return hip_status(e);
@@ -321,17 +352,21 @@ mb_status_t mb_bias_dropout_add_infer(const void* x, const void* bias, const voi
 // shape depend on the residual dtype (fp32 beside bf16/fp16 or not), which the
 // workspace query does not take: it returns the larger of the two layouts'
 // partial rows.
-static mb::Tiling bda_bwd_tiling(int64_t tokens, int64_t hidden, mb_dtype_t dt, mb_dtype_t residual_dt) {
+static mb::Tiling bda_bwd_tiling(int64_t tokens, int64_t hidden, mb_dtype_t dt, mb_dtype_t residual_dt, int cus) {
   const int lanes = static_cast<int>(hidden / mb::bda_elems_per_lane(dt, residual_dt));
   const bool mixed = residual_dt == MB_F32 && dt != MB_F32;
-  return mb::plan_tiling(tokens, lanes, mixed ? MB_BDA_BWD_MIXED_BLOCKS : MB_BDA_BWD_BLOCKS);
+  return mb::plan_tiling(tokens, lanes, mixed ? MB_BDA_BWD_MIXED_BLOCKS : MB_BDA_BWD_BLOCKS, cus);
+}
+
+static size_t bda_bwd_ws(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias, int cus) {
+  if (!with_dbias || !dt_ok(dt) || check_shape(tokens, hidden, dt) != MB_OK || tokens == 0) return 0;
+  const size_t same = col_partials_bytes(bda_bwd_tiling(tokens, hidden, dt, dt, cus), hidden);
+  const size_t mixed = col_partials_bytes(bda_bwd_tiling(tokens, hidden, dt, MB_F32, cus), hidden);
+  return same > mixed ? same : mixed;
 }
 
 size_t mb_bias_dropout_add_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias) {
-  if (!with_dbias || !dt_ok(dt) || check_shape(tokens, hidden, dt) != MB_OK || tokens == 0) return 0;
-  const size_t same = col_partials_bytes(bda_bwd_tiling(tokens, hidden, dt, dt), hidden);
-  const size_t mixed = col_partials_bytes(bda_bwd_tiling(tokens, hidden, dt, MB_F32), hidden);
-  return same > mixed ? same : mixed;
+  return bda_bwd_ws(tokens, hidden, dt, with_dbias, current_cus());
 }
 
 mb_status_t mb_bias_dropout_add_bwd(const void* g, void* dx, void* dresidual, mb_dtype_t residual_dt, float* dbias,
@@ -344,7 +379,8 @@ mb_status_t mb_bias_dropout_add_bwd(const void* g, void* dx, void* dresidual, mb
   const size_t tb = static_cast<size_t>(tokens) * hidden * esize(dt);
   const size_t rb = static_cast<size_t>(tokens) * hidden * esize(residual_dt);
   if (!need(g, tb) || !need(dx, tb)) return MB_ERR_NULL;
-  const size_t need_ws = mb_bias_dropout_add_bwd_workspace(tokens, hidden, dt, dbias != nullptr);
+  const int cus = stream_cus(s);
+  const size_t need_ws = bda_bwd_ws(tokens, hidden, dt, dbias != nullptr, cus);
   if (!aligned(g, 16) || !aligned(dx, 16) || !aligned(dresidual, 16) || !aligned(dbias, 4) ||
       (need_ws && !aligned(ws, 16)))
     return MB_ERR_ALIGN;
@@ -362,7 +398,7 @@ mb_status_t mb_bias_dropout_add_bwd(const void* g, void* dx, void* dresidual, mb
     if (hipError_t e = mb::launch_fill_zero(dbias, hidden, s)) return hip_status(e);
     return finish();
   }
-  const mb::Tiling t = bda_bwd_tiling(tokens, hidden, dt, residual_dt);
+  const mb::Tiling t = bda_bwd_tiling(tokens, hidden, dt, residual_dt, cus);
   float* partials = dbias ? static_cast<float*>(ws) : nullptr;
   if (hipError_t e = mb::launch_bda_bwd(dt, residual_dt, g, dx, dresidual, partials, hidden, t,
                                         dropout_args(p, seed, offset), s))
@@ -403,7 +439,7 @@ static mb_status_t glu_fwd_common(int act, const void* in, const void* bias, con
     return MB_ERR_ALIGN;
   if (!aliasing_ok({{out, ob}}, {{in, ib}, {bias, bias ? bb : 0}, {weights, wb}}, {})) return MB_ERR_ALIAS;
   if (tokens == 0) return MB_OK;
-  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GLU_FWD_BLOCKS);
+  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GLU_FWD_BLOCKS, stream_cus(s));
   if (hipError_t e = mb::launch_glu_fwd(act, dt, in, bias, weights, weights ? weights_dt : dt, out, hidden, t, s))
     return hip_status(e);
   return finish();
@@ -423,10 +459,13 @@ namespace {
 struct GluWs {
   size_t bias_off, bias_bytes, w_off, w_bytes, total;
 };
-GluWs glu_ws(int64_t tokens, int64_t hidden, mb_dtype_t dt, bool with_dbias, bool with_dw) {
+mb::Tiling glu_bwd_tiling(int64_t tokens, int64_t hidden, mb_dtype_t dt, int cus) {
+  return mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GLU_BWD_BLOCKS, cus);
+}
+GluWs glu_ws(int64_t tokens, int64_t hidden, mb_dtype_t dt, bool with_dbias, bool with_dw, int cus) {
   GluWs w{0, 0, 0, 0, 0};
   if (tokens == 0) return w;
-  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GLU_BWD_BLOCKS);
+  const mb::Tiling t = glu_bwd_tiling(tokens, hidden, dt, cus);
   w.bias_bytes = with_dbias ? col_partials_bytes(t, 2 * hidden) : 0;
   w.w_off = round_up(w.bias_bytes, 256);
   w.w_bytes = with_dw ? static_cast<size_t>(t.strips) * tokens * 4 : 0;
@@ -437,7 +476,7 @@ GluWs glu_ws(int64_t tokens, int64_t hidden, mb_dtype_t dt, bool with_dbias, boo
 
 size_t mb_bias_glu_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias, int with_dweights) {
   if (!dt_ok(dt) || check_shape(tokens, hidden, dt, 2) != MB_OK) return 0;
-  return glu_ws(tokens, hidden, dt, with_dbias != 0, with_dweights != 0).total;
+  return glu_ws(tokens, hidden, dt, with_dbias != 0, with_dweights != 0, current_cus()).total;
 }
 
 static mb_status_t glu_bwd_common(int act, const void* g, const void* in, const void* bias, const void* weights,
@@ -451,7 +490,8 @@ static mb_status_t glu_bwd_common(int act, const void* g, const void* in, const 
   const size_t wb = weights ? static_cast<size_t>(tokens) * esize(weights_dt) : 0;
   if (!need(g, gb) || !need(in, ib) || !need(din, ib)) return MB_ERR_NULL;
   if (dweights && !weights) return MB_ERR_NULL;
-  const GluWs w = glu_ws(tokens, hidden, dt, dbias != nullptr, dweights != nullptr);
+  const int cus = stream_cus(s);
+  const GluWs w = glu_ws(tokens, hidden, dt, dbias != nullptr, dweights != nullptr, cus);
   if (!aligned(g, 16) || !aligned(in, 16) || !aligned(din, 16) || !aligned(bias, 16) || !aligned(dbias, 4) ||
       !aligned(dweights, 4) || (weights && !aligned(weights, esize(weights_dt))) || (w.total && !aligned(ws, 16)))
     return MB_ERR_ALIGN;
@@ -466,7 +506,7 @@ static mb_status_t glu_bwd_common(int act, const void* g, const void* in, const 
     if (hipError_t e = mb::launch_fill_zero(dbias, 2 * hidden, s)) return hip_status(e);
     return finish();
   }
-  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GLU_BWD_BLOCKS);
+  const mb::Tiling t = glu_bwd_tiling(tokens, hidden, dt, cus);
   float* bp = dbias ? static_cast<float*>(ws) : nullptr;
   float* wp = dweights ? reinterpret_cast<float*>(static_cast<char*>(ws) + w.w_off) : nullptr;
   if (hipError_t e = mb::launch_glu_bwd(act, dt, g, in, bias, weights, weights ? weights_dt : dt, din, bp, wp, hidden,
@@ -509,19 +549,23 @@ mb_status_t mb_weighted_squared_relu_fwd(const void* x, const void* weights, mb_
   if (!aligned(x, 16) || !aligned(out, 16) || (weights && !aligned(weights, esize(weights_dt)))) return MB_ERR_ALIGN;
   if (!aliasing_ok({{out, tb}}, {{x, tb}, {weights, wb}}, {{0, 0}})) return MB_ERR_ALIAS;
   if (tokens == 0) return MB_OK;
-  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_SRELU_FWD_BLOCKS);
+  const mb::Tiling t = mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_SRELU_FWD_BLOCKS, stream_cus(s));
   if (hipError_t e = mb::launch_srelu_fwd(dt, weights_dt, x, weights, out, t, s)) return hip_status(e);
   return finish();
 }
 
-static mb::Tiling srelu_bwd_tiling(int64_t tokens, int64_t hidden, mb_dtype_t dt) {
-  return mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_SRELU_BWD_BLOCKS);
+static mb::Tiling srelu_bwd_tiling(int64_t tokens, int64_t hidden, mb_dtype_t dt, int cus) {
+  return mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_SRELU_BWD_BLOCKS, cus);
+}
+
+static size_t srelu_bwd_ws(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dweights, int cus) {
+  if (!with_dweights || !dt_ok(dt) || check_shape(tokens, hidden, dt) != MB_OK || tokens == 0) return 0;
+  const mb::Tiling t = srelu_bwd_tiling(tokens, hidden, dt, cus);
+  return static_cast<size_t>(t.strips) * tokens * 4;
 }
 
 size_t mb_weighted_squared_relu_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dweights) {
-  if (!with_dweights || !dt_ok(dt) || check_shape(tokens, hidden, dt) != MB_OK || tokens == 0) return 0;
-  const mb::Tiling t = srelu_bwd_tiling(tokens, hidden, dt);
-  return static_cast<size_t>(t.strips) * tokens * 4;
+  return srelu_bwd_ws(tokens, hidden, dt, with_dweights, current_cus());
 }
 
 mb_status_t mb_weighted_squared_relu_bwd(const void* g, const void* x, const void* weights, mb_dtype_t weights_dt,
@@ -536,13 +580,14 @@ mb_status_t mb_weighted_squared_relu_bwd(const void* g, const void* x, const voi
   if (!aligned(g, 16) || !aligned(x, 16) || !aligned(dx, 16) || (weights && !aligned(weights, esize(weights_dt))) ||
       !aligned(dweights, 4) || !aligned(ws, 16))
     return MB_ERR_ALIGN;
-  const size_t need_ws = dweights ? mb_weighted_squared_relu_bwd_workspace(tokens, hidden, dt, 1) : 0;
+  const int cus = stream_cus(s);
+  const size_t need_ws = dweights ? srelu_bwd_ws(tokens, hidden, dt, 1, cus) : 0;
   if (need_ws && (!ws || ws_bytes < need_ws)) return MB_ERR_WORKSPACE;
   if (!aliasing_ok({{dx, tb}, {dweights, dweights ? static_cast<size_t>(tokens) * 4 : 0}, {ws, need_ws}},
                    {{g, tb}, {x, tb}, {weights, wb}}, {{0, 0}, {0, 1}}))
     return MB_ERR_ALIAS;
   if (tokens == 0) return MB_OK;
-  const mb::Tiling t = srelu_bwd_tiling(tokens, hidden, dt);
+  const mb::Tiling t = srelu_bwd_tiling(tokens, hidden, dt, cus);
   float* wpart = dweights ? static_cast<float*>(ws) : nullptr;
   if (hipError_t e = mb::launch_srelu_bwd(dt, weights_dt, g, x, weights, dx, wpart, t, s)) return hip_status(e);
   if (dweights)
@@ -556,12 +601,12 @@ static bool ln_dtypes_ok(mb_dtype_t dt, mb_dtype_t rdt) { return dt_ok(dt) && (r
 
 // Shape rule of the LayerNorm rows: whole vectors, a row-group shape that holds
 // the row, sizes within the kernels' index math.
-static mb_status_t ln_shape(int64_t T, int64_t H, mb_dtype_t dt, mb_dtype_t rdt, mb::LnPlan* plan) {
+static mb_status_t ln_shape(int64_t T, int64_t H, mb_dtype_t dt, mb_dtype_t rdt, int cus, mb::LnPlan* plan) {
   if (T < 0 || H <= 0 || T > (int64_t{1} << 40) || H > (int64_t{1} << 20)) return MB_ERR_SHAPE;
   const int E = mb::ln_elems_per_vector(dt, rdt);
   if (H % E != 0) return MB_ERR_SHAPE;
   const int blocks = H / E >= 1024 ? MB_LN_BWD_BLOCKS_WIDE : MB_LN_BWD_BLOCKS;
-  *plan = mb::plan_ln(T, H, dt, rdt, blocks, MB_LN_BWD_NV);
+  *plan = mb::plan_ln(T, H, dt, rdt, blocks, MB_LN_BWD_NV, cus);
   if (plan->shape < 0) return MB_ERR_SHAPE;
   return MB_OK;
 }
@@ -574,7 +619,8 @@ mb_status_t mb_add_layer_norm_fwd(const void* x, const void* residual, mb_dtype_
                                   hipStream_t s) {
   if (!ln_dtypes_ok(dt, residual_dt)) return MB_ERR_DTYPE;
   mb::LnPlan plan;
-  if (mb_status_t st = ln_shape(tokens, hidden, dt, residual_dt, &plan)) return st;
+  const int cus = stream_cus(s);
+  if (mb_status_t st = ln_shape(tokens, hidden, dt, residual_dt, cus, &plan)) return st;
   if (!eps_ok(eps)) return MB_ERR_PROB;
   const size_t n = static_cast<size_t>(tokens) * hidden;
   const size_t tb = n * esize(dt), rb = n * esize(residual_dt), hb = static_cast<size_t>(hidden) * esize(dt),
@@ -603,9 +649,9 @@ mb_status_t mb_add_layer_norm_fwd(const void* x, const void* residual, mb_dtype_
   a.y = y;
   a.mean = mean;
   a.rstd = rstd;
-  mb::LnPlan fp = mb::plan_ln(tokens, hidden, dt, residual_dt, MB_LN_FWD_BLOCKS, MB_LN_FWD_NV);
+  mb::LnPlan fp = mb::plan_ln(tokens, hidden, dt, residual_dt, MB_LN_FWD_BLOCKS, MB_LN_FWD_NV, cus);
   if (MB_LN_FWD_WIDE_HALF && mb::ln_plan_is(fp, 1024, 4)) {
-    const mb::LnPlan half = mb::plan_ln(tokens, hidden, dt, residual_dt, MB_LN_FWD_BLOCKS, 8);
+    const mb::LnPlan half = mb::plan_ln(tokens, hidden, dt, residual_dt, MB_LN_FWD_BLOCKS, 8, cus);
     if (mb::ln_plan_is(half, 512, 8)) fp = half;
   }
   if (fp.shape < 0) return MB_ERR_SHAPE;
@@ -634,7 +680,7 @@ size_t mb_add_layer_norm_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_
                                        int with_param_grads) {
   if (!with_param_grads || !ln_dtypes_ok(dt, residual_dt) || tokens == 0) return 0;
   mb::LnPlan plan;
-  if (ln_shape(tokens, hidden, dt, residual_dt, &plan) != MB_OK) return 0;
+  if (ln_shape(tokens, hidden, dt, residual_dt, current_cus(), &plan) != MB_OK) return 0;
   return ln_ws_layout(plan, hidden).total;
 }
 
@@ -645,7 +691,7 @@ mb_status_t mb_add_layer_norm_bwd(const void* dy, const void* h, const void* gam
                                   hipStream_t s) {
   if (!ln_dtypes_ok(dt, residual_dt)) return MB_ERR_DTYPE;
   mb::LnPlan plan;
-  if (mb_status_t st = ln_shape(tokens, hidden, dt, residual_dt, &plan)) return st;
+  if (mb_status_t st = ln_shape(tokens, hidden, dt, residual_dt, stream_cus(s), &plan)) return st;
   const size_t n = static_cast<size_t>(tokens) * hidden;
   const size_t tb = n * esize(dt), rb = n * esize(residual_dt), hb = static_cast<size_t>(hidden) * esize(dt),
                sb = static_cast<size_t>(tokens) * 4;

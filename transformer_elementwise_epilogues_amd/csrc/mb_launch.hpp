@@ -6,133 +6,10 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "mb_plan.hpp"
+
 namespace mb {
 
-// Row tiling of a [T, nvec] array of 16-byte column vectors: grid.x covers
-// column strips of 64 vectors (one wave each), grid.y = G row groups; wave w
-// of row group y walks rows y*4 + w, y*4 + w + 4G, ...
-struct Tiling {
-  int64_t T = 0;     // rows
-  int nvec = 0;      // 16-byte vectors per (output) row
-  int strips = 0;    // ceil(nvec / 64)
-  int G = 0;         // row groups
-};
-
-// Launch shape per kernel family: blocks of 256 threads to aim for (row groups
-// are rounded down so the grid never exceeds it by a partial wave of blocks)
-// and rows in flight per wave, measured on MI355X (bench-order sweeps). The
-// forward kernels without reductions stream best as many short-lived blocks
-// (one to four rows per wave). Of the backward kernels that keep bias-gradient
-// sums per lane, the GeLU pair also runs many blocks (8 rows per wave, 4 in
-// flight): the dispatcher's balancing beat a persistent grid of one block per
-// CU by 3-4 % and removed its slow calls, although the partial rows grow to
-// 1/16 of dgrad's bytes. The others do best with few resident blocks.
-#ifndef MB_GELU_FWD_BLOCKS
-#define MB_GELU_FWD_BLOCKS 65536
-#endif
-#ifndef MB_GELU_FWD_UNROLL
-#define MB_GELU_FWD_UNROLL 1
-#endif
-#ifndef MB_GELU_BWD_BLOCKS
-#define MB_GELU_BWD_BLOCKS 32768
-#endif
-#ifndef MB_GELU_BWD_UNROLL
-#define MB_GELU_BWD_UNROLL 4
-#endif
-#ifndef MB_GELU_ERF_BWD_BLOCKS
-#define MB_GELU_ERF_BWD_BLOCKS 32768
-#endif
-#ifndef MB_GELU_ERF_BWD_UNROLL
-#define MB_GELU_ERF_BWD_UNROLL 4
-#endif
-#ifndef MB_BDA_BLOCKS
-#define MB_BDA_BLOCKS 65536
-#endif
-#ifndef MB_BDA_UNROLL
-#define MB_BDA_UNROLL 1
-#endif
-#ifndef MB_BDA_MIXED_BLOCKS
-#define MB_BDA_MIXED_BLOCKS 512
-#endif
-#ifndef MB_BDA_MIXED_UNROLL
-#define MB_BDA_MIXED_UNROLL 2
-#endif
-// its training pass (with the mask) streams best as many blocks (+4 % over
-// 512 with buffer nt sc1 stores); the in-place inference pass does not
-#ifndef MB_BDA_MIXED_TRAIN_BLOCKS
-#define MB_BDA_MIXED_TRAIN_BLOCKS 16384
-#endif
-#ifndef MB_BDA_MIXED_TRAIN_UNROLL
-#define MB_BDA_MIXED_TRAIN_UNROLL 1
-#endif
-#ifndef MB_BDA_BWD_BLOCKS
-#define MB_BDA_BWD_BLOCKS 768
-#endif
-#ifndef MB_BDA_BWD_UNROLL
-#define MB_BDA_BWD_UNROLL 2
-#endif
-// fp32 residual gradient beside bf16/fp16: the grid that splits the rows
-// evenly over the waves (64 rows each at [8192, 4096]) beat 768 blocks by 5 %
-#ifndef MB_BDA_BWD_MIXED_BLOCKS
-#define MB_BDA_BWD_MIXED_BLOCKS 512
-#endif
-#ifndef MB_BDA_BWD_MIXED_UNROLL
-#define MB_BDA_BWD_MIXED_UNROLL 2
-#endif
-#ifndef MB_GLU_FWD_BLOCKS
-#define MB_GLU_FWD_BLOCKS 65536
-#endif
-#ifndef MB_GLU_FWD_UNROLL
-#define MB_GLU_FWD_UNROLL 1
-#endif
-#ifndef MB_GLU_BWD_BLOCKS
-#define MB_GLU_BWD_BLOCKS 512
-#endif
-#ifndef MB_GLU_BWD_UNROLL
-#define MB_GLU_BWD_UNROLL 1
-#endif
-
-// The tiling every kernel of one call uses; also sizes the workspaces.
-#ifndef MB_SRELU_FWD_BLOCKS
-#define MB_SRELU_FWD_BLOCKS 65536
-#endif
-#ifndef MB_SRELU_FWD_UNROLL
-#define MB_SRELU_FWD_UNROLL 1
-#endif
-#ifndef MB_SRELU_BWD_BLOCKS
-#define MB_SRELU_BWD_BLOCKS 16384
-#endif
-#ifndef MB_SRELU_BWD_UNROLL
-#define MB_SRELU_BWD_UNROLL 1
-#endif
-#ifndef MB_LN_FWD_BLOCKS
-#define MB_LN_FWD_BLOCKS 2048
-#endif
-// backward blocks = partial rows of dgamma / dbeta: fewer for wide rows
-// (1024 or more vectors), where each partial row is large
-#ifndef MB_LN_BWD_BLOCKS
-#define MB_LN_BWD_BLOCKS 512
-#endif
-#ifndef MB_LN_BWD_BLOCKS_WIDE
-#define MB_LN_BWD_BLOCKS_WIDE 256
-#endif
-#ifndef MB_LN_DGB_BLOCKS
-#define MB_LN_DGB_BLOCKS 512
-#endif
-// preferred vectors per thread (the row is split over more threads below it)
-#ifndef MB_LN_FWD_NV
-#define MB_LN_FWD_NV 4
-#endif
-// forward rows of 4096 vectors: 512 threads of 8 (two blocks per CU) instead
-// of 1024 threads of 4 (one)
-#ifndef MB_LN_FWD_WIDE_HALF
-#define MB_LN_FWD_WIDE_HALF 1
-#endif
-#ifndef MB_LN_BWD_NV
-#define MB_LN_BWD_NV 2
-#endif
-
-Tiling plan_tiling(int64_t T, int nvec, int target_blocks);
 
 // Bytes of the static device scratch that holds the bias gradient's partial
 // rows for the entry point that allocates nothing (one copy per device).
@@ -233,18 +110,6 @@ struct LnArgs {
   float* pg = nullptr;   // partial rows of dgamma / dbeta [partial_rows, H]; nullable
   float* pb = nullptr;
 };
-struct LnPlan {
-  int nvec = 0;           // vectors of ln_elems_per_vector elements per row
-  int shape = -1;         // row-group shape; -1: the row is too wide
-  int grid = 0;           // blocks of the row kernels
-  bool split = false;     // dgamma / dbeta by the column-strip kernel
-  Tiling dgb;             // its tiling
-  int partial_rows = 0;   // partial rows the backward writes
-};
-int ln_elems_per_vector(int dt, int rdt);
-LnPlan plan_ln(int64_t T, int64_t H, int dt, int rdt, int target_blocks, int nv_pref);
-// the plan's row group is `tpr` threads of `nv` vectors
-bool ln_plan_is(const LnPlan& p, int tpr, int nv);
 hipError_t launch_ln_fwd(const LnArgs& a, const LnPlan& p, hipStream_t s);
 hipError_t launch_ln_bwd(const LnArgs& a, const LnPlan& p, hipStream_t s);
 

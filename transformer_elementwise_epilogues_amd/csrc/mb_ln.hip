@@ -599,32 +599,9 @@ __global__ __launch_bounds__(kThreads) void ln_dgb_kernel(const char* __restrict
   }
 }
 
-// Row-group shapes: (threads per row, vectors per thread, rows per block).
-// Groups of 64 threads run 4 rows per block (no barrier); wider groups are the
-// whole block.
-struct Shape {
-  int tpr, nv, rpb;
-};
-constexpr Shape kShapes[] = {{64, 1, 4},  {64, 2, 4},  {64, 4, 4},  {256, 1, 1},  {256, 2, 1},
-                             {256, 4, 1}, {512, 1, 1}, {512, 2, 1}, {512, 4, 1},  {1024, 1, 1},
-                             {1024, 2, 1}, {1024, 4, 1}, {1024, 8, 1}, {512, 8, 1}};
-constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
-// dgamma / dbeta come from the column-strip kernel (which reads dy and h once
-// more) for 1024-thread rows of 2 or more vectors per thread: beyond 2 the
-// per-thread accumulators would not fit beside the row in the 128 registers
-// a thread of such a block has, and at 2 (rows of 2048 vectors) holding them
-// in LDS (128 KiB per block, one block per CU) ran 22 % slower than the
-// column-strip kernel on MI355X. (MB_LN_SPLIT_MIN_NV 4 restores the LDS sums.)
-#ifndef MB_LN_SPLIT_MIN_NV
-#define MB_LN_SPLIT_MIN_NV 2
-#endif
-constexpr bool split_shape(int s) {
-  return (kShapes[s].tpr == 1024 && kShapes[s].nv >= MB_LN_SPLIT_MIN_NV) || kShapes[s].nv >= 8;
-}
-
 template <DT D, DT R, int S>
 hipError_t fwd_shape(const LnArgs& a, const LnPlan& p, hipStream_t s) {
-  constexpr Shape sh = kShapes[S];
+  constexpr LnShape sh = kLnShapes[S];
   hipLaunchKernelGGL((ln_fwd_kernel<D, R, sh.tpr, sh.nv, sh.rpb>), dim3(p.grid), dim3(sh.tpr * sh.rpb), 0, s,
                      static_cast<const char*>(a.x), static_cast<const char*>(a.res),
                      static_cast<const char*>(a.gamma), static_cast<const char*>(a.beta),
@@ -635,7 +612,7 @@ hipError_t fwd_shape(const LnArgs& a, const LnPlan& p, hipStream_t s) {
 
 template <DT D, DT R, int S>
 hipError_t bwd_shape(const LnArgs& a, const LnPlan& p, hipStream_t s) {
-  constexpr Shape sh = kShapes[S];
+  constexpr LnShape sh = kLnShapes[S];
   const auto dy = static_cast<const char*>(a.dy);
   const auto h = static_cast<const char*>(a.h);
   const auto gamma = static_cast<const char*>(a.gamma);
@@ -644,7 +621,7 @@ hipError_t bwd_shape(const LnArgs& a, const LnPlan& p, hipStream_t s) {
   const auto dres = static_cast<char*>(a.dres);
   const int H = static_cast<int>(a.H);
   const dim3 grid(p.grid), block(sh.tpr * sh.rpb);
-  if constexpr (split_shape(S)) {
+  if constexpr (ln_split_shape(S)) {
     // the column pass reads dy and h before the row pass may overwrite them
     // (dx and dresidual may alias dy or h)
     if (a.pg) {
@@ -667,7 +644,7 @@ hipError_t bwd_shape(const LnArgs& a, const LnPlan& p, hipStream_t s) {
 
 template <DT D, DT R, bool BWD, int S = 0>
 hipError_t by_shape(const LnArgs& a, const LnPlan& p, hipStream_t s) {
-  if constexpr (S < kNumShapes) {
+  if constexpr (S < kLnNumShapes) {
     if (p.shape == S) return BWD ? bwd_shape<D, R, S>(a, p, s) : fwd_shape<D, R, S>(a, p, s);
     return by_shape<D, R, BWD, S + 1>(a, p, s);
   } else {
@@ -687,40 +664,6 @@ hipError_t by_dtype(const LnArgs& a, const LnPlan& p, hipStream_t s) {
 }
 
 }  // namespace
-
-int ln_elems_per_vector(int dt, int rdt) {
-  if (rdt == static_cast<int>(DT::F32) && dt != static_cast<int>(DT::F32)) return 4;
-  return dt == static_cast<int>(DT::F32) ? 4 : 8;
-}
-
-// Threads per row: the smallest of 64, 256, 512, 1024 that holds the row in
-// at most `nv_pref` vectors per thread (1024 takes up to 8).
-LnPlan plan_ln(int64_t T, int64_t H, int dt, int rdt, int target_blocks, int nv_pref) {
-  LnPlan p;
-  const int E = ln_elems_per_vector(dt, rdt);
-  p.nvec = static_cast<int>(H / E);
-  p.shape = -1;
-  int tpr = 64;
-  while (tpr < 1024 && static_cast<int64_t>(tpr) * nv_pref < p.nvec) tpr = tpr == 64 ? 256 : tpr * 2;
-  int nv = 1;
-  while (nv < 8 && static_cast<int64_t>(tpr) * nv < p.nvec) nv *= 2;
-  if (static_cast<int64_t>(tpr) * nv < p.nvec) return p;  // wider than 8192 vectors
-  for (int i = 0; i < kNumShapes; ++i)
-    if (kShapes[i].tpr == tpr && kShapes[i].nv == nv) p.shape = i;
-  if (p.shape < 0) return p;
-  const Shape sh = kShapes[p.shape];
-  const int64_t groups = (T + sh.rpb - 1) / sh.rpb;
-  p.grid = static_cast<int>(std::min<int64_t>(std::max<int64_t>(groups, 1), target_blocks));
-  p.split = split_shape(p.shape);
-  const int v16 = static_cast<int>(H * (dt == static_cast<int>(DT::F32) ? 4 : 2) / 16);
-  p.dgb = plan_tiling(T, v16, MB_LN_DGB_BLOCKS);
-  p.partial_rows = p.split ? p.dgb.G : p.grid;
-  return p;
-}
-
-bool ln_plan_is(const LnPlan& p, int tpr, int nv) {
-  return p.shape >= 0 && kShapes[p.shape].tpr == tpr && kShapes[p.shape].nv == nv;
-}
 
 hipError_t launch_ln_fwd(const LnArgs& a, const LnPlan& p, hipStream_t s) { return by_dtype<false>(a, p, s); }
 hipError_t launch_ln_bwd(const LnArgs& a, const LnPlan& p, hipStream_t s) { return by_dtype<true>(a, p, s); }

@@ -1,0 +1,67 @@
+// mb_plan.cpp -- launch planning (see mb_plan.hpp): host arithmetic only.
+#include "mb_plan.hpp"
+
+#include <algorithm>
+
+namespace mb {
+
+namespace {
+constexpr int kWavesPerBlock = 4;  // every tiled kernel: blocks of 4 waves
+constexpr int kStripVectors = 64;  // a wave covers 64 16-byte column vectors
+}  // namespace
+
+int scaled_blocks(int target_blocks, int cus) {
+  if (cus <= 0) cus = kTunedCUs;
+  const int64_t b = static_cast<int64_t>(target_blocks) * cus / kTunedCUs;
+  return static_cast<int>(std::max<int64_t>(1, b));
+}
+
+Tiling plan_tiling(int64_t T, int nvec, int target_blocks, int cus, int min_rows) {
+  Tiling t;
+  t.T = T;
+  t.nvec = nvec;
+  t.strips = (nvec + kStripVectors - 1) / kStripVectors;
+  // Round down: a grid slightly larger than the resident capacity would leave a
+  // few straggler blocks running alone after the rest finish.
+  const int64_t want = std::max<int64_t>(1, scaled_blocks(target_blocks, cus) / t.strips);
+  const int64_t rows_per_group = static_cast<int64_t>(kWavesPerBlock) * std::max(1, min_rows);
+  const int64_t most = std::max<int64_t>(1, (T + rows_per_group - 1) / rows_per_group);
+  t.G = static_cast<int>(std::min<int64_t>(std::min(want, most), 65535));
+  return t;
+}
+
+int ln_elems_per_vector(int dt, int rdt) {
+  if (rdt == 0 && dt != 0) return 4;
+  return dt == 0 ? 4 : 8;
+}
+
+// Threads per row: the smallest of 64, 256, 512, 1024 that holds the row in
+// at most `nv_pref` vectors per thread (1024 takes up to 8).
+LnPlan plan_ln(int64_t T, int64_t H, int dt, int rdt, int target_blocks, int nv_pref, int cus) {
+  LnPlan p;
+  const int E = ln_elems_per_vector(dt, rdt);
+  p.nvec = static_cast<int>(H / E);
+  p.shape = -1;
+  int tpr = 64;
+  while (tpr < 1024 && static_cast<int64_t>(tpr) * nv_pref < p.nvec) tpr = tpr == 64 ? 256 : tpr * 2;
+  int nv = 1;
+  while (nv < 8 && static_cast<int64_t>(tpr) * nv < p.nvec) nv *= 2;
+  if (static_cast<int64_t>(tpr) * nv < p.nvec) return p;  // wider than 8192 vectors
+  for (int i = 0; i < kLnNumShapes; ++i)
+    if (kLnShapes[i].tpr == tpr && kLnShapes[i].nv == nv) p.shape = i;
+  if (p.shape < 0) return p;
+  const LnShape sh = kLnShapes[p.shape];
+  const int64_t groups = (T + sh.rpb - 1) / sh.rpb;
+  p.grid = static_cast<int>(std::min<int64_t>(std::max<int64_t>(groups, 1), scaled_blocks(target_blocks, cus)));
+  p.split = ln_split_shape(p.shape);
+  const int v16 = static_cast<int>(H * (dt == 0 ? 4 : 2) / 16);
+  p.dgb = plan_tiling(T, v16, MB_LN_DGB_BLOCKS, cus);
+  p.partial_rows = p.split ? p.dgb.G : p.grid;
+  return p;
+}
+
+bool ln_plan_is(const LnPlan& p, int tpr, int nv) {
+  return p.shape >= 0 && kLnShapes[p.shape].tpr == tpr && kLnShapes[p.shape].nv == nv;
+}
+
+}  // namespace mb

@@ -1,0 +1,201 @@
+// mb_plan.hpp -- launch planning: the launch shape of every kernel family,
+// as plain host arithmetic (no HIP call), shared by the C ABI (mb_abi.cpp),
+// the kernels (compile-time shapes) and a CPU test of the plans.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mb {
+
+// Block counts below are tuned on a whole MI355X (256 compute units); a plan
+// scales them by the compute units of the device it runs on (a partitioned
+// device has fewer), so that the persistent grids keep the same number of
+// resident blocks per CU instead of running in several rounds.
+constexpr int kTunedCUs = 256;
+
+// Row tiling of a [T, nvec] array of 16-byte column vectors: grid.x covers
+// column strips of 64 vectors (one wave each), grid.y = G row groups; wave w
+// of row group y walks rows y*4 + w, y*4 + w + 4G, ...
+struct Tiling {
+  int64_t T = 0;     // rows
+  int nvec = 0;      // 16-byte vectors per (output) row
+  int strips = 0;    // ceil(nvec / 64)
+  int G = 0;         // row groups
+};
+
+// Launch shape per kernel family: blocks of 256 threads to aim for (row groups
+// are rounded down so the grid never exceeds it by a partial wave of blocks)
+// and rows in flight per wave, measured on MI355X (bench-order sweeps). The
+// forward kernels without reductions stream best as many short-lived blocks
+// (one to four rows per wave). Of the backward kernels that keep bias-gradient
+// sums per lane, the GeLU pair also runs many blocks (8 rows per wave, 4 in
+// flight): the dispatcher's balancing beat a persistent grid of one block per
+// CU by 3-4 % and removed its slow calls, although the partial rows grow to
+// 1/16 of dgrad's bytes. The others do best with few resident blocks.
+#ifndef MB_GELU_FWD_BLOCKS
+#define MB_GELU_FWD_BLOCKS 65536
+#endif
+#ifndef MB_GELU_FWD_UNROLL
+#define MB_GELU_FWD_UNROLL 1
+#endif
+#ifndef MB_GELU_BWD_BLOCKS
+#define MB_GELU_BWD_BLOCKS 32768
+#endif
+#ifndef MB_GELU_BWD_UNROLL
+#define MB_GELU_BWD_UNROLL 4
+#endif
+// rows every wave of the GeLU backward walks at least: its partial rows (one
+// per row group) then stay a small fraction of the bytes at any row count.
+// With one row per wave, [4096, 8192] bf16 wrote 1024 partial rows (a sixth of
+// its bytes) and ran at 2.75 TB/s; 4 rows per wave took it to 4.4 TB/s and
+// [8192, 8192], [32768, 4096], [2048, 14336], [1024, 32768] from 2.7-3.8 to
+// 4.2-5.3 TB/s, with [16384, 32768] unchanged (8 rows per wave already; MI355X,
+// same process).
+#ifndef MB_GELU_BWD_MIN_ROWS
+#define MB_GELU_BWD_MIN_ROWS 4
+#endif
+#ifndef MB_GELU_ERF_BWD_MIN_ROWS
+#define MB_GELU_ERF_BWD_MIN_ROWS 4
+#endif
+#ifndef MB_GELU_ERF_BWD_BLOCKS
+#define MB_GELU_ERF_BWD_BLOCKS 32768
+#endif
+#ifndef MB_GELU_ERF_BWD_UNROLL
+#define MB_GELU_ERF_BWD_UNROLL 4
+#endif
+#ifndef MB_BDA_BLOCKS
+#define MB_BDA_BLOCKS 65536
+#endif
+#ifndef MB_BDA_UNROLL
+#define MB_BDA_UNROLL 1
+#endif
+#ifndef MB_BDA_MIXED_BLOCKS
+#define MB_BDA_MIXED_BLOCKS 512
+#endif
+#ifndef MB_BDA_MIXED_UNROLL
+#define MB_BDA_MIXED_UNROLL 2
+#endif
+// its training pass (with the mask) streams best as many blocks (+4 % over
+// 512 with buffer nt sc1 stores); the in-place inference pass does not
+#ifndef MB_BDA_MIXED_TRAIN_BLOCKS
+#define MB_BDA_MIXED_TRAIN_BLOCKS 16384
+#endif
+#ifndef MB_BDA_MIXED_TRAIN_UNROLL
+#define MB_BDA_MIXED_TRAIN_UNROLL 1
+#endif
+#ifndef MB_BDA_BWD_BLOCKS
+#define MB_BDA_BWD_BLOCKS 768
+#endif
+#ifndef MB_BDA_BWD_UNROLL
+#define MB_BDA_BWD_UNROLL 2
+#endif
+// fp32 residual gradient beside bf16/fp16: the grid that splits the rows
+// evenly over the waves (64 rows each at [8192, 4096]) beat 768 blocks by 5 %
+#ifndef MB_BDA_BWD_MIXED_BLOCKS
+#define MB_BDA_BWD_MIXED_BLOCKS 512
+#endif
+#ifndef MB_BDA_BWD_MIXED_UNROLL
+#define MB_BDA_BWD_MIXED_UNROLL 2
+#endif
+#ifndef MB_GLU_FWD_BLOCKS
+#define MB_GLU_FWD_BLOCKS 65536
+#endif
+#ifndef MB_GLU_FWD_UNROLL
+#define MB_GLU_FWD_UNROLL 1
+#endif
+#ifndef MB_GLU_BWD_BLOCKS
+#define MB_GLU_BWD_BLOCKS 512
+#endif
+#ifndef MB_GLU_BWD_UNROLL
+#define MB_GLU_BWD_UNROLL 1
+#endif
+
+#ifndef MB_SRELU_FWD_BLOCKS
+#define MB_SRELU_FWD_BLOCKS 65536
+#endif
+#ifndef MB_SRELU_FWD_UNROLL
+#define MB_SRELU_FWD_UNROLL 1
+#endif
+#ifndef MB_SRELU_BWD_BLOCKS
+#define MB_SRELU_BWD_BLOCKS 16384
+#endif
+#ifndef MB_SRELU_BWD_UNROLL
+#define MB_SRELU_BWD_UNROLL 1
+#endif
+#ifndef MB_LN_FWD_BLOCKS
+#define MB_LN_FWD_BLOCKS 2048
+#endif
+// backward blocks = partial rows of dgamma / dbeta: fewer for wide rows
+// (1024 or more vectors), where each partial row is large
+#ifndef MB_LN_BWD_BLOCKS
+#define MB_LN_BWD_BLOCKS 512
+#endif
+#ifndef MB_LN_BWD_BLOCKS_WIDE
+#define MB_LN_BWD_BLOCKS_WIDE 256
+#endif
+#ifndef MB_LN_DGB_BLOCKS
+#define MB_LN_DGB_BLOCKS 512
+#endif
+// preferred vectors per thread (the row is split over more threads below it)
+#ifndef MB_LN_FWD_NV
+#define MB_LN_FWD_NV 4
+#endif
+// forward rows of 4096 vectors: 512 threads of 8 (two blocks per CU) instead
+// of 1024 threads of 4 (one)
+#ifndef MB_LN_FWD_WIDE_HALF
+#define MB_LN_FWD_WIDE_HALF 1
+#endif
+#ifndef MB_LN_BWD_NV
+#define MB_LN_BWD_NV 2
+#endif
+
+
+// Blocks to aim for on a device of `cus` compute units (at least 1).
+int scaled_blocks(int target_blocks, int cus);
+
+// The tiling of one call (it also sizes the workspaces): target_blocks as
+// tuned for kTunedCUs, scaled to `cus`; G rounded down so that the grid never
+// exceeds the scaled target, at most ceil(T / 4) (every row group owns a row),
+// at most ceil(T / (4 min_rows)) so that every wave walks at least min_rows
+// rows (fewer partial rows for the reductions), and at most 65535.
+Tiling plan_tiling(int64_t T, int nvec, int target_blocks, int cus, int min_rows = 1);
+
+// ---- residual add + LayerNorm row kernels
+// Row-group shapes: (threads per row, vectors per thread, rows per block).
+// Groups of 64 threads run 4 rows per block (no barrier); wider groups are the
+// whole block.
+struct LnShape {
+  int tpr, nv, rpb;
+};
+constexpr LnShape kLnShapes[] = {{64, 1, 4},  {64, 2, 4},  {64, 4, 4},  {256, 1, 1},  {256, 2, 1},
+                                 {256, 4, 1}, {512, 1, 1}, {512, 2, 1}, {512, 4, 1},  {1024, 1, 1},
+                                 {1024, 2, 1}, {1024, 4, 1}, {1024, 8, 1}, {512, 8, 1}};
+constexpr int kLnNumShapes = sizeof(kLnShapes) / sizeof(kLnShapes[0]);
+// dgamma / dbeta come from the column-strip kernel (which reads dy and h once
+// more) for 1024-thread rows of 2 or more vectors per thread: beyond 2 the
+// per-thread accumulators would not fit beside the row in the 128 registers
+// a thread of such a block has, and at 2 (rows of 2048 vectors) holding them
+// in LDS (128 KiB per block, one block per CU) ran 22 % slower than the
+// column-strip kernel on MI355X. (MB_LN_SPLIT_MIN_NV 4 restores the LDS sums.)
+#ifndef MB_LN_SPLIT_MIN_NV
+#define MB_LN_SPLIT_MIN_NV 2
+#endif
+constexpr bool ln_split_shape(int s) {
+  return (kLnShapes[s].tpr == 1024 && kLnShapes[s].nv >= MB_LN_SPLIT_MIN_NV) || kLnShapes[s].nv >= 8;
+}
+
+struct LnPlan {
+  int nvec = 0;           // vectors of ln_elems_per_vector elements per row
+  int shape = -1;         // row-group shape; -1: the row is too wide
+  int grid = 0;           // blocks of the row kernels
+  bool split = false;     // dgamma / dbeta by the column-strip kernel
+  Tiling dgb;             // its tiling
+  int partial_rows = 0;   // partial rows the backward writes
+};
+int ln_elems_per_vector(int dt, int rdt);
+LnPlan plan_ln(int64_t T, int64_t H, int dt, int rdt, int target_blocks, int nv_pref, int cus);
+// the plan's row group is `tpr` threads of `nv` vectors
+bool ln_plan_is(const LnPlan& p, int tpr, int nv);
+
+}  // namespace mb

@@ -100,19 +100,6 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
 
 }  // namespace
 
-Tiling plan_tiling(int64_t T, int nvec, int target_blocks) {
-  Tiling t;
-  t.T = T;
-  t.nvec = nvec;
-  t.strips = (nvec + kStrip - 1) / kStrip;
-  // Round down: a grid slightly larger than the resident capacity would leave a
-  // few straggler blocks running alone after the rest finish.
-  const int64_t want = std::max<int64_t>(1, target_blocks / t.strips);
-  const int64_t most = std::max<int64_t>(1, (T + kWaves - 1) / kWaves);  // every row group owns a row
-  t.G = static_cast<int>(std::min<int64_t>(std::min(want, most), 65535));
-  return t;
-}
-
 static unsigned col_blocks(int64_t C) { return static_cast<unsigned>((C + 255) / 256); }
 
 hipError_t launch_colsum2(const ColSum& a, const ColSum& b, hipStream_t s) {
