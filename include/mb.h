@@ -44,7 +44,16 @@
 extern "C" {
 #endif
 
-typedef enum { MB_F32 = 0, MB_F16 = 1, MB_BF16 = 2 } mb_dtype_t;
+/* The last two enumerators only widen the type's range to every 32-bit int, so
+ * that an unknown value from a caller is a value the library can check and
+ * refuse (MB_ERR_DTYPE) rather than an out-of-range enum in C++. */
+typedef enum {
+  MB_F32 = 0,
+  MB_F16 = 1,
+  MB_BF16 = 2,
+  MB_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  MB_DTYPE_RANGE_MAX_ = 2147483647
+} mb_dtype_t;
 
 typedef enum {
   MB_OK = 0,

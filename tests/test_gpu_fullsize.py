@@ -23,6 +23,9 @@ from tolerances import assert_close, assert_close_bounded, assert_reduction_clos
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
+# floor-only passes on natural data: at most 1e-5 of the elements (about 2e-6
+# expected at the roots of the derivatives, where the fp32 sum cancels)
+FLOOR_FRAC = 1e-5
 
 
 def say(msg):
@@ -57,24 +60,44 @@ def check_rows_dt(kernel_out, oracle_fn, blocks, dt, what):
     stats = []
     for r0, n in blocks:
         o, o64, mag = oracle_fn(r0, n)
-        stats.append(assert_close(st(kernel_out[r0:r0 + n]), o, o64, mag, dt, f"{what} rows {r0}+{n}"))
+        stats.append(assert_close(st(kernel_out[r0:r0 + n]), o, o64, mag, dt, f"{what} rows {r0}+{n}",
+                                  max_floor_frac=FLOOR_FRAC))
     say(f"{what}: {stats}")
 
 
 # ------------------------------------------------------------------ GeLU fp32 [512, 4096], entire tensor
 
+def exponent_size(z, exact):
+    """|E|, the exponent the GeLU evaluates at z: 2|u| with u the tanh
+    argument (0.79788456 z (1 + 0.044715 z^2)), or z^2/2 for the exact form."""
+    if exact:
+        return 0.5 * z * z
+    return 2.0 * np.abs(0.79788456 * z * (1.0 + 0.044715 * z * z))
+
+
 @pytest.mark.parametrize("exact", [False, True], ids=["tanh", "erf"])
 def test_gelu_f32_512x4096_full(exact):
+    """Every element of the fp32 workload, with no absolute term. Forward: the
+    pure 1e-6 relative bound holds for all but the negative tail, where the
+    exponent's rounding (|E| 2^-24 relative) exceeds it; those (at most a
+    thousandth of the elements; 1323 measured) pass within 8 2^-24 (1 + |E|)
+    of the value. Backward: the fp32 sum of the derivative's two terms carries
+    a few ulps of the larger term, about 1e-6 relative, so a few per cent of the
+    elements (3.2 % measured) pass within 8 2^-24 (1 + |E|) of that term
+    instead; at most 5 % may."""
     w = WORKLOADS["gelu_f32_512x4096"]
     y, b, g = (w.tensor(k) for k in ("y", "bias", "g"))
     fwd, bwd = ((mb.mb_bias_gelu_erf_fwd, mb.mb_bias_gelu_erf_bwd) if exact
                 else (mb.mb_bias_gelu_fwd, mb.mb_bias_gelu_bwd))
+    cond = exponent_size(y.double().numpy() + b.double().numpy()[None, :], exact)
     out = fwd(y.to(DEV), b.to(DEV))
     o, o64 = oracle.bias_gelu_fwd("f32", st(y), st(b), exact=exact)
-    say(f"gelu fwd exact={exact} f32 full: {assert_close(st(out), o, o64, None, 'f32', 'gelu fwd C1')}")
+    say(f"gelu fwd exact={exact} f32 full: "
+        f"{assert_close(st(out), o, o64, None, 'f32', 'gelu fwd C1', max_floor_frac=1e-3, cond=cond)}")
     dg, db = bwd(g.to(DEV), y.to(DEV), b.to(DEV))
     d, d64, mag, db64 = oracle.bias_gelu_bwd("f32", st(g), st(y), st(b), exact=exact)
-    say(f"gelu bwd exact={exact} f32 full: {assert_close(st(dg), d, d64, mag, 'f32', 'gelu bwd C1')}")
+    say(f"gelu bwd exact={exact} f32 full: "
+        f"{assert_close(st(dg), d, d64, mag, 'f32', 'gelu bwd C1', max_floor_frac=0.05, cond=cond)}")
     say(f"gelu dbias exact={exact} f32 full: {assert_reduction_close(db.cpu().numpy(), db64, 'gelu dbias C1')}")
 
 

@@ -135,6 +135,10 @@ mb::DropoutArgs dropout_args(float p, uint64_t seed, uint64_t offset) {
   return d;
 }
 
+mb::Tiling glu_bwd_tiling(int64_t tokens, int64_t hidden, mb_dtype_t dt, int cus) {
+  return mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GLU_BWD_BLOCKS, cus);
+}
+
 // Partial-row workspace of a column reduction.
 size_t col_partials_bytes(const mb::Tiling& t, int64_t cols) { return static_cast<size_t>(t.G) * cols * 4; }
 
@@ -459,9 +463,6 @@ namespace {
 struct GluWs {
   size_t bias_off, bias_bytes, w_off, w_bytes, total;
 };
-mb::Tiling glu_bwd_tiling(int64_t tokens, int64_t hidden, mb_dtype_t dt, int cus) {
-  return mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GLU_BWD_BLOCKS, cus);
-}
 GluWs glu_ws(int64_t tokens, int64_t hidden, mb_dtype_t dt, bool with_dbias, bool with_dw, int cus) {
   GluWs w{0, 0, 0, 0, 0};
   if (tokens == 0) return w;

@@ -332,11 +332,6 @@ hipError_t bda_bwd_dispatch(const void* g, void* dx, void* dres, float* partials
 
 }  // namespace
 
-int bda_elems_per_lane(int dt, int res_dt) {
-  if (static_cast<DT>(dt) == DT::F32) return 4;
-  return static_cast<DT>(res_dt) == DT::F32 ? 4 : 8;
-}
-
 hipError_t launch_bda_bwd(int dt, int res_dt, const void* g, void* dx, void* dres, float* partials, int64_t H,
                           const Tiling& t, const DropoutArgs& d, hipStream_t s) {
   const DT D = static_cast<DT>(dt), R = static_cast<DT>(res_dt);

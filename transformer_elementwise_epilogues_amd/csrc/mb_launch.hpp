@@ -37,7 +37,6 @@ hipError_t launch_colsum_tall(const float* in, int R, int64_t C, float* tmp, flo
 // tmp0, in1 -> out1 through tmp1).
 hipError_t launch_colsum_tall2(const float* in0, const float* in1, int R, int64_t C, float* tmp0, float* tmp1,
                                float* out0, float* out1, hipStream_t s);
-int64_t colsum_tall_tmp_floats(int R, int64_t C);
 // out[c] = sum over r < R of in[r * C + c], r ascending (fp32).
 hipError_t launch_colsum(const float* in, int R, int64_t C, float* out, hipStream_t s);
 
@@ -58,10 +57,6 @@ struct DropoutArgs {
   uint32_t k0, k1; // key = seed
   uint32_t o0, o1; // counter high words = offset
 };
-// Elements a dropout-add lane handles: 8 bf16/fp16 values, or 4 when the
-// residual (and so its gradient) is fp32 beside them, or 4 fp32 values. The
-// tiling's vectors per row are hidden / this.
-int bda_elems_per_lane(int dt, int res_dt);
 hipError_t launch_bda(int dt, int res_dt, bool train, const void* x, const void* bias,
                       const void* residual, void* out, int64_t H, const Tiling& t,
                       const DropoutArgs& d, hipStream_t s);

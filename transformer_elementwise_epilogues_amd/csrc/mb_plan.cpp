@@ -20,7 +20,7 @@ Tiling plan_tiling(int64_t T, int nvec, int target_blocks, int cus, int min_rows
   Tiling t;
   t.T = T;
   t.nvec = nvec;
-  t.strips = (nvec + kStripVectors - 1) / kStripVectors;
+  t.strips = std::max(1, (nvec + kStripVectors - 1) / kStripVectors);  // at least one strip, even for nvec 0
   // Round down: a grid slightly larger than the resident capacity would leave a
   // few straggler blocks running alone after the rest finish.
   const int64_t want = std::max<int64_t>(1, scaled_blocks(target_blocks, cus) / t.strips);
@@ -28,6 +28,13 @@ Tiling plan_tiling(int64_t T, int nvec, int target_blocks, int cus, int min_rows
   const int64_t most = std::max<int64_t>(1, (T + rows_per_group - 1) / rows_per_group);
   t.G = static_cast<int>(std::min<int64_t>(std::min(want, most), 65535));
   return t;
+}
+
+int64_t colsum_tall_tmp_floats(int R, int64_t C) { return R <= 32 ? 0 : static_cast<int64_t>((R + 31) / 32) * C; }
+
+int bda_elems_per_lane(int dt, int res_dt) {
+  if (dt == 0) return 4;
+  return res_dt == 0 ? 4 : 8;
 }
 
 int ln_elems_per_vector(int dt, int rdt) {
@@ -54,7 +61,9 @@ LnPlan plan_ln(int64_t T, int64_t H, int dt, int rdt, int target_blocks, int nv_
   const int64_t groups = (T + sh.rpb - 1) / sh.rpb;
   p.grid = static_cast<int>(std::min<int64_t>(std::max<int64_t>(groups, 1), scaled_blocks(target_blocks, cus)));
   p.split = ln_split_shape(p.shape);
-  const int v16 = static_cast<int>(H * (dt == 0 ? 4 : 2) / 16);
+  // the column-strip kernel's 16-byte vectors (only used when split, for rows
+  // of 16384 or more elements; a row narrower than one vector still plans)
+  const int v16 = std::max(1, static_cast<int>(H * (dt == 0 ? 4 : 2) / 16));
   p.dgb = plan_tiling(T, v16, MB_LN_DGB_BLOCKS, cus);
   p.partial_rows = p.split ? p.dgb.G : p.grid;
   return p;

@@ -161,6 +161,15 @@ int scaled_blocks(int target_blocks, int cus);
 // rows (fewer partial rows for the reductions), and at most 65535.
 Tiling plan_tiling(int64_t T, int nvec, int target_blocks, int cus, int min_rows = 1);
 
+// Floats of chunk sums launch_colsum_tall needs for R partial rows of C
+// columns (none up to 32 rows).
+int64_t colsum_tall_tmp_floats(int R, int64_t C);
+
+// Elements a dropout-add lane handles: 8 bf16/fp16 values, or 4 when the
+// residual (and so its gradient) is fp32 beside them, or 4 fp32 values. The
+// tiling's vectors per row are hidden / this. (dt: 0 fp32, 1 fp16, 2 bf16)
+int bda_elems_per_lane(int dt, int res_dt);
+
 // ---- residual add + LayerNorm row kernels
 // Row-group shapes: (threads per row, vectors per thread, rows per block).
 // Groups of 64 threads run 4 rows per block (no barrier); wider groups are the

@@ -113,7 +113,6 @@ hipError_t launch_colsum(const float* in, int R, int64_t C, float* out, hipStrea
   return hipGetLastError();
 }
 
-int64_t colsum_tall_tmp_floats(int R, int64_t C) { return R <= 32 ? 0 : static_cast<int64_t>((R + 31) / 32) * C; }
 
 // a, b: the partial rows; ta, tb: the same with their chunk-sum buffers as `out`
 static hipError_t colsum_tall_pair(const ColSum& a, const ColSum& b, float* tmp_a, float* tmp_b, unsigned arrays,
