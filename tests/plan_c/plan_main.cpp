@@ -1,7 +1,8 @@
 // Prints launch plans (mb_plan.cpp, host arithmetic only) for queries read
 // from stdin, one per line:
 //   tiling T nvec target_blocks cus min_rows   -> "tiling strips G"
-//   ln T H dt rdt target_blocks nv_pref cus     -> "ln nvec shape tpr nv grid split dgb_G partial_rows"
+//   ln T H dt rdt target_blocks nv_pref cus     -> "ln nvec shape tpr nv grid partial_rows"
+//   ln2 T H dt rdt cus                          -> "ln2 applies nvec rows_grid strips G"
 #include <cstdio>
 #include <cstring>
 
@@ -22,8 +23,13 @@ int main() {
       if (std::scanf("%lld %lld %d %d %d %d %d", &T, &H, &dt, &rdt, &target, &nv_pref, &cus) != 7) return 2;
       const mb::LnPlan p = mb::plan_ln(T, H, dt, rdt, target, nv_pref, cus);
       const int tpr = p.shape >= 0 ? mb::kLnShapes[p.shape].tpr : 0, nv = p.shape >= 0 ? mb::kLnShapes[p.shape].nv : 0;
-      std::printf("ln %d %d %d %d %d %d %d %d\n", p.nvec, p.shape, tpr, nv, p.grid, p.split ? 1 : 0, p.dgb.G,
-                  p.partial_rows);
+      std::printf("ln %d %d %d %d %d %d\n", p.nvec, p.shape, tpr, nv, p.grid, p.partial_rows);
+    } else if (std::strcmp(kind, "ln2") == 0) {
+      long long T, H;
+      int dt, rdt, cus;
+      if (std::scanf("%lld %lld %d %d %d", &T, &H, &dt, &rdt, &cus) != 5) return 2;
+      const mb::Ln2Plan p = mb::plan_ln2(T, H, dt, rdt, cus);
+      std::printf("ln2 %d %d %d %d %d\n", mb::ln2_applies(H, dt, rdt) ? 1 : 0, p.nvec, p.rows_grid, p.strips, p.G);
     } else {
       return 3;
     }

@@ -3,7 +3,7 @@ oracle, through the C ABI.
 
 Shapes cover every row-group shape the kernels pick (4 rows of 64 threads per
 block with 1, 2 or 4 vectors per thread; 256 and 1024 threads per row; the
-widest rows, whose parameter gradients come from the column-strip kernel),
+wide rows, whose backward is a row-sum kernel and a column-strip kernel),
 ragged rows (vectors that exist for only some threads), more rows than
 blocks (grid-stride rows and more than 32 partial rows), and every dtype
 pair. h is compared bit for bit; y, dx and dresidual within the derived
@@ -33,8 +33,9 @@ PAIRS = [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"), ("f16", "f16"), ("f1
 def hidden_cases(dt, rdt):
     """(T, H) per row-group shape, for elements-per-vector E."""
     E = 4 if (dt == "f32" or rdt == "f32") else 8
-    # vectors per row; from 2048 on the parameter-gradient sums come from the
-    # column-strip kernel, and the forward of 4096 runs 512 threads of 8
+    # vectors per row; beyond 1024 the backward is the wide-row pair (row
+    # sums, then column strips walking the rows backwards), and the forward
+    # of 4096 runs 512 threads of 8
     # (one vector per row: 4 bf16 beside an fp32 residual planned a column
     # strip of zero vectors for the unused parameter-gradient kernel, a host
     # division by zero that the sanitized build of the planner found)
@@ -136,6 +137,32 @@ def test_ln_many_rows_tall_partials():
     assert torch.equal(dx.view(torch.int16), dx2.view(torch.int16))
     assert torch.equal(dgam.view(torch.int32), dgam2.view(torch.int32))
     assert torch.equal(dbet.view(torch.int32), dbet2.view(torch.int32))
+
+
+@pytest.mark.parametrize("dt,rdt,T,H", [("bf16", "bf16", 1100, 16384), ("bf16", "bf16", 700, 12296),
+                                         ("f16", "f32", 257, 8196), ("bf16", "bf16", 37, 65536)])
+def test_ln_wide_backward_many_rows(dt, rdt, T, H):
+    """The wide-row backward over many rows: every row group walks several rows
+    from the last one down, the last column strip is ragged (12296 bf16 is
+    1537 vectors, 8196 beside an fp32 residual 2049), and dx, dresidual,
+    dgamma and dbeta match the oracle and reproduce bit for bit."""
+    say(f"wide bwd {dt}/{rdt} {T}x{H}")
+    x, r, g, b = inputs(dt, rdt, T, H, 31)
+    out = mb.mb_add_layer_norm_fwd(x.to(DEV), r.to(DEV), g.to(DEV), b.to(DEV))
+    _, oh = check_fwd(dt, rdt, x, r, g, b, 1e-5, False, out, "wide")
+    y, h, mean, rstd = out
+    dy = synthetic.draw(32, (T, H), "normal", 1.0, dt).to(DEV)
+    up = synthetic.draw(33, (T, H), "normal", 1.0, rdt).to(DEV)
+    dx, dres, dgam, dbet = mb.mb_add_layer_norm_bwd(dy, h, g.to(DEV), mean, rstd, dh_in=up, dresidual=True)
+    odx, odx64, omag, odres, odg, odb = oracle.add_layer_norm_bwd(dt, st(dy), oh, st(g), 1e-5, False,
+                                                                  dh_in=st(up), res_dt=rdt)
+    assert_close_bounded(st(dx), odx, odx64, K * U * omag, dt, "wide dx")
+    assert_close_bounded(st(dres), odres, odx64, K * U * omag, rdt, "wide dresidual")
+    say(f"wide dgamma {assert_reduction_close(dgam.cpu().numpy(), odg, 'dgamma')}")
+    assert_reduction_close(dbet.cpu().numpy(), odb, "dbeta")
+    dx2, dres2, dgam2, dbet2 = mb.mb_add_layer_norm_bwd(dy, h, g.to(DEV), mean, rstd, dh_in=up, dresidual=True)
+    for a, b2 in ((dx, dx2), (dres, dres2), (dgam, dgam2), (dbet, dbet2)):
+        assert torch.equal(a.view(torch.uint8), b2.view(torch.uint8))
 
 
 @pytest.mark.parametrize("H", [1024, 24576])

@@ -76,12 +76,35 @@ def test_layernorm_plans(planner, cus):
         for T in (1, 3, 4096, 16384):
             queries.append(f"ln {T} {H} 2 2 512 2 {cus}")
             keys.append((T, H))
-    for (T, H), (nvec, shape, tpr, nv, grid, split, dgb_g, partial_rows) in zip(keys, planner(queries)):
+    for (T, H), (nvec, shape, tpr, nv, grid, partial_rows) in zip(keys, planner(queries)):
         assert nvec == H // 8 and shape >= 0
         assert tpr * nv >= nvec  # the row group holds the row
         assert 1 <= grid <= max(1, 512 * cus // 256)
         assert grid <= T or T == 0
-        assert partial_rows == (dgb_g if split else grid)
+        assert partial_rows == grid
     # a row wider than 8192 vectors has no shape
     (nvec, shape, *_), = planner([f"ln 16 {8192 * 8 + 8} 2 2 512 2 {cus}"])
     assert shape == -1
+
+
+@pytest.mark.parametrize("cus", CUS)
+def test_wide_layernorm_backward_plans(planner, cus):
+    """Wide-row backward (more than 1024 vectors): one row-sum block per row (a
+    grid-stride loop past 2^20 rows); the column-strip kernel's strips cover
+    the row and its row groups (the partial rows of dgamma / dbeta) own at
+    least one row each and scale with the device."""
+    queries, keys = [], []
+    for dt, rdt in ((2, 2), (2, 0), (0, 0), (1, 1)):
+        for H in (4096, 8192, 16384, 32768, 65536):
+            for T in (1, 3, 300, 4096, 16384, 1 << 22):
+                queries.append(f"ln2 {T} {H} {dt} {rdt} {cus}")
+                keys.append((T, H, dt, rdt))
+    for (T, H, dt, rdt), (applies, nvec, rows_grid, strips, G) in zip(keys, planner(queries)):
+        E = 4 if (dt == 0 or rdt == 0) else 8
+        assert nvec == H // E and applies == (nvec > 1024)
+        assert rows_grid == min(T, 1 << 20)
+        assert strips * 64 >= nvec > (strips - 1) * 64
+        assert 1 <= G <= max(1, (T + 3) // 4) and strips * G <= max(strips, 512 * cus // 256)
+    # the tuned widths on the whole device: 4 row groups of 128 strips at 65536, 16 of 32 at 16384
+    (_, _, _, s1, g1), (_, _, _, s2, g2) = planner(["ln2 2048 65536 2 2 256", "ln2 8192 16384 2 2 256"])
+    assert (s1, g1) == (128, 4) and (s2, g2) == (32, 16)

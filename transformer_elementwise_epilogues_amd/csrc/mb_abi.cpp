@@ -660,29 +660,40 @@ mb_status_t mb_add_layer_norm_fwd(const void* x, const void* residual, mb_dtype_
   return finish();
 }
 
-// Workspace layout: partial rows of dgamma, then of dbeta, then the chunk sums
-// of each when there are more than 32 partial rows (256-byte aligned pieces).
+// Workspace layout: for the wide-row backward, the row sums ([T][2] floats);
+// then, with parameter gradients, partial rows of dgamma, of dbeta, and the
+// chunk sums of each when there are more than 32 partial rows (256-byte
+// aligned pieces).
 struct LnWs {
-  size_t pg = 0, pb = 0, tg = 0, tb = 0, total = 0;
+  bool wide = false;
+  int partial_rows = 0;
+  size_t rows = 0, pg = 0, pb = 0, tg = 0, tb = 0, total = 0;
 };
-static LnWs ln_ws_layout(const mb::LnPlan& p, int64_t H) {
+static LnWs ln_ws_layout(int64_t T, int64_t H, mb_dtype_t dt, mb_dtype_t rdt, const mb::LnPlan& p, int cus,
+                         bool params) {
   LnWs w;
-  const size_t part = round_up(static_cast<size_t>(p.partial_rows) * H * 4, 256);
-  const size_t tmp = round_up(static_cast<size_t>(mb::colsum_tall_tmp_floats(p.partial_rows, H)) * 4, 256);
-  w.pg = 0;
-  w.pb = part;
-  w.tg = 2 * part;
-  w.tb = 2 * part + tmp;
-  w.total = 2 * part + 2 * tmp;
+  w.wide = mb::ln2_applies(H, dt, rdt);
+  w.partial_rows = w.wide ? mb::plan_ln2(T, H, dt, rdt, cus).G : p.partial_rows;
+  const size_t rows = w.wide ? round_up(static_cast<size_t>(T) * 8, 256) : 0;
+  const size_t part = params ? round_up(static_cast<size_t>(w.partial_rows) * H * 4, 256) : 0;
+  const size_t tmp =
+      params ? round_up(static_cast<size_t>(mb::colsum_tall_tmp_floats(w.partial_rows, H)) * 4, 256) : 0;
+  w.rows = 0;
+  w.pg = rows;
+  w.pb = rows + part;
+  w.tg = rows + 2 * part;
+  w.tb = rows + 2 * part + tmp;
+  w.total = rows + 2 * part + 2 * tmp;
   return w;
 }
 
 size_t mb_add_layer_norm_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt, mb_dtype_t residual_dt,
                                        int with_param_grads) {
-  if (!with_param_grads || !ln_dtypes_ok(dt, residual_dt) || tokens == 0) return 0;
+  if (!ln_dtypes_ok(dt, residual_dt) || tokens <= 0) return 0;
   mb::LnPlan plan;
-  if (ln_shape(tokens, hidden, dt, residual_dt, current_cus(), &plan) != MB_OK) return 0;
-  return ln_ws_layout(plan, hidden).total;
+  const int cus = current_cus();
+  if (ln_shape(tokens, hidden, dt, residual_dt, cus, &plan) != MB_OK) return 0;
+  return ln_ws_layout(tokens, hidden, dt, residual_dt, plan, cus, with_param_grads != 0).total;
 }
 
 mb_status_t mb_add_layer_norm_bwd(const void* dy, const void* h, const void* gamma, const float* mean,
@@ -692,7 +703,8 @@ mb_status_t mb_add_layer_norm_bwd(const void* dy, const void* h, const void* gam
                                   hipStream_t s) {
   if (!ln_dtypes_ok(dt, residual_dt)) return MB_ERR_DTYPE;
   mb::LnPlan plan;
-  if (mb_status_t st = ln_shape(tokens, hidden, dt, residual_dt, stream_cus(s), &plan)) return st;
+  const int cus = stream_cus(s);
+  if (mb_status_t st = ln_shape(tokens, hidden, dt, residual_dt, cus, &plan)) return st;
   const size_t n = static_cast<size_t>(tokens) * hidden;
   const size_t tb = n * esize(dt), rb = n * esize(residual_dt), hb = static_cast<size_t>(hidden) * esize(dt),
                sb = static_cast<size_t>(tokens) * 4;
@@ -703,8 +715,8 @@ mb_status_t mb_add_layer_norm_bwd(const void* dy, const void* h, const void* gam
       !aligned(dbeta, 16) || !aligned(ws, 16))
     return MB_ERR_ALIGN;
   const bool params = dgamma || dbeta;
-  const LnWs lay = ln_ws_layout(plan, hidden);
-  const size_t need_ws = params && tokens > 0 ? lay.total : 0;
+  const LnWs lay = ln_ws_layout(tokens, hidden, dt, residual_dt, plan, cus, params);
+  const size_t need_ws = tokens > 0 ? lay.total : 0;
   if (need_ws && (!ws || ws_bytes < need_ws)) return MB_ERR_WORKSPACE;
   const size_t pb4 = static_cast<size_t>(hidden) * 4;
   if (!aliasing_ok({{dx, tb}, {dresidual, dresidual ? rb : 0}, {dgamma, dgamma ? pb4 : 0},
@@ -738,16 +750,23 @@ mb_status_t mb_add_layer_norm_bwd(const void* dy, const void* h, const void* gam
     a.pg = reinterpret_cast<float*>(w + lay.pg);
     a.pb = reinterpret_cast<float*>(w + lay.pb);
   }
-  if (hipError_t e = mb::launch_ln_bwd(a, plan, s)) return hip_status(e);
+  if (lay.wide) {
+    a.rowsums = reinterpret_cast<float*>(w + lay.rows);
+    const mb::Ln2Plan p2 = mb::plan_ln2(tokens, hidden, dt, residual_dt, cus);
+    if (hipError_t e = mb::launch_ln2_bwd(a, p2, s)) return hip_status(e);
+  } else {
+    if (hipError_t e = mb::launch_ln_bwd(a, plan, s)) return hip_status(e);
+  }
+  const int R = lay.partial_rows;
   float* tg = reinterpret_cast<float*>(w + lay.tg);
   float* tbeta = reinterpret_cast<float*>(w + lay.tb);
   if (dgamma && dbeta) {
-    if (hipError_t e = mb::launch_colsum_tall2(a.pg, a.pb, plan.partial_rows, hidden, tg, tbeta, dgamma, dbeta, s))
+    if (hipError_t e = mb::launch_colsum_tall2(a.pg, a.pb, R, hidden, tg, tbeta, dgamma, dbeta, s))
       return hip_status(e);
   } else if (dgamma) {
-    if (hipError_t e = mb::launch_colsum_tall(a.pg, plan.partial_rows, hidden, tg, dgamma, s)) return hip_status(e);
+    if (hipError_t e = mb::launch_colsum_tall(a.pg, R, hidden, tg, dgamma, s)) return hip_status(e);
   } else if (dbeta) {
-    if (hipError_t e = mb::launch_colsum_tall(a.pb, plan.partial_rows, hidden, tbeta, dbeta, s)) return hip_status(e);
+    if (hipError_t e = mb::launch_colsum_tall(a.pb, R, hidden, tbeta, dbeta, s)) return hip_status(e);
   }
   return finish();
 }

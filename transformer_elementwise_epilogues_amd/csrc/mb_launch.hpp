@@ -104,8 +104,12 @@ struct LnArgs {
   void* dres = nullptr;  // nullable
   float* pg = nullptr;   // partial rows of dgamma / dbeta [partial_rows, H]; nullable
   float* pb = nullptr;
+  float* rowsums = nullptr;  // wide-row backward: [T][2] (mean_j a, mean_j a xhat) per row
 };
 hipError_t launch_ln_fwd(const LnArgs& a, const LnPlan& p, hipStream_t s);
 hipError_t launch_ln_bwd(const LnArgs& a, const LnPlan& p, hipStream_t s);
+// backward of wide rows (plan_ln2): needs a.rowsums, and a.pg / a.pb
+// ([p.G, H]) for the parameter gradients
+hipError_t launch_ln2_bwd(const LnArgs& a, const Ln2Plan& p, hipStream_t s);
 
 }  // namespace mb

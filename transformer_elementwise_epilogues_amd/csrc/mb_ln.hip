@@ -25,10 +25,9 @@
 // dgamma = sum_t dy xhat and dbeta = sum_t dy accumulate per thread over the
 // block's rows (a block owns the same columns on every row it visits), are
 // written as one partial row per block, and summed in a fixed order by the
-// column-sum passes. For rows wider than 16384 bf16 elements (1024 threads of
-// 4 or 8 vectors each) the accumulators would not fit in registers beside the
-// row; there the row kernel writes dx only and a column-strip kernel re-reads
-// dy and h for the two parameter gradients.
+// column-sum passes. Rows of more than 1024 vectors leave no registers for
+// those sums beside a register-resident row: their backward is two kernels,
+// a row-sum kernel and a column-strip kernel (see "wide rows" below).
 #include <algorithm>
 #include <type_traits>
 
@@ -137,11 +136,6 @@ __device__ __forceinline__ void row_sum2(float& a, float& b, RowLds<W, RPB>& lds
     }
   }
 }
-
-// 1024-thread rows of 2 vectors per thread keep the parameter-gradient sums
-// in LDS (2 H floats: at most 128 KiB, as such rows hold at most 16384
-// elements).
-constexpr bool acc_in_lds(int tpr, int nv) { return tpr == 1024 && nv == 2; }
 
 #ifndef MB_LN_PREFETCH
 #define MB_LN_PREFETCH 1
@@ -313,14 +307,11 @@ __global__ __launch_bounds__(TPR* RPB) void ln_bwd_kernel(const char* __restrict
 #pragma unroll
     for (int k = 0; k < NV; ++k) gp[k] = pk_load_keep<D, E>(gamma + static_cast<size_t>(vc[k]) * XB);
   }
-  // parameter-gradient sums: in registers, or (ACC_LDS) in this block's LDS,
-  // [2][H] floats of which each thread touches only its own columns (so no
-  // barrier is needed), to leave the registers to the next row's prefetch.
-  // The register sums are added every kFlushRows rows into a second level in
-  // LDS ([RPB][2][H], again touched by the owning thread only), so their
-  // rounding error does not grow with the rows a block visits.
-  constexpr bool ACC_LDS = acc_in_lds(TPR, NV);
-  constexpr bool REG = DGB && !ACC_LDS;
+  // parameter-gradient sums in registers, added every kFlushRows rows into a
+  // second level in LDS ([RPB][2][H] floats, each touched by its owning
+  // thread only, so no barrier is needed), so that their rounding error does
+  // not grow with the rows a block visits
+  constexpr bool REG = DGB;
   extern __shared__ float lds_acc[];
   float ag[REG ? NV : 1][E], ab[REG ? NV : 1][E];
   float* hig = lds_acc + static_cast<size_t>(sub) * 2 * H;
@@ -336,13 +327,6 @@ __global__ __launch_bounds__(TPR* RPB) void ln_bwd_kernel(const char* __restrict
       if (ok[k])
 #pragma unroll
         for (int e = 0; e < E; ++e) hig[vc[k] * E + e] = hib[vc[k] * E + e] = 0.0f;
-  }
-  if constexpr (DGB && ACC_LDS) {
-#pragma unroll
-    for (int k = 0; k < NV; ++k)
-      if (ok[k])
-#pragma unroll
-        for (int e = 0; e < E; ++e) lds_acc[vc[k] * E + e] = lds_acc[H + vc[k] * E + e] = 0.0f;
   }
 
   int slot = 0;  // alternates between the two pairs of LDS slots by row
@@ -409,17 +393,6 @@ __global__ __launch_bounds__(TPR* RPB) void ln_bwd_kernel(const char* __restrict
         for (int e = 0; e < E; ++e) {
           ag[k][e] = __builtin_fmaf(gv[e], xa[e], ag[k][e]);
           ab[k][e] += gv[e];
-        }
-      }
-      if constexpr (DGB && ACC_LDS) {
-        if (ok[k]) {
-          float* cg = lds_acc + vc[k] * E;
-          float* cb = cg + H;
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            cg[e] = __builtin_fmaf(gv[e], xa[e], cg[e]);
-            cb[e] += gv[e];
-          }
         }
       }
     }
@@ -492,17 +465,7 @@ __global__ __launch_bounds__(TPR* RPB) void ln_bwd_kernel(const char* __restrict
     // one partial row per block: the RPB rows in flight combined in order
     float* rowg = pg + static_cast<size_t>(blockIdx.x) * H;
     float* rowb = pb + static_cast<size_t>(blockIdx.x) * H;
-    if constexpr (ACC_LDS) {
-#pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        if (!ok[k]) continue;
-#pragma unroll
-        for (int q = 0; q < E / 4; ++q) {
-          store_f32x4(rowg + static_cast<size_t>(vc[k]) * E + 4 * q, lds_acc + vc[k] * E + 4 * q);
-          store_f32x4(rowb + static_cast<size_t>(vc[k]) * E + 4 * q, lds_acc + H + vc[k] * E + 4 * q);
-        }
-      }
-    } else if constexpr (RPB == 1) {
+    if constexpr (RPB == 1) {
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
         if (!ok[k]) continue;
@@ -542,61 +505,192 @@ __global__ __launch_bounds__(TPR* RPB) void ln_bwd_kernel(const char* __restrict
   }
 }
 
-// dgamma / dbeta partials by column strips (the widest rows): lane = one
-// 16-byte vector of dy and h, wave w of row group y walks rows 4y + w + 4Gk.
-template <DT D>
-__global__ __launch_bounds__(kThreads) void ln_dgb_kernel(const char* __restrict__ dy, const char* __restrict__ h,
-                                                          const float* __restrict__ mean,
-                                                          const float* __restrict__ rstd, float* __restrict__ pg,
-                                                          float* __restrict__ pb, int64_t T, int nvec) {
-  constexpr int V = Vec<D>::N;
+// ---------------------------------------------------------------- wide rows
+// The backward of rows of 2048 or more vectors, whose parameter-gradient sums
+// do not fit beside a register-resident row, runs as two kernels:
+//   ln2_rowsums_kernel, one block per row: mean_j a and mean_j a xhat, read
+//     from dy and h;
+//   ln2_dx_kernel, column strips (a wave keeps the same columns on every row,
+//     so gamma and the dgamma / dbeta sums stay in registers): dx (and
+//     dresidual) from the row sums, reading dy and h a second time.
+// The second kernel walks the rows from the last one down: the rows the first
+// kernel read last are still in the memory-side cache (256 MB on MI355X), so
+// part of the second read of dy and h does not reach HBM.
+
+#ifndef MB_LN2_A_THREADS
+#define MB_LN2_A_THREADS 256  // threads per row in ln2_rowsums_kernel
+#endif
+#ifndef MB_LN2_A_UNROLL
+#define MB_LN2_A_UNROLL 4  // vectors in flight per thread there
+#endif
+#ifndef MB_LN2_B_UNROLL
+#define MB_LN2_B_UNROLL 2  // rows in flight per wave in ln2_dx_kernel
+#endif
+
+template <DT D, DT R>
+__global__ __launch_bounds__(MB_LN2_A_THREADS) void ln2_rowsums_kernel(LnArgs a, int nvec) {
+  constexpr int E = ln_epl<D, R>();
+  constexpr int XB = E * Vec<D>::BYTES, U = MB_LN2_A_UNROLL, TA = MB_LN2_A_THREADS, W = TA / 64;
+  using PD = typename Pk<D, E>::T;
+  __shared__ float part[W][2];
+  const int lt = threadIdx.x, lane = lt & 63, w = lt >> 6;
+  const char* gm = static_cast<const char*>(a.gamma);
+  for (int64_t row = blockIdx.x; row < a.T; row += gridDim.x) {
+    const size_t ro = static_cast<size_t>(row) * a.H * Vec<D>::BYTES;
+    const char* dyr = static_cast<const char*>(a.dy) + ro;
+    const char* hr = static_cast<const char*>(a.h) + ro;
+    const float mu = a.cmean[row], rs = a.crstd[row];
+    float sa = 0.0f, sax = 0.0f;
+    for (int v0 = lt; v0 < nvec; v0 += U * TA) {
+      PD gy[U], hp[U], gp[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * TA;
+        if (v < nvec) {
+          gy[u] = pk_load_keep<D, E>(dyr + static_cast<size_t>(v) * XB);
+          hp[u] = pk_load_keep<D, E>(hr + static_cast<size_t>(v) * XB);
+          gp[u] = pk_load_keep<D, E>(gm + static_cast<size_t>(v) * XB);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (v0 + u * TA >= nvec) break;
+        float gv[E], hv[E], g[E];
+        pk_unpack<D, E>(gy[u], gv);
+        pk_unpack<D, E>(hp[u], hv);
+        pk_unpack<D, E>(gp[u], g);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float xv = (hv[e] - mu) * rs;
+          const float av = gv[e] * (g[e] + a.gshift);
+          sa += av;
+          sax = __builtin_fmaf(av, xv, sax);
+        }
+      }
+    }
+    sa = wave_sum(sa);
+    sax = wave_sum(sax);
+    if (lane == 0) {
+      part[w][0] = sa;
+      part[w][1] = sax;
+    }
+    __syncthreads();
+    if (lt == 0) {
+      float ta = part[0][0], tx = part[0][1];
+#pragma unroll
+      for (int k = 1; k < W; ++k) {
+        ta += part[k][0];
+        tx += part[k][1];
+      }
+      const float fh = static_cast<float>(a.H);
+      a.rowsums[2 * row] = ta / fh;
+      a.rowsums[2 * row + 1] = tx / fh;
+    }
+    __syncthreads();  // part is reused by the block's next row
+  }
+}
+
+// dx (and dresidual) for the strip's columns on every row, and the strip's
+// dgamma / dbeta sums as partial row rg ([G][H] in a.pg / a.pb). Wave w of row
+// group rg takes the rows T - 1 - (4 rg + w + 4 G k).
+template <DT D, DT R> __global__ __launch_bounds__(kThreads) void ln2_dx_kernel(LnArgs a, int nvec) {
+  constexpr int E = ln_epl<D, R>();
+  constexpr int XB = E * Vec<D>::BYTES, RB = E * Vec<R>::BYTES, U = MB_LN2_B_UNROLL;
+  using PD = typename Pk<D, E>::T;
+  using PR = typename Pk<R, E>::T;
+  __shared__ float red[kWaves][2 * E][64];
+  const int lane = threadIdx.x & 63, w = wave_index<true>();
   const TileIdx ti = tile_idx();
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int cv = ti.strip * kStrip + lane;
   const bool active = cv < nvec;
-  const size_t pitch = static_cast<size_t>(nvec) * 16, col = static_cast<size_t>(cv) * 16;
-  ColAcc<V> cg, cb;
+  const size_t cx = static_cast<size_t>(cv) * XB, cr = static_cast<size_t>(cv) * RB;
+  ColAcc<E> cg, cb;
   cg.init();
   cb.init();
   if (active) {
-    for (int64_t t = static_cast<int64_t>(ti.rg) * kWaves + w; t < T; t += static_cast<int64_t>(kWaves) * ti.G) {
-      float g[V], x[V];
-      unpack<D>(ld_stream(dy + t * pitch + col), g);
-      unpack<D>(ld_stream(h + t * pitch + col), x);
-      const float mu = mean[t], rs = rstd[t];
+    float g[E];
+    pk_unpack<D, E>(pk_load_keep<D, E>(static_cast<const char*>(a.gamma) + cx), g);
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        cg.lo[e] = __builtin_fmaf(g[e], (x[e] - mu) * rs, cg.lo[e]);
-        cb.lo[e] += g[e];
+    for (int e = 0; e < E; ++e) g[e] += a.gshift;
+    const size_t px = static_cast<size_t>(a.H) * Vec<D>::BYTES, pr = static_cast<size_t>(a.H) * Vec<R>::BYTES;
+    const char* dy = static_cast<const char*>(a.dy);
+    const char* h = static_cast<const char*>(a.h);
+    const char* up = static_cast<const char*>(a.dh_in);
+    char* dx = static_cast<char*>(a.dx);
+    char* dres = static_cast<char*>(a.dres);
+    const int64_t T = a.T, S = static_cast<int64_t>(kWaves) * ti.G;
+    for (int64_t t = static_cast<int64_t>(ti.rg) * kWaves + w; t < T; t += U * S) {
+      PD gy[U], hp[U];
+      PR uu[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (t + u * S < T) {
+          const int64_t tt = T - 1 - (t + u * S);
+          gy[u] = pk_load_keep<D, E>(dy + tt * px + cx);
+          hp[u] = pk_load_keep<D, E>(h + tt * px + cx);
+          if (up) uu[u] = pk_load<R, E>(up + tt * pr + cr);
+        }
       }
-      cg.tick(1);
-      cb.tick(1);
+      int rows = 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (t + u * S >= T) break;
+        const int64_t tt = T - 1 - (t + u * S);
+        ++rows;
+        const float mu = a.cmean[tt], rs = a.crstd[tt], ma = a.rowsums[2 * tt], mx = a.rowsums[2 * tt + 1];
+        float gv[E], hv[E], uv[E];
+        pk_unpack<D, E>(gy[u], gv);
+        pk_unpack<D, E>(hp[u], hv);
+        if (up) {
+          pk_unpack<R, E>(uu[u], uv);
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) uv[e] = 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float xv = (hv[e] - mu) * rs;
+          cg.lo[e] = __builtin_fmaf(gv[e], xv, cg.lo[e]);
+          cb.lo[e] += gv[e];
+          gv[e] = __builtin_fmaf(rs, __builtin_fmaf(-xv, mx, gv[e] * g[e] - ma), uv[e]);
+        }
+        pk_store<D, E>(dx + tt * px + cx, pk_pack<D, E>(gv));
+        if (dres) pk_store<R, E>(dres + tt * pr + cr, pk_pack<R, E>(gv));
+      }
+      cg.tick(rows);
+      cb.tick(rows);
     }
   }
-  float ag[V], ab[V];
-  cg.total(ag);
-  cb.total(ab);
-  __shared__ float red[kWaves][2 * V][64];
+  if (!a.pg) return;  // uniform over the launch
+  float sg[E], sb[E];
+  cg.total(sg);
+  cb.total(sb);
 #pragma unroll
-  for (int e = 0; e < V; ++e) {
-    red[w][e][lane] = ag[e];
-    red[w][V + e][lane] = ab[e];
+  for (int e = 0; e < E; ++e) {
+    red[w][e][lane] = sg[e];
+    red[w][E + e][lane] = sb[e];
   }
   __syncthreads();
   if (w == 0 && active) {
-    float sg[V], sb[V];
 #pragma unroll
-    for (int e = 0; e < V; ++e) {
+    for (int e = 0; e < E; ++e) {
       sg[e] = ((red[0][e][lane] + red[1][e][lane]) + red[2][e][lane]) + red[3][e][lane];
-      sb[e] = ((red[0][V + e][lane] + red[1][V + e][lane]) + red[2][V + e][lane]) + red[3][V + e][lane];
+      sb[e] = ((red[0][E + e][lane] + red[1][E + e][lane]) + red[2][E + e][lane]) + red[3][E + e][lane];
     }
-    const size_t o = static_cast<size_t>(ti.rg) * nvec * V + static_cast<size_t>(cv) * V;
+    const size_t o = static_cast<size_t>(ti.rg) * a.H + static_cast<size_t>(cv) * E;
 #pragma unroll
-    for (int q = 0; q < V / 4; ++q) {
-      store_f32x4(pg + o + 4 * q, sg + 4 * q);
-      store_f32x4(pb + o + 4 * q, sb + 4 * q);
+    for (int q = 0; q < E / 4; ++q) {
+      store_f32x4(a.pg + o + 4 * q, sg + 4 * q);
+      store_f32x4(a.pb + o + 4 * q, sb + 4 * q);
     }
   }
+}
+
+template <DT D, DT R> hipError_t ln2_bwd_run(const LnArgs& a, const Ln2Plan& p, hipStream_t s) {
+  hipLaunchKernelGGL((ln2_rowsums_kernel<D, R>), dim3(p.rows_grid), dim3(MB_LN2_A_THREADS), 0, s, a, p.nvec);
+  if (hipError_t e = hipGetLastError()) return e;
+  hipLaunchKernelGGL((ln2_dx_kernel<D, R>), tile_grid(p.strips, p.G), dim3(kThreads), 0, s, a, p.nvec);
+  return hipGetLastError();
 }
 
 template <DT D, DT R, int S>
@@ -610,36 +704,34 @@ hipError_t fwd_shape(const LnArgs& a, const LnPlan& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Backward rows of at most 1024 vectors (wider ones take the wide-row kernels),
+// so the row kernel's shapes hold at most 1024 vectors here.
+template <int S> constexpr bool bwd_shape_used() { return kLnShapes[S].tpr * kLnShapes[S].nv <= MB_LN2_ROW_VEC; }
+
 template <DT D, DT R, int S>
 hipError_t bwd_shape(const LnArgs& a, const LnPlan& p, hipStream_t s) {
   constexpr LnShape sh = kLnShapes[S];
-  const auto dy = static_cast<const char*>(a.dy);
-  const auto h = static_cast<const char*>(a.h);
-  const auto gamma = static_cast<const char*>(a.gamma);
-  const auto dh_in = static_cast<const char*>(a.dh_in);
-  const auto dx = static_cast<char*>(a.dx);
-  const auto dres = static_cast<char*>(a.dres);
-  const int H = static_cast<int>(a.H);
-  const dim3 grid(p.grid), block(sh.tpr * sh.rpb);
-  if constexpr (ln_split_shape(S)) {
-    // the column pass reads dy and h before the row pass may overwrite them
-    // (dx and dresidual may alias dy or h)
-    if (a.pg) {
-      hipLaunchKernelGGL((ln_dgb_kernel<D>), tile_grid(p.dgb.strips, p.dgb.G), dim3(kThreads), 0, s, dy, h, a.cmean,
-                         a.crstd, a.pg, a.pb, a.T, p.dgb.nvec);
-      if (hipError_t e = hipGetLastError()) return e;
-    }
-    hipLaunchKernelGGL((ln_bwd_kernel<D, R, sh.tpr, sh.nv, sh.rpb, false>), grid, block, 0, s, dy, h, gamma, a.cmean,
-                       a.crstd, dh_in, dx, dres, nullptr, nullptr, a.T, H, a.gshift);
-  } else if (a.pg) {
-    const size_t shm = (acc_in_lds(sh.tpr, sh.nv) ? 1 : sh.rpb) * 2 * static_cast<size_t>(H) * sizeof(float);
-    hipLaunchKernelGGL((ln_bwd_kernel<D, R, sh.tpr, sh.nv, sh.rpb, true>), grid, block, shm, s, dy, h, gamma,
-                       a.cmean, a.crstd, dh_in, dx, dres, a.pg, a.pb, a.T, H, a.gshift);
+  if constexpr (!bwd_shape_used<S>()) {
+    return hipErrorInvalidValue;
   } else {
-    hipLaunchKernelGGL((ln_bwd_kernel<D, R, sh.tpr, sh.nv, sh.rpb, false>), grid, block, 0, s, dy, h, gamma, a.cmean,
-                       a.crstd, dh_in, dx, dres, nullptr, nullptr, a.T, H, a.gshift);
+    const auto dy = static_cast<const char*>(a.dy);
+    const auto h = static_cast<const char*>(a.h);
+    const auto gamma = static_cast<const char*>(a.gamma);
+    const auto dh_in = static_cast<const char*>(a.dh_in);
+    const auto dx = static_cast<char*>(a.dx);
+    const auto dres = static_cast<char*>(a.dres);
+    const int H = static_cast<int>(a.H);
+    const dim3 grid(p.grid), block(sh.tpr * sh.rpb);
+    if (a.pg) {
+      const size_t shm = sh.rpb * 2 * static_cast<size_t>(H) * sizeof(float);
+      hipLaunchKernelGGL((ln_bwd_kernel<D, R, sh.tpr, sh.nv, sh.rpb, true>), grid, block, shm, s, dy, h, gamma,
+                         a.cmean, a.crstd, dh_in, dx, dres, a.pg, a.pb, a.T, H, a.gshift);
+    } else {
+      hipLaunchKernelGGL((ln_bwd_kernel<D, R, sh.tpr, sh.nv, sh.rpb, false>), grid, block, 0, s, dy, h, gamma,
+                         a.cmean, a.crstd, dh_in, dx, dres, nullptr, nullptr, a.T, H, a.gshift);
+    }
+    return hipGetLastError();
   }
-  return hipGetLastError();
 }
 
 template <DT D, DT R, bool BWD, int S = 0>
@@ -667,5 +759,14 @@ hipError_t by_dtype(const LnArgs& a, const LnPlan& p, hipStream_t s) {
 
 hipError_t launch_ln_fwd(const LnArgs& a, const LnPlan& p, hipStream_t s) { return by_dtype<false>(a, p, s); }
 hipError_t launch_ln_bwd(const LnArgs& a, const LnPlan& p, hipStream_t s) { return by_dtype<true>(a, p, s); }
+hipError_t launch_ln2_bwd(const LnArgs& a, const Ln2Plan& p, hipStream_t s) {
+  const DT d = static_cast<DT>(a.dt), r = static_cast<DT>(a.rdt);
+  if (d == DT::F32 && r == DT::F32) return ln2_bwd_run<DT::F32, DT::F32>(a, p, s);
+  if (d == DT::BF16 && r == DT::BF16) return ln2_bwd_run<DT::BF16, DT::BF16>(a, p, s);
+  if (d == DT::BF16 && r == DT::F32) return ln2_bwd_run<DT::BF16, DT::F32>(a, p, s);
+  if (d == DT::F16 && r == DT::F16) return ln2_bwd_run<DT::F16, DT::F16>(a, p, s);
+  if (d == DT::F16 && r == DT::F32) return ln2_bwd_run<DT::F16, DT::F32>(a, p, s);
+  return hipErrorInvalidValue;
+}
 
 }  // namespace mb

@@ -60,12 +60,19 @@ LnPlan plan_ln(int64_t T, int64_t H, int dt, int rdt, int target_blocks, int nv_
   const LnShape sh = kLnShapes[p.shape];
   const int64_t groups = (T + sh.rpb - 1) / sh.rpb;
   p.grid = static_cast<int>(std::min<int64_t>(std::max<int64_t>(groups, 1), scaled_blocks(target_blocks, cus)));
-  p.split = ln_split_shape(p.shape);
-  // the column-strip kernel's 16-byte vectors (only used when split, for rows
-  // of 16384 or more elements; a row narrower than one vector still plans)
-  const int v16 = std::max(1, static_cast<int>(H * (dt == 0 ? 4 : 2) / 16));
-  p.dgb = plan_tiling(T, v16, MB_LN_DGB_BLOCKS, cus);
-  p.partial_rows = p.split ? p.dgb.G : p.grid;
+  p.partial_rows = p.grid;
+  return p;
+}
+
+bool ln2_applies(int64_t H, int dt, int rdt) { return H / ln_elems_per_vector(dt, rdt) > MB_LN2_ROW_VEC; }
+
+Ln2Plan plan_ln2(int64_t T, int64_t H, int dt, int rdt, int cus) {
+  Ln2Plan p;
+  p.nvec = static_cast<int>(H / ln_elems_per_vector(dt, rdt));
+  p.rows_grid = static_cast<int>(std::min<int64_t>(std::max<int64_t>(T, 1), 1 << 20));
+  const Tiling t = plan_tiling(T, p.nvec, MB_LN2_B_BLOCKS, cus);
+  p.strips = t.strips;
+  p.G = t.G;
   return p;
 }
 

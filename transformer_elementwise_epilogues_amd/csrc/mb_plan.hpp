@@ -134,9 +134,6 @@ struct Tiling {
 #ifndef MB_LN_BWD_BLOCKS_WIDE
 #define MB_LN_BWD_BLOCKS_WIDE 256
 #endif
-#ifndef MB_LN_DGB_BLOCKS
-#define MB_LN_DGB_BLOCKS 512
-#endif
 // preferred vectors per thread (the row is split over more threads below it)
 #ifndef MB_LN_FWD_NV
 #define MB_LN_FWD_NV 4
@@ -181,29 +178,34 @@ constexpr LnShape kLnShapes[] = {{64, 1, 4},  {64, 2, 4},  {64, 4, 4},  {256, 1,
                                  {256, 4, 1}, {512, 1, 1}, {512, 2, 1}, {512, 4, 1},  {1024, 1, 1},
                                  {1024, 2, 1}, {1024, 4, 1}, {1024, 8, 1}, {512, 8, 1}};
 constexpr int kLnNumShapes = sizeof(kLnShapes) / sizeof(kLnShapes[0]);
-// dgamma / dbeta come from the column-strip kernel (which reads dy and h once
-// more) for 1024-thread rows of 2 or more vectors per thread: beyond 2 the
-// per-thread accumulators would not fit beside the row in the 128 registers
-// a thread of such a block has, and at 2 (rows of 2048 vectors) holding them
-// in LDS (128 KiB per block, one block per CU) ran 22 % slower than the
-// column-strip kernel on MI355X. (MB_LN_SPLIT_MIN_NV 4 restores the LDS sums.)
-#ifndef MB_LN_SPLIT_MIN_NV
-#define MB_LN_SPLIT_MIN_NV 2
-#endif
-constexpr bool ln_split_shape(int s) {
-  return (kLnShapes[s].tpr == 1024 && kLnShapes[s].nv >= MB_LN_SPLIT_MIN_NV) || kLnShapes[s].nv >= 8;
-}
-
 struct LnPlan {
   int nvec = 0;           // vectors of ln_elems_per_vector elements per row
   int shape = -1;         // row-group shape; -1: the row is too wide
   int grid = 0;           // blocks of the row kernels
-  bool split = false;     // dgamma / dbeta by the column-strip kernel
-  Tiling dgb;             // its tiling
-  int partial_rows = 0;   // partial rows the backward writes
+  int partial_rows = 0;   // partial rows the backward writes (one per block)
 };
 int ln_elems_per_vector(int dt, int rdt);
 LnPlan plan_ln(int64_t T, int64_t H, int dt, int rdt, int target_blocks, int nv_pref, int cus);
+
+// ---- backward of wide LayerNorm rows (more than MB_LN2_ROW_VEC vectors,
+// too wide to keep the parameter-gradient sums beside a register-resident
+// row): a row-sum kernel (one block per row), then a column-strip kernel for
+// dx and the parameter-gradient partial rows
+#ifndef MB_LN2_ROW_VEC
+#define MB_LN2_ROW_VEC 1024
+#endif
+#ifndef MB_LN2_B_BLOCKS
+#define MB_LN2_B_BLOCKS 512
+#endif
+struct Ln2Plan {
+  int nvec = 0;       // vectors of ln_elems_per_vector elements per row
+  int rows_grid = 0;  // blocks of the row-sum kernel (one row each, grid-stride)
+  int strips = 0;     // column strips of 64 vectors
+  int G = 0;          // row groups of the column-strip kernel: dgamma / dbeta partial rows
+};
+// rows of H elements take the wide-row backward (H a whole number of vectors)
+bool ln2_applies(int64_t H, int dt, int rdt);
+Ln2Plan plan_ln2(int64_t T, int64_t H, int dt, int rdt, int cus);
 // the plan's row group is `tpr` threads of `nv` vectors
 bool ln_plan_is(const LnPlan& p, int tpr, int nv);
 
