@@ -550,11 +550,13 @@ def cpu_info():
 
 def oracle_plan(host):
     """Per op name: (oracle over rows [r0, r1) -> {output: (kind, expected...)},
-    algorithmic bytes of n rows, rows of the op). Kinds: "elem" (storage, o64,
-    mag), "bounded" (storage, o64, bound), "exact" (storage), "rowsum" (o64)."""
+    algorithmic bytes of n rows, rows of the op, oracle32 over rows [r0, r1) ->
+    {output: storage}). Kinds: "elem" (storage, o64, mag), "bounded"
+    (storage, o64, bound), "exact" (storage), "rowsum" (o64)."""
     import numpy as np
 
     import oracle
+    from oracle import oracle32
     from oracle.tolerances import to_storage
 
     def rows(w, t, r0, r1):
@@ -583,6 +585,55 @@ def oracle_plan(host):
                 res["dresidual"] = ("exact", dres)
             return res
         return f
+
+    # oracle32: the same rows in binary32, the secondary statistic and the fp32 CPU baseline
+    plan32 = {}
+
+    def bda32(w, xn, bn, rn, rdt, train, p, seed):
+        return lambda r0, r1: {"out": oracle32.bias_dropout_add("bf16", rows(w, xn, r0, r1), vec(w, bn),
+                                                                rows(w, rn, r0, r1), rdt, train, p, seed, 0, row0=r0)}
+
+    def bda_bwd32(w, gn, rdt, p, seed):
+        return lambda r0, r1: {"dx": oracle32.bias_dropout_add_bwd("bf16", rows(w, gn, r0, r1), rdt, p, seed, 0,
+                                                                   row0=r0, want_dres=False)[0]}
+
+    plan32["bda_train_bf16_res_f32_8192x4096"] = bda32(c2, "x", "bias", "residual", "f32", True, 0.1, 1234)
+    plan32["bda_bwd_bf16_res_f32_8192x4096"] = bda_bwd32(c2, "g", "f32", 0.1, 1234)
+    plan32["bda_infer_inplace_bf16_res_f32_8192x4096"] = bda32(c2, "x", "bias", "residual", "f32", False, 0.0, 0)
+    plan32["chain_attn_bda_train_bf16_16384x8192"] = bda32(c5, "attn_x", "attn_bias", "attn_residual", "bf16", True,
+                                                           0.1, 5001)
+    plan32["chain_mlp_bda_train_bf16_16384x8192"] = bda32(c5, "mlp_x", "mlp_bias", "mlp_residual", "bf16", True, 0.1,
+                                                          5002)
+    plan32["chain_mlp_bda_bwd_bf16_16384x8192"] = bda_bwd32(c5, "mlp_g", "bf16", 0.1, 5002)
+    plan32["chain_attn_bda_bwd_bf16_16384x8192"] = bda_bwd32(c5, "attn_g", "bf16", 0.1, 5001)
+
+    def glu32(w, act, wt, bwd):
+        def f(r0, r1):
+            wts = None if wt is None else rows(w, wt, r0, r1)
+            if bwd:
+                return {"din": oracle32.bias_glu_bwd(act, "bf16", rows(w, "g", r0, r1), rows(w, "in", r0, r1),
+                                                     vec(w, "bias"), wts)[0]}
+            return {"out": oracle32.bias_glu_fwd(act, "bf16", rows(w, "in", r0, r1), vec(w, "bias"), wts)}
+        return f
+
+    for name, wt in (("swiglu", None), ("weighted_swiglu", "weights")):
+        plan32[f"{name}_fwd_bf16_8192x14336"] = glu32(c3, "swiglu", wt, False)
+        plan32[f"{name}_bwd_bf16_8192x14336"] = glu32(c3, "swiglu", wt, True)
+    plan32["geglu_fwd_bf16_16384x8192"] = glu32(c4, "geglu", None, False)
+    plan32["geglu_bwd_bf16_16384x8192"] = glu32(c4, "geglu", None, True)
+
+    def gelu32(exact, bwd):
+        def f(r0, r1):
+            y, b = rows(c5, "gelu_y", r0, r1), vec(c5, "gelu_bias")
+            if bwd:
+                return {"dgrad": oracle32.bias_gelu_bwd("bf16", rows(c5, "gelu_g", r0, r1), y, b, exact=exact)[0]}
+            return {"out": oracle32.bias_gelu_fwd("bf16", y, b, exact=exact)}
+        return f
+
+    plan32["chain_gelu_fwd_bf16_16384x32768"] = gelu32(False, False)
+    plan32["chain_gelu_bwd_bf16_16384x32768"] = gelu32(False, True)
+    plan32["erf_gelu_fwd_bf16_16384x32768"] = gelu32(True, False)
+    plan32["erf_gelu_bwd_bf16_16384x32768"] = gelu32(True, True)
 
     plan["bda_train_bf16_res_f32_8192x4096"] = (bda(c2, "x", "bias", "residual", "f32", True, 0.1, 1234),
                                                 lambda n: n * 4096 * 8 + 4096 * 2)
@@ -657,8 +708,21 @@ def oracle_plan(host):
                                                                True, dh_in=rows(w, "dh_in", r0, r1), want_dres=False)
             return {"dx": ("bounded", dx, dx64, kb * mag)}
 
+        def ln_fwd32(r0, r1, w=wname):
+            h, y, _, _ = oracle32.add_layer_norm_fwd("bf16", rows(w, "x", r0, r1), rows(w, "residual", r0, r1), "bf16",
+                                                     vec(w, "gamma"), vec(w, "beta"), 1e-5, True)
+            return {"h": h, "y": y}
+
+        def ln_bwd32(r0, r1, w=wname):
+            h = ln_fwd32(r0, r1, w)["h"]
+            dx, _, _, _ = oracle32.add_layer_norm_bwd("bf16", rows(w, "dy", r0, r1), h, vec(w, "gamma"), 1e-5, True,
+                                                      dh_in=rows(w, "dh_in", r0, r1), want_dres=False)
+            return {"dx": dx}
+
         plan[f"add_ln_fwd_{tag}"] = (ln_fwd, lambda n, H=H: n * H * 8 + H * 4 + n * 8)
         plan[f"add_ln_bwd_{tag}"] = (ln_bwd, lambda n, H=H: n * H * 8 + H * 2 + n * 8 + H * 8)
+        plan32[f"add_ln_fwd_{tag}"] = ln_fwd32
+        plan32[f"add_ln_bwd_{tag}"] = ln_bwd32
 
     c7 = "wsrelu_bf16_8192x14336"
 
@@ -673,6 +737,10 @@ def oracle_plan(host):
 
     plan["weighted_squared_relu_fwd_bf16_8192x14336"] = (srelu_fwd, lambda n: n * 14336 * 4 + n * 4)
     plan["weighted_squared_relu_bwd_bf16_8192x14336"] = (srelu_bwd, lambda n: n * 14336 * 6 + n * 8)
+    plan32["weighted_squared_relu_fwd_bf16_8192x14336"] = lambda r0, r1: {"out": oracle32.weighted_squared_relu_fwd(
+        "bf16", rows(c7, "x", r0, r1), rows(c7, "weights", r0, r1), "f32")}
+    plan32["weighted_squared_relu_bwd_bf16_8192x14336"] = lambda r0, r1: {"dx": oracle32.weighted_squared_relu_bwd(
+        "bf16", rows(c7, "g", r0, r1), rows(c7, "x", r0, r1), rows(c7, "weights", r0, r1), "f32")[0]}
     del np
     rows_of = {"bda_": c2, "swiglu": c3, "weighted_swiglu": c3, "geglu": c4, "chain_": c5, "erf_gelu": c5,
                "weighted_squared": "wsrelu_bf16_8192x14336"}
@@ -683,7 +751,7 @@ def oracle_plan(host):
         else:
             w = next(v for k, v in rows_of.items() if name.startswith(k))
         first = next(t for (wn, _), t in host.items() if wn == w and t.dim() == 2)
-        out[name] = (f, nb, first.shape[0])
+        out[name] = (f, nb, first.shape[0], plan32[name])
     return out
 
 
@@ -726,11 +794,37 @@ def parity_stats(expected, got):
     return res
 
 
+def oracle32_stats(exp32, got):
+    """Secondary statistic per output: the GPU's storage against oracle32's
+    (the formulas in binary32): elements bit-equal, and the largest distance in
+    units of the last place of the storage type."""
+    import numpy as np
+
+    res = {}
+    for name, e in exp32.items():
+        if name not in got:
+            continue
+        k = got[name]
+        if k.dtype == np.float32:
+            ki, ei = k.view(np.int32).astype(np.int64), e.view(np.int32).astype(np.int64)
+            ki = np.where(ki < 0, -(ki & 0x7FFFFFFF), ki)
+            ei = np.where(ei < 0, -(ei & 0x7FFFFFFF), ei)
+        else:
+            ki, ei = k.view(np.int16).astype(np.int64), e.view(np.int16).astype(np.int64)
+            ki = np.where(ki < 0, -(ki & 0x7FFF), ki)
+            ei = np.where(ei < 0, -(ei & 0x7FFF), ei)
+        d = np.abs(ki - ei)
+        res[name] = {"n": int(d.size), "bit_equal": int((d == 0).sum()), "max_ulp": int(d.max()) if d.size else 0}
+    return res
+
+
 def cpu_baseline(host, gpu_rows, seconds, max_rows=512, max_threads=16):
     """The oracle (C, fp64) on the first rows of every op's inputs, as the same
     algorithmic bytes per second: on one pinned core, and on a pool of threads
     over row chunks (the oracle's calls release the interpreter lock); the
-    single-core outputs are compared with the GPU's rows."""
+    single-core outputs are compared with the GPU's rows. oracle32 (the same
+    formulas in binary32) is timed the same way on the same rows, and the GPU's
+    rows are compared with it as a secondary statistic."""
     from oracle.tolerances import to_storage
 
     plan = oracle_plan(host)
@@ -749,43 +843,58 @@ def cpu_baseline(host, gpu_rows, seconds, max_rows=512, max_threads=16):
         probe = time.perf_counter() - t0
         n1 = max(2, min(max_rows, int(2 * seconds / max(probe, 1e-6))))
         tot_b, tot_s, per, parity = 0, 0.0, {}, {}
+        tot_s32, per32 = 0.0, {}
         for name in names:
-            f, nb, _ = plan[name]
+            f, nb, _, f32 = plan[name]
             t0 = time.perf_counter()
             exp = f(0, n1)
             dt = time.perf_counter() - t0
             tot_b += nb(n1)
             tot_s += dt
             per[name] = round(nb(n1) / dt / 1e9, 4)
+            t0 = time.perf_counter()
+            exp32 = f32(0, n1)
+            dt32 = time.perf_counter() - t0
+            tot_s32 += dt32
+            per32[name] = round(nb(n1) / dt32 / 1e9, 4)
             got = {k: (to_storage(v[:n1]) if v.dim() == 2 else v[:n1].double().numpy()) for k, v in gpu_rows[name].items()}
             parity[name] = parity_stats(exp, got)
+            parity[name]["vs_oracle32"] = oracle32_stats(exp32, got)
         single = {"value": round(tot_b / tot_s / 1e9, 4), "cores": 1, "rows": n1, "seconds": round(tot_s, 2),
                   "per_op_gbs": per}
+        single32 = {"value": round(tot_b / tot_s32 / 1e9, 4), "cores": 1, "rows": n1, "seconds": round(tot_s32, 2),
+                    "per_op_gbs": per32}
     finally:
         if old_aff is not None:
             os.sched_setaffinity(0, old_aff)
     # the thread pool: row chunks of a larger sample (the oracle is row-local;
     # the dropout rows carry their global row index), same ops
     want = max(threads * 2, n1 * threads)
-    tot_b, tot_s, rows_used = 0, 0.0, {}
+    tot_b, tot_s, tot_s32, rows_used = 0, 0.0, 0.0, {}
     with ThreadPoolExecutor(threads) as ex:
         for name in names:
-            f, nb, T = plan[name]
+            f, nb, T, f32 = plan[name]
             nt = min(want, T)
             step = (nt + threads - 1) // threads
             chunks = [(r0, min(nt, r0 + step)) for r0 in range(0, nt, step)]
             t0 = time.perf_counter()
             list(ex.map(lambda c: f(*c), chunks))
             tot_s += time.perf_counter() - t0
+            t0 = time.perf_counter()
+            list(ex.map(lambda c: f32(*c), chunks))
+            tot_s32 += time.perf_counter() - t0
             tot_b += nb(nt)
             rows_used[name] = nt
     nt = max(rows_used.values())
     pool = {"value": round(tot_b / tot_s / 1e9, 4), "cores": threads, "rows": rows_used, "seconds": round(tot_s, 2)}
+    pool32 = {"value": round(tot_b / tot_s32 / 1e9, 4), "cores": threads, "seconds": round(tot_s32, 2)}
     return {"value": pool["value"], "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"first min({want}, T) rows of every op's inputs (same ops, shapes and seeds as the GPU "
                       f"step and next rows), fp64 C oracle over {threads} threads in row chunks, {pool['seconds']} s; "
                       f"single pinned core: first {n1} rows, {single['value']} GB/s",
-            "cpu": info, "single_core": single, "thread_pool": pool}, parity
+            "cpu": info, "single_core": single, "thread_pool": pool,
+            "oracle32": {"note": "the same formulas in binary32 (plain fp32 scalar C), same rows",
+                         "single_core": single32, "thread_pool": pool32}}, parity
 
 
 # ------------------------------------------------------------------ main

@@ -21,6 +21,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
+_SRCS = [_SRC, os.path.join(_HERE, "oracle32.c")]  # oracle32.c: the same formulas in binary32
 _LIB = os.path.join(_HERE, "liboracle.so")
 _CFLAGS = ["-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 
@@ -33,10 +34,10 @@ _lib = None
 
 def build(force: bool = False) -> str:
     """Compile liboracle.so with gcc (no fast-math, no FMA contraction)."""
-    stale = not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)
+    stale = not os.path.exists(_LIB) or any(os.path.getmtime(_LIB) < os.path.getmtime(f) for f in _SRCS)
     if force or stale:
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.run(["gcc", *_CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        subprocess.run(["gcc", *_CFLAGS, *_SRCS, "-o", tmp, "-lm"], check=True)
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -84,6 +85,17 @@ def lib() -> ctypes.CDLL:
             L.orc_keep_scale.restype = F
             L.orc_decode.argtypes = [I, P, I64]
             L.orc_decode.restype = D
+            # oracle32 (oracle32.c)
+            L.orc32_bias_gelu_fwd.argtypes = [I, I, P, P, P, I64, I64]
+            L.orc32_bias_gelu_bwd.argtypes = [I, I, P, P, P, P, P, I64, I64]
+            L.orc32_bias_dropout_add.argtypes = [I, P, P, P, I, P, I64, I64, I, F, U64, U64, I64]
+            L.orc32_bias_dropout_add_bwd.argtypes = [I, P, I, P, P, P, I64, I64, F, U64, U64, I64]
+            L.orc32_bias_glu_fwd.argtypes = [I, I, P, P, P, I, P, I64, I64]
+            L.orc32_bias_glu_bwd.argtypes = [I, I, P, P, P, P, I, P, P, P, I64, I64]
+            L.orc32_add_layer_norm_fwd.argtypes = [I, P, P, I, P, P, I, F, P, P, P, P, I64, I64]
+            L.orc32_add_layer_norm_bwd.argtypes = [I, P, P, P, I, F, P, I, P, P, P, P, I64, I64]
+            L.orc32_weighted_squared_relu_fwd.argtypes = [I, P, P, I, P, I64, I64]
+            L.orc32_weighted_squared_relu_bwd.argtypes = [I, P, P, P, I, P, P, I64, I64]
             _lib = L
     return _lib
 

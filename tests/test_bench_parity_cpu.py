@@ -1,7 +1,8 @@
 """The benchmark's CPU-baseline leg on small inputs, without a GPU: every op
-of the step and of the next rows has an oracle plan, the thread-pool leg
-covers row chunks, and the parity statistics of outputs equal to the
-oracle's report no failures (and do report a planted one)."""
+of the step and of the next rows has an oracle plan (fp64, and its binary32
+twin oracle32), the thread-pool leg covers row chunks, and the parity
+statistics of outputs equal to the oracle's report no failures (and do report
+a planted one)."""
 import numpy as np
 import torch
 
@@ -33,8 +34,10 @@ def test_cpu_baseline_and_parity_plumbing():
     plan = bench.oracle_plan(host)
     assert len(plan) == 25
     gpu_rows = {}
-    for name, (f, _, T) in plan.items():
+    for name, (f, _, T, f32) in plan.items():
         assert T == ROWS
+        o32 = f32(0, ROWS)  # the binary32 twin covers the op's primary outputs
+        assert o32 and set(o32) <= set(f(0, ROWS))
         exp = f(0, ROWS)
         gpu_rows[name] = {}
         for k, e in exp.items():
@@ -49,7 +52,13 @@ def test_cpu_baseline_and_parity_plumbing():
     assert set(parity) == set(plan)
     for name, outs in parity.items():
         for out, st in outs.items():
+            if out == "vs_oracle32":
+                for o, s32 in st.items():  # the GPU rows here are the fp64 oracle's: close to oracle32's
+                    assert 0 < s32["bit_equal"] <= s32["n"] and s32["max_ulp"] >= 0, (name, o, s32)
+                continue
             assert st["fail"] == 0, (name, out, st)
+    o32 = cpu["oracle32"]
+    assert o32["single_core"]["value"] > 0 and o32["thread_pool"]["value"] > 0
     # a planted difference in one output element is counted
     g = gpu_rows["chain_gelu_fwd_bf16_16384x32768"]["out"]
     g.view(torch.int16)[0, 0] += 3

@@ -1,6 +1,6 @@
 """Host code under the address and undefined-behaviour sanitizers (no GPU):
-the oracle (oracle/oracle.c) on every entry point with edge and special
-values, and the C ABI's validation, workspace queries and launch planning
+the oracle (oracle/oracle.c, and its binary32 twin oracle32.c) on every
+entry point with edge and special values, and the C ABI's validation, workspace queries and launch planning
 (mb_abi.cpp, mb_plan.cpp) with hostile arguments, linked against launch
 stand-ins. Any out-of-bounds access, signed overflow, misaligned or invalid
 operation aborts the program and fails the test."""
@@ -30,6 +30,14 @@ def test_oracle_sanitized(tmp_path):
     exe = str(tmp_path / "oracle_san")
     run(["gcc", "-std=c11", "-ffp-contract=off", "-fno-fast-math", *SAN, os.path.join(ROOT, "oracle", "oracle.c"),
          os.path.join(HERE, "oracle_driver.c"), "-o", exe, "-lm"], exe)
+
+
+def test_oracle32_sanitized(tmp_path):
+    if not shutil.which("gcc"):
+        pytest.skip("gcc not found")
+    exe = str(tmp_path / "oracle32_san")
+    run(["gcc", "-std=c11", "-ffp-contract=off", "-fno-fast-math", *SAN, os.path.join(ROOT, "oracle", "oracle.c"),
+         os.path.join(ROOT, "oracle", "oracle32.c"), os.path.join(HERE, "oracle32_driver.c"), "-o", exe, "-lm"], exe)
 
 
 def test_abi_host_code_sanitized(tmp_path):
