@@ -1,0 +1,213 @@
+"""Property tests (hypothesis) on small shapes, CPU only: identities the pages
+and the arithmetic fix, checked over drawn shapes, probabilities, seeds,
+offsets and values rather than a few hand-picked cases.
+
+Oracle (fp64 storage where an identity is exact in double):
+- dropout-add [fusions §3.2, §3.3]: p = 0 training equals inference bit for
+  bit; p = 1 leaves the cast residual; the backward's zeros are exactly the
+  dropped elements of the exported mask; evaluating rows [r0, r1) with their
+  global row index reproduces those rows of the whole tensor; dbias is the
+  column sum of the unrounded dx;
+- bias broadcast [fusions §4.2]: bias_gelu(y, b) equals bias_gelu(y + b, 0);
+- weighted SwiGLU [fusions §9]: equals unweighted SwiGLU times the weights,
+  and its input gradient equals the unweighted one taken with g * w;
+- LayerNorm: y is invariant under x -> a x + c (a > 0, no residual);
+  dbeta is the column sum of dy;
+- squared ReLU: weights of one equal no weights;
+launch planner (mb_plan.cpp): every tiling and wide-row plan stays inside the
+grid limits and its row groups own rows;
+comparator: a value passes against itself and one ulp away, and fails three
+ulps away where no floor applies.
+"""
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+import oracle
+from oracle.tolerances import compare
+
+SETTINGS = settings(max_examples=60, deadline=None, derandomize=True,
+                    suppress_health_check=[HealthCheck.function_scoped_fixture])
+
+shapes = st.tuples(st.integers(1, 6), st.integers(1, 40))
+seeds = st.integers(0, 2**64 - 1)
+probs = st.one_of(st.sampled_from([0.0, 1.0, 0.5]), st.floats(0.0, 1.0, width=32))
+
+
+def bf16_bits(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def normal(seed, shape, scale=1.0):
+    return np.random.default_rng(seed % 2**32).standard_normal(shape) * scale
+
+
+# ---------------------------------------------------------------- dropout-add
+
+@SETTINGS
+@given(shape=shapes, p=probs, seed=seeds, offset=st.integers(0, 2**40), s=st.integers(0, 2**31))
+def test_dropout_add_identities(shape, p, seed, offset, s):
+    T, H = shape
+    x, b, r, g = (bf16_bits(normal(s + k, sh)) for k, sh in enumerate([(T, H), (H,), (T, H), (T, H)]))
+    out0, _, _ = oracle.bias_dropout_add("bf16", x, b, r, "bf16", True, 0.0, seed, offset)
+    inf, _, _ = oracle.bias_dropout_add("bf16", x, b, r, "bf16", False)
+    assert np.array_equal(out0, inf)
+    out1, _, _ = oracle.bias_dropout_add("bf16", x, b, r, "bf16", True, 1.0, seed, offset)
+    assert np.array_equal(out1, r)
+    out, out64, _ = oracle.bias_dropout_add("bf16", x, b, r, "bf16", True, p, seed, offset)
+    keep = np.unpackbits(oracle.dropout_mask(T, H, p, seed, offset), bitorder="little")[:T * H].reshape(T, H) == 1
+    dx, dx64, dres, db = oracle.bias_dropout_add_bwd("bf16", g, "bf16", p, seed, offset)
+    gv = oracle.decode("bf16", g)
+    assert np.array_equal(dx64 == 0, ~keep | (gv == 0))
+    assert np.array_equal(dres, g)
+    assert np.array_equal(db, np.add.accumulate(dx64, axis=0)[-1])
+    # rows [r0, r1) with their global index
+    r0 = s % T
+    part, _, _ = oracle.bias_dropout_add("bf16", x[r0:], b, r[r0:], "bf16", True, p, seed, offset, row0=r0)
+    assert np.array_equal(part, out[r0:])
+    pdx, _, _, _ = oracle.bias_dropout_add_bwd("bf16", g[r0:], "bf16", p, seed, offset, row0=r0)
+    assert np.array_equal(pdx, dx[r0:])
+
+
+# ---------------------------------------------------------------- GeLU, GLU
+
+@SETTINGS
+@given(shape=shapes, s=st.integers(0, 2**31), exact=st.booleans(), scale=st.floats(0.1, 8.0))
+def test_bias_broadcast_is_exact(shape, s, exact, scale):
+    T, H = shape
+    y, b = normal(s, (T, H), scale), normal(s + 1, (H,), scale)
+    o1, _ = oracle.bias_gelu_fwd("f64", y, b, exact=exact)
+    o2, _ = oracle.bias_gelu_fwd("f64", y + b[None, :], None, exact=exact)
+    assert np.array_equal(o1, o2)
+    g = normal(s + 2, (T, H))
+    d1, _, _, db1 = oracle.bias_gelu_bwd("f64", g, y, b, exact=exact)
+    d2, _, _, db2 = oracle.bias_gelu_bwd("f64", g, y + b[None, :], None, exact=exact)
+    assert np.array_equal(d1, d2) and np.array_equal(db1, db2)
+    assert np.array_equal(db1, np.add.accumulate(d1, axis=0)[-1])
+
+
+@SETTINGS
+@given(shape=shapes, s=st.integers(0, 2**31))
+def test_weighted_swiglu_is_unweighted_times_weights(shape, s):
+    T, H = shape
+    inp, b, g = normal(s, (T, 2 * H), 2.0), normal(s + 1, (2 * H,), 0.2), normal(s + 2, (T, H))
+    w = np.random.default_rng(s).random(T)
+    ow, _ = oracle.bias_glu_fwd("swiglu", "f64", inp, b, w, "f64")
+    ou, _ = oracle.bias_glu_fwd("swiglu", "f64", inp, b)
+    assert np.array_equal(ow, ou * w[:, None])
+    dw_in, _, _, dbw, _ = oracle.bias_glu_bwd("swiglu", "f64", g, inp, b, w, "f64")
+    du_in, _, _, dbu, _ = oracle.bias_glu_bwd("swiglu", "f64", g * w[:, None], inp, b)
+    assert np.array_equal(dw_in, du_in) and np.array_equal(dbw, dbu)
+
+
+# ---------------------------------------------------------------- LayerNorm, squared ReLU
+
+@SETTINGS
+@given(shape=st.tuples(st.integers(1, 5), st.integers(2, 64)), s=st.integers(0, 2**31),
+       a=st.floats(0.25, 4.0), c=st.floats(-8.0, 8.0))
+def test_layer_norm_is_affine_invariant(shape, s, a, c):
+    T, H = shape
+    x = normal(s, (T, H))
+    zero = np.zeros((T, H))
+    gm, bt = 1 + 0.2 * normal(s + 1, (H,)), 0.1 * normal(s + 2, (H,))
+    _, y1, _, _, _, _ = oracle.add_layer_norm_fwd("f64", x, zero, "f64", gm, bt, eps=0.0)
+    _, y2, _, _, _, _ = oracle.add_layer_norm_fwd("f64", a * x + c, zero, "f64", gm, bt, eps=0.0)
+    spread = np.ptp(x, axis=1, keepdims=True)
+    if np.all(spread > 1e-3):  # a row of (nearly) equal values has no defined normalisation at eps = 0
+        assert np.allclose(y1, y2, rtol=1e-8, atol=1e-8 * (1 + np.abs(c) / spread).max())
+    dy = normal(s + 3, (T, H))
+    h, _, _, _, _, _ = oracle.add_layer_norm_fwd("f64", x, zero, "f64", gm, bt)
+    _, _, _, _, _, dbeta = oracle.add_layer_norm_bwd("f64", dy, h, gm)
+    assert np.array_equal(dbeta, np.add.accumulate(dy, axis=0)[-1])
+
+
+@SETTINGS
+@given(shape=shapes, s=st.integers(0, 2**31))
+def test_squared_relu_weights_of_one(shape, s):
+    T, H = shape
+    x, g = bf16_bits(normal(s, (T, H), 2.0)), bf16_bits(normal(s + 1, (T, H)))
+    ones = np.ones(T, np.float32)
+    o1, _ = oracle.weighted_squared_relu_fwd("bf16", x, ones, "f32")
+    o0, _ = oracle.weighted_squared_relu_fwd("bf16", x)
+    assert np.array_equal(o1, o0)
+    d1, _, dw = oracle.weighted_squared_relu_bwd("bf16", g, x, ones, "f32")
+    d0, _, _ = oracle.weighted_squared_relu_bwd("bf16", g, x)
+    assert np.array_equal(d1, d0)
+    xr = np.maximum(oracle.decode("bf16", x), 0)
+    assert np.array_equal(dw, np.add.accumulate(oracle.decode("bf16", g) * xr * xr, axis=1)[:, -1])
+
+
+# ---------------------------------------------------------------- launch planner
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "transformer_elementwise_epilogues_amd", "csrc")
+
+
+@pytest.fixture(scope="module")
+def planner(tmp_path_factory):
+    if not shutil.which("g++"):
+        pytest.skip("g++ not found")
+    exe = tmp_path_factory.mktemp("plan_prop") / "plan"
+    r = subprocess.run(["g++", "-std=c++17", "-O1", "-I", CSRC, os.path.join(ROOT, "tests", "plan_c", "plan_main.cpp"),
+                        os.path.join(CSRC, "mb_plan.cpp"), "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+    def run(queries):
+        out = subprocess.run([str(exe)], input="\n".join(queries) + "\n", capture_output=True, text=True, timeout=60)
+        assert out.returncode == 0, out.stderr
+        return [list(map(int, line.split()[1:])) for line in out.stdout.splitlines()]
+    return run
+
+
+@settings(max_examples=40, deadline=None, derandomize=True,
+          suppress_health_check=[HealthCheck.function_scoped_fixture])
+@given(qs=st.lists(st.tuples(st.integers(0, 1 << 30), st.integers(0, 1 << 21), st.integers(1, 1 << 17),
+                             st.integers(1, 512), st.integers(1, 16)), min_size=1, max_size=20))
+def test_tiling_plans_stay_in_bounds(planner, qs):
+    res = planner([f"tiling {T} {nvec} {tb} {cus} {mr}" for T, nvec, tb, cus, mr in qs])
+    for (T, nvec, tb, cus, mr), (strips, G) in zip(qs, res):
+        assert strips >= 1 and strips * 64 >= nvec and (nvec == 0 or (strips - 1) * 64 < nvec)
+        assert 1 <= G <= 65535
+        assert G <= max(1, -(-T // (4 * mr)))              # every row group owns rows (min_rows each)
+        assert G <= max(1, max(1, tb * cus // 256) // strips)  # never beyond the scaled target
+
+
+@settings(max_examples=40, deadline=None, derandomize=True,
+          suppress_health_check=[HealthCheck.function_scoped_fixture])
+@given(qs=st.lists(st.tuples(st.integers(0, 1 << 24), st.integers(1, 1 << 14), st.sampled_from([(2, 2), (2, 0), (0, 0),
+                                                                                               (1, 1), (1, 0)]),
+                             st.integers(1, 512)), min_size=1, max_size=20))
+def test_wide_layer_norm_plans_stay_in_bounds(planner, qs):
+    qs = [(T, 8 * hv, dts, cus) for T, hv, dts, cus in qs]
+    res = planner([f"ln2 {T} {H} {d} {r} {cus}" for T, H, (d, r), cus in qs])
+    for (T, H, (d, r), cus), (applies, nvec, rows_grid, strips, G) in zip(qs, res):
+        E = 4 if (d == 0 or r == 0) else 8
+        assert nvec == H // E and applies == (nvec > 1024)
+        assert 1 <= rows_grid <= max(1, min(T, 1 << 20))
+        assert strips * 64 >= nvec and 1 <= G <= 65535 and G <= max(1, -(-T // 4))
+
+
+# ---------------------------------------------------------------- comparator
+
+@SETTINGS
+@given(s=st.integers(0, 2**31), n=st.integers(1, 200))
+def test_comparator_passes_one_ulp_and_fails_three(s, n):
+    v = normal(s, n, 4.0)
+    o = bf16_bits(v)
+    o64 = oracle.decode("bf16", o)  # the oracle's value sits exactly on a bf16 value: no rounding slack
+    ok, _ = compare(o.copy(), o, o64, None, "bf16")
+    assert ok.all()
+    nz = (o & 0x7FFF) > 0x0080  # away from zero and subnormals
+    up1 = np.where(nz, o + 1, o).astype(np.uint16)
+    ok, _ = compare(up1, o, o64, None, "bf16")
+    assert ok.all()
+    if nz.any():
+        up3 = np.where(nz, o + 3, o).astype(np.uint16)
+        ok, st3 = compare(up3, o, o64, None, "bf16")
+        assert np.array_equal(ok, ~nz) and st3["fail"] == int(nz.sum())
