@@ -33,9 +33,12 @@ weighted squared ReLU) are timed after the step loop, the same way, and
 reported under "next_rows"; the fp32 bias-GeLU at [512, 4096] is timed cold
 (48 rotating copies) and warm under "c1". Neither is part of `value`.
 
-The CPU baseline runs the oracle on the first rows of every op's inputs, on
-one pinned core and on a pool of threads (row chunks), and compares the GPU
-outputs of those rows with it (per-op parity statistics).
+The CPU baseline runs the oracle (fp64 C, the parity reference) on the
+first rows of every op's inputs, on one pinned core and on a pool of threads
+(row chunks), and compares the GPU outputs of those rows with it (per-op
+parity statistics); oracle32 (the same formulas in binary32) is timed on the
+same rows and the GPU rows' agreement with it reported as a secondary
+statistic.
 
 Prints one JSON line (see the keys below). `--gpus N` with N > 1 exits: the
 benchmark runs on a single GPU.
@@ -532,20 +535,27 @@ def measured_traffic():
 # ------------------------------------------------------------------ CPU baseline and parity statistics
 
 def cpu_info():
-    model = None
+    """The host CPU as /proc/cpuinfo names it (a virtualised host may give only
+    a family name; vendor, family and model number identify the core)."""
+    fields = {"model name": "model", "vendor_id": "vendor", "cpu family": "family", "model": "model_number",
+              "cpu MHz": "mhz", "cache size": "cache"}
+    info = {v: None for v in fields.values()}
     try:
         with open("/proc/cpuinfo") as fh:
             for line in fh:
-                if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
+                if not line.strip():
+                    break  # the first processor's block is enough
+                key, _, val = line.partition(":")
+                if key.strip() in fields:
+                    info[fields[key.strip()]] = val.strip()
     except OSError:
         pass
     try:
         avail = len(os.sched_getaffinity(0))
     except AttributeError:
         avail = os.cpu_count() or 1
-    return {"model": model, "nproc": os.cpu_count(), "available": avail}
+    info.update({"nproc": os.cpu_count(), "available": avail})
+    return info
 
 
 def oracle_plan(host):

@@ -559,13 +559,18 @@ __global__ __launch_bounds__(MB_LN2_A_THREADS) void ln2_rowsums_kernel(LnArgs a,
         pk_unpack<D, E>(gy[u], gv);
         pk_unpack<D, E>(hp[u], hv);
         pk_unpack<D, E>(gp[u], g);
+        // the vector's own sums first, then the thread's: a term passes
+        // through at most E - 1 + nvec / TA additions in the thread
+        float va = 0.0f, vx = 0.0f;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const float xv = (hv[e] - mu) * rs;
           const float av = gv[e] * (g[e] + a.gshift);
-          sa += av;
-          sax = __builtin_fmaf(av, xv, sax);
+          va += av;
+          vx = __builtin_fmaf(av, xv, vx);
         }
+        sa += va;
+        sax += vx;
       }
     }
     sa = wave_sum(sa);
