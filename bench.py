@@ -88,6 +88,9 @@ def parse(argv=None):
     ap.add_argument("--ceiling-table", default=None, help="write every swept shape's time per op to this JSON file")
     ap.add_argument("--eager", action="store_true",
                     help="time the step as eager launches instead of HIP graph replays")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy one 1 GiB buffer device to device (the runtime's copy kernel), so that a "
+                         "counter run can scale FETCH_SIZE / WRITE_SIZE by a kernel of known bytes")
     return ap.parse_args(argv)
 
 
@@ -516,6 +519,8 @@ TRAFFIC_SOURCES = ["transformer_elementwise_epilogues_amd/csrc/mb_gelu.hip",
                    "transformer_elementwise_epilogues_amd/csrc/mb_device.hpp",
                    "transformer_elementwise_epilogues_amd/csrc/mb_reduce.hip",
                    "transformer_elementwise_epilogues_amd/csrc/mb_launch.hpp",
+                   "transformer_elementwise_epilogues_amd/csrc/mb_plan.hpp",
+                   "transformer_elementwise_epilogues_amd/csrc/mb_plan.cpp",
                    "transformer_elementwise_epilogues_amd/csrc/mb_abi.cpp"]
 
 
@@ -958,6 +963,14 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     K, W = args.steps, args.warmup
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        torch.cuda.empty_cache()
     t_setup = time.perf_counter()
     log("building inputs")
     ops, extra, host = build_ops(dev, max(K, W, 1))
