@@ -98,8 +98,11 @@ def test_ln_fwd_bwd(dt, rdt, T, H):
 
 @pytest.mark.parametrize("dt,rdt", PAIRS)
 @pytest.mark.parametrize("zc", [False, True])
-def test_ln_options_beta_none_small_variance(dt, rdt, zc):
-    T, H = 40, 1024
+@pytest.mark.parametrize("wide", [False, True], ids=["row", "wide"])
+def test_ln_options_beta_none_small_variance(dt, rdt, zc, wide):
+    # wide: 2048 vectors, the two-kernel backward
+    E = 4 if (dt == "f32" or rdt == "f32") else 8
+    T, H = (12, 2048 * E) if wide else (40, 1024)
     x, r, g, _ = inputs(dt, rdt, T, H, 7, scale=2e-3, shift=0.25)
     if zc:
         g = (g.float() - 1.0).to(TD[dt])  # zero-centred weights
@@ -211,17 +214,18 @@ def test_ln_edge_cases():
 
 
 @pytest.mark.parametrize("dt,rdt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")])
-def test_ln_non_finite_and_extreme_magnitude_rows(dt, rdt):
+@pytest.mark.parametrize("H", [1024, 16384])
+def test_ln_non_finite_and_extreme_magnitude_rows(dt, rdt, H):
     """Rows holding a NaN, a +inf or a -inf (the whole row is NaN, as in the
     oracle: the mean is NaN or +-inf and the variance NaN), rows scaled to
     1e15 and to 1e-30 (the variance 1e30 and 1e-60, the latter far below eps),
     a row at 3 with a spread of 1e-3, and an ordinary row. The finite rows also go through the backward. Rows
     stay below 1e19: beyond it (x - mean)^2 overflows fp32 while the oracle's
     fp64 variance stays finite."""
-    T, H = 7, 1024
+    T = 7
     x, r, g, b = inputs(dt, rdt, T, H, 61)
     xf, rf = x.float(), r.float()
-    xf[1, 17], xf[2, 300], xf[3, 1023] = float("nan"), float("inf"), float("-inf")
+    xf[1, 17], xf[2, 300], xf[3, H - 1] = float("nan"), float("inf"), float("-inf")
     xf[4] *= 1e15
     rf[4] *= 1e15
     xf[5] *= 1e-30
@@ -275,11 +279,12 @@ def test_ln_errors_on_device_tensors():
         mb.mb_add_layer_norm_bwd(x, h, g, m, s, ws=torch.zeros(4, dtype=torch.uint8, device=DEV))
 
 
-@pytest.mark.parametrize("T,H", [(3000, 512), (40, 2048)])
+@pytest.mark.parametrize("T,H", [(3000, 512), (40, 2048), (300, 16384)])
 def test_ln_bwd_each_param_gradient_alone_matches_both(T, H):
     """dgamma and dbeta share their column-sum launches when both are asked
     for; each alone comes out bit for bit the same (3000 rows: more than 32
-    partial rows, the two-level sum)."""
+    partial rows, the two-level sum; 16384: the wide-row kernels), and dx
+    does not depend on which parameter gradients are asked for."""
     dt = "bf16"
     x = synthetic.draw(501, (T, H), "normal", 1.0, dt).to(DEV)
     r = synthetic.draw(502, (T, H), "normal", 1.0, dt).to(DEV)
@@ -293,3 +298,7 @@ def test_ln_bwd_each_param_gradient_alone_matches_both(T, H):
     assert none_b is None and none_g is None
     assert torch.equal(dg_both.view(torch.int32), dg_only.view(torch.int32))
     assert torch.equal(dbt_both.view(torch.int32), dbt_only.view(torch.int32))
+    dx_both, _, _, _ = mb.mb_add_layer_norm_bwd(dy, h, g, mean, rstd)
+    dx_none, _, ng, nb = mb.mb_add_layer_norm_bwd(dy, h, g, mean, rstd, dgamma=False, dbeta=False)
+    assert ng is None and nb is None
+    assert torch.equal(dx_both.view(torch.int16), dx_none.view(torch.int16))
