@@ -168,6 +168,26 @@ def test_ln_wide_backward_many_rows(dt, rdt, T, H):
         assert torch.equal(a.view(torch.uint8), b2.view(torch.uint8))
 
 
+@pytest.mark.parametrize("dt,rdt,T,H", [("bf16", "bf16", 520, 65536), ("f32", "f32", 300, 32768),
+                                         ("bf16", "f32", 261, 32768)])
+def test_ln_fwd_widest_rows_walk(dt, rdt, T, H):
+    """The widest rows (8192 vectors) keep h in LDS and prefetch the next row:
+    more rows than compute units, so blocks walk several rows (and the last
+    ones fewer); every element against the oracle, bit-reproducible."""
+    say(f"widest fwd {dt}/{rdt} {T}x{H}")
+    x, r, g, b = inputs(dt, rdt, T, H, 71)
+    out = mb.mb_add_layer_norm_fwd(x.to(DEV), r.to(DEV), g.to(DEV), b.to(DEV), 1e-5, True)
+    s1, _ = check_fwd(dt, rdt, x, r, g, b, 1e-5, True, out, f"widest {dt}/{rdt} {T}x{H}")
+    say(f"widest fwd: {s1}")
+    again = mb.mb_add_layer_norm_fwd(x.to(DEV), r.to(DEV), g.to(DEV), b.to(DEV), 1e-5, True)
+    for a, c in zip(out, again):
+        assert torch.equal(a.view(torch.uint8), c.view(torch.uint8))
+    # no stats and no h: the same y
+    y2, h2, m2, s2 = mb.mb_add_layer_norm_fwd(x.to(DEV), r.to(DEV), g.to(DEV), b.to(DEV), 1e-5, True, h_out=False,
+                                              stats=False)
+    assert h2 is None and m2 is None and torch.equal(y2.view(torch.uint8), out[0].view(torch.uint8))
+
+
 @pytest.mark.parametrize("H", [1024, 24576])
 def test_ln_in_place(H):
     dt = "bf16"

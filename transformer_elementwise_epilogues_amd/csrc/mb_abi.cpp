@@ -655,6 +655,12 @@ mb_status_t mb_add_layer_norm_fwd(const void* x, const void* residual, mb_dtype_
     const mb::LnPlan half = mb::plan_ln(tokens, hidden, dt, residual_dt, MB_LN_FWD_BLOCKS, 8, cus);
     if (mb::ln_plan_is(half, 512, 8)) fp = half;
   }
+  if (mb::ln_plan_is(fp, 1024, 8)) {
+    // rows of more than 4096 vectors: 512 threads of 16 (the LDS-staged kernel
+    // fits that in registers; 1024 threads of 8 would spill)
+    const mb::LnPlan half = mb::plan_ln(tokens, hidden, dt, residual_dt, MB_LN_FWD_BLOCKS, 16, cus);
+    if (mb::ln_plan_is(half, 512, 16)) fp = half;
+  }
   if (fp.shape < 0) return MB_ERR_SHAPE;
   if (hipError_t e = mb::launch_ln_fwd(a, fp, s)) return hip_status(e);
   return finish();

@@ -66,6 +66,21 @@ template <DT D, int E> __device__ __forceinline__ void pk_store(char* p, typenam
   else
     *reinterpret_cast<T*>(p) = v;
 }
+// A packed piece at byte voff + soff of the `bytes`-byte buffer at base, read
+// through a buffer descriptor (a read past `bytes` returns zeros): the lane's
+// offset is one register and a per-vector step a scalar, where the compiler
+// would keep a 64-bit address per vector, hoisted out of a loop, in registers.
+template <DT D, int E>
+__device__ __forceinline__ typename Pk<D, E>::T pk_load_rsrc(const char* base, uint32_t bytes, uint32_t voff,
+                                                             uint32_t soff, bool nt) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, 0x00020000);
+  if constexpr (Pk<D, E>::BYTES == 16) {
+    return nt ? __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2) : __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  } else {
+    return nt ? __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 2) : __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  }
+}
+
 template <DT D, int E> __device__ __forceinline__ void pk_unpack(typename Pk<D, E>::T v, float* f) {
   if constexpr (Pk<D, E>::BYTES == 16) {
     unpack<D>(v, f);
@@ -272,6 +287,114 @@ __global__ __launch_bounds__(TPR* RPB) void ln_fwd_kernel(const char* __restrict
     }
     if constexpr (!prefetch<TPR, NV>()) {
       if (row + step < T) fetch(row + step);
+    }
+  }
+}
+
+// The forward of the widest rows (8192 vectors): h goes to LDS (each thread
+// writes and reads only its own vectors, slot k TPR + l, so it needs no
+// barrier of its own), which leaves the registers to the next row's x and
+// residual, loaded while this row is reduced and its y stored. Blocks stay
+// resident (one per CU) and walk rows. LDS: TPR NV h pieces (128 KiB for a
+// 65536-element bf16 row).
+template <DT D, DT R, int TPR, int NV>
+__global__ __launch_bounds__(TPR) void ln_fwd_lds_kernel(const char* __restrict__ x, const char* __restrict__ res,
+                                                         const char* __restrict__ gamma, const char* __restrict__ beta,
+                                                         char* hout, char* y, float* __restrict__ mean_out,
+                                                         float* __restrict__ rstd_out, int64_t T, int H, float eps,
+                                                         float gshift) {
+  constexpr int E = ln_epl<D, R>();
+  constexpr int W = TPR / 64;
+  constexpr int XB = E * Vec<D>::BYTES, RB = E * Vec<R>::BYTES;
+  using PD = typename Pk<D, E>::T;
+  using PR = typename Pk<R, E>::T;
+  __shared__ RowLds<W, 1> lds;
+  extern __shared__ __align__(16) unsigned char hrow_raw[];
+  PD* hrow = reinterpret_cast<PD*>(hrow_raw);
+  const int lt = threadIdx.x, wr = lt / 64, lane = lt & 63;
+  const int nvec = H / E;
+  const float fh = static_cast<float>(H);
+  // Vector k of this thread is lt + k TPR (clamped to 0 past the row, where
+  // it is loaded but neither stored nor counted). Addresses are a row base,
+  // the same for the whole block, plus a 32-bit offset: the per-vector
+  // offsets are then one register each, where 64-bit addresses of every
+  // vector of two tensors, hoisted out of the row loop, would not fit.
+  auto in_row = [&](int k) { return lt + k * TPR < nvec; };
+  auto vec_of = [&](int k) { return static_cast<uint32_t>(in_row(k) ? lt + k * TPR : 0); };
+  const int64_t step = gridDim.x;
+  const size_t px = static_cast<size_t>(H) * Vec<D>::BYTES, pr = static_cast<size_t>(H) * Vec<R>::BYTES;
+  PD xn[NV];
+  PR rn[NV];
+  const uint32_t xbytes = static_cast<uint32_t>(nvec) * XB, rbytes = static_cast<uint32_t>(nvec) * RB;
+  auto fetch = [&](int64_t r) {
+    const char* xr = x + static_cast<size_t>(r) * px;
+    const char* rr = res + static_cast<size_t>(r) * pr;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {  // past the row: zeros, neither stored nor counted
+      xn[k] = pk_load_rsrc<D, E>(xr, xbytes, lt * XB, k * TPR * XB, MB_NT_LOAD);
+      rn[k] = pk_load_rsrc<R, E>(rr, rbytes, lt * RB, k * TPR * RB, MB_NT_LOAD);
+    }
+  };
+  int64_t row = blockIdx.x;
+  if (row < T) fetch(row);
+  for (; row < T; row += step) {
+    char* hr = hout ? hout + static_cast<size_t>(row) * px : nullptr;
+    char* yr = y + static_cast<size_t>(row) * px;
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      float xv[E], rv[E];
+      pk_unpack<D, E>(xn[k], xv);
+      pk_unpack<R, E>(rn[k], rv);
+#pragma unroll
+      for (int e = 0; e < E; ++e) xv[e] += R == D ? rv[e] : round_to<D>(rv[e]);
+      const PD hp = pk_pack<D, E>(xv);
+      hrow[k * TPR + lt] = hp;
+      if (hr && in_row(k)) pk_store<D, E>(hr + vec_of(k) * static_cast<uint32_t>(XB), hp);
+      float hv[E];
+      pk_unpack<D, E>(hp, hv);
+#pragma unroll
+      for (int e = 0; e < E; ++e) s += in_row(k) ? hv[e] : 0.0f;
+    }
+    // the registers are free: the next row's loads go out now (the scheduling
+    // barrier keeps the compiler from hoisting them above the pass that still
+    // reads this row's registers, which would need both rows in registers)
+    __builtin_amdgcn_sched_barrier(0);
+    if (row + step < T) fetch(row + step);
+    const float mean = row_sum<W, 1>(s, lds, 0, wr, lane, 0) / fh;
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      float hv[E];
+      pk_unpack<D, E>(hrow[k * TPR + lt], hv);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float d = hv[e] - mean;
+        ss += in_row(k) ? d * d : 0.0f;
+      }
+    }
+    const float var = row_sum<W, 1>(ss, lds, 0, wr, lane, 1) / fh;
+    const float rstd = 1.0f / __builtin_sqrtf(var + eps);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      if (!in_row(k)) continue;
+      const uint32_t cv = vec_of(k) * static_cast<uint32_t>(XB);
+      float hv[E], g[E], b[E];
+      pk_unpack<D, E>(hrow[k * TPR + lt], hv);
+      pk_unpack<D, E>(pk_load_rsrc<D, E>(gamma, xbytes, lt * XB, k * TPR * XB, false), g);
+      if (beta) {
+        pk_unpack<D, E>(pk_load_rsrc<D, E>(beta, xbytes, lt * XB, k * TPR * XB, false), b);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) b[e] = 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) hv[e] = __builtin_fmaf((hv[e] - mean) * rstd, g[e] + gshift, b[e]);
+      pk_store<D, E>(yr + cv, pk_pack<D, E>(hv));
+    }
+    if (lt == 0 && mean_out) {
+      mean_out[row] = mean;
+      rstd_out[row] = rstd;
     }
   }
 }
@@ -698,14 +821,39 @@ template <DT D, DT R> hipError_t ln2_bwd_run(const LnArgs& a, const Ln2Plan& p, 
   return hipGetLastError();
 }
 
+// Row-group shapes of this many vectors or more keep h in LDS: 512 threads of
+// 16 (65536 bf16, 32768 fp32) ran 234 -> 208 us at [2048, 65536] bf16; at
+// 4096 vectors (512 threads of 8) the register-resident row was as fast.
+#ifndef MB_LN_FWD_LDS_MIN_VEC
+#define MB_LN_FWD_LDS_MIN_VEC 8192
+#endif
+#ifndef MB_LN_FWD_LDS_BLOCKS_PER_CU
+#define MB_LN_FWD_LDS_BLOCKS_PER_CU 1
+#endif
+template <int S> constexpr bool fwd_lds_shape() {
+  return kLnShapes[S].tpr * kLnShapes[S].nv >= MB_LN_FWD_LDS_MIN_VEC && kLnShapes[S].rpb == 1;
+}
+
 template <DT D, DT R, int S>
 hipError_t fwd_shape(const LnArgs& a, const LnPlan& p, hipStream_t s) {
   constexpr LnShape sh = kLnShapes[S];
-  hipLaunchKernelGGL((ln_fwd_kernel<D, R, sh.tpr, sh.nv, sh.rpb>), dim3(p.grid), dim3(sh.tpr * sh.rpb), 0, s,
-                     static_cast<const char*>(a.x), static_cast<const char*>(a.res),
-                     static_cast<const char*>(a.gamma), static_cast<const char*>(a.beta),
-                     static_cast<char*>(a.hout), static_cast<char*>(a.y), a.mean, a.rstd, a.T,
-                     static_cast<int>(a.H), a.eps, a.gshift);
+  if constexpr (fwd_lds_shape<S>()) {
+    constexpr int E = ln_epl<D, R>();
+    const size_t shm = static_cast<size_t>(sh.tpr) * sh.nv * E * Vec<D>::BYTES;
+    const int64_t resident = static_cast<int64_t>(p.cus) * MB_LN_FWD_LDS_BLOCKS_PER_CU;
+    const unsigned grid = static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>(a.T, resident)));
+    hipLaunchKernelGGL((ln_fwd_lds_kernel<D, R, sh.tpr, sh.nv>), dim3(grid), dim3(sh.tpr), shm, s,
+                       static_cast<const char*>(a.x), static_cast<const char*>(a.res),
+                       static_cast<const char*>(a.gamma), static_cast<const char*>(a.beta),
+                       static_cast<char*>(a.hout), static_cast<char*>(a.y), a.mean, a.rstd, a.T,
+                       static_cast<int>(a.H), a.eps, a.gshift);
+  } else {
+    hipLaunchKernelGGL((ln_fwd_kernel<D, R, sh.tpr, sh.nv, sh.rpb>), dim3(p.grid), dim3(sh.tpr * sh.rpb), 0, s,
+                       static_cast<const char*>(a.x), static_cast<const char*>(a.res),
+                       static_cast<const char*>(a.gamma), static_cast<const char*>(a.beta),
+                       static_cast<char*>(a.hout), static_cast<char*>(a.y), a.mean, a.rstd, a.T,
+                       static_cast<int>(a.H), a.eps, a.gshift);
+  }
   return hipGetLastError();
 }
 

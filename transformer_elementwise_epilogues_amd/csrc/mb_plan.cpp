@@ -52,7 +52,7 @@ LnPlan plan_ln(int64_t T, int64_t H, int dt, int rdt, int target_blocks, int nv_
   int tpr = 64;
   while (tpr < 1024 && static_cast<int64_t>(tpr) * nv_pref < p.nvec) tpr = tpr == 64 ? 256 : tpr * 2;
   int nv = 1;
-  while (nv < 8 && static_cast<int64_t>(tpr) * nv < p.nvec) nv *= 2;
+  while (nv < 16 && static_cast<int64_t>(tpr) * nv < p.nvec) nv *= 2;
   if (static_cast<int64_t>(tpr) * nv < p.nvec) return p;  // wider than 8192 vectors
   for (int i = 0; i < kLnNumShapes; ++i)
     if (kLnShapes[i].tpr == tpr && kLnShapes[i].nv == nv) p.shape = i;
@@ -61,6 +61,7 @@ LnPlan plan_ln(int64_t T, int64_t H, int dt, int rdt, int target_blocks, int nv_
   const int64_t groups = (T + sh.rpb - 1) / sh.rpb;
   p.grid = static_cast<int>(std::min<int64_t>(std::max<int64_t>(groups, 1), scaled_blocks(target_blocks, cus)));
   p.partial_rows = p.grid;
+  p.cus = cus > 0 ? cus : kTunedCUs;
   return p;
 }
 

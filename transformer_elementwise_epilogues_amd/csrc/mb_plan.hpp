@@ -176,13 +176,14 @@ struct LnShape {
 };
 constexpr LnShape kLnShapes[] = {{64, 1, 4},  {64, 2, 4},  {64, 4, 4},  {256, 1, 1},  {256, 2, 1},
                                  {256, 4, 1}, {512, 1, 1}, {512, 2, 1}, {512, 4, 1},  {1024, 1, 1},
-                                 {1024, 2, 1}, {1024, 4, 1}, {1024, 8, 1}, {512, 8, 1}};
+                                 {1024, 2, 1}, {1024, 4, 1}, {1024, 8, 1}, {512, 8, 1}, {512, 16, 1}};
 constexpr int kLnNumShapes = sizeof(kLnShapes) / sizeof(kLnShapes[0]);
 struct LnPlan {
   int nvec = 0;           // vectors of ln_elems_per_vector elements per row
   int shape = -1;         // row-group shape; -1: the row is too wide
   int grid = 0;           // blocks of the row kernels
   int partial_rows = 0;   // partial rows the backward writes (one per block)
+  int cus = 0;            // compute units of the device planned for
 };
 int ln_elems_per_vector(int dt, int rdt);
 LnPlan plan_ln(int64_t T, int64_t H, int dt, int rdt, int target_blocks, int nv_pref, int cus);
