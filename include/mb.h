@@ -296,10 +296,11 @@ mb_status_t mb_add_layer_norm_fwd(const void* x, const void* residual, mb_dtype_
                                   float* rstd, int64_t tokens, int64_t hidden, mb_dtype_t dt,
                                   hipStream_t s);
 
-/* Workspace bytes for mb_add_layer_norm_bwd: rows of 2048 or more vectors
- * (16384 fp16/bf16 elements, 8192 fp32 or beside an fp32 residual) keep two
- * fp32 row sums per row there; with parameter gradients it also holds their
- * partial rows. 0 when neither applies (and for tokens 0). */
+/* Workspace bytes for mb_add_layer_norm_bwd: rows of more than 2048 16-byte
+ * vectors (over 16384 fp16/bf16 elements, over 8192 fp32 or beside an fp32
+ * residual) keep two fp32 row sums per row there; with parameter gradients
+ * it also holds their partial rows. 0 when neither applies (and for tokens
+ * 0). */
 size_t mb_add_layer_norm_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt,
                                        mb_dtype_t residual_dt, int with_param_grads);
 

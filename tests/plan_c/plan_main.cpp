@@ -3,6 +3,7 @@
 //   tiling T nvec target_blocks cus min_rows   -> "tiling strips G"
 //   ln T H dt rdt target_blocks nv_pref cus     -> "ln nvec shape tpr nv grid partial_rows"
 //   ln2 T H dt rdt cus                          -> "ln2 applies nvec rows_grid strips G"
+//   lnb T H dt rdt cus                          -> "lnb applies nvec rows_per_block grid"
 #include <cstdio>
 #include <cstring>
 
@@ -30,6 +31,13 @@ int main() {
       if (std::scanf("%lld %lld %d %d %d", &T, &H, &dt, &rdt, &cus) != 5) return 2;
       const mb::Ln2Plan p = mb::plan_ln2(T, H, dt, rdt, cus);
       std::printf("ln2 %d %d %d %d %d\n", mb::ln2_applies(H, dt, rdt) ? 1 : 0, p.nvec, p.rows_grid, p.strips, p.G);
+    } else if (std::strcmp(kind, "lnb") == 0) {
+      long long T, H;
+      int dt, rdt, cus;
+      if (std::scanf("%lld %lld %d %d %d", &T, &H, &dt, &rdt, &cus) != 5) return 2;
+      const mb::LnBlockPlan p = mb::plan_ln_block(T, H, dt, rdt, cus);
+      std::printf("lnb %d %d %lld %d\n", mb::ln_block_applies(H, dt, rdt) ? 1 : 0, p.nvec,
+                  static_cast<long long>(p.rows_per_block), p.grid);
     } else {
       return 3;
     }

@@ -59,5 +59,6 @@ hipError_t launch_srelu_bwd(int, int, const void*, const void*, const void*, voi
 hipError_t launch_ln_fwd(const LnArgs&, const LnPlan&, hipStream_t) { return launched(); }
 hipError_t launch_ln_bwd(const LnArgs&, const LnPlan&, hipStream_t) { return launched(); }
 hipError_t launch_ln2_bwd(const LnArgs&, const Ln2Plan&, hipStream_t) { return launched(); }
+hipError_t launch_ln_block_bwd(const LnArgs&, const LnBlockPlan&, hipStream_t) { return launched(); }
 
 }  // namespace mb

@@ -145,9 +145,12 @@ def test_layer_norm_validation():
     ws = wsf(1024, 8192, BF16, BF16, 1)
     assert ws > 0 and wsf(1024, 8192, BF16, BF16, 0) == 0 and wsf(0, 8192, BF16, BF16, 1) == 0
     assert wsf(1024, 65536, BF16, BF16, 1) > 0
-    # two-pass rows keep 2 fp32 row sums per row even without parameter gradients
-    assert wsf(1024, 65536, BF16, BF16, 0) == 1024 * 8 and wsf(1000, 16384, BF16, BF16, 0) == 8192
-    assert wsf(1024, 8192, BF16, F32, 0) == 1024 * 8 and wsf(1024, 8192, F32, F32, 0) == 1024 * 8
+    # two-pass rows (more than 2048 vectors) keep 2 fp32 row sums per row even
+    # without parameter gradients; rows of 1025-2048 vectors need none
+    assert wsf(1024, 65536, BF16, BF16, 0) == 1024 * 8 and wsf(1000, 32768, BF16, BF16, 0) == 8192
+    assert wsf(1024, 16384, BF16, F32, 0) == 1024 * 8 and wsf(1024, 16384, F32, F32, 0) == 1024 * 8
+    assert wsf(1000, 16384, BF16, BF16, 0) == 0 and wsf(1024, 8192, BF16, F32, 0) == 0
+    assert wsf(1024, 8200, BF16, BF16, 1) > 0
     assert bw(A, B, C, D, E, 0, None, BF16, 0x60000000, None, None, None, None, 0, 1024, 65536, BF16,
               None) == WORKSPACE
     assert bw(A, B, C, D, E, 0, None, BF16, 0x60000000, None, 0x70000000, None, None, 0, 1024, 8192, BF16,
@@ -156,8 +159,8 @@ def test_layer_norm_validation():
               None) == NULL
     assert bw(A, B, C, D, E, 0, None, BF16, A + 16, None, None, None, None, 0, 1024, 8192, BF16, None) == ALIAS
     assert bw(A, B, C, D, E, 0, None, BF16, A, B, None, None, None, 0, 0, 8192, BF16, None) == OK  # dx = dy, dres = h
-    # (bf16 beside an fp32 residual: 2048 vectors of 4, a two-pass row that needs its row-sum workspace)
-    assert bw(A, B, C, D, E, 0, None, F32, A, B, None, None, 0x60000000, 4096, 4, 8192, BF16, None) == ALIAS
+    # (bf16 beside an fp32 residual: 4096 vectors of 4, a two-pass row that needs its row-sum workspace)
+    assert bw(A, B, C, D, E, 0, None, F32, A, B, None, None, 0x60000000, 4096, 4, 16384, BF16, None) == ALIAS
 
 
 def test_squared_relu_validation():

@@ -2,8 +2,10 @@
 oracle, through the C ABI.
 
 Shapes cover every row-group shape the kernels pick (4 rows of 64 threads per
-block with 1, 2 or 4 vectors per thread; 256 and 1024 threads per row; the
-wide rows, whose backward is a row-sum kernel and a column-strip kernel),
+block with 1, 2 or 4 vectors per thread; 256 and 1024 threads per row; rows
+of 1025-2048 vectors, whose backward is a resident block per compute unit
+walking a range of rows; the wide rows, whose backward is a row-sum kernel
+and a column-strip kernel),
 ragged rows (vectors that exist for only some threads), more rows than
 blocks (grid-stride rows and more than 32 partial rows), and every dtype
 pair. h is compared bit for bit; y, dx and dresidual within the derived
@@ -33,9 +35,10 @@ PAIRS = [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"), ("f16", "f16"), ("f1
 def hidden_cases(dt, rdt):
     """(T, H) per row-group shape, for elements-per-vector E."""
     E = 4 if (dt == "f32" or rdt == "f32") else 8
-    # vectors per row; beyond 1024 the backward is the wide-row pair (row
-    # sums, then column strips walking the rows backwards), and the forward
-    # of 4096 runs 512 threads of 8
+    # vectors per row; from 1025 to 2048 the backward is the resident block
+    # walking a range of rows, beyond 2048 the wide-row pair (row sums, then
+    # column strips walking the rows backwards), and the forward of 4096 runs
+    # 512 threads of 8
     # (one vector per row: 4 bf16 beside an fp32 residual planned a column
     # strip of zero vectors for the unused parameter-gradient kernel, a host
     # division by zero that the sanitized build of the planner found)
@@ -98,11 +101,11 @@ def test_ln_fwd_bwd(dt, rdt, T, H):
 
 @pytest.mark.parametrize("dt,rdt", PAIRS)
 @pytest.mark.parametrize("zc", [False, True])
-@pytest.mark.parametrize("wide", [False, True], ids=["row", "wide"])
-def test_ln_options_beta_none_small_variance(dt, rdt, zc, wide):
-    # wide: 2048 vectors, the two-kernel backward
+@pytest.mark.parametrize("width", ["row", "block", "wide"])
+def test_ln_options_beta_none_small_variance(dt, rdt, zc, width):
+    # block: 2048 vectors, the resident-block backward; wide: 4096, the two-kernel one
     E = 4 if (dt == "f32" or rdt == "f32") else 8
-    T, H = (12, 2048 * E) if wide else (40, 1024)
+    T, H = {"row": (40, 1024), "block": (12, 2048 * E), "wide": (12, 4096 * E)}[width]
     x, r, g, _ = inputs(dt, rdt, T, H, 7, scale=2e-3, shift=0.25)
     if zc:
         g = (g.float() - 1.0).to(TD[dt])  # zero-centred weights
@@ -145,10 +148,13 @@ def test_ln_many_rows_tall_partials():
 @pytest.mark.parametrize("dt,rdt,T,H", [("bf16", "bf16", 1100, 16384), ("bf16", "bf16", 700, 12296),
                                          ("f16", "f32", 257, 8196), ("bf16", "bf16", 37, 65536)])
 def test_ln_wide_backward_many_rows(dt, rdt, T, H):
-    """The wide-row backward over many rows: every row group walks several rows
-    from the last one down, the last column strip is ragged (12296 bf16 is
-    1537 vectors, 8196 beside an fp32 residual 2049), and dx, dresidual,
-    dgamma and dbeta match the oracle and reproduce bit for bit."""
+    """The backward of rows over 1024 vectors over many rows: the resident
+    blocks (2048 vectors, and 12296 bf16, 1537 vectors, ragged in a thread's
+    last vector) walk several rows each; the wide-row pair (8196 beside an
+    fp32 residual: 2049 vectors, the narrowest wide row, its last column
+    strip ragged; and 8192 vectors) walks each row group from its last row
+    down. dx, dresidual, dgamma and dbeta match the oracle and reproduce bit
+    for bit."""
     say(f"wide bwd {dt}/{rdt} {T}x{H}")
     x, r, g, b = inputs(dt, rdt, T, H, 31)
     out = mb.mb_add_layer_norm_fwd(x.to(DEV), r.to(DEV), g.to(DEV), b.to(DEV))
@@ -166,6 +172,42 @@ def test_ln_wide_backward_many_rows(dt, rdt, T, H):
     dx2, dres2, dgam2, dbet2 = mb.mb_add_layer_norm_bwd(dy, h, g.to(DEV), mean, rstd, dh_in=up, dresidual=True)
     for a, b2 in ((dx, dx2), (dres, dres2), (dgam, dgam2), (dbet, dbet2)):
         assert torch.equal(a.view(torch.uint8), b2.view(torch.uint8))
+
+
+def test_ln_block_backward_flushes_column_sums():
+    """Rows of 1025 vectors (8200 bf16: the last of a thread's four vectors
+    exists for one thread only) over 16640 rows: on 256 compute units each
+    resident block walks 65 rows, so it stores its dgamma / dbeta sums into
+    its partial row after 64 rows and adds the last row's to them. Every
+    element of dx and dresidual, and both column sums, against the oracle
+    (evaluated over row chunks, its column sums added in fp64); the result
+    reproduces bit for bit."""
+    dt = rdt = "bf16"
+    T, H = 16640, 8200
+    say(f"block bwd flush {dt}/{rdt} {T}x{H}")
+    x, r, g, b = inputs(dt, rdt, T, H, 81)
+    y, h, mean, rstd = mb.mb_add_layer_norm_fwd(x.to(DEV), r.to(DEV), g.to(DEV), b.to(DEV))
+    dy = synthetic.draw(82, (T, H), "normal", 1.0, dt)
+    up = synthetic.draw(83, (T, H), "normal", 1.0, rdt)
+    dx, dres, dgam, dbet = mb.mb_add_layer_norm_bwd(dy.to(DEV), h, g.to(DEV), mean, rstd, dh_in=up.to(DEV),
+                                                    dresidual=True)
+    again = mb.mb_add_layer_norm_bwd(dy.to(DEV), h, g.to(DEV), mean, rstd, dh_in=up.to(DEV), dresidual=True)
+    for a, c in zip((dx, dres, dgam, dbet), again):
+        assert torch.equal(a.view(torch.uint8), c.view(torch.uint8))
+    hh, dx, dres = st(h), st(dx), st(dres)
+    odg, odb = np.zeros(H), np.zeros(H)
+    C = 2080
+    for i in range(0, T, C):
+        oh, *_ = oracle.add_layer_norm_fwd(dt, st(x[i:i + C]), st(r[i:i + C]), rdt, st(g), st(b), 1e-5, False)
+        assert np.array_equal(hh[i:i + C], oh), f"h rows {i}.."
+        odx, odx64, omag, odres, cg, cb = oracle.add_layer_norm_bwd(dt, st(dy[i:i + C]), oh, st(g), 1e-5, False,
+                                                                    dh_in=st(up[i:i + C]), res_dt=rdt)
+        assert_close_bounded(dx[i:i + C], odx, odx64, K * U * omag, dt, f"block dx rows {i}..")
+        assert_close_bounded(dres[i:i + C], odres, odx64, K * U * omag, rdt, f"block dresidual rows {i}..")
+        odg += cg
+        odb += cb
+    say(f"block dgamma {assert_reduction_close(dgam.cpu().numpy(), odg, 'dgamma')}")
+    assert_reduction_close(dbet.cpu().numpy(), odb, "dbeta")
 
 
 @pytest.mark.parametrize("dt,rdt,T,H", [("bf16", "bf16", 520, 65536), ("f32", "f32", 300, 32768),
@@ -234,7 +276,7 @@ def test_ln_edge_cases():
 
 
 @pytest.mark.parametrize("dt,rdt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")])
-@pytest.mark.parametrize("H", [1024, 16384])
+@pytest.mark.parametrize("H", [1024, 16384, 32768])
 def test_ln_non_finite_and_extreme_magnitude_rows(dt, rdt, H):
     """Rows holding a NaN, a +inf or a -inf (the whole row is NaN, as in the
     oracle: the mean is NaN or +-inf and the variance NaN), rows scaled to
@@ -299,12 +341,13 @@ def test_ln_errors_on_device_tensors():
         mb.mb_add_layer_norm_bwd(x, h, g, m, s, ws=torch.zeros(4, dtype=torch.uint8, device=DEV))
 
 
-@pytest.mark.parametrize("T,H", [(3000, 512), (40, 2048), (300, 16384)])
+@pytest.mark.parametrize("T,H", [(3000, 512), (40, 2048), (300, 16384), (300, 32768)])
 def test_ln_bwd_each_param_gradient_alone_matches_both(T, H):
     """dgamma and dbeta share their column-sum launches when both are asked
     for; each alone comes out bit for bit the same (3000 rows: more than 32
-    partial rows, the two-level sum; 16384: the wide-row kernels), and dx
-    does not depend on which parameter gradients are asked for."""
+    partial rows, the two-level sum; 16384: the resident-block kernel; 32768:
+    the wide-row kernels), and dx does not depend on which parameter
+    gradients are asked for."""
     dt = "bf16"
     x = synthetic.draw(501, (T, H), "normal", 1.0, dt).to(DEV)
     r = synthetic.draw(502, (T, H), "normal", 1.0, dt).to(DEV)

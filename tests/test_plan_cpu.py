@@ -89,7 +89,7 @@ def test_layernorm_plans(planner, cus):
 
 @pytest.mark.parametrize("cus", CUS)
 def test_wide_layernorm_backward_plans(planner, cus):
-    """Wide-row backward (more than 1024 vectors): one row-sum block per row (a
+    """Wide-row backward (more than 2048 vectors): one row-sum block per row (a
     grid-stride loop past 2^20 rows); the column-strip kernel's strips cover
     the row and its row groups (the partial rows of dgamma / dbeta) own at
     least one row each and scale with the device."""
@@ -101,10 +101,33 @@ def test_wide_layernorm_backward_plans(planner, cus):
                 keys.append((T, H, dt, rdt))
     for (T, H, dt, rdt), (applies, nvec, rows_grid, strips, G) in zip(keys, planner(queries)):
         E = 4 if (dt == 0 or rdt == 0) else 8
-        assert nvec == H // E and applies == (nvec > 1024)
+        assert nvec == H // E and applies == (nvec > 2048)
         assert rows_grid == min(T, 1 << 20)
         assert strips * 64 >= nvec > (strips - 1) * 64
         assert 1 <= G <= max(1, (T + 3) // 4) and strips * G <= max(strips, 512 * cus // 256)
-    # the tuned widths on the whole device: 4 row groups of 128 strips at 65536, 16 of 32 at 16384
-    (_, _, _, s1, g1), (_, _, _, s2, g2) = planner(["ln2 2048 65536 2 2 256", "ln2 8192 16384 2 2 256"])
-    assert (s1, g1) == (128, 4) and (s2, g2) == (32, 16)
+    # the tuned width on the whole device: 4 row groups of 128 strips at 65536
+    (_, _, _, s1, g1), = planner(["ln2 2048 65536 2 2 256"])
+    assert (s1, g1) == (128, 4)
+
+
+@pytest.mark.parametrize("cus", CUS)
+def test_block_layernorm_backward_plans(planner, cus):
+    """Rows of 1025-2048 vectors: one resident block per compute unit at most,
+    each walking a contiguous range of at least one row; the ranges cover the
+    rows once. The three backward paths split the widths between them."""
+    queries, keys = [], []
+    for dt, rdt in ((2, 2), (2, 0), (0, 0), (1, 1)):
+        for H in (4096, 8192, 8200, 12288, 16384, 32768):
+            for T in (1, 3, 300, 4096, 16640, 1 << 22):
+                queries.append(f"lnb {T} {H} {dt} {rdt} {cus}")
+                queries.append(f"ln2 {T} {H} {dt} {rdt} {cus}")
+                keys.append((T, H, dt, rdt))
+    out = planner(queries)
+    for (T, H, dt, rdt), (applies, nvec, rpb, grid), (wide, *_) in zip(keys, out[0::2], out[1::2]):
+        E = 4 if (dt == 0 or rdt == 0) else 8
+        assert nvec == H // E and applies == (1024 < nvec <= 2048)
+        assert not (applies and wide) and (applies or wide or nvec <= 1024)
+        assert 1 <= grid <= min(T, cus) and rpb >= 1
+        assert grid * rpb >= T > (grid - 1) * rpb  # every block has rows, none past the last
+    (_, _, rpb, grid), = planner([f"lnb 16640 8200 2 2 256"])
+    assert (rpb, grid) == (65, 256)  # more rows per block than one flush of the column sums

@@ -186,11 +186,13 @@ def test_tiling_plans_stay_in_bounds(planner, qs):
 def test_wide_layer_norm_plans_stay_in_bounds(planner, qs):
     qs = [(T, 8 * hv, dts, cus) for T, hv, dts, cus in qs]
     res = planner([f"ln2 {T} {H} {d} {r} {cus}" for T, H, (d, r), cus in qs])
-    for (T, H, (d, r), cus), (applies, nvec, rows_grid, strips, G) in zip(qs, res):
+    blk = planner([f"lnb {T} {H} {d} {r} {cus}" for T, H, (d, r), cus in qs])
+    for (T, H, (d, r), cus), (applies, nvec, rows_grid, strips, G), (bapplies, _, rpb, grid) in zip(qs, res, blk):
         E = 4 if (d == 0 or r == 0) else 8
-        assert nvec == H // E and applies == (nvec > 1024)
+        assert nvec == H // E and applies == (nvec > 2048) and bapplies == (1024 < nvec <= 2048)
         assert 1 <= rows_grid <= max(1, min(T, 1 << 20))
         assert strips * 64 >= nvec and 1 <= G <= 65535 and G <= max(1, -(-T // 4))
+        assert 1 <= grid <= max(1, min(T, cus)) and grid * rpb >= T and (T == 0 or (grid - 1) * rpb < T)
 
 
 # ---------------------------------------------------------------- comparator

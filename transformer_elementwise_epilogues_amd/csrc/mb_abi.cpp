@@ -671,7 +671,7 @@ mb_status_t mb_add_layer_norm_fwd(const void* x, const void* residual, mb_dtype_
 // chunk sums of each when there are more than 32 partial rows (256-byte
 // aligned pieces).
 struct LnWs {
-  bool wide = false;
+  bool wide = false, block = false;
   int partial_rows = 0;
   size_t rows = 0, pg = 0, pb = 0, tg = 0, tb = 0, total = 0;
 };
@@ -679,7 +679,9 @@ static LnWs ln_ws_layout(int64_t T, int64_t H, mb_dtype_t dt, mb_dtype_t rdt, co
                          bool params) {
   LnWs w;
   w.wide = mb::ln2_applies(H, dt, rdt);
-  w.partial_rows = w.wide ? mb::plan_ln2(T, H, dt, rdt, cus).G : p.partial_rows;
+  w.block = mb::ln_block_applies(H, dt, rdt);
+  w.partial_rows = w.wide ? mb::plan_ln2(T, H, dt, rdt, cus).G
+                          : w.block ? mb::plan_ln_block(T, H, dt, rdt, cus).grid : p.partial_rows;
   const size_t rows = w.wide ? round_up(static_cast<size_t>(T) * 8, 256) : 0;
   const size_t part = params ? round_up(static_cast<size_t>(w.partial_rows) * H * 4, 256) : 0;
   const size_t tmp =
@@ -760,6 +762,9 @@ mb_status_t mb_add_layer_norm_bwd(const void* dy, const void* h, const void* gam
     a.rowsums = reinterpret_cast<float*>(w + lay.rows);
     const mb::Ln2Plan p2 = mb::plan_ln2(tokens, hidden, dt, residual_dt, cus);
     if (hipError_t e = mb::launch_ln2_bwd(a, p2, s)) return hip_status(e);
+  } else if (lay.block) {
+    if (hipError_t e = mb::launch_ln_block_bwd(a, mb::plan_ln_block(tokens, hidden, dt, residual_dt, cus), s))
+      return hip_status(e);
   } else {
     if (hipError_t e = mb::launch_ln_bwd(a, plan, s)) return hip_status(e);
   }

@@ -111,5 +111,8 @@ hipError_t launch_ln_bwd(const LnArgs& a, const LnPlan& p, hipStream_t s);
 // backward of wide rows (plan_ln2): needs a.rowsums, and a.pg / a.pb
 // ([p.G, H]) for the parameter gradients
 hipError_t launch_ln2_bwd(const LnArgs& a, const Ln2Plan& p, hipStream_t s);
+// backward of rows of 1025-2048 vectors (plan_ln_block): a.pg / a.pb
+// ([p.grid, H]) for the parameter gradients
+hipError_t launch_ln_block_bwd(const LnArgs& a, const LnBlockPlan& p, hipStream_t s);
 
 }  // namespace mb

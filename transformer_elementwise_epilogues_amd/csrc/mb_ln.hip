@@ -628,6 +628,192 @@ __global__ __launch_bounds__(TPR* RPB) void ln_bwd_kernel(const char* __restrict
   }
 }
 
+// Sum over the wave, the same in every lane: each 32-lane half by swizzles
+// (xor of the lane index with 16, 8, 4, 2, 1; the pattern is an immediate),
+// then the two halves' totals read as scalars and added. Unlike a permute
+// butterfly it keeps no lane-address registers, which a row loop would hoist.
+__device__ __forceinline__ float wave_sum_uniform(float v) {
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (16 << 10) | 0x1F));
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (8 << 10) | 0x1F));
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (4 << 10) | 0x1F));
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (2 << 10) | 0x1F));
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (1 << 10) | 0x1F));
+  const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  return lo + hi;
+}
+
+// Backward of rows of up to NV TPR vectors (1024 < vectors <= 2048 with 512
+// threads of 4): a resident block walks a contiguous range of rows with the
+// whole row in registers (each thread its NV vectors of dy, h, dh_in) and the
+// next row's loaded while this one is reduced; each thread owns the same
+// columns on every row, so its dgamma / dbeta sums stay in registers, added
+// into the block's partial row (its own columns: no reduction across threads)
+// every kFlushRows rows and at the end. Loads go through buffer descriptors
+// (row base + 32-bit lane offset, the per-vector step a scalar), so no 64-bit
+// address per vector is kept in registers.
+template <DT D, DT R, int TPR, int NV>
+__global__ __launch_bounds__(TPR) void ln_bwd_block_kernel(LnArgs a, int64_t rows_per_block) {
+  constexpr int E = ln_epl<D, R>();
+  constexpr int W = TPR / 64;
+  constexpr int XB = E * Vec<D>::BYTES, RB = E * Vec<R>::BYTES;
+  using PD = typename Pk<D, E>::T;
+  using PR = typename Pk<R, E>::T;
+  __shared__ RowLds<W, 1> lds;
+  const int lt = threadIdx.x, wr = lt / 64, lane = lt & 63;
+  const int nvec = static_cast<int>(a.H / E);
+  const float fh = static_cast<float>(a.H);
+  auto in_row = [&](int k) { return lt + k * TPR < nvec; };
+  const uint32_t xbytes = static_cast<uint32_t>(nvec) * XB, rbytes = static_cast<uint32_t>(nvec) * RB;
+  const size_t px = static_cast<size_t>(a.H) * Vec<D>::BYTES, pr = static_cast<size_t>(a.H) * Vec<R>::BYTES;
+  const char* dy = static_cast<const char*>(a.dy);
+  const char* hh = static_cast<const char*>(a.h);
+  const char* up = static_cast<const char*>(a.dh_in);
+  char* dx = static_cast<char*>(a.dx);
+  char* dres = static_cast<char*>(a.dres);
+  PD gp[NV];  // gamma, packed (unpacked where used: fewer registers)
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+    gp[k] = pk_load_rsrc<D, E>(static_cast<const char*>(a.gamma), xbytes, lt * XB, k * TPR * XB, false);
+  const bool dgb = a.pg != nullptr;
+  float sg[NV][E], sb[NV][E];
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+#pragma unroll
+    for (int e = 0; e < E; ++e) sg[k][e] = sb[k][e] = 0.0f;
+  float* pgr = dgb ? a.pg + static_cast<size_t>(blockIdx.x) * a.H : nullptr;
+  float* pbr = dgb ? a.pb + static_cast<size_t>(blockIdx.x) * a.H : nullptr;
+  bool first_flush = true;
+  auto flush = [&]() {  // add the sums into the block's partial row (this thread's columns)
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      if (!in_row(k)) continue;
+      uint32_t ci = static_cast<uint32_t>(lt + k * TPR) * E;
+      opaque(ci);  // formed here, not kept in registers across the row loop
+      const size_t c = ci;
+#pragma unroll
+      for (int q = 0; q < E / 4; ++q) {
+        float tg[4], tb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          tg[e] = first_flush ? sg[k][4 * q + e] : pgr[c + 4 * q + e] + sg[k][4 * q + e];
+          tb[e] = first_flush ? sb[k][4 * q + e] : pbr[c + 4 * q + e] + sb[k][4 * q + e];
+        }
+        store_f32x4(pgr + c + 4 * q, tg);
+        store_f32x4(pbr + c + 4 * q, tb);
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) sg[k][e] = sb[k][e] = 0.0f;
+    }
+    first_flush = false;
+  };
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rows_per_block;
+  const int64_t r1 = r0 + rows_per_block < a.T ? r0 + rows_per_block : a.T;
+  PD gyn[NV], hn[NV];
+  auto fetch = [&](int64_t r) {
+    const char* dyr = dy + static_cast<size_t>(r) * px;
+    const char* hr = hh + static_cast<size_t>(r) * px;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {  // past the row: zeros, neither stored nor summed
+      gyn[k] = pk_load_rsrc<D, E>(dyr, xbytes, lt * XB, k * TPR * XB, MB_NT_LOAD);
+      hn[k] = pk_load_rsrc<D, E>(hr, xbytes, lt * XB, k * TPR * XB, MB_NT_LOAD);
+    }
+  };
+  int nrows = 0;
+  if (r0 < r1) fetch(r0);
+  for (int64_t row = r0; row < r1; ++row) {
+    PD gy[NV], hp[NV];
+    PR uu[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      gy[k] = gyn[k];
+      hp[k] = hn[k];
+    }
+    // dh_in is first used after the row sums: loaded for this row, ahead of
+    // the next row's dy and h (one row of it in registers, not two)
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+      if (up) uu[k] = pk_load_rsrc<R, E>(up + static_cast<size_t>(row) * pr, rbytes, lt * RB, k * TPR * RB, MB_NT_LOAD);
+    if (row + 1 < r1) fetch(row + 1);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) opaque(gp[k]);  // unpacked per row, not kept unpacked across rows
+    const float mu = a.cmean[row], rs = a.crstd[row];
+    float sa = 0.0f, sax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      float gv[E], hv[E], g[E];
+      pk_unpack<D, E>(gy[k], gv);
+      pk_unpack<D, E>(hp[k], hv);
+      pk_unpack<D, E>(gp[k], g);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float xv = (hv[e] - mu) * rs;
+        const float av = gv[e] * (g[e] + a.gshift);
+        sa += av;
+        sax = __builtin_fmaf(av, xv, sax);
+        sg[k][e] = __builtin_fmaf(gv[e], xv, sg[k][e]);
+        sb[k][e] += gv[e];
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one vector unpacked at a time
+    }
+    {
+      // the two row sums: the waves' sums through LDS in wave order (slots
+      // alternate by row, so a wave ahead never overwrites a slot still read)
+      const int slot = static_cast<int>(row & 1) * 2;
+      sa = wave_sum_uniform(sa);
+      sax = wave_sum_uniform(sax);
+      if (lane == 0) {
+        lds.v[0][slot][wr] = sa;
+        lds.v[0][slot + 1][wr] = sax;
+      }
+      __syncthreads();
+      sa = lds.v[0][slot][0];
+      sax = lds.v[0][slot + 1][0];
+#pragma unroll
+      for (int w = 1; w < W; ++w) {
+        sa += lds.v[0][slot][w];
+        sax += lds.v[0][slot + 1][w];
+      }
+    }
+    const float ma = sa / fh, mx = sax / fh;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {  // unpacked again below, not kept unpacked across the row sums
+      opaque(gy[k]);
+      opaque(hp[k]);
+      opaque(gp[k]);
+    }
+    const size_t xo = static_cast<size_t>(row) * px, ro = static_cast<size_t>(row) * pr;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      if (!in_row(k)) continue;
+      float gv[E], hv[E], uv[E], g[E];
+      pk_unpack<D, E>(gy[k], gv);
+      pk_unpack<D, E>(hp[k], hv);
+      pk_unpack<D, E>(gp[k], g);
+      if (up) {
+        pk_unpack<R, E>(uu[k], uv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) uv[e] = 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float xv = (hv[e] - mu) * rs;
+        gv[e] = __builtin_fmaf(rs, __builtin_fmaf(-xv, mx, gv[e] * (g[e] + a.gshift) - ma), uv[e]);
+      }
+      const uint32_t v = static_cast<uint32_t>(lt + k * TPR);
+      pk_store<D, E>(dx + xo + v * XB, pk_pack<D, E>(gv));
+      if (dres) pk_store<R, E>(dres + ro + v * RB, pk_pack<R, E>(gv));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (dgb && ++nrows == kFlushRows) {
+      flush();
+      nrows = 0;
+    }
+  }
+  if (dgb && (nrows > 0 || first_flush)) flush();
+}
+
 // ---------------------------------------------------------------- wide rows
 // The backward of rows of 2048 or more vectors, whose parameter-gradient sums
 // do not fit beside a register-resident row, runs as two kernels:
@@ -912,6 +1098,29 @@ hipError_t by_dtype(const LnArgs& a, const LnPlan& p, hipStream_t s) {
 
 hipError_t launch_ln_fwd(const LnArgs& a, const LnPlan& p, hipStream_t s) { return by_dtype<false>(a, p, s); }
 hipError_t launch_ln_bwd(const LnArgs& a, const LnPlan& p, hipStream_t s) { return by_dtype<true>(a, p, s); }
+// Threads of the resident-block backward (each holds 2048 / MB_LN_BLOCK_TPR
+// vectors of a row). 1024 threads of 2 leave 128 registers a thread, which
+// the fp16 / bf16 builds overflow into scratch: 1.7-1.8x slower than 512.
+#ifndef MB_LN_BLOCK_TPR
+#define MB_LN_BLOCK_TPR 512
+#endif
+template <DT D, DT R> hipError_t ln_block_run(const LnArgs& a, const LnBlockPlan& p, hipStream_t s) {
+  constexpr int TPR = MB_LN_BLOCK_TPR, NV = 2048 / TPR;
+  hipLaunchKernelGGL((ln_bwd_block_kernel<D, R, TPR, NV>), dim3(p.grid), dim3(TPR), 0, s, a, p.rows_per_block);
+  return hipGetLastError();
+}
+
+hipError_t launch_ln_block_bwd(const LnArgs& a, const LnBlockPlan& p, hipStream_t s) {
+  if (p.nvec > 2048) return hipErrorInvalidValue;  // the kernel holds 2048 vectors per block
+  const DT d = static_cast<DT>(a.dt), r = static_cast<DT>(a.rdt);
+  if (d == DT::F32 && r == DT::F32) return ln_block_run<DT::F32, DT::F32>(a, p, s);
+  if (d == DT::BF16 && r == DT::BF16) return ln_block_run<DT::BF16, DT::BF16>(a, p, s);
+  if (d == DT::BF16 && r == DT::F32) return ln_block_run<DT::BF16, DT::F32>(a, p, s);
+  if (d == DT::F16 && r == DT::F16) return ln_block_run<DT::F16, DT::F16>(a, p, s);
+  if (d == DT::F16 && r == DT::F32) return ln_block_run<DT::F16, DT::F32>(a, p, s);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_ln2_bwd(const LnArgs& a, const Ln2Plan& p, hipStream_t s) {
   const DT d = static_cast<DT>(a.dt), r = static_cast<DT>(a.rdt);
   if (d == DT::F32 && r == DT::F32) return ln2_bwd_run<DT::F32, DT::F32>(a, p, s);

@@ -65,7 +65,24 @@ LnPlan plan_ln(int64_t T, int64_t H, int dt, int rdt, int target_blocks, int nv_
   return p;
 }
 
-bool ln2_applies(int64_t H, int dt, int rdt) { return H / ln_elems_per_vector(dt, rdt) > MB_LN2_ROW_VEC; }
+bool ln_block_applies(int64_t H, int dt, int rdt) {
+  const int64_t nvec = H / ln_elems_per_vector(dt, rdt);
+  return nvec > MB_LN2_ROW_VEC && nvec <= MB_LN_BLOCK_MAX_VEC;
+}
+
+bool ln2_applies(int64_t H, int dt, int rdt) {
+  return H / ln_elems_per_vector(dt, rdt) > std::max<int64_t>(MB_LN2_ROW_VEC, MB_LN_BLOCK_MAX_VEC);
+}
+
+LnBlockPlan plan_ln_block(int64_t T, int64_t H, int dt, int rdt, int cus) {
+  LnBlockPlan p;
+  p.nvec = static_cast<int>(H / ln_elems_per_vector(dt, rdt));
+  const int64_t resident = std::max<int64_t>(1, cus > 0 ? cus : kTunedCUs);
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(T, resident));
+  p.rows_per_block = std::max<int64_t>(1, (T + blocks - 1) / blocks);
+  p.grid = static_cast<int>(std::max<int64_t>(1, (T + p.rows_per_block - 1) / p.rows_per_block));
+  return p;
+}
 
 Ln2Plan plan_ln2(int64_t T, int64_t H, int dt, int rdt, int cus) {
   Ln2Plan p;

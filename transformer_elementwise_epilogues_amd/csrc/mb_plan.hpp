@@ -206,6 +206,22 @@ struct Ln2Plan {
 };
 // rows of H elements take the wide-row backward (H a whole number of vectors)
 bool ln2_applies(int64_t H, int dt, int rdt);
+
+// ---- backward of rows of more than MB_LN2_ROW_VEC and at most
+// MB_LN_BLOCK_MAX_VEC vectors: a resident block of 512 threads (4 vectors
+// each) per CU walks a range of rows with the row and its thread's parameter
+// sums in registers; the blocks' partial rows are summed after (0: off, such
+// rows then take the wide-row kernels)
+#ifndef MB_LN_BLOCK_MAX_VEC
+#define MB_LN_BLOCK_MAX_VEC 2048
+#endif
+struct LnBlockPlan {
+  int nvec = 0;
+  int64_t rows_per_block = 0;
+  int grid = 0;  // blocks, and partial rows of dgamma / dbeta
+};
+bool ln_block_applies(int64_t H, int dt, int rdt);
+LnBlockPlan plan_ln_block(int64_t T, int64_t H, int dt, int rdt, int cus);
 Ln2Plan plan_ln2(int64_t T, int64_t H, int dt, int rdt, int cus);
 // the plan's row group is `tpr` threads of `nv` vectors
 bool ln_plan_is(const LnPlan& p, int tpr, int nv);
