@@ -298,9 +298,10 @@ mb_status_t mb_add_layer_norm_fwd(const void* x, const void* residual, mb_dtype_
 
 /* Workspace bytes for mb_add_layer_norm_bwd: rows of more than 2048 16-byte
  * vectors (over 16384 fp16/bf16 elements, over 8192 fp32 or beside an fp32
- * residual) keep two fp32 row sums per row there; with parameter gradients
- * it also holds their partial rows. 0 when neither applies (and for tokens
- * 0). */
+ * residual) keep their row sums there (a pair of fp32 partial sums per row
+ * and block of the row when a row is split over up to 8 blocks, else two
+ * fp32 sums per row); with parameter gradients it also holds their partial
+ * rows. 0 when neither applies (and for tokens 0). */
 size_t mb_add_layer_norm_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_t dt,
                                        mb_dtype_t residual_dt, int with_param_grads);
 
@@ -313,13 +314,28 @@ size_t mb_add_layer_norm_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_
  * next residual. dx may equal dy or h exactly; dresidual may equal dh_in, or
  * dy or h when residual_dt == dt. The parameter gradients are deterministic
  * and atomic-free (partials in ws, sized by mb_add_layer_norm_bwd_workspace,
- * then ordered column sums). Errors as for the forward, plus MB_ERR_WORKSPACE. */
+ * then ordered column sums). Rows of 2049-8192 vectors are split over teams
+ * of blocks that exchange their partial row sums through ws (agent-scope
+ * atomic stores and loads; a block that waits in vain past a bound leaves the
+ * row to a second pass that recomputes the sums the same way, so results do
+ * not depend on timing). With an output over an input such rows take two
+ * passes over dy and h instead: the same values within the stated bound, not
+ * bit for bit those of the out-of-place call. Errors as for the forward, plus
+ * MB_ERR_WORKSPACE. */
 mb_status_t mb_add_layer_norm_bwd(const void* dy, const void* h, const void* gamma,
                                   const float* mean, const float* rstd, int zero_centered_gamma,
                                   const void* dh_in, mb_dtype_t residual_dt, void* dx,
                                   void* dresidual, float* dgamma, float* dbeta, void* ws,
                                   size_t ws_bytes, int64_t tokens, int64_t hidden, mb_dtype_t dt,
                                   hipStream_t s);
+
+/* Test-only. Rows of 2049-8192 vectors are split over a team of blocks that
+ * exchange their partial row sums [fusions §5.3: the widest hidden sizes];
+ * a block polls for a partner's sums at most `polls` times (negative: the
+ * default, 4096) and then computes them itself, with the same arithmetic,
+ * so outputs do not depend on it: a test sets 0 to run every row through
+ * that path and compares. Applies to later calls in this process. */
+void mb_set_layer_norm_team_wait(int polls);
 
 #ifdef __cplusplus
 }

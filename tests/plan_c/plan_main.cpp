@@ -4,6 +4,7 @@
 //   ln T H dt rdt target_blocks nv_pref cus     -> "ln nvec shape tpr nv grid partial_rows"
 //   ln2 T H dt rdt cus                          -> "ln2 applies nvec rows_grid strips G"
 //   lnb T H dt rdt cus                          -> "lnb applies nvec rows_per_block grid"
+//   lnt T H dt rdt cus blocks_per_cu            -> "lnt applies nvec members slice teams rows_per_team grid"
 #include <cstdio>
 #include <cstring>
 
@@ -38,6 +39,13 @@ int main() {
       const mb::LnBlockPlan p = mb::plan_ln_block(T, H, dt, rdt, cus);
       std::printf("lnb %d %d %lld %d\n", mb::ln_block_applies(H, dt, rdt) ? 1 : 0, p.nvec,
                   static_cast<long long>(p.rows_per_block), p.grid);
+    } else if (std::strcmp(kind, "lnt") == 0) {
+      long long T, H;
+      int dt, rdt, cus, bpc;
+      if (std::scanf("%lld %lld %d %d %d %d", &T, &H, &dt, &rdt, &cus, &bpc) != 6) return 2;
+      const mb::LnTeamPlan p = mb::plan_ln_team(T, H, dt, rdt, cus, bpc);
+      std::printf("lnt %d %d %d %d %d %lld %d\n", mb::ln_team_applies(H, dt, rdt) ? 1 : 0, p.nvec, p.members,
+                  p.slice, p.teams, static_cast<long long>(p.rows_per_team), p.grid);
     } else {
       return 3;
     }

@@ -60,5 +60,8 @@ hipError_t launch_ln_fwd(const LnArgs&, const LnPlan&, hipStream_t) { return lau
 hipError_t launch_ln_bwd(const LnArgs&, const LnPlan&, hipStream_t) { return launched(); }
 hipError_t launch_ln2_bwd(const LnArgs&, const Ln2Plan&, hipStream_t) { return launched(); }
 hipError_t launch_ln_block_bwd(const LnArgs&, const LnBlockPlan&, hipStream_t) { return launched(); }
+hipError_t launch_ln_team_bwd(const LnArgs&, const LnTeamPlan&, hipStream_t) { return launched(); }
+int ln_team_blocks_per_cu(int, int) { return 2; }
+void set_ln_team_spin_limit(int) {}
 
 }  // namespace mb

@@ -145,10 +145,14 @@ def test_layer_norm_validation():
     ws = wsf(1024, 8192, BF16, BF16, 1)
     assert ws > 0 and wsf(1024, 8192, BF16, BF16, 0) == 0 and wsf(0, 8192, BF16, BF16, 1) == 0
     assert wsf(1024, 65536, BF16, BF16, 1) > 0
-    # two-pass rows (more than 2048 vectors) keep 2 fp32 row sums per row even
-    # without parameter gradients; rows of 1025-2048 vectors need none
-    assert wsf(1024, 65536, BF16, BF16, 0) == 1024 * 8 and wsf(1000, 32768, BF16, BF16, 0) == 8192
-    assert wsf(1024, 16384, BF16, F32, 0) == 1024 * 8 and wsf(1024, 16384, F32, F32, 0) == 1024 * 8
+    # rows of more than 2048 vectors keep row sums even without parameter
+    # gradients: a team of ceil(vectors / 1024) blocks exchanges one pair of
+    # fp32 partial sums per row and member, plus a row flag (the in-place
+    # wide-row kernels need less: 2 fp32 sums per row); rows of 1025-2048
+    # vectors need none
+    team = lambda T, members: -(-T * (members * 8 + 4) // 256) * 256
+    assert wsf(1024, 65536, BF16, BF16, 0) == team(1024, 8) and wsf(1000, 32768, BF16, BF16, 0) == team(1000, 4)
+    assert wsf(1024, 16384, BF16, F32, 0) == team(1024, 4) and wsf(1024, 16384, F32, F32, 0) == team(1024, 4)
     assert wsf(1000, 16384, BF16, BF16, 0) == 0 and wsf(1024, 8192, BF16, F32, 0) == 0
     assert wsf(1024, 8200, BF16, BF16, 1) > 0
     assert bw(A, B, C, D, E, 0, None, BF16, 0x60000000, None, None, None, None, 0, 1024, 65536, BF16,

@@ -75,3 +75,64 @@ def test_capture_and_replay_matches_eager():
         got = results()
         for i, (a, e) in enumerate(zip(got, eager)):
             assert torch.equal(bits(a), bits(e)), f"replay {rep}: output {i} differs from the eager run"
+
+
+@pytest.mark.parametrize("H,in_place,wait", [(16384, False, -1), (32768, False, -1), (32768, False, 0),
+                                             (32768, True, -1)],
+                         ids=["block", "team", "team-recomputed", "wide-in-place"])
+def test_capture_and_replay_wide_layer_norm_backward(H, in_place, wait):
+    """The LayerNorm backward of wide rows under capture: 2048 vectors (one
+    resident block per CU walking rows), 4096 vectors split over teams of
+    blocks (a slot-filling launch, the team kernel, the fix-up launch; also
+    with no wait, so every row goes through the fix-up), and 4096 vectors in
+    place (the wide-row kernels). Every replay equals the eager result bit
+    for bit."""
+    T = 300
+    dt = "bf16"
+    x = synthetic.draw(11, (T, H), "normal", 1.0, dt).to(DEV)
+    r = synthetic.draw(12, (T, H), "normal", 1.0, dt).to(DEV)
+    g = synthetic.draw(13, (T, H), "normal", 1.0, dt).to(DEV)
+    up = synthetic.draw(14, (T, H), "normal", 1.0, dt).to(DEV)
+    gm = (synthetic.draw(15, (H,), "normal", 0.3, dt).float() + 1.0).to(torch.bfloat16).to(DEV)
+    _, h, mean, rstd = mb.mb_add_layer_norm_fwd(x, r, gm)
+    ws = torch.empty(mb.mb_add_layer_norm_bwd_workspace(T, H, x.dtype), dtype=torch.uint8, device=DEV)
+    dx, dres = torch.empty_like(x), torch.empty_like(x)
+    dg, dbt = (torch.empty(H, dtype=torch.float32, device=DEV) for _ in range(2))
+    gi, upi = g.clone(), up.clone()
+
+    def step():
+        if in_place:
+            gi.copy_(g)
+            upi.copy_(up)
+            mb.mb_add_layer_norm_bwd(gi, h, gm, mean, rstd, dh_in=upi, dx=gi, dresidual=upi, dgamma=dg, dbeta=dbt,
+                                     ws=ws)
+        else:
+            mb.mb_add_layer_norm_bwd(g, h, gm, mean, rstd, dh_in=up, dx=dx, dresidual=dres, dgamma=dg, dbeta=dbt,
+                                     ws=ws)
+
+    outs = (gi, upi, dg, dbt) if in_place else (dx, dres, dg, dbt)
+    mb.mb_set_layer_norm_team_wait(wait)
+    try:
+        step()
+        torch.cuda.synchronize()
+        eager = [t.clone() for t in outs]
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step()
+        for rep in range(4):
+            for t in outs:
+                t.fill_(float("nan"))
+            ws.fill_(0xA5)  # the launches set their slots and flags themselves
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for i, (a, e) in enumerate(zip(outs, eager)):
+                assert torch.equal(bits(a), bits(e)), f"replay {rep}: output {i} differs from the eager run"
+    finally:
+        mb.mb_set_layer_norm_team_wait(-1)

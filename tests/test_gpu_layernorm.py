@@ -210,6 +210,40 @@ def test_ln_block_backward_flushes_column_sums():
     assert_reduction_close(dbet.cpu().numpy(), odb, "dbeta")
 
 
+@pytest.mark.parametrize("dt,rdt,T,H", [("bf16", "bf16", 300, 32768), ("f16", "f32", 257, 8196),
+                                         ("f32", "f32", 64, 32768), ("bf16", "bf16", 1100, 20480)])
+def test_ln_team_backward_same_whether_partners_sums_arrive(dt, rdt, T, H):
+    """Rows of 2049-8192 vectors split over a team of blocks (4, 3 of 683,
+    8, and 3 of 854 vectors here, 1100 rows walking several per team): each
+    block takes its partners' partial row sums from their published slots, or
+    after its bounded wait computes them itself. With no wait at all every
+    row goes the second way; dx, dresidual, dgamma and dbeta come out bit for
+    bit the same, and match the oracle."""
+    say(f"team bwd {dt}/{rdt} {T}x{H}")
+    x, r, g, b = inputs(dt, rdt, T, H, 91)
+    _, h, mean, rstd = mb.mb_add_layer_norm_fwd(x.to(DEV), r.to(DEV), g.to(DEV), b.to(DEV))
+    dy = synthetic.draw(92, (T, H), "normal", 1.0, dt).to(DEV)
+    up = synthetic.draw(93, (T, H), "normal", 1.0, rdt).to(DEV)
+    run = lambda: mb.mb_add_layer_norm_bwd(dy, h, g.to(DEV), mean, rstd, dh_in=up, dresidual=True)
+    first = run()
+    try:
+        mb.mb_set_layer_norm_team_wait(0)
+        alone = run()
+    finally:
+        mb.mb_set_layer_norm_team_wait(-1)
+    for a, c in zip(first, alone):
+        assert torch.equal(a.view(torch.uint8), c.view(torch.uint8))
+    oh, *_ = oracle.add_layer_norm_fwd(dt, st(x), st(r), rdt, st(g), st(b), 1e-5, False)
+    assert np.array_equal(st(h), oh)
+    odx, odx64, omag, odres, odg, odb = oracle.add_layer_norm_bwd(dt, st(dy), oh, st(g), 1e-5, False,
+                                                                  dh_in=st(up), res_dt=rdt)
+    dx, dres, dgam, dbet = first
+    assert_close_bounded(st(dx), odx, odx64, K * U * omag, dt, "team dx")
+    assert_close_bounded(st(dres), odres, odx64, K * U * omag, rdt, "team dresidual")
+    say(f"team dgamma {assert_reduction_close(dgam.cpu().numpy(), odg, 'dgamma')}")
+    assert_reduction_close(dbet.cpu().numpy(), odb, "dbeta")
+
+
 @pytest.mark.parametrize("dt,rdt,T,H", [("bf16", "bf16", 520, 65536), ("f32", "f32", 300, 32768),
                                          ("bf16", "f32", 261, 32768)])
 def test_ln_fwd_widest_rows_walk(dt, rdt, T, H):
@@ -230,8 +264,14 @@ def test_ln_fwd_widest_rows_walk(dt, rdt, T, H):
     assert h2 is None and m2 is None and torch.equal(y2.view(torch.uint8), out[0].view(torch.uint8))
 
 
-@pytest.mark.parametrize("H", [1024, 24576])
+@pytest.mark.parametrize("H", [1024, 16384, 24576])
 def test_ln_in_place(H):
+    """h over x and y over the residual; dx over dy and dresidual over dh_in.
+    Up to 2048 vectors the in-place backward is the same kernel as the
+    out-of-place one, bit for bit; wider rows split over a team of blocks
+    out of place take the wide-row kernels in place (a team's fix-up pass
+    rereads whole rows of dy, h and dh_in), so there the two are compared
+    with the oracle."""
     dt = "bf16"
     T = 6
     x, r, g, b = inputs(dt, dt, T, H, 31)
@@ -243,12 +283,27 @@ def test_ln_in_place(H):
     assert torch.equal(xi.view(torch.int16), h_ref.view(torch.int16))
     assert torch.equal(ri.view(torch.int16), y_ref.view(torch.int16))
     dy = synthetic.draw(32, (T, H), "normal", 1.0, dt).to(DEV)
-    dx_ref, _, dg_ref, db_ref = mb.mb_add_layer_norm_bwd(dy, h_ref, gd, m_ref, s_ref)
-    dyi = dy.clone()
-    dx, _, dg, db = mb.mb_add_layer_norm_bwd(dyi, h_ref, gd, m_ref, s_ref, dx=dyi)  # dx over dy
-    assert torch.equal(dyi.view(torch.int16), dx_ref.view(torch.int16))
-    assert torch.equal(dg.view(torch.int32), dg_ref.view(torch.int32))
-    assert torch.equal(db.view(torch.int32), db_ref.view(torch.int32))
+    up = synthetic.draw(33, (T, H), "normal", 1.0, dt).to(DEV)
+    dx_ref, dr_ref, dg_ref, db_ref = mb.mb_add_layer_norm_bwd(dy, h_ref, gd, m_ref, s_ref, dh_in=up, dresidual=True)
+    dyi, upi = dy.clone(), up.clone()
+    dx, dr, dg, db = mb.mb_add_layer_norm_bwd(dyi, h_ref, gd, m_ref, s_ref, dh_in=upi, dx=dyi,
+                                              dresidual=upi)  # dx over dy, dresidual over dh_in
+    assert dx.data_ptr() == dyi.data_ptr() and dr.data_ptr() == upi.data_ptr()
+    if H // 8 <= 2048:
+        assert torch.equal(dyi.view(torch.int16), dx_ref.view(torch.int16))
+        assert torch.equal(upi.view(torch.int16), dr_ref.view(torch.int16))
+        assert torch.equal(dg.view(torch.int32), dg_ref.view(torch.int32))
+        assert torch.equal(db.view(torch.int32), db_ref.view(torch.int32))
+    oh, *_ = oracle.add_layer_norm_fwd(dt, st(x), st(r), dt, st(g), st(b), 1e-5, False)
+    odx, odx64, omag, odres, odg, odb = oracle.add_layer_norm_bwd(dt, st(dy), oh, st(g), 1e-5, False,
+                                                                  dh_in=st(up), res_dt=dt)
+    for got in (dyi, dx_ref):
+        assert_close_bounded(st(got), odx, odx64, K * U * omag, dt, f"in place dx {H}")
+    for got in (upi, dr_ref):
+        assert_close_bounded(st(got), odres, odx64, K * U * omag, dt, f"in place dresidual {H}")
+    for got_g, got_b in ((dg, db), (dg_ref, db_ref)):
+        assert_reduction_close(got_g.cpu().numpy(), odg, "in place dgamma")
+        assert_reduction_close(got_b.cpu().numpy(), odb, "in place dbeta")
 
 
 def test_ln_edge_cases():

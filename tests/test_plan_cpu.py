@@ -131,3 +131,30 @@ def test_block_layernorm_backward_plans(planner, cus):
         assert grid * rpb >= T > (grid - 1) * rpb  # every block has rows, none past the last
     (_, _, rpb, grid), = planner([f"lnb 16640 8200 2 2 256"])
     assert (rpb, grid) == (65, 256)  # more rows per block than one flush of the column sums
+
+
+@pytest.mark.parametrize("cus", CUS)
+@pytest.mark.parametrize("bpc", [1, 2, 3])
+def test_team_layernorm_backward_plans(planner, cus, bpc):
+    """Rows of 2049-8192 vectors split over a team: members of at most 1024
+    vectors whose slices cover the row (each at least one vector); the whole
+    grid resident at once (at most 2 blocks per CU counted); teams own
+    contiguous row ranges that cover the rows once."""
+    queries, keys = [], []
+    for dt, rdt in ((2, 2), (2, 0), (0, 0), (1, 1)):
+        for H in (8192, 16392, 20480, 32768, 65536):
+            for T in (1, 3, 300, 4096, 1 << 22):
+                queries.append(f"lnt {T} {H} {dt} {rdt} {cus} {bpc}")
+                keys.append((T, H, dt, rdt))
+    for (T, H, dt, rdt), (applies, nvec, members, slice_, teams, rpt, grid) in zip(keys, planner(queries)):
+        E = 4 if (dt == 0 or rdt == 0) else 8
+        assert nvec == H // E and applies == (2048 < nvec <= 8192)
+        if not applies:
+            continue
+        assert members == -(-nvec // 1024) and 1 <= slice_ <= 1024
+        assert members * slice_ >= nvec > (members - 1) * slice_
+        assert grid == teams * members <= max(members, cus * min(bpc, 2))
+        assert 1 <= teams <= T and teams * rpt >= T > (teams - 1) * rpt
+    # 65536 bf16 on the whole device, two blocks per CU: 64 teams of 8 members of 1024 vectors
+    (_, _, members, slice_, teams, rpt, grid), = planner(["lnt 2048 65536 2 2 256 2"])
+    assert (members, slice_, teams, rpt, grid) == (8, 1024, 64, 32, 512)

@@ -193,6 +193,14 @@ def test_wide_layer_norm_plans_stay_in_bounds(planner, qs):
         assert 1 <= rows_grid <= max(1, min(T, 1 << 20))
         assert strips * 64 >= nvec and 1 <= G <= 65535 and G <= max(1, -(-T // 4))
         assert 1 <= grid <= max(1, min(T, cus)) and grid * rpb >= T and (T == 0 or (grid - 1) * rpb < T)
+    team = planner([f"lnt {max(T, 1)} {H} {d} {r} {cus} 2" for T, H, (d, r), cus in qs])
+    for (T, H, (d, r), cus), (tapplies, nvec, members, slice_, teams, rpt, grid) in zip(qs, team):
+        assert tapplies == (2048 < nvec <= 8192)
+        if tapplies:
+            assert members * slice_ >= nvec > (members - 1) * slice_ and slice_ <= 1024
+            assert grid == teams * members <= max(members, 2 * cus)
+            T1 = max(T, 1)
+            assert teams * rpt >= T1 > (teams - 1) * rpt
 
 
 # ---------------------------------------------------------------- comparator

@@ -25,6 +25,7 @@ __all__ = [
     "mb_bias_glu_bwd_workspace",
     "mb_add_layer_norm_fwd", "mb_add_layer_norm_bwd", "mb_add_layer_norm_bwd_workspace",
     "mb_weighted_squared_relu_fwd", "mb_weighted_squared_relu_bwd", "mb_weighted_squared_relu_bwd_workspace",
+    "mb_set_layer_norm_team_wait",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmb.so")
@@ -79,6 +80,7 @@ def lib() -> ctypes.CDLL:
                 "mb_weighted_squared_relu_bwd_workspace": ([I64, I64, I, I], SZ),
                 "mb_weighted_squared_relu_bwd": ([P, P, P, I, P, P, P, SZ, I64, I64, I, P], I),
                 "mb_add_layer_norm_bwd": ([P, P, P, P, P, I, P, I, P, P, P, P, P, SZ, I64, I64, I, P], I),
+                "mb_set_layer_norm_team_wait": ([I], None),
             }
             for name, (args, res) in sig.items():
                 f = getattr(L, name)
@@ -461,6 +463,13 @@ def mb_add_layer_norm_bwd_workspace(tokens, hidden, dtype, residual_dtype=None, 
     rdt = residual_dtype or dtype
     return int(lib().mb_add_layer_norm_bwd_workspace(tokens, hidden, DTYPES[dtype], DTYPES[rdt],
                                                      int(bool(with_param_grads))))
+
+
+def mb_set_layer_norm_team_wait(polls: int) -> None:
+    """Test-only: polls a block of the team-split LayerNorm backward makes for
+    a partner's row sums before computing them itself (negative: the
+    default). Outputs do not depend on it."""
+    lib().mb_set_layer_norm_team_wait(int(polls))
 
 
 def mb_add_layer_norm_bwd(dy, h, gamma, mean, rstd, zero_centered_gamma=False, dh_in=None, residual_dtype=None,

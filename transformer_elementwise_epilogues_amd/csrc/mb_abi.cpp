@@ -671,18 +671,29 @@ mb_status_t mb_add_layer_norm_fwd(const void* x, const void* residual, mb_dtype_
 // chunk sums of each when there are more than 32 partial rows (256-byte
 // aligned pieces).
 struct LnWs {
-  bool wide = false, block = false;
+  bool wide = false, block = false, team = false;
+  mb::LnTeamPlan tp;
   int partial_rows = 0;
   size_t rows = 0, pg = 0, pb = 0, tg = 0, tb = 0, total = 0;
 };
+// team_ok: the team backward may be used (no output overwrites an input:
+// its fix-up pass rereads whole rows of dy, h and dh_in)
 static LnWs ln_ws_layout(int64_t T, int64_t H, mb_dtype_t dt, mb_dtype_t rdt, const mb::LnPlan& p, int cus,
-                         bool params) {
+                         bool params, bool team_ok) {
   LnWs w;
-  w.wide = mb::ln2_applies(H, dt, rdt);
+  w.team = team_ok && mb::ln_team_applies(H, dt, rdt);
+  w.wide = mb::ln2_applies(H, dt, rdt) && !w.team;
   w.block = mb::ln_block_applies(H, dt, rdt);
-  w.partial_rows = w.wide ? mb::plan_ln2(T, H, dt, rdt, cus).G
-                          : w.block ? mb::plan_ln_block(T, H, dt, rdt, cus).grid : p.partial_rows;
-  const size_t rows = w.wide ? round_up(static_cast<size_t>(T) * 8, 256) : 0;
+  if (w.team) w.tp = mb::plan_ln_team(T, H, dt, rdt, cus, mb::ln_team_blocks_per_cu(dt, rdt));
+  w.partial_rows = w.wide    ? mb::plan_ln2(T, H, dt, rdt, cus).G
+                   : w.block ? mb::plan_ln_block(T, H, dt, rdt, cus).grid
+                   : w.team  ? w.tp.teams
+                             : p.partial_rows;
+  // the wide rows' two row sums, or the team rows' exchange slots (one pair
+  // of floats per row and member) and a flag per row
+  const size_t rows = w.wide   ? round_up(static_cast<size_t>(T) * 8, 256)
+                      : w.team ? round_up(static_cast<size_t>(T) * (w.tp.members * 8 + 4), 256)
+                               : 0;
   const size_t part = params ? round_up(static_cast<size_t>(w.partial_rows) * H * 4, 256) : 0;
   const size_t tmp =
       params ? round_up(static_cast<size_t>(mb::colsum_tall_tmp_floats(w.partial_rows, H)) * 4, 256) : 0;
@@ -701,7 +712,9 @@ size_t mb_add_layer_norm_bwd_workspace(int64_t tokens, int64_t hidden, mb_dtype_
   mb::LnPlan plan;
   const int cus = current_cus();
   if (ln_shape(tokens, hidden, dt, residual_dt, cus, &plan) != MB_OK) return 0;
-  return ln_ws_layout(tokens, hidden, dt, residual_dt, plan, cus, with_param_grads != 0).total;
+  // enough for either backward of the widest rows (in place or not)
+  return std::max(ln_ws_layout(tokens, hidden, dt, residual_dt, plan, cus, with_param_grads != 0, true).total,
+                  ln_ws_layout(tokens, hidden, dt, residual_dt, plan, cus, with_param_grads != 0, false).total);
 }
 
 mb_status_t mb_add_layer_norm_bwd(const void* dy, const void* h, const void* gamma, const float* mean,
@@ -723,7 +736,8 @@ mb_status_t mb_add_layer_norm_bwd(const void* dy, const void* h, const void* gam
       !aligned(dbeta, 16) || !aligned(ws, 16))
     return MB_ERR_ALIGN;
   const bool params = dgamma || dbeta;
-  const LnWs lay = ln_ws_layout(tokens, hidden, dt, residual_dt, plan, cus, params);
+  const bool in_place = dx == dy || dx == h || (dresidual && (dresidual == dy || dresidual == h || dresidual == dh_in));
+  const LnWs lay = ln_ws_layout(tokens, hidden, dt, residual_dt, plan, cus, params, !in_place);
   const size_t need_ws = tokens > 0 ? lay.total : 0;
   if (need_ws && (!ws || ws_bytes < need_ws)) return MB_ERR_WORKSPACE;
   const size_t pb4 = static_cast<size_t>(hidden) * 4;
@@ -765,6 +779,9 @@ mb_status_t mb_add_layer_norm_bwd(const void* dy, const void* h, const void* gam
   } else if (lay.block) {
     if (hipError_t e = mb::launch_ln_block_bwd(a, mb::plan_ln_block(tokens, hidden, dt, residual_dt, cus), s))
       return hip_status(e);
+  } else if (lay.team) {
+    a.rowsums = reinterpret_cast<float*>(w + lay.rows);
+    if (hipError_t e = mb::launch_ln_team_bwd(a, lay.tp, s)) return hip_status(e);
   } else {
     if (hipError_t e = mb::launch_ln_bwd(a, plan, s)) return hip_status(e);
   }
@@ -781,5 +798,7 @@ mb_status_t mb_add_layer_norm_bwd(const void* dy, const void* h, const void* gam
   }
   return finish();
 }
+
+void mb_set_layer_norm_team_wait(int polls) { mb::set_ln_team_spin_limit(polls); }
 
 }  // extern "C"

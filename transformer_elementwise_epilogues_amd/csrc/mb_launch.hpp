@@ -114,5 +114,16 @@ hipError_t launch_ln2_bwd(const LnArgs& a, const Ln2Plan& p, hipStream_t s);
 // backward of rows of 1025-2048 vectors (plan_ln_block): a.pg / a.pb
 // ([p.grid, H]) for the parameter gradients
 hipError_t launch_ln_block_bwd(const LnArgs& a, const LnBlockPlan& p, hipStream_t s);
+// backward of rows split over teams of blocks (plan_ln_team): a.rowsums holds
+// the exchange slots ([T][p.members] pairs of floats) and then T row flags,
+// both set by the launch itself; a.pg / a.pb ([p.teams, H]) the parameter
+// gradients
+hipError_t launch_ln_team_bwd(const LnArgs& a, const LnTeamPlan& p, hipStream_t s);
+// blocks of the team kernel one compute unit holds (dtype pair dt, rdt); 1
+// when the device cannot be asked
+int ln_team_blocks_per_cu(int dt, int rdt);
+// polls of a team's wait before a block recomputes a partner's terms
+// (negative: the default); later launches use it
+void set_ln_team_spin_limit(int polls);
 
 }  // namespace mb

@@ -29,6 +29,7 @@
 // those sums beside a register-resident row: their backward is two kernels,
 // a row-sum kernel and a column-strip kernel (see "wide rows" below).
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "mb_device.hpp"
@@ -814,6 +815,365 @@ __global__ __launch_bounds__(TPR) void ln_bwd_block_kernel(LnArgs a, int64_t row
   if (dgb && (nrows > 0 || first_flush)) flush();
 }
 
+// ---------------------------------------------------------------- team rows
+// The backward of rows too wide for one block's registers (2049-8192
+// vectors): a row is split over a team of `members` blocks, member m holding
+// the `slice` vectors from m slice on of every row the team walks (its part
+// of dy and h in registers, the next row's loaded while this one is reduced,
+// its part of gamma and of the dgamma / dbeta sums kept as in the block
+// kernel above). The two row sums need the whole row: each member publishes
+// its partial pair as one 64-bit atomic store (agent scope) into the row's
+// slot, and wave 0 polls the other members' slots with atomic loads; every
+// member then adds the pairs in member order, so all get the same sums. A
+// fill kernel sets the slots to kTeamEmpty (and the row flags to 0) before
+// the launch. The grid is sized to the blocks the device holds at once, so a
+// partner's pair normally arrives within microseconds; the wait is still
+// bounded: after `spin_limit` polls (and for the rest of the launch once
+// that happened) a block flags the row (its dx from the incomplete sums is
+// then rewritten) for ln_team_fixup_kernel, launched after, which recomputes
+// every member's pair
+// of each flagged row from the row's slices, with the same per-thread,
+// per-wave and member-order arithmetic, and writes the row's dx: the result
+// is the same bit for bit whether the pairs arrive or not (when other work
+// holds part of the device, say). Kept out of the row loop, that path costs
+// the loop nothing (inside it, even as a call, it cost 6 %).
+
+// No published pair has this bit pattern: a NaN sum is published as the
+// canonical quiet NaN, whose high word differs.
+constexpr uint64_t kTeamEmpty = ~0ull;
+
+__global__ __launch_bounds__(256) void team_fill_kernel(uint64_t* slots, int64_t nslots, uint32_t* flags,
+                                                        int64_t rows) {
+  const int64_t step = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < nslots; i += step)
+    slots[i] = kTeamEmpty;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < rows; i += step) flags[i] = 0;
+}
+
+__device__ __forceinline__ uint32_t canonical_bits(float v) { return v != v ? 0x7FC00000u : __float_as_uint(v); }
+
+// A thread's terms of the two row sums over its vectors of a slice (k < nk,
+// the vectors that exist): sum a and sum a xhat with a = dy gamma', xhat =
+// (h - mean) rstd; with SUMS also its dgamma / dbeta terms (dy xhat, dy). No
+// contraction, so that both kernels round them alike.
+template <DT D, int E, int NV, bool SUMS>
+__device__ __forceinline__ void team_terms(const typename Pk<D, E>::T* gy, const typename Pk<D, E>::T* hp,
+                                           const typename Pk<D, E>::T* gp, int nk, float mu, float rs,
+                                           float gshift, float& sa, float& sax, float (*sg)[E], float (*sb)[E]) {
+#pragma clang fp contract(off)
+  sa = 0.0f;
+  sax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    if (k >= nk) break;
+    float gv[E], hv[E], g[E];
+    pk_unpack<D, E>(gy[k], gv);
+    pk_unpack<D, E>(hp[k], hv);
+    pk_unpack<D, E>(gp[k], g);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float xv = (hv[e] - mu) * rs;
+      const float av = gv[e] * (g[e] + gshift);
+      sa = sa + av;
+      sax = __builtin_fmaf(av, xv, sax);
+      if constexpr (SUMS) {
+        sg[k][e] = __builtin_fmaf(gv[e], xv, sg[k][e]);
+        sb[k][e] = sb[k][e] + gv[e];
+      }
+    }
+  }
+}
+
+// dh of one vector from the row's means ma = mean_j a, mx = mean_j a xhat
+// (into gv), every fused step written out (both kernels round it alike).
+template <int E>
+__device__ __forceinline__ void team_dh(float* gv, const float* hv, const float* g, const float* uv, float mu,
+                                        float rs, float gshift, float ma, float mx) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const float xv = (hv[e] - mu) * rs;
+    const float t = __builtin_fmaf(gv[e], g[e] + gshift, -ma);
+    gv[e] = __builtin_fmaf(rs, __builtin_fmaf(-xv, mx, t), uv[e]);
+  }
+}
+
+// The block's sum of per-wave values in wave order, in every thread (two
+// barriers; `buf` holds W pairs).
+template <int W>
+__device__ __forceinline__ void team_block_pair(float& a, float& b, float (*buf)[2]) {
+  const int wr = threadIdx.x / 64, lane = threadIdx.x & 63;
+  a = wave_sum_uniform(a);
+  b = wave_sum_uniform(b);
+  if (lane == 0) {
+    buf[wr][0] = a;
+    buf[wr][1] = b;
+  }
+  __syncthreads();
+  a = buf[0][0];
+  b = buf[0][1];
+#pragma unroll
+  for (int w = 1; w < W; ++w) {
+    a += buf[w][0];
+    b += buf[w][1];
+  }
+  __syncthreads();
+}
+
+template <DT D, DT R, int TPR, int NV>
+__global__ __launch_bounds__(TPR, 2) void ln_bwd_team_kernel(LnArgs a, int members, int slice,
+                                                              int64_t rows_per_team, int spin_limit,
+                                                              uint32_t* flags) {
+  constexpr int E = ln_epl<D, R>();
+  constexpr int W = TPR / 64;
+  constexpr int XB = E * Vec<D>::BYTES, RB = E * Vec<R>::BYTES;
+  using PD = typename Pk<D, E>::T;
+  using PR = typename Pk<R, E>::T;
+  __shared__ RowLds<W, 1> lds;
+  __shared__ float pairs[2][kLnTeamMaxMembers][2];  // the members' pairs, by row parity
+  const int lt = threadIdx.x, wr = lt / 64, lane = lt & 63;
+  const int m = static_cast<int>(blockIdx.x) % members, team = static_cast<int>(blockIdx.x) / members;
+  const int nvec = static_cast<int>(a.H / E);
+  const float fh = static_cast<float>(a.H);
+  const int nvm = nvec - m * slice < slice ? nvec - m * slice : slice;  // >= 1
+  const int nk = lt < nvm ? (nvm - lt + TPR - 1) / TPR : 0;           // this thread's vectors in the slice
+  auto in_row = [&](int k) { return k < nk; };
+  const size_t px = static_cast<size_t>(a.H) * Vec<D>::BYTES, pr = static_cast<size_t>(a.H) * Vec<R>::BYTES;
+  const size_t xs = static_cast<size_t>(m) * slice * XB, rsl = static_cast<size_t>(m) * slice * RB;
+  const uint32_t xbytes = static_cast<uint32_t>(nvm) * XB, rbytes = static_cast<uint32_t>(nvm) * RB;
+  const char* dy = static_cast<const char*>(a.dy) + xs;
+  const char* hh = static_cast<const char*>(a.h) + xs;
+  const char* up = a.dh_in ? static_cast<const char*>(a.dh_in) + rsl : nullptr;
+  char* dx = static_cast<char*>(a.dx) + xs;
+  char* dres = a.dres ? static_cast<char*>(a.dres) + rsl : nullptr;
+  uint64_t* slots = reinterpret_cast<uint64_t*>(a.rowsums);
+  PD gp[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+    gp[k] = pk_load_rsrc<D, E>(static_cast<const char*>(a.gamma) + xs, xbytes, lt * XB, k * TPR * XB, false);
+  const bool dgb = a.pg != nullptr;
+  float sg[NV][E], sb[NV][E];
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+#pragma unroll
+    for (int e = 0; e < E; ++e) sg[k][e] = sb[k][e] = 0.0f;
+  float* pgr = dgb ? a.pg + static_cast<size_t>(team) * a.H + static_cast<size_t>(m) * slice * E : nullptr;
+  float* pbr = dgb ? a.pb + static_cast<size_t>(team) * a.H + static_cast<size_t>(m) * slice * E : nullptr;
+  bool first_flush = true;
+  auto flush = [&]() {  // add the sums into the team's partial row (this thread's columns)
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      if (!in_row(k)) continue;
+      uint32_t ci = static_cast<uint32_t>(lt + k * TPR) * E;
+      opaque(ci);
+      const size_t c = ci;
+#pragma unroll
+      for (int q = 0; q < E / 4; ++q) {
+        float tg[4], tb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          tg[e] = first_flush ? sg[k][4 * q + e] : pgr[c + 4 * q + e] + sg[k][4 * q + e];
+          tb[e] = first_flush ? sb[k][4 * q + e] : pbr[c + 4 * q + e] + sb[k][4 * q + e];
+        }
+        store_f32x4(pgr + c + 4 * q, tg);
+        store_f32x4(pbr + c + 4 * q, tb);
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) sg[k][e] = sb[k][e] = 0.0f;
+    }
+    first_flush = false;
+  };
+  const int64_t r0 = static_cast<int64_t>(team) * rows_per_team;
+  const int64_t r1 = r0 + rows_per_team < a.T ? r0 + rows_per_team : a.T;
+  PD gyn[NV], hn[NV];
+  auto fetch = [&](int64_t r) {
+    const char* dyr = dy + static_cast<size_t>(r) * px;
+    const char* hr = hh + static_cast<size_t>(r) * px;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {  // past the slice: zeros, neither stored nor summed
+      gyn[k] = pk_load_rsrc<D, E>(dyr, xbytes, lt * XB, k * TPR * XB, MB_NT_LOAD);
+      hn[k] = pk_load_rsrc<D, E>(hr, xbytes, lt * XB, k * TPR * XB, MB_NT_LOAD);
+    }
+  };
+  bool waiting = true;  // wave 0: false once a wait has run out (the rest of the launch is left to the fix-up)
+  int nrows = 0;
+  if (r0 < r1) fetch(r0);
+  for (int64_t row = r0; row < r1; ++row) {
+    PD gy[NV], hp[NV];
+    PR uu[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      gy[k] = gyn[k];
+      hp[k] = hn[k];
+    }
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+      if (up) uu[k] = pk_load_rsrc<R, E>(up + static_cast<size_t>(row) * pr, rbytes, lt * RB, k * TPR * RB, MB_NT_LOAD);
+    if (row + 1 < r1) fetch(row + 1);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) opaque(gp[k]);
+    const float mu = a.cmean[row], rs = a.crstd[row];
+    float sa, sax;
+    team_terms<D, E, NV, true>(gy, hp, gp, nk, mu, rs, a.gshift, sa, sax, sg, sb);
+    const int par = static_cast<int>(row & 1);
+    // this member's pair: the waves' sums in wave order through LDS
+    sa = wave_sum_uniform(sa);
+    sax = wave_sum_uniform(sax);
+    if (lane == 0) {
+      lds.v[0][2 * par][wr] = sa;
+      lds.v[0][2 * par + 1][wr] = sax;
+    }
+    __syncthreads();
+    if (wr == 0) {
+      float pa = lds.v[0][2 * par][0], pax = lds.v[0][2 * par + 1][0];
+#pragma unroll
+      for (int w = 1; w < W; ++w) {
+        pa += lds.v[0][2 * par][w];
+        pax += lds.v[0][2 * par + 1][w];
+      }
+      uint64_t* rslots = slots + static_cast<size_t>(row) * members;
+      if (lane == 0)
+        __hip_atomic_store(rslots + m, (static_cast<uint64_t>(canonical_bits(pax)) << 32) | canonical_bits(pa),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      uint64_t got = kTeamEmpty;
+      const bool partner = lane < members && lane != m;
+      if (partner && waiting) {
+        got = __hip_atomic_load(rslots + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int spins = 0; got == kTeamEmpty && spins < spin_limit; ++spins) {
+          __builtin_amdgcn_s_sleep(2);
+          got = __hip_atomic_load(rslots + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      const bool miss = __ballot(partner && got == kTeamEmpty) != 0;  // the same in every lane of wave 0
+      if (miss) waiting = false;
+      if (lane < members) {
+        pairs[par][lane][0] = lane == m ? pa : __uint_as_float(static_cast<uint32_t>(got));
+        pairs[par][lane][1] = lane == m ? pax : __uint_as_float(static_cast<uint32_t>(got >> 32));
+      }
+      if (lane == 0 && miss) flags[row] = 1u;  // its dx is rewritten by the fix-up
+    }
+    __syncthreads();
+    {
+      // the team's sums in member order (the same in every member)
+      float ta = 0.0f, tax = 0.0f;
+      for (int j = 0; j < members; ++j) {
+        ta += pairs[par][j][0];
+        tax += pairs[par][j][1];
+      }
+      const float ma = ta / fh, mx = tax / fh;
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        opaque(gy[k]);
+        opaque(hp[k]);
+        opaque(gp[k]);
+      }
+      const size_t xo = static_cast<size_t>(row) * px, ro = static_cast<size_t>(row) * pr;
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        if (!in_row(k)) continue;
+        float gv[E], hv[E], uv[E], g[E];
+        pk_unpack<D, E>(gy[k], gv);
+        pk_unpack<D, E>(hp[k], hv);
+        pk_unpack<D, E>(gp[k], g);
+        if (up) {
+          pk_unpack<R, E>(uu[k], uv);
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) uv[e] = 0.0f;
+        }
+        team_dh<E>(gv, hv, g, uv, mu, rs, a.gshift, ma, mx);
+        const uint32_t v = static_cast<uint32_t>(lt + k * TPR);
+        pk_store<D, E>(dx + xo + v * XB, pk_pack<D, E>(gv));
+        if (dres) pk_store<R, E>(dres + ro + v * RB, pk_pack<R, E>(gv));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (dgb && ++nrows == kFlushRows) {
+      flush();
+      nrows = 0;
+    }
+  }
+  if (dgb && (nrows > 0 || first_flush)) flush();
+}
+
+// dx (and dresidual) of the rows ln_bwd_team_kernel flagged: each member's
+// pair recomputed from its slice exactly as the member computes it (the same
+// thread layout, terms, wave sums and wave order), the pairs added in member
+// order, then dh of every vector of the row. Block b looks after rows
+// [b TPR, (b + 1) TPR): its threads read their flags at once, and a block
+// without a flagged row returns after one barrier.
+template <DT D, DT R, int TPR, int NV>
+__global__ __launch_bounds__(TPR) void ln_team_fixup_kernel(LnArgs a, int members, int slice,
+                                                            const uint32_t* flags) {
+  constexpr int E = ln_epl<D, R>();
+  constexpr int W = TPR / 64;
+  constexpr int XB = E * Vec<D>::BYTES, RB = E * Vec<R>::BYTES;
+  using PD = typename Pk<D, E>::T;
+  using PR = typename Pk<R, E>::T;
+  __shared__ float buf[W][2];
+  __shared__ uint32_t fl[TPR];
+  const int lt = threadIdx.x;
+  const int nvec = static_cast<int>(a.H / E);
+  const float fh = static_cast<float>(a.H);
+  const size_t px = static_cast<size_t>(a.H) * Vec<D>::BYTES, pr = static_cast<size_t>(a.H) * Vec<R>::BYTES;
+  const char* dy0 = static_cast<const char*>(a.dy);
+  const char* h0 = static_cast<const char*>(a.h);
+  const char* gm0 = static_cast<const char*>(a.gamma);
+  const char* up0 = static_cast<const char*>(a.dh_in);
+  char* dx0 = static_cast<char*>(a.dx);
+  char* dres0 = static_cast<char*>(a.dres);
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * TPR;
+  const uint32_t mine = base + lt < a.T ? flags[base + lt] : 0u;
+  fl[lt] = mine;
+  if (__syncthreads_count(mine != 0) == 0) return;  // the same in every thread
+  for (int i = 0; i < TPR && base + i < a.T; ++i) {
+    if (fl[i] == 0) continue;  // the same in every thread
+    const int64_t row = base + i;
+    const float mu = a.cmean[row], rs = a.crstd[row];
+    float ta = 0.0f, tax = 0.0f;
+    for (int j = 0; j < members; ++j) {
+      const int nj = nvec - j * slice < slice ? nvec - j * slice : slice;
+      const int nk = lt < nj ? (nj - lt + TPR - 1) / TPR : 0;
+      const uint32_t jb = static_cast<uint32_t>(nj) * XB;
+      const size_t jo = static_cast<size_t>(j) * slice * XB;
+      PD ty[NV], th[NV], tg[NV];
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        ty[k] = pk_load_rsrc<D, E>(dy0 + static_cast<size_t>(row) * px + jo, jb, lt * XB, k * TPR * XB, false);
+        th[k] = pk_load_rsrc<D, E>(h0 + static_cast<size_t>(row) * px + jo, jb, lt * XB, k * TPR * XB, false);
+        tg[k] = pk_load_rsrc<D, E>(gm0 + jo, jb, lt * XB, k * TPR * XB, false);
+      }
+      float ja, jax;
+      team_terms<D, E, NV, false>(ty, th, tg, nk, mu, rs, a.gshift, ja, jax, nullptr, nullptr);
+      team_block_pair<W>(ja, jax, buf);
+      ta += ja;
+      tax += jax;
+    }
+    const float ma = ta / fh, mx = tax / fh;
+    for (int j = 0; j < members; ++j) {
+      const int nj = nvec - j * slice < slice ? nvec - j * slice : slice;
+      const size_t jo = static_cast<size_t>(j) * slice;
+      for (int v = lt; v < nj; v += TPR) {
+        const size_t xo = static_cast<size_t>(row) * px + (jo + v) * XB;
+        const size_t ro = static_cast<size_t>(row) * pr + (jo + v) * RB;
+        float gv[E], hv[E], uv[E], g[E];
+        pk_unpack<D, E>(pk_load<D, E>(dy0 + xo), gv);
+        pk_unpack<D, E>(pk_load<D, E>(h0 + xo), hv);
+        pk_unpack<D, E>(pk_load_keep<D, E>(gm0 + (jo + v) * XB), g);
+        if (up0) {
+          pk_unpack<R, E>(pk_load<R, E>(up0 + ro), uv);
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) uv[e] = 0.0f;
+        }
+        team_dh<E>(gv, hv, g, uv, mu, rs, a.gshift, ma, mx);
+        pk_store<D, E>(dx0 + xo, pk_pack<D, E>(gv));
+        if (dres0) pk_store<R, E>(dres0 + ro, pk_pack<R, E>(gv));
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- wide rows
 // The backward of rows of 2048 or more vectors, whose parameter-gradient sums
 // do not fit beside a register-resident row, runs as two kernels:
@@ -1118,6 +1478,70 @@ hipError_t launch_ln_block_bwd(const LnArgs& a, const LnBlockPlan& p, hipStream_
   if (d == DT::BF16 && r == DT::F32) return ln_block_run<DT::BF16, DT::F32>(a, p, s);
   if (d == DT::F16 && r == DT::F16) return ln_block_run<DT::F16, DT::F16>(a, p, s);
   if (d == DT::F16 && r == DT::F32) return ln_block_run<DT::F16, DT::F32>(a, p, s);
+  return hipErrorInvalidValue;
+}
+
+namespace {
+
+std::atomic<int> g_team_spin_limit{MB_LN_TEAM_SPIN_LIMIT};
+int team_spin_limit() { return g_team_spin_limit.load(std::memory_order_relaxed); }
+
+constexpr int kTeamTpr = 256, kTeamNv = kLnTeamVec / kTeamTpr;  // 256 threads of 4 vectors
+
+template <DT D, DT R> hipError_t ln_team_run(const LnArgs& a, const LnTeamPlan& p, hipStream_t s) {
+  constexpr int TPR = kTeamTpr, NV = kTeamNv;
+  const int64_t nslots = a.T * p.members;
+  uint64_t* slots = reinterpret_cast<uint64_t*>(a.rowsums);
+  uint32_t* flags = reinterpret_cast<uint32_t*>(slots + nslots);
+  const unsigned fill_grid = static_cast<unsigned>(std::min<int64_t>((nslots + 255) / 256, 4096));
+  hipLaunchKernelGGL(team_fill_kernel, dim3(fill_grid), dim3(256), 0, s, slots, nslots, flags, a.T);
+  if (hipError_t e = hipGetLastError()) return e;
+  hipLaunchKernelGGL((ln_bwd_team_kernel<D, R, TPR, NV>), dim3(p.grid), dim3(TPR), 0, s, a, p.members, p.slice,
+                     p.rows_per_team, team_spin_limit(), flags);
+  if (hipError_t e = hipGetLastError()) return e;
+  const unsigned fix_grid = static_cast<unsigned>((a.T + TPR - 1) / TPR);
+  hipLaunchKernelGGL((ln_team_fixup_kernel<D, R, TPR, NV>), dim3(fix_grid), dim3(TPR), 0, s, a, p.members, p.slice,
+                     static_cast<const uint32_t*>(flags));
+  return hipGetLastError();
+}
+
+template <DT D, DT R> int team_occupancy() {
+  constexpr int TPR = kTeamTpr, NV = kTeamNv;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ln_bwd_team_kernel<D, R, TPR, NV>, TPR, 0) != hipSuccess ||
+      n < 1) {
+    (void)hipGetLastError();
+    return 1;
+  }
+  return std::min(n, kLnTeamMaxBlocksPerCu);
+}
+
+}  // namespace
+
+void set_ln_team_spin_limit(int polls) {
+  g_team_spin_limit.store(polls < 0 ? MB_LN_TEAM_SPIN_LIMIT : polls, std::memory_order_relaxed);
+}
+
+int ln_team_blocks_per_cu(int dt, int rdt) {
+  const DT d = static_cast<DT>(dt), r = static_cast<DT>(rdt);
+  if (d == DT::F32 && r == DT::F32) return team_occupancy<DT::F32, DT::F32>();
+  if (d == DT::BF16 && r == DT::BF16) return team_occupancy<DT::BF16, DT::BF16>();
+  if (d == DT::BF16 && r == DT::F32) return team_occupancy<DT::BF16, DT::F32>();
+  if (d == DT::F16 && r == DT::F16) return team_occupancy<DT::F16, DT::F16>();
+  if (d == DT::F16 && r == DT::F32) return team_occupancy<DT::F16, DT::F32>();
+  return 1;
+}
+
+hipError_t launch_ln_team_bwd(const LnArgs& a, const LnTeamPlan& p, hipStream_t s) {
+  if (p.members < 1 || p.members > kLnTeamMaxMembers || p.slice < 1 || p.slice > kLnTeamVec ||
+      static_cast<int64_t>(p.members) * p.slice < p.nvec || static_cast<int64_t>(p.members - 1) * p.slice >= p.nvec)
+    return hipErrorInvalidValue;  // the slices cover the row, each holds at least one vector
+  const DT d = static_cast<DT>(a.dt), r = static_cast<DT>(a.rdt);
+  if (d == DT::F32 && r == DT::F32) return ln_team_run<DT::F32, DT::F32>(a, p, s);
+  if (d == DT::BF16 && r == DT::BF16) return ln_team_run<DT::BF16, DT::BF16>(a, p, s);
+  if (d == DT::BF16 && r == DT::F32) return ln_team_run<DT::BF16, DT::F32>(a, p, s);
+  if (d == DT::F16 && r == DT::F16) return ln_team_run<DT::F16, DT::F16>(a, p, s);
+  if (d == DT::F16 && r == DT::F32) return ln_team_run<DT::F16, DT::F32>(a, p, s);
   return hipErrorInvalidValue;
 }
 

@@ -70,8 +70,28 @@ bool ln_block_applies(int64_t H, int dt, int rdt) {
   return nvec > MB_LN2_ROW_VEC && nvec <= MB_LN_BLOCK_MAX_VEC;
 }
 
+bool ln_team_applies(int64_t H, int dt, int rdt) {
+  const int64_t nvec = H / ln_elems_per_vector(dt, rdt);
+  return MB_LN_TEAM && nvec > std::max<int64_t>(MB_LN2_ROW_VEC, MB_LN_BLOCK_MAX_VEC) &&
+         nvec <= static_cast<int64_t>(kLnTeamMaxMembers) * kLnTeamVec;
+}
+
 bool ln2_applies(int64_t H, int dt, int rdt) {
   return H / ln_elems_per_vector(dt, rdt) > std::max<int64_t>(MB_LN2_ROW_VEC, MB_LN_BLOCK_MAX_VEC);
+}
+
+LnTeamPlan plan_ln_team(int64_t T, int64_t H, int dt, int rdt, int cus, int blocks_per_cu) {
+  LnTeamPlan p;
+  p.nvec = static_cast<int>(H / ln_elems_per_vector(dt, rdt));
+  p.members = std::max(1, (p.nvec + kLnTeamVec - 1) / kLnTeamVec);
+  p.slice = (p.nvec + p.members - 1) / p.members;  // balanced: the slices differ by at most members - 1
+  const int64_t resident = static_cast<int64_t>(cus > 0 ? cus : kTunedCUs) *
+                           std::max(1, std::min(blocks_per_cu, kLnTeamMaxBlocksPerCu));
+  const int64_t teams = std::max<int64_t>(1, std::min<int64_t>(T, resident / p.members));
+  p.rows_per_team = std::max<int64_t>(1, (T + teams - 1) / teams);
+  p.teams = static_cast<int>(std::max<int64_t>(1, (T + p.rows_per_team - 1) / p.rows_per_team));
+  p.grid = p.teams * p.members;
+  return p;
 }
 
 LnBlockPlan plan_ln_block(int64_t T, int64_t H, int dt, int rdt, int cus) {

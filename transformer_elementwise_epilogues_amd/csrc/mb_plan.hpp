@@ -204,7 +204,9 @@ struct Ln2Plan {
   int strips = 0;     // column strips of 64 vectors
   int G = 0;          // row groups of the column-strip kernel: dgamma / dbeta partial rows
 };
-// rows of H elements take the wide-row backward (H a whole number of vectors)
+// rows of H elements are too wide for the block backward (H a whole number of
+// vectors): they take the team backward where it applies and no output
+// overwrites an input, else the wide-row kernels
 bool ln2_applies(int64_t H, int dt, int rdt);
 
 // ---- backward of rows of more than MB_LN2_ROW_VEC and at most
@@ -222,6 +224,36 @@ struct LnBlockPlan {
 };
 bool ln_block_applies(int64_t H, int dt, int rdt);
 LnBlockPlan plan_ln_block(int64_t T, int64_t H, int dt, int rdt, int cus);
+
+// ---- backward of rows of more than MB_LN_BLOCK_MAX_VEC and at most
+// kLnTeamMaxMembers * kLnTeamVec vectors: a row is split over a team of
+// blocks (up to kLnTeamVec vectors each) that exchange their two partial row
+// sums through the workspace; a team walks a contiguous range of rows (0:
+// off, such rows then take the wide-row kernels, as they do when an output
+// overwrites an input)
+#ifndef MB_LN_TEAM
+#define MB_LN_TEAM 1
+#endif
+constexpr int kLnTeamVec = 1024;       // vectors per member: 256 threads of 4
+constexpr int kLnTeamMaxMembers = 8;   // 8192 vectors, the widest row
+constexpr int kLnTeamMaxBlocksPerCu = 2;
+// polls of a partner's slot before a block computes the partner's row-sum
+// terms itself (a pair normally arrives within a few polls)
+#ifndef MB_LN_TEAM_SPIN_LIMIT
+#define MB_LN_TEAM_SPIN_LIMIT 4096
+#endif
+struct LnTeamPlan {
+  int nvec = 0;
+  int members = 0;             // blocks per row
+  int slice = 0;               // vectors per member (the last one may hold fewer)
+  int teams = 0;               // and partial rows of dgamma / dbeta
+  int64_t rows_per_team = 0;
+  int grid = 0;                // teams * members
+};
+bool ln_team_applies(int64_t H, int dt, int rdt);
+// blocks_per_cu: how many of the kernel's blocks a compute unit holds at once
+// (at most kLnTeamMaxBlocksPerCu): every block of the grid is resident
+LnTeamPlan plan_ln_team(int64_t T, int64_t H, int dt, int rdt, int cus, int blocks_per_cu);
 Ln2Plan plan_ln2(int64_t T, int64_t H, int dt, int rdt, int cus);
 // the plan's row group is `tpr` threads of `nv` vectors
 bool ln_plan_is(const LnPlan& p, int tpr, int nv);
