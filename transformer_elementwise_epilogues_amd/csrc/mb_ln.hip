@@ -1208,7 +1208,10 @@ __global__ __launch_bounds__(TPR, 2) void ln_bwd_team_kernel(LnArgs a, int membe
   const int64_t r1 = r0 + rows_per_team < a.T ? r0 + rows_per_team : a.T;
   // rows staged through LDS as in ln_bwd_block_lds_kernel: the slice's dy and
   // h of row r into stage st, always 2 NV vector-memory operations (a row past
-  // the range reads nothing); its lane reads back only what it loaded
+  // the range reads nothing); its lane reads back only what it loaded. LDS
+  // loads come in 16 bytes: an 8-byte piece (16-bit rows beside an fp32
+  // residual) is loaded with the next piece's 8 bytes (or zeros past the
+  // slice) and the lane keeps the first 8, the same cache lines either way
   auto chunk = [&](int st, int t, int k) {
     return stage_raw + static_cast<size_t>(((st * 2 + t) * NV + k) * W + wr) * 1024;
   };
