@@ -1771,8 +1771,12 @@ template <DT D, DT R> hipError_t ln_team_run(const LnArgs& a, const LnTeamPlan& 
   return hipGetLastError();
 }
 
+// Asked of the runtime once per dtype pair (the workspace query and every
+// launch use it); 1 when no device answers, and then asked again next time.
 template <DT D, DT R> int team_occupancy() {
   constexpr int TPR = kTeamTpr, NV = kTeamNv;
+  static std::atomic<int> cached{0};
+  if (const int c = cached.load(std::memory_order_relaxed)) return c;
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ln_bwd_team_kernel<D, R, TPR, NV>, TPR,
                                                    team_stage_bytes()) != hipSuccess ||
@@ -1780,7 +1784,9 @@ template <DT D, DT R> int team_occupancy() {
     (void)hipGetLastError();
     return 1;
   }
-  return std::min(n, kLnTeamMaxBlocksPerCu);
+  n = std::min(n, kLnTeamMaxBlocksPerCu);
+  cached.store(n, std::memory_order_relaxed);
+  return n;
 }
 
 }  // namespace
