@@ -849,6 +849,8 @@ __device__ __forceinline__ void bare_barrier() {
 // wave's vector-memory counter (the loads retire in issue order; the count
 // of those issued since is a fixed lower bound, every row issuing the same
 // loads) is all the row needs; the row-sum barrier leaves them in flight.
+// The row's mean and rstd reach it through LDS as well and its dh_in a row
+// ahead in registers, so that no load is waited for before it is needed.
 template <DT D, DT R, int TPR, int NV>
 __global__ __launch_bounds__(TPR) void ln_bwd_block_lds_kernel(LnArgs a, int64_t rows_per_block) {
   constexpr int E = ln_epl<D, R>();
@@ -858,7 +860,8 @@ __global__ __launch_bounds__(TPR) void ln_bwd_block_lds_kernel(LnArgs a, int64_t
   using PD = typename Pk<D, E>::T;
   using PR = typename Pk<R, E>::T;
   __shared__ RowLds<W, 1> lds;
-  extern __shared__ __align__(16) unsigned char stage_raw[];  // [2 stages][dy, h][NV][W] chunks of 64 x 16 B
+  // [2 stages][dy, h][NV][W] chunks of 64 x 16 B, then the row statistics
+  extern __shared__ __align__(16) unsigned char stage_raw[];
   const int lt = threadIdx.x, wr = lt / 64, lane = lt & 63;
   const int nvec = static_cast<int>(a.H / E);
   const float fh = static_cast<float>(a.H);
@@ -929,29 +932,58 @@ __global__ __launch_bounds__(TPR) void ln_bwd_block_lds_kernel(LnArgs a, int64_t
                                                lt * XB, k * TPR * XB, 0, 2);
     }
   };
-  const int U = up ? NV : 0;          // dh_in loads per row
+  // mean and rstd come through LDS too: every 64 rows each wave copies the
+  // next 64 rows' statistics into its own ring of two chunks, so that a row
+  // reads them from LDS; as vector loads, the wait for them would also wait
+  // for the dh_in loads issued after them (the ring follows the stages:
+  // [W][2 chunks][mean, rstd][64] floats)
+  float* const ring = reinterpret_cast<float*>(stage_raw + static_cast<size_t>(2 * 2 * NV * W) * 1024);
+  auto stats = [&](int buf, int which) { return ring + ((wr * 2 + buf) * 2 + which) * 64; };
+  auto stats_dma = [&](int64_t c0, int buf) {  // rows c0 .. c0 + 63, clipped at r1
+    const int64_t n = r1 - c0;
+    const bool real = n > 0;
+    const uint32_t nb = real ? static_cast<uint32_t>(n < 64 ? n : 64) * 4u : 0u;
+    const size_t off = real ? static_cast<size_t>(c0) : 0;
+    const __amdgpu_buffer_rsrc_t rm =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.cmean + off), 0, nb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.crstd + off), 0, nb, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (__attribute__((address_space(3))) void*)stats(buf, 0), 4, lane * 4,
+                                             0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (__attribute__((address_space(3))) void*)stats(buf, 1), 4, lane * 4,
+                                             0, 0, 0);
+  };
+  // dh_in, first used after the row sums, is loaded a row ahead into one of
+  // two register sets; always NV loads (an empty buffer past r1 or without
+  // dh_in: zeros, nothing read)
+  PR ua[NV], ub[NV];
+  auto load_up = [&](int64_t r, PR(&u)[NV]) {
+    const bool real = up != nullptr && r < r1;
+    const char* base = real ? up + static_cast<size_t>(r) * pr : up;
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+      u[k] = pk_load_rsrc<R, E>(base, real ? rbytes : 0u, lt * RB, k * TPR * RB, MB_NT_LOAD);
+  };
   int nrows = 0;
-  dma(r0, 0);
-  dma(r0 + 1, 1);
-  for (int64_t row = r0; row < r1; ++row) {
-    const int st = static_cast<int>((row - r0) & 1);
-    // this row's loads were issued two rows ago; the next row's loads and the
-    // previous row's dh_in loads, issued since, may stay outstanding
-    {
-      const int64_t i = row - r0;
-      vm_wait_at_most(i == 0 ? 2 * NV : U + 2 * NV);
-    }
+  // the loads of one row, in issue order: [statistics of the next 64 rows,
+  // every 64th row], the next row's dh_in (NV), the dy and h of the row after
+  // next (2 NV), this row's stores
+  auto do_row = [&](int64_t row, PR(&cur)[NV], PR(&nxt)[NV]) {
+    const int64_t i = row - r0;
+    const int st = static_cast<int>(i & 1);
+    // this row's dy and h were issued two rows ago; the next row's dh_in, dy
+    // and h, issued since, may stay outstanding
+    vm_wait_at_most(i == 0 ? 2 * NV : 3 * NV);
+    if ((i & 63) == 0) stats_dma(row + 64, static_cast<int>(((i >> 6) + 1) & 1));
     PD gy[NV], hp[NV];
-    PR uu[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       gy[k] = *reinterpret_cast<const PD*>(chunk(st, 0, k) + lane * 16);
       hp[k] = *reinterpret_cast<const PD*>(chunk(st, 1, k) + lane * 16);
     }
-    const float mu = a.cmean[row], rs = a.crstd[row];
-#pragma unroll
-    for (int k = 0; k < NV; ++k)
-      if (up) uu[k] = pk_load_rsrc<R, E>(up + static_cast<size_t>(row) * pr, rbytes, lt * RB, k * TPR * RB, MB_NT_LOAD);
+    const int cb = static_cast<int>((i >> 6) & 1), ci = static_cast<int>(i & 63);
+    const float mu = stats(cb, 0)[ci], rs = stats(cb, 1)[ci];
+    load_up(row + 1, nxt);
     lgkm_wait0();  // the stage is read: it may be filled again
     asm volatile("" ::: "memory");
     dma(row + 2, st);
@@ -1003,6 +1035,9 @@ __global__ __launch_bounds__(TPR) void ln_bwd_block_lds_kernel(LnArgs a, int64_t
       opaque(gp[k]);
     }
     const size_t xo = static_cast<size_t>(row) * px, ro = static_cast<size_t>(row) * pr;
+    // this row's dh_in was issued before the next row's dy and h, the next
+    // row's dh_in and the dy and h of the row after
+    vm_wait_at_most(5 * NV);
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       if (!in_row(k)) continue;
@@ -1010,12 +1045,7 @@ __global__ __launch_bounds__(TPR) void ln_bwd_block_lds_kernel(LnArgs a, int64_t
       pk_unpack<D, E>(gy[k], gv);
       pk_unpack<D, E>(hp[k], hv);
       pk_unpack<D, E>(gp[k], g);
-      if (up) {
-        pk_unpack<R, E>(uu[k], uv);
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) uv[e] = 0.0f;
-      }
+      pk_unpack<R, E>(cur[k], uv);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const float xv = (hv[e] - mu) * rs;
@@ -1030,8 +1060,24 @@ __global__ __launch_bounds__(TPR) void ln_bwd_block_lds_kernel(LnArgs a, int64_t
       flush();
       nrows = 0;
     }
+  };
+  stats_dma(r0, 0);
+  load_up(r0, ua);
+  asm volatile("" ::: "memory");
+  dma(r0, 0);
+  dma(r0 + 1, 1);
+  // two rows per trip, so that the two dh_in register sets alternate
+  // without copies (the odd last row after the loop: inside it, the path
+  // that skips the second row would leave a load in flight at the back edge)
+  const int n = static_cast<int>(r1 - r0);
+  int i = 0;
+  for (; i + 1 < n; i += 2) {
+    do_row(r0 + i, ua, ub);
+    do_row(r0 + i + 1, ub, ua);
   }
+  if (i < n) do_row(r0 + i, ua, ub);
   if (dgb && (nrows > 0 || first_flush)) flush();
+  vm_wait_at_most(0);  // no LDS write of the (empty) loads past the range still in flight at exit
 }
 
 // ---------------------------------------------------------------- team rows
@@ -1726,7 +1772,9 @@ hipError_t launch_ln_bwd(const LnArgs& a, const LnPlan& p, hipStream_t s) { retu
 template <DT D, DT R> hipError_t ln_block_run(const LnArgs& a, const LnBlockPlan& p, hipStream_t s) {
   constexpr int TPR = MB_LN_BLOCK_TPR, NV = 2048 / TPR;
   if constexpr (MB_LN_BLOCK_LDS && ln_epl<D, R>() * Vec<D>::BYTES == 16) {
-    const size_t shm = static_cast<size_t>(2 * 2 * NV * TPR) * 16;  // two stages of dy and h
+    // two stages of dy and h, and two chunks of 64 rows' mean and rstd per wave
+    const size_t shm = static_cast<size_t>(2 * 2 * NV * TPR) * 16 + static_cast<size_t>(TPR / 64) * 2 * 2 * 64 * 4;
+    static_assert(2 * 2 * NV * TPR * 16 + (TPR / 64) * 2 * 2 * 64 * 4 <= 160 * 1024, "fits a CU's LDS");
     hipLaunchKernelGGL((ln_bwd_block_lds_kernel<D, R, TPR, NV>), dim3(p.grid), dim3(TPR), shm, s, a,
                        p.rows_per_block);
   } else {
