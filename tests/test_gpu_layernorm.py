@@ -178,7 +178,9 @@ def test_ln_block_backward_flushes_column_sums():
     """Rows of 1025 vectors (8200 bf16: the last of a thread's four vectors
     exists for one thread only) over 16640 rows: on 256 compute units each
     resident block walks 65 rows, so it stores its dgamma / dbeta sums into
-    its partial row after 64 rows and adds the last row's to them. Every
+    its partial row after 64 rows and adds the last row's to them; the 65th
+    row also reads its mean and rstd from the second chunk of the wave's
+    statistics ring and runs as the odd row after the two-row loop. Every
     element of dx and dresidual, and both column sums, against the oracle
     (evaluated over row chunks, its column sums added in fp64); the result
     reproduces bit for bit."""
