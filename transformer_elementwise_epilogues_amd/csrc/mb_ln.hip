@@ -1084,19 +1084,18 @@ __global__ __launch_bounds__(TPR) void ln_bwd_block_lds_kernel(LnArgs a, int64_t
 // The backward of rows too wide for one block's registers (2049-8192
 // vectors): a row is split over a team of `members` blocks, member m holding
 // the `slice` vectors from m slice on of every row the team walks (its part
-// of dy and h in registers, the next row's loaded while this one is reduced,
-// its part of gamma and of the dgamma / dbeta sums kept as in the block
-// kernel above). The two row sums need the whole row: each member publishes
-// its partial pair as one 64-bit atomic store (agent scope) into the row's
-// slot, and wave 0 polls the other members' slots with atomic loads; every
-// member then adds the pairs in member order, so all get the same sums. A
-// fill kernel sets the slots to kTeamEmpty (and the row flags to 0) before
-// the launch. The grid is sized to the blocks the device holds at once, so a
-// partner's pair normally arrives within microseconds; the wait is still
-// bounded: after `spin_limit` polls (and for the rest of the launch once
-// that happened) a block flags the row (its dx from the incomplete sums is
-// then rewritten) for ln_team_fixup_kernel, launched after, which recomputes
-// every member's pair
+// of dy and h staged through LDS two rows ahead as in the block kernel above,
+// its part of gamma and of the dgamma / dbeta sums in registers). The two row
+// sums need the whole row: each member publishes its partial pair as one
+// 64-bit atomic store (agent scope) into the row's slot, and wave 0 polls the
+// other members' slots with atomic loads; every member then adds the pairs in
+// member order, so all get the same sums. A fill kernel sets the slots to
+// kTeamEmpty (and the row flags to 0) before the launch. The grid is sized to
+// the blocks the device holds at once, so a partner's pair normally arrives
+// within microseconds; the wait is still bounded: after `spin_limit` polls
+// (and for the rest of the launch once that happened) a block flags the row
+// (its dx from the incomplete sums is then rewritten) for
+// ln_team_fixup_kernel, launched after, which recomputes every member's pair
 // of each flagged row from the row's slices, with the same per-thread,
 // per-wave and member-order arithmetic, and writes the row's dx: the result
 // is the same bit for bit whether the pairs arrive or not (when other work
