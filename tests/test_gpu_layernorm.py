@@ -246,6 +246,46 @@ def test_ln_team_backward_same_whether_partners_sums_arrive(dt, rdt, T, H):
     assert_reduction_close(dbet.cpu().numpy(), odb, "dbeta")
 
 
+def test_ln_team_backward_beside_another_stream():
+    """The team backward, its grid sized to the blocks the device holds at
+    once, launched while a long streaming kernel on a second stream holds part
+    of the device (either launch order): a block whose partners are not yet
+    resident waits, within its bound, or leaves the row to the fix-up pass, and
+    dx, dresidual, dgamma and dbeta come out bit for bit those of the call run
+    alone."""
+    dt = rdt = "bf16"
+    T, H = 2048, 32768  # 4096 vectors: teams of 4
+    say(f"team bwd beside a second stream {dt}/{rdt} {T}x{H}")
+    x, r, g, b = inputs(dt, rdt, T, H, 95)
+    gd = g.to(DEV)
+    _, h, mean, rstd = mb.mb_add_layer_norm_fwd(x.to(DEV), r.to(DEV), gd, b.to(DEV))
+    dy = synthetic.draw(96, (T, H), "normal", 1.0, dt).to(DEV)
+    up = synthetic.draw(97, (T, H), "normal", 1.0, rdt).to(DEV)
+    ref = mb.mb_add_layer_norm_bwd(dy, h, gd, mean, rstd, dh_in=up, dresidual=True)
+    # a GeLU forward over 1 GiB in and out (a few hundred microseconds) on the other stream
+    big = torch.full((16384, 32768), 0.5, dtype=torch.bfloat16, device=DEV)  # its values do not matter
+    big_out = torch.empty_like(big)
+    # outputs and workspace allocated up front, on the default stream
+    outs = [tuple(torch.empty_like(t) for t in ref) for _ in range(4)]
+    ws = torch.empty(mb.mb_add_layer_norm_bwd_workspace(T, H, h.dtype, up.dtype, True), dtype=torch.uint8,
+                     device=DEV)
+    torch.cuda.synchronize()
+    s_ln, s_other = torch.cuda.Stream(), torch.cuda.Stream()
+    for i, (dx, dres, dg, db) in enumerate(outs):
+        ln = lambda: mb.mb_add_layer_norm_bwd(dy, h, gd, mean, rstd, dh_in=up, dx=dx, dresidual=dres, dgamma=dg,
+                                              dbeta=db, ws=ws, stream=s_ln)
+        other = lambda: mb.mb_bias_gelu_fwd(big, None, out=big_out, stream=s_other)
+        if i % 2 == 0:
+            other()
+            ln()
+        else:
+            ln()
+            other()
+        torch.cuda.synchronize()
+        for a, c in zip(ref, (dx, dres, dg, db)):
+            assert torch.equal(a.view(torch.uint8), c.view(torch.uint8)), f"launch {i}"
+
+
 @pytest.mark.parametrize("dt,rdt,T,H", [("bf16", "bf16", 520, 65536), ("f32", "f32", 300, 32768),
                                          ("bf16", "f32", 261, 32768)])
 def test_ln_fwd_widest_rows_walk(dt, rdt, T, H):
