@@ -1412,7 +1412,6 @@ __global__ __launch_bounds__(TPR) void ln_team_fixup_kernel(LnArgs a, int member
   constexpr int W = TPR / 64;
   constexpr int XB = E * Vec<D>::BYTES, RB = E * Vec<R>::BYTES;
   using PD = typename Pk<D, E>::T;
-  using PR = typename Pk<R, E>::T;
   __shared__ float buf[W][2];
   __shared__ uint32_t fl[TPR];
   const int lt = threadIdx.x;
