@@ -17,8 +17,8 @@ size_t esize(mb_dtype_t dt) {
     case MB_F32: return 4;
     case MB_F16: return 2;
     case MB_BF16: return 2;
+    default: return 0;  // any other value a caller passes through the C ABI
   }
-  return 0;
 }
 
 bool dt_ok(mb_dtype_t dt) { return esize(dt) != 0; }
