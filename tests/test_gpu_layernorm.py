@@ -99,6 +99,45 @@ def test_ln_fwd_bwd(dt, rdt, T, H):
         f"dbeta {assert_reduction_close(dbet.cpu().numpy(), odb, 'dbeta')}")
 
 
+# The hidden sizes the page lists for the persistent LayerNorm kernel [fusions
+# §5.3]: every one runs here, bf16 with an fp32 residual (its 8-byte pieces)
+# and with a bf16 one, zero-centred gamma on alternate sizes.
+PAGE_HIDDEN = [1024, 1536, 2048, 2304, 3072, 3840, 4096, 5120, 6144, 8192, 10240, 12288, 12800, 15360, 16384,
+               18432, 20480, 24576, 25600, 30720, 32768, 40960, 49152, 65536]
+
+
+@pytest.mark.parametrize("rdt", ["bf16", "f32"])
+@pytest.mark.parametrize("H", PAGE_HIDDEN)
+def test_ln_page_hidden_sizes(H, rdt):
+    """Forward and backward (with dh_in, dresidual and both parameter
+    gradients) at each listed hidden size over 300 rows (rows of 65536
+    bf16 beside an fp32 residual exceed the supported 32768: skipped),
+    against the oracle: h bit for bit, y, dx and dresidual within the derived
+    bound, dgamma and dbeta to 1e-3 of the fp64 sums."""
+    dt = "bf16"
+    if rdt == "f32" and H > 32768:
+        pytest.skip("rows of 16-bit elements beside an fp32 residual go up to 32768")
+    T = 300
+    zc = PAGE_HIDDEN.index(H) % 2 == 1
+    seed = 700 + PAGE_HIDDEN.index(H)
+    x, r, g, b = inputs(dt, rdt, T, H, seed)
+    if zc:
+        g = (g.float() - 1.0).to(TD[dt])  # zero-centred: the kernel applies gamma + 1
+    out = mb.mb_add_layer_norm_fwd(x.to(DEV), r.to(DEV), g.to(DEV), b.to(DEV), eps=1e-5, zero_centered_gamma=zc)
+    s1, oh = check_fwd(dt, rdt, x, r, g, b, 1e-5, zc, out, f"page fwd {dt}/{rdt} {T}x{H}")
+    y, h, mean, rstd = out
+    dy = synthetic.draw(seed + 4, (T, H), "normal", 1.0, dt).to(DEV)
+    up = synthetic.draw(seed + 5, (T, H), "normal", 0.5, rdt).to(DEV)
+    dx, dres, dgam, dbet = mb.mb_add_layer_norm_bwd(dy, h, g.to(DEV), mean, rstd, zc, dh_in=up, dresidual=True)
+    odx, odx64, omag, odres, odg, odb = oracle.add_layer_norm_bwd(dt, st(dy), oh, st(g), 1e-5, zc,
+                                                                  dh_in=st(up), res_dt=rdt)
+    s2 = assert_close_bounded(st(dx), odx, odx64, K * U * omag, dt, f"page bwd {dt}/{rdt} {T}x{H} dx")
+    assert_close_bounded(st(dres), odres, odx64, K * U * omag, rdt, f"page bwd {dt}/{rdt} {T}x{H} dres")
+    say(f"page {dt}/{rdt} {T}x{H} zc={zc}: fwd {s1} dx {s2}")
+    assert_reduction_close(dgam.cpu().numpy(), odg, "dgamma")
+    assert_reduction_close(dbet.cpu().numpy(), odb, "dbeta")
+
+
 @pytest.mark.parametrize("dt,rdt", PAIRS)
 @pytest.mark.parametrize("zc", [False, True])
 @pytest.mark.parametrize("width", ["row", "block", "wide"])
