@@ -31,6 +31,12 @@
  *           throws across the ABI.
  * Empty:    T == 0 enqueues nothing, except that a requested bias gradient is
  *           written as zeros.
+ * Reductions: bias, weight and LayerNorm parameter gradients are fixed-order
+ *           sums with no atomic accumulation. Their grouping of rows follows
+ *           the shape and the device's compute-unit count, so repeated calls
+ *           on one device give the same bits; devices with another CU count
+ *           (a partitioned one, say) round differently within the stated
+ *           tolerance.
  */
 #ifndef MB_H
 #define MB_H
