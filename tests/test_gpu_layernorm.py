@@ -285,6 +285,41 @@ def test_ln_team_backward_same_whether_partners_sums_arrive(dt, rdt, T, H):
     assert_reduction_close(dbet.cpu().numpy(), odb, "dbeta")
 
 
+def test_ln_block_backward_long_walk_sampled_rows():
+    """Rows of 1025 vectors (8200 bf16) over 130 rows per resident block (on
+    256 compute units; more rows on fewer): each block reads its rows' mean
+    and rstd from a two-chunk ring refilled every 64 rows, so rows 64, 128
+    and 129 of a block read the second chunk, the first chunk refilled, and
+    the second again. The oracle recomputes sampled rows one by one (each row's
+    h, y, dx and dresidual depend on that row alone) from the same seeded
+    inputs; every element of those rows within the derived bound."""
+    dt = rdt = "bf16"
+    H = 8200
+    T = 256 * 130
+    say(f"block bwd long walk {dt}/{rdt} {T}x{H}")
+    gen = torch.Generator(device=DEV).manual_seed(4242)
+    draw = lambda shape, sc: (torch.randn(shape, generator=gen, device=DEV) * sc).to(torch.bfloat16)
+    x, r, dy, up = draw((T, H), 1.0), draw((T, H), 1.0), draw((T, H), 1.0), draw((T, H), 0.5)
+    g = (draw((H,), 0.3).float() + 1.0).to(torch.bfloat16)
+    b = draw((H,), 0.2)
+    y, h, mean, rstd = mb.mb_add_layer_norm_fwd(x, r, g, b)
+    dx, dres, _, _ = mb.mb_add_layer_norm_bwd(dy, h, g, mean, rstd, dh_in=up, dresidual=True)
+    rpb = -(-T // min(T, torch.cuda.get_device_properties(0).multi_processor_count))
+    rows = sorted({blk * rpb + o for blk in (0, 97, 255) for o in (0, 1, 63, 64, 65, 127, 128, 129)
+                   if blk * rpb + o < T})
+    idx = torch.tensor(rows, device=DEV)
+    pick = lambda t: st(t.index_select(0, idx).cpu())
+    oh, oy, oy64, omag, _, _ = oracle.add_layer_norm_fwd(dt, pick(x), pick(r), rdt, st(g.cpu()), st(b.cpu()),
+                                                         1e-5, False)
+    assert np.array_equal(pick(h), oh)
+    assert_close_bounded(pick(y), oy, oy64, K * U * omag, dt, "long walk y")
+    odx, odx64, bmag, odres, _, _ = oracle.add_layer_norm_bwd(dt, pick(dy), oh, st(g.cpu()), 1e-5, False,
+                                                              dh_in=pick(up), res_dt=rdt)
+    s1 = assert_close_bounded(pick(dx), odx, odx64, K * U * bmag, dt, "long walk dx")
+    assert_close_bounded(pick(dres), odres, odx64, K * U * bmag, rdt, "long walk dresidual")
+    say(f"long walk rows {rows[:4]}...: dx {s1}")
+
+
 def test_ln_team_backward_beside_another_stream():
     """The team backward, its grid sized to the blocks the device holds at
     once, launched while a long streaming kernel on a second stream holds part
