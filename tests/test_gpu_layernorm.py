@@ -110,14 +110,20 @@ PAGE_HIDDEN = [1024, 1536, 2048, 2304, 3072, 3840, 4096, 5120, 6144, 8192, 10240
 @pytest.mark.parametrize("H", PAGE_HIDDEN)
 def test_ln_page_hidden_sizes(H, rdt):
     """Forward and backward (with dh_in, dresidual and both parameter
-    gradients) at each listed hidden size over 300 rows (rows of 65536
-    bf16 beside an fp32 residual exceed the supported 32768: skipped),
-    against the oracle: h bit for bit, y, dx and dresidual within the derived
-    bound, dgamma and dbeta to 1e-3 of the fp64 sums."""
+    gradients) at each listed hidden size over 300 rows against the oracle:
+    h bit for bit, y, dx and dresidual within the derived bound, dgamma and
+    dbeta to 1e-3 of the fp64 sums. Rows of 16-bit elements beside an fp32
+    residual go up to 32768: the wider listed sizes must be refused
+    (MB_ERR_SHAPE)."""
     dt = "bf16"
-    if rdt == "f32" and H > 32768:
-        pytest.skip("rows of 16-bit elements beside an fp32 residual go up to 32768")
     T = 300
+    if rdt == "f32" and H > 32768:
+        x = torch.zeros(4, H, dtype=torch.bfloat16, device=DEV)
+        r = torch.zeros(4, H, dtype=torch.float32, device=DEV)
+        gm = torch.ones(H, dtype=torch.bfloat16, device=DEV)
+        with pytest.raises(mb.MBError, match="MB_ERR_SHAPE"):
+            mb.mb_add_layer_norm_fwd(x, r, gm)
+        return
     zc = PAGE_HIDDEN.index(H) % 2 == 1
     seed = 700 + PAGE_HIDDEN.index(H)
     x, r, g, b = inputs(dt, rdt, T, H, seed)
