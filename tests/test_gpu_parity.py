@@ -414,6 +414,26 @@ def test_bda_bwd(dt, rdt, p, offset):
     assert torch.count_nonzero(dx.cpu()[dropped]).item() == 0
 
 
+@pytest.mark.parametrize("dt,rdt", BDA_TYPES)
+@pytest.mark.parametrize("T,H", [(1000, 1576), (3, 8), (140001, 64)])
+def test_bda_bwd_without_dbias(dt, rdt, T, H):
+    """Without the bias gradient the backward takes its own launch shape (many
+    short-lived blocks; at [140001, 64] the waves walk a second sweep of rows):
+    dx and dresidual equal the oracle's and, bit for bit, those of the call
+    that also sums dbias."""
+    g = gen(131, (T, H), dt)
+    p, seed, off = 0.1, 2468, 9
+    gd = g.to(DEV)
+    dx, dres, none = mb.mb_bias_dropout_add_bwd(gd, p, seed, off, residual_dtype=TD[rdt], dbias=False)
+    assert none is None
+    dx2, dres2, _ = mb.mb_bias_dropout_add_bwd(gd, p, seed, off, residual_dtype=TD[rdt])
+    assert np.array_equal(st(dx).view(np.uint8), st(dx2).view(np.uint8))
+    assert np.array_equal(st(dres).view(np.uint8), st(dres2).view(np.uint8))
+    odx, odx64, odres, _ = oracle.bias_dropout_add_bwd(dt, st(g), rdt, p, seed, off)
+    log(f"bda_bwd no dbias {dt}/{rdt} {T}x{H}", assert_close(st(dx), odx, odx64, None, dt, "bda bwd dx, no dbias"))
+    assert np.array_equal(st(dres), odres)
+
+
 def test_bda_bwd_matches_forward_mask_in_place_and_deterministic():
     T, H, p, seed, off = 640, 2048, 0.1, 99, 3
     x = gen(121, (T, H), "bf16").to(DEV)

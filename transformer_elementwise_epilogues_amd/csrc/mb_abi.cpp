@@ -355,17 +355,19 @@ mb_status_t mb_bias_dropout_add_infer(const void* x, const void* bias, const voi
 // Row groups of the dropout-add backward. The lane layout and the launch
 // shape depend on the residual dtype (fp32 beside bf16/fp16 or not), which the
 // workspace query does not take: it returns the larger of the two layouts'
-// partial rows.
-static mb::Tiling bda_bwd_tiling(int64_t tokens, int64_t hidden, mb_dtype_t dt, mb_dtype_t residual_dt, int cus) {
+// partial rows. Without the bias gradient the launch shape is its own.
+static mb::Tiling bda_bwd_tiling(int64_t tokens, int64_t hidden, mb_dtype_t dt, mb_dtype_t residual_dt, bool dbias,
+                                 int cus) {
   const int lanes = static_cast<int>(hidden / mb::bda_elems_per_lane(dt, residual_dt));
   const bool mixed = residual_dt == MB_F32 && dt != MB_F32;
-  return mb::plan_tiling(tokens, lanes, mixed ? MB_BDA_BWD_MIXED_BLOCKS : MB_BDA_BWD_BLOCKS, cus);
+  const int blocks = !dbias ? MB_BDA_BWD_NODBIAS_BLOCKS : mixed ? MB_BDA_BWD_MIXED_BLOCKS : MB_BDA_BWD_BLOCKS;
+  return mb::plan_tiling(tokens, lanes, blocks, cus);
 }
 
 static size_t bda_bwd_ws(int64_t tokens, int64_t hidden, mb_dtype_t dt, int with_dbias, int cus) {
   if (!with_dbias || !dt_ok(dt) || check_shape(tokens, hidden, dt) != MB_OK || tokens == 0) return 0;
-  const size_t same = col_partials_bytes(bda_bwd_tiling(tokens, hidden, dt, dt, cus), hidden);
-  const size_t mixed = col_partials_bytes(bda_bwd_tiling(tokens, hidden, dt, MB_F32, cus), hidden);
+  const size_t same = col_partials_bytes(bda_bwd_tiling(tokens, hidden, dt, dt, true, cus), hidden);
+  const size_t mixed = col_partials_bytes(bda_bwd_tiling(tokens, hidden, dt, MB_F32, true, cus), hidden);
   return same > mixed ? same : mixed;
 }
 
@@ -402,7 +404,7 @@ mb_status_t mb_bias_dropout_add_bwd(const void* g, void* dx, void* dresidual, mb
     if (hipError_t e = mb::launch_fill_zero(dbias, hidden, s)) return hip_status(e);
     return finish();
   }
-  const mb::Tiling t = bda_bwd_tiling(tokens, hidden, dt, residual_dt, cus);
+  const mb::Tiling t = bda_bwd_tiling(tokens, hidden, dt, residual_dt, dbias != nullptr, cus);
   float* partials = dbias ? static_cast<float*>(ws) : nullptr;
   if (hipError_t e = mb::launch_bda_bwd(dt, residual_dt, g, dx, dresidual, partials, hidden, t,
                                         dropout_args(p, seed, offset), s))

@@ -319,14 +319,15 @@ hipError_t bda_bwd_dispatch(const void* g, void* dx, void* dres, float* partials
   auto xp = static_cast<char*>(dx);
   auto rp = static_cast<char*>(dres);
   constexpr int U = (R == DT::F32 && D != DT::F32) ? MB_BDA_BWD_MIXED_UNROLL : MB_BDA_BWD_UNROLL;
+  constexpr int UN = MB_BDA_BWD_NODBIAS_UNROLL;  // rows in flight without the bias gradient
   if (partials && dres)
     hipLaunchKernelGGL((bda_bwd_kernel<D, R, U, true, true>), grid, dim3(kThreads), 0, s, gp, xp, rp, partials, t.T, t.nvec, H, d);
   else if (partials)
     hipLaunchKernelGGL((bda_bwd_kernel<D, R, U, true, false>), grid, dim3(kThreads), 0, s, gp, xp, rp, partials, t.T, t.nvec, H, d);
   else if (dres)
-    hipLaunchKernelGGL((bda_bwd_kernel<D, R, U, false, true>), grid, dim3(kThreads), 0, s, gp, xp, rp, partials, t.T, t.nvec, H, d);
+    hipLaunchKernelGGL((bda_bwd_kernel<D, R, UN, false, true>), grid, dim3(kThreads), 0, s, gp, xp, rp, partials, t.T, t.nvec, H, d);
   else
-    hipLaunchKernelGGL((bda_bwd_kernel<D, R, U, false, false>), grid, dim3(kThreads), 0, s, gp, xp, rp, partials, t.T, t.nvec, H, d);
+    hipLaunchKernelGGL((bda_bwd_kernel<D, R, UN, false, false>), grid, dim3(kThreads), 0, s, gp, xp, rp, partials, t.T, t.nvec, H, d);
   return hipGetLastError();
 }
 

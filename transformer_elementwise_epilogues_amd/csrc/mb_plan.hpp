@@ -98,6 +98,18 @@ struct Tiling {
 #ifndef MB_BDA_BWD_MIXED_UNROLL
 #define MB_BDA_BWD_MIXED_UNROLL 2
 #endif
+// Without the bias gradient nothing is summed over rows, so the backward
+// streams as many short-lived blocks, either residual dtype: 32768 blocks of
+// one row per wave took [16384, 8192] from 93.2 to 86.8 us and the
+// fp32-residual [8192, 4096] from 51.3 to 48.4 us against the persistent
+// grid (MI355X, same process; 16384 or 65536 blocks, or 4096 of two rows,
+// were up to 10 % slower on one of the two)
+#ifndef MB_BDA_BWD_NODBIAS_BLOCKS
+#define MB_BDA_BWD_NODBIAS_BLOCKS 32768
+#endif
+#ifndef MB_BDA_BWD_NODBIAS_UNROLL
+#define MB_BDA_BWD_NODBIAS_UNROLL 1
+#endif
 #ifndef MB_GLU_FWD_BLOCKS
 #define MB_GLU_FWD_BLOCKS 65536
 #endif
