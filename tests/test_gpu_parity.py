@@ -288,6 +288,34 @@ def test_glu_bwd_in_place_optional_outputs_and_deterministic():
     assert torch.equal(db1.view(torch.int32), db4.view(torch.int32))
 
 
+@pytest.mark.parametrize("act", ["swiglu", "wswiglu", "geglu"])
+@pytest.mark.parametrize("dt,T,H", [("bf16", 600, 1576), ("f16", 5, 8), ("f32", 130, 512), ("bf16", 262150, 64)])
+def test_glu_bwd_without_dbias(act, dt, T, H):
+    """Without the bias gradient the gated backward takes its own launch shape
+    (many short-lived blocks; at [262150, 64] the waves walk a second sweep of
+    rows): din equals the oracle's and, bit for bit, that of the call that also
+    sums dbias; the weights gradient (summed per row) is bit for bit the same."""
+    x, _, g, w = _glu_inputs(dt, dt if act == "wswiglu" else None, T, H, 611)
+    xd, gd = x.to(DEV), g.to(DEV)
+    if act == "geglu":
+        din, none_b = mb.mb_bias_geglu_bwd(gd, xd, None, dbias=False)
+        din2, _ = mb.mb_bias_geglu_bwd(gd, xd, None)
+        dw = dw2 = None
+    else:
+        wd = None if w is None else w.to(DEV)
+        din, none_b, dw = mb.mb_bias_swiglu_bwd(gd, xd, None, wd, dbias=False, dweights=wd is not None)
+        din2, _, dw2 = mb.mb_bias_swiglu_bwd(gd, xd, None, wd)
+    assert none_b is None
+    assert np.array_equal(st(din).view(np.uint8), st(din2).view(np.uint8))
+    if dw is not None:
+        assert torch.equal(dw.view(torch.int32), dw2.view(torch.int32))
+    kind = "geglu" if act == "geglu" else "swiglu"
+    d, d64, mag, _, dw64 = oracle.bias_glu_bwd(kind, dt, st(g), st(x), None, None if w is None else st(w), dt)
+    log(f"{act}_bwd no dbias {dt} {T}x{H}", assert_close(st(din), d, d64, mag, dt, f"{act} bwd din, no dbias"))
+    if dw is not None:
+        assert_reduction_close(dw.cpu().numpy(), dw64, f"{act} dweights, no dbias")
+
+
 def test_weighted_with_unit_weights_equals_unweighted():
     T, H = 257, 1536
     x, b, g, _ = _glu_inputs("bf16", None, T, H, 401)

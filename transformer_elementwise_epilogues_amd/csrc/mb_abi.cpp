@@ -135,8 +135,11 @@ mb::DropoutArgs dropout_args(float p, uint64_t seed, uint64_t offset) {
   return d;
 }
 
-mb::Tiling glu_bwd_tiling(int64_t tokens, int64_t hidden, mb_dtype_t dt, int cus) {
-  return mb::plan_tiling(tokens, nvec_of(hidden, dt), MB_GLU_BWD_BLOCKS, cus);
+// Row groups of the gated backward: the bias gradient's per-lane column sums
+// want a persistent grid; without them (the weights gradient is summed per row)
+// the launch shape is its own.
+static mb::Tiling glu_bwd_tiling(int64_t tokens, int64_t hidden, mb_dtype_t dt, bool dbias, int cus) {
+  return mb::plan_tiling(tokens, nvec_of(hidden, dt), dbias ? MB_GLU_BWD_BLOCKS : MB_GLU_BWD_NODBIAS_BLOCKS, cus);
 }
 
 // Partial-row workspace of a column reduction.
@@ -468,7 +471,7 @@ struct GluWs {
 GluWs glu_ws(int64_t tokens, int64_t hidden, mb_dtype_t dt, bool with_dbias, bool with_dw, int cus) {
   GluWs w{0, 0, 0, 0, 0};
   if (tokens == 0) return w;
-  const mb::Tiling t = glu_bwd_tiling(tokens, hidden, dt, cus);
+  const mb::Tiling t = glu_bwd_tiling(tokens, hidden, dt, with_dbias, cus);
   w.bias_bytes = with_dbias ? col_partials_bytes(t, 2 * hidden) : 0;
   w.w_off = round_up(w.bias_bytes, 256);
   w.w_bytes = with_dw ? static_cast<size_t>(t.strips) * tokens * 4 : 0;
@@ -509,7 +512,7 @@ static mb_status_t glu_bwd_common(int act, const void* g, const void* in, const 
     if (hipError_t e = mb::launch_fill_zero(dbias, 2 * hidden, s)) return hip_status(e);
     return finish();
   }
-  const mb::Tiling t = glu_bwd_tiling(tokens, hidden, dt, cus);
+  const mb::Tiling t = glu_bwd_tiling(tokens, hidden, dt, dbias != nullptr, cus);
   float* bp = dbias ? static_cast<float*>(ws) : nullptr;
   float* wp = dweights ? reinterpret_cast<float*>(static_cast<char*>(ws) + w.w_off) : nullptr;
   if (hipError_t e = mb::launch_glu_bwd(act, dt, g, in, bias, weights, weights ? weights_dt : dt, din, bp, wp, hidden,

@@ -122,6 +122,15 @@ struct Tiling {
 #ifndef MB_GLU_BWD_UNROLL
 #define MB_GLU_BWD_UNROLL 1
 #endif
+// Without the bias gradient (bias-free layers) the gated backward streams as
+// many short-lived blocks, like the forward: 65536 blocks took the SwiGLU,
+// weighted SwiGLU (with dweights) and GEGLU backward at [8192, 14336] from
+// 185.0 / 201.7 / 185.1 to 174.3 / 182.0 / 176.6 us and at [16384, 8192] from
+// 203.0 / 223.9 / 201.9 to 200.0 / 201.3 / 197.1 us against 512 blocks
+// (MI355X, same process; 4096 or 16384 blocks were slower than both)
+#ifndef MB_GLU_BWD_NODBIAS_BLOCKS
+#define MB_GLU_BWD_NODBIAS_BLOCKS 65536
+#endif
 
 #ifndef MB_SRELU_FWD_BLOCKS
 #define MB_SRELU_FWD_BLOCKS 65536
