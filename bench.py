@@ -27,9 +27,11 @@ same pieces per lane and non-temporal loads and stores, and does no
 arithmetic; the fastest of a sweep of launch shapes and store forms is the
 ceiling, and `frac_ceiling` = ceiling time / op time.
 
-The ops beyond the step (the exact erf GeLU at the chain's MLP shape,
-residual add + LayerNorm at hidden 8192, 16384 and 65536, and the MoE
-weighted squared ReLU) are timed after the step loop, the same way, and
+The ops beyond the step (the exact erf GeLU at the chain's MLP shape, the
+backward of bias-free layers -- SwiGLU, weighted SwiGLU and the dropout-add
+without a bias gradient --, residual add + LayerNorm at hidden 8192, 16384
+and 65536, and the MoE weighted squared ReLU) are timed after the step loop,
+the same way, and
 reported under "next_rows"; the fp32 bias-GeLU at [512, 4096] is timed cold
 (48 rotating copies) and warm under "c1". Neither is part of `value`.
 
@@ -337,6 +339,20 @@ def build_ops(dev, ncopies):
                 [lambda: mb.mb_bias_gelu_erf_bwd(gg, gy, gb, dgrad=dgr, dbias=dbg, ws=wse)],
                 [rows_mix([gg, gy], [dgr], T, H * 2)], {"dgrad": dgr})]
 
+    # -- beyond the step: the backward of bias-free layers (no bias gradient, so
+    # no partial rows: each takes its own many-block launch shape)
+    T3 = xin.shape[0]
+    H3 = xin.shape[1] // 2
+    extra.append(Op("swiglu_bwd_nobias_bf16_8192x14336", T3 * H3 * 10, ["glu_bwd"],
+                    [lambda: mb.mb_bias_swiglu_bwd(g3, xin, None, din=din3, dbias=False, dweights=False)],
+                    [glu_bwd_mix(g3, xin, din3)], {"din": din3}))
+    extra.append(Op("weighted_swiglu_bwd_nobias_bf16_8192x14336", T3 * H3 * 10 + T3 * 6, ["glu_bwd", "colsum"],
+                    [lambda: mb.mb_bias_swiglu_bwd(g3, xin, None, wt, din=din3, dbias=False, dweights=dw3, ws=ws3)],
+                    [glu_bwd_mix(g3, xin, din3)], {"din": din3, "dweights": dw3}))
+    extra.append(Op("chain_mlp_bda_bwd_nodbias_bf16_16384x8192", Ta * Ha * 4, ["bda_bwd"],
+                    [lambda: mb.mb_bias_dropout_add_bwd(mg, p5, s_mlp, off5, dx=mdx, dresidual=False, dbias=False)],
+                    [rows_mix([mg], [mdx], Ta, Ha * 2)], {"dx": mdx}))
+
     # -- beyond the step: residual add + LayerNorm, bf16, hidden 8192, 16384 and 65536
     for wname in ("add_ln_bf16_16384x8192", "add_ln_bf16_8192x16384", "add_ln_bf16_2048x65536"):
         w = WORKLOADS[wname]
@@ -623,18 +639,20 @@ def oracle_plan(host):
     plan32["chain_mlp_bda_bwd_bf16_16384x8192"] = bda_bwd32(c5, "mlp_g", "bf16", 0.1, 5002)
     plan32["chain_attn_bda_bwd_bf16_16384x8192"] = bda_bwd32(c5, "attn_g", "bf16", 0.1, 5001)
 
-    def glu32(w, act, wt, bwd):
+    def glu32(w, act, wt, bwd, bias=True):
         def f(r0, r1):
             wts = None if wt is None else rows(w, wt, r0, r1)
             if bwd:
                 return {"din": oracle32.bias_glu_bwd(act, "bf16", rows(w, "g", r0, r1), rows(w, "in", r0, r1),
-                                                     vec(w, "bias"), wts)[0]}
+                                                     vec(w, "bias") if bias else None, wts)[0]}
             return {"out": oracle32.bias_glu_fwd(act, "bf16", rows(w, "in", r0, r1), vec(w, "bias"), wts)}
         return f
 
     for name, wt in (("swiglu", None), ("weighted_swiglu", "weights")):
         plan32[f"{name}_fwd_bf16_8192x14336"] = glu32(c3, "swiglu", wt, False)
         plan32[f"{name}_bwd_bf16_8192x14336"] = glu32(c3, "swiglu", wt, True)
+        plan32[f"{name}_bwd_nobias_bf16_8192x14336"] = glu32(c3, "swiglu", wt, True, bias=False)
+    plan32["chain_mlp_bda_bwd_nodbias_bf16_16384x8192"] = bda_bwd32(c5, "mlp_g", "bf16", 0.1, 5002)
     plan32["geglu_fwd_bf16_16384x8192"] = glu32(c4, "geglu", None, False)
     plan32["geglu_bwd_bf16_16384x8192"] = glu32(c4, "geglu", None, True)
 
@@ -665,10 +683,11 @@ def oracle_plan(host):
             return {"out": ("elem", o, o64, None)}
         return f
 
-    def glu_bwd(w, act, wt):
+    def glu_bwd(w, act, wt, bias=True):
         def f(r0, r1):
             d, d64, mag, _, dw = oracle.bias_glu_bwd(act, "bf16", rows(w, "g", r0, r1), rows(w, "in", r0, r1),
-                                                     vec(w, "bias"), None if wt is None else rows(w, wt, r0, r1))
+                                                     vec(w, "bias") if bias else None,
+                                                     None if wt is None else rows(w, wt, r0, r1))
             res = {"din": ("elem", d, d64, mag)}
             if dw is not None:
                 res["dweights"] = ("rowsum", dw)
@@ -678,6 +697,9 @@ def oracle_plan(host):
     for name, wt in (("swiglu", None), ("weighted_swiglu", "weights")):
         plan[f"{name}_fwd_bf16_8192x14336"] = (glu_fwd(c3, "swiglu", wt), lambda n: n * 14336 * 6 + 28672 * 2)
         plan[f"{name}_bwd_bf16_8192x14336"] = (glu_bwd(c3, "swiglu", wt), lambda n: n * 14336 * 10 + 28672 * 6)
+        plan[f"{name}_bwd_nobias_bf16_8192x14336"] = (glu_bwd(c3, "swiglu", wt, bias=False),
+                                                      (lambda n: n * 14336 * 10) if wt is None
+                                                      else (lambda n: n * 14336 * 10 + n * 6))
     plan["geglu_fwd_bf16_16384x8192"] = (glu_fwd(c4, "geglu", None), lambda n: n * 8192 * 6 + 16384 * 2)
     plan["geglu_bwd_bf16_16384x8192"] = (glu_bwd(c4, "geglu", None), lambda n: n * 8192 * 10 + 16384 * 6)
 
@@ -702,6 +724,8 @@ def oracle_plan(host):
     plan["chain_mlp_bda_bwd_bf16_16384x8192"] = (bda_bwd(c5, "mlp_g", "bf16", 0.1, 5002, False),
                                                  lambda n: n * 8192 * 4 + 8192 * 4)
     plan["chain_gelu_bwd_bf16_16384x32768"] = (gelu_bwd(False), lambda n: n * 32768 * 6 + 32768 * 6)
+    plan["chain_mlp_bda_bwd_nodbias_bf16_16384x8192"] = (bda_bwd(c5, "mlp_g", "bf16", 0.1, 5002, False),
+                                                         lambda n: n * 8192 * 4)
     plan["chain_attn_bda_bwd_bf16_16384x8192"] = (bda_bwd(c5, "attn_g", "bf16", 0.1, 5001, False),
                                                   lambda n: n * 8192 * 4 + 8192 * 4)
     plan["erf_gelu_fwd_bf16_16384x32768"] = (gelu_fwd(True), lambda n: n * 32768 * 4 + 32768 * 2)
