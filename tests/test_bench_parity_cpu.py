@@ -32,7 +32,7 @@ def small_host():
 def test_cpu_baseline_and_parity_plumbing():
     host = small_host()
     plan = bench.oracle_plan(host)
-    assert len(plan) == 25
+    assert len(plan) == 28  # 15 step ops and 13 beyond the step
     gpu_rows = {}
     for name, (f, _, T, f32) in plan.items():
         assert T == ROWS
